@@ -1,0 +1,131 @@
+"""Grouped-expert (MoE) SiLU-gated FFN with NVFP4 expert weights (oracle).
+
+The pages give the shape of the problem, not a formula: a 512-expert mixture where each token
+is routed to 10 experts ("NVFP4 vs 2:4 sparse", robertz.co, sections "Concurrency, not
+sparsity, is the lever" and "The sparsity that does pay is already running"), whose expert
+weights are NVFP4 and whose gate/up projections share one global scale ("NVFP4 Without FP4
+Hardware", ai-muninn.com, section "The shared global scale"); the same robertz.co page, section
+"Why it cannot run on this cluster", notes that no 2:4 grouped GEMM exists for such a model.
+The plain reading taken here, for every expert e:
+
+* g = X_e . W_gate,e^T and u = X_e . W_up,e^T, where X_e are the rows of the tokens routed to e
+  and W_up,e = [W_gate,e; W_up,e] is one [2I, D] NVFP4 tensor (one shared tensor scale);
+* H = bf16(silu(g) * u) with silu(g) = g / (1 + exp(-g)) — H is stored in bf16;
+* Yd = H . W_down,e^T with W_down,e an NVFP4 [D, I] tensor;
+* out[t] = sum_j r[t, j] * Yd[row(t, j)] over the token's selected experts, with the router's
+  combine weights r.
+
+Routing bookkeeping: rows are grouped by expert (ascending); inside an expert, rows follow the
+flat (token, slot) order t * k + j. ``expert_offsets[e]`` is the first row of expert e.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import bf16_round, bf16_ulp, bf16_decode
+from .gemm import REL_TOL, gemm_dense, gemm_sp24
+from .quant import dequantize
+from .sp24 import decompress
+
+SILU_SLOPE_MAX = 1.0999  # max |d silu / dg| (attained near g = 2.4)
+
+
+def route(topk_ids: np.ndarray, E: int):
+    """(counts [E], expert_offsets [E+1], row_token [T*k], row_slot [T*k])."""
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    if flat.size and (flat.min() < 0 or flat.max() >= E):
+        raise ValueError("expert id out of range")
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    order = np.argsort(flat, kind="stable")       # by expert, then by flat index
+    return counts, offsets, (order // k).astype(np.int64), (order % k).astype(np.int64)
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def _product(x_bits, wq, rows=None):
+    """wq = ('dense', codes, scales, s_t) or ('sp24', vals, meta, scales, s_t)."""
+    if wq[0] == "dense":
+        return gemm_dense(x_bits, wq[1], wq[2], wq[3], rows=rows)
+    return gemm_sp24(x_bits, wq[1], wq[2], wq[3], wq[4], rows=rows)
+
+
+def up_stage(x_bits: np.ndarray, up_q, I: int):
+    """Gate/up products of one expert on its rows x_bits [r, D].
+
+    Returns dict with g, u (float64 [r, I]), their bound bases Bg, Bu, h = silu(g) * u and
+    H = bf16(h) (float64 holding bf16 values)."""
+    g, Bg = _product(x_bits, up_q, rows=np.arange(0, I))
+    u, Bu = _product(x_bits, up_q, rows=np.arange(I, 2 * I))
+    h = silu(g) * u
+    return dict(g=g, u=u, Bg=Bg, Bu=Bu, h=h, H=bf16_round(h))
+
+
+def h_bound(st: dict) -> np.ndarray:
+    """Allowed |H_gpu - H| when g and u carry the GEMM bound and H_gpu is bf16(silu(g)u) in f32."""
+    dg = REL_TOL * st["Bg"]
+    du = REL_TOL * st["Bu"]
+    sg = np.abs(silu(st["g"]))
+    dh = SILU_SLOPE_MAX * dg * (np.abs(st["u"]) + du) + (sg + SILU_SLOPE_MAX * dg) * du
+    dh = dh + 1e-6 * np.abs(st["h"])                   # float32 evaluation of silu(g) * u
+    return dh + bf16_ulp(np.abs(st["h"]) + dh)          # both sides round to bf16
+
+
+def f64_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that are already bf16 (float64 holding bf16 values)."""
+    f = np.asarray(v, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def down_stage(H: np.ndarray, down_q):
+    """Yd = H . W_down^T for one expert (H float64 holding bf16 values, [r, I]); returns (Yd, B)."""
+    return _product(f64_to_bf16_bits(H), down_q)
+
+
+def moe_ffn(x_bits: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, up_q, down_q, E: int,
+            I: int, tokens=None):
+    """End-to-end MoE output (float64 [T', D]) for ``tokens`` (default all) and its parity bound.
+
+    up_q[e] / down_q[e] give the quantised weights of expert e (see ``_product``); they are
+    only read for experts that the selected tokens use. Returns (out, bound, route tuple).
+    """
+    counts, offsets, row_token, row_slot = route(topk_ids, E)
+    T, k = topk_ids.shape
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    want = np.zeros(T, dtype=bool)
+    want[toks] = True
+    D = bf16_decode(x_bits[:1]).shape[1]
+    out = np.zeros((T, D))
+    tol = np.zeros((T, D))
+    for e in range(E):
+        r0, r1 = offsets[e], offsets[e + 1]
+        rt, rs = row_token[r0:r1], row_slot[r0:r1]
+        sel = want[rt]
+        if not sel.any():
+            continue
+        rt, rs = rt[sel], rs[sel]
+        st = up_stage(x_bits[rt], up_q(e), I)
+        dH = h_bound(st)
+        yd, byd = down_stage(st["H"], down_q(e))
+        # |W_down| weighted sums of |H| and of the H error, via the same product on |.|
+        absw = _abs_product(np.abs(st["H"]), down_q(e))
+        errw = _abs_product(dH, down_q(e))
+        dyd = errw + REL_TOL * (absw + errw)
+        r = topk_w[rt, rs].astype(np.float64)
+        np.add.at(out, rt, r[:, None] * yd)
+        np.add.at(tol, rt, np.abs(r)[:, None] * dyd)
+    tol = tol + 1e-6 * np.abs(out) + 1e-30
+    return out[toks], tol[toks], (counts, offsets, row_token, row_slot)
+
+
+def _abs_product(a: np.ndarray, wq) -> np.ndarray:
+    """sum_i a[:, i] * |w_hat[n, i]| for a >= 0 (float64), any weight form."""
+    if wq[0] == "dense":
+        w = dequantize(wq[1], wq[2], wq[3])
+    else:
+        w = dequantize(decompress(wq[1], wq[2]), wq[3], wq[4])
+    return a @ np.abs(w).T
