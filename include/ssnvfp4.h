@@ -1,0 +1,177 @@
+/*
+ * ssnvfp4.h — NVFP4 weight-quantised GEMM/GEMV with optional 2:4 structured sparsity,
+ * hand-written for AMD Instinct MI355X (gfx950).
+ *
+ * The problem, as stated on the pages this library follows:
+ *  - NVFP4 weights: 4-bit E2M1 values, one FP8 E4M3 scale per 16 consecutive values along the
+ *    reduction axis, one FP32 tensor scale ("NVFP4 Without FP4 Hardware", ai-muninn.com, section
+ *    "Convert BF16 to NVFP4 yourself"); a scale may be shared by a group of tensors (same page,
+ *    section "The shared global scale").
+ *  - 2:4 sparsity along the reduction axis K: every group of four has at least two zeros
+ *    ("Sparse GPU FLOPS Need the Right Zeros in the Right Places", leviathansystems.co, section
+ *    "The operation determines which four entries belong together"), checked per group ("Two
+ *    half-zero vectors produce different pattern answers"); stored as the two kept values plus a
+ *    2-bit position each ("NVFP4 vs 2:4 sparse", robertz.co, section "What 2:4 actually is").
+ *  - Reporting which implementation actually ran (leviathansystems.co page, section "Ask which
+ *    sparse implementations were actually selected"): every GEMM call reports its algorithm.
+ *
+ * Layouts (all row-major, K = reduction axis, contiguous):
+ *   W (input to quantise / prune)  f32 or bf16 [N, K]
+ *   codes   u8 [N, K/2]   element k=2j in the low nibble of byte j, k=2j+1 in the high nibble
+ *   scales  u8 [N, K/16]  E4M3 (OCP "FN": bias 7, 0x7E = 448, no Inf) block scale of K/16 blocks
+ *   tensor_scale  f32 [1] s_t; decoded weight = E2M1(code) * E4M3(scale) * s_t
+ *   vals    u8 [N, K/4]   2:4 kept codes: byte g = code[4g+i0] | code[4g+i1] << 4, i0 < i1
+ *   meta    u8 [N, K/8]   positions: nib(g) = i0 | i1 << 2; byte j = nib(2j) | nib(2j+1) << 4
+ *   X       bf16 bit patterns (uint16) [M, K]
+ *   Y       f32 or bf16 [M, N];  Y = X . W_hat^T with f32 accumulation
+ *
+ * Conventions:
+ *  - Every pointer is caller-owned DEVICE memory unless marked "host". The library never
+ *    allocates or frees memory and keeps no pointer after a call returns. Inputs and outputs
+ *    must stay alive until the stream has passed the call's kernels.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Calls are
+ *    stream-ordered and asynchronous; results are ready when the stream reaches them.
+ *  - Every call validates its arguments on the host before launching anything and returns a
+ *    status code; it never throws and never silently falls back. On a non-OK return nothing
+ *    was launched (except SSN_E_HIP, where a launch itself failed) and ssn_last_error() gives a
+ *    thread-local message.
+ *  - Sizes: N, M >= 0 (a zero size is a no-op that returns SSN_OK); K % 32 == 0 for the
+ *    NVFP4/2:4 calls (so a 32-bit word of meta covers whole groups and rows of every array
+ *    are 2-byte aligned). Device pointers must be 16-byte aligned.
+ *  - Data-dependent failures (a group that is not 2:4) are reported in device counters, not
+ *    in the return code.
+ *  - Calls that write the same output buffers and overlap on one stream or across streams race.
+ */
+#ifndef SSNVFP4_H
+#define SSNVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSN_OK = 0,
+  SSN_E_NULL = 1,   /* a required pointer is NULL */
+  SSN_E_SHAPE = 2,  /* a size is negative, K % 32 != 0, or sizes are inconsistent */
+  SSN_E_ALIGN = 3,  /* a device pointer is not 16-byte aligned */
+  SSN_E_DTYPE = 4,  /* unknown dtype code */
+  SSN_E_ALGO = 5,   /* unknown algorithm, or an explicit algorithm that does not apply to the shape */
+  SSN_E_HIP = 6,    /* a HIP launch or runtime call failed */
+  SSN_E_RANGE = 7   /* an argument is outside its documented range (e.g. top-k, expert count) */
+} ssn_status;
+
+enum { SSN_F32 = 0, SSN_BF16 = 1 };
+
+/* GEMM algorithms. Each call writes the one it ran to *algo_used (host int, nullable). */
+enum {
+  SSN_ALGO_AUTO = 0,             /* let the library choose; the choice is reported */
+  SSN_ALGO_VALU = 1,             /* plain vector-ALU kernel, any K % 32 == 0 (dense: FMA per
+                                    weight; 2:4: skip-and-gather of x at the stored positions) */
+  SSN_ALGO_MFMA = 2,             /* dense: bf16 MFMA on weights decoded in registers/LDS */
+  SSN_ALGO_SMFMAC = 3,           /* 2:4 only: sparse MFMA (v_smfmac) with the compressed weights
+                                    as the sparse operand; needs K % 64 == 0 */
+  SSN_ALGO_DECOMPRESS_MFMA = 5   /* 2:4 only: expand vals+meta to a dense tile and run the
+                                    dense bf16 MFMA (computes on the zeros) */
+};
+
+enum { SSN_EPI_NONE = 0, SSN_EPI_SILU_GATE = 1 };
+
+/* Thread-local message describing the last non-OK return on this thread ("" if none). */
+const char* ssn_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ssn_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * nvfp4_quantize — NVFP4 quantisation of one tensor ("NVFP4 Without FP4 Hardware",
+ * ai-muninn.com, section "Convert BF16 to NVFP4 yourself"; shared scale: section "The shared
+ * global scale").
+ *   s_t = fl32(amax|W| / 2688) unless tensor_scale_in is given (then s_t = *tensor_scale_in);
+ *   per block of 16 along K: S = E4M3 nearest-even of min(amax_block / (6 s_t), 448);
+ *   code = sign(w) | E2M1 nearest-even of |w| / (s_t * S), saturating at 6 (a negative value
+ *   that rounds to zero gives the FP4 negative zero 0x8); a block with S = 0 stores code 0.
+ *   Rounding decisions are exact (taken in float64 on the exact quotients).
+ * W: f32 or bf16 (w_dtype) [N, K]; codes [N, K/2]; scales [N, K/16]; tensor_scale_in: f32 [1]
+ * or NULL; tensor_scale_out: f32 [1], receives s_t (may equal tensor_scale_in).
+ * W must be finite. Errors: NULL, SHAPE (K % 32), ALIGN, DTYPE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int nvfp4_quantize(const void* W, int w_dtype, int64_t N, int64_t K, const float* tensor_scale_in,
+                   uint8_t* codes, uint8_t* scales, float* tensor_scale_out, void* stream);
+
+/* nvfp4_dequantize — decoded weights out[n,k] = E2M1(code) * E4M3(S) * s_t, written as f32 or
+ * bf16 (out_dtype; bf16 is rounded to nearest-even). Same layouts as above. */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     int64_t N, int64_t K, void* out, int out_dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * sp24_prune — magnitude pruning to 2:4 along K: in every group of four keep the two entries
+ * of largest |w| (equal magnitudes: the lower index wins) and write +0.0 to the other two.
+ * This produces weights that pass sp24_check after quantisation. W, W_out: f32 or bf16
+ * [N, K] (same dtype; W_out may equal W for in place). Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int sp24_prune(const void* W, int w_dtype, int64_t N, int64_t K, void* W_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * sp24_check — per-group 2:4 eligibility of NVFP4 codes ("Sparse GPU FLOPS Need the Right Zeros
+ * in the Right Places", leviathansystems.co, sections "The operation determines which four
+ * entries belong together" and "Two half-zero vectors produce different pattern answers").
+ * A code is zero when its magnitude bits are 0 (0x0 and 0x8). A group passes when it holds at
+ * least two zero codes.
+ * codes [N, K/2]; bad_groups: int64 [1] = number of failing groups; first_bad: int64 [1]
+ * (nullable) = smallest flat index n*(K/4)+g of a failing group, or -1 if none.
+ * Errors: NULL, SHAPE, ALIGN, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int sp24_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad_groups, int64_t* first_bad,
+               void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * sp24_compress — 2:4 compression of NVFP4 codes into two kept codes plus two 2-bit positions
+ * per group ("NVFP4 vs 2:4 sparse", robertz.co, section "What 2:4 actually is" and its figure:
+ * w0 0 0 w3 is stored as w0 w3 with positions 0 and 3).
+ * Kept positions: the nonzero codes first, then the lowest-index zero codes, ascending
+ * (i0 < i1); kept codes are copied verbatim. A failing group (fewer than two zeros) is written
+ * as vals 0x00 and positions (0, 1), and counted in *bad_groups.
+ * codes [N, K/2] -> vals [N, K/4], meta [N, K/8]; bad_groups int64 [1].
+ * Errors: NULL, SHAPE, ALIGN, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int sp24_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* vals, uint8_t* meta,
+                  int64_t* bad_groups, void* stream);
+
+/* sp24_decompress — inverse of sp24_compress: writes the kept codes at their positions and
+ * code 0 elsewhere (if i0 == i1 the second kept code wins). vals [N,K/4], meta [N,K/8] ->
+ * codes [N,K/2]. Errors: NULL, SHAPE, ALIGN, HIP. */
+int sp24_decompress(const uint8_t* vals, const uint8_t* meta, int64_t N, int64_t K, uint8_t* codes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * gemm_nvfp4_dense — Y = X . W_hat^T with W_hat[n,k] = E2M1(code) * E4M3(S[n,k/16]) * s_t,
+ * f32 accumulation; weights are decoded in registers ("NVFP4 Without FP4 Hardware",
+ * ai-muninn.com, section "Why NVFP4 helps without FP4 hardware": the 4-bit weights stay 4-bit
+ * in memory and are unpacked inside the kernel).
+ * X bf16 [M, K]; codes [N, K/2]; scales [N, K/16]; tensor_scale f32 [1]; Y [M, N] of y_dtype
+ * (SSN_F32 or SSN_BF16, nearest-even). algo: AUTO, VALU or MFMA. algo_used: host int, nullable.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int gemm_nvfp4_dense(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* codes,
+                     const uint8_t* scales, const float* tensor_scale, void* Y, int y_dtype, int algo,
+                     int* algo_used, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * gemm_nvfp4_sp24 — the same product from the 2:4-compressed weights: only the two kept
+ * values of each group of four contribute, at their stored positions ("NVFP4 vs 2:4 sparse",
+ * robertz.co, section "What 2:4 actually is": the pruned lanes are skipped).
+ * vals [N, K/4], meta [N, K/8] (positions must satisfy i0 < i1, as sp24_compress writes them),
+ * scales [N, K/16] (original K). algo: AUTO, VALU (skip-and-gather), SMFMAC (K % 64 == 0),
+ * DECOMPRESS_MFMA. Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int gemm_nvfp4_sp24(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* vals,
+                    const uint8_t* meta, const uint8_t* scales, const float* tensor_scale, void* Y,
+                    int y_dtype, int algo, int* algo_used, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSNVFP4_H */

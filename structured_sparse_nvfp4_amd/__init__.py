@@ -1,0 +1,217 @@
+"""Python binding of ``libssnvfp4.so`` — NVFP4 / 2:4 weight-quantised GEMM for MI355X (gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels. PyTorch supplies
+device memory and the current stream. The functions have the names of the C entry points
+declared in ``include/ssnvfp4.h``; outputs are allocated here with torch when not given.
+If the shared library is missing, every call raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssnvfp4.so")
+
+SSN_OK, SSN_E_NULL, SSN_E_SHAPE, SSN_E_ALIGN, SSN_E_DTYPE, SSN_E_ALGO, SSN_E_HIP, SSN_E_RANGE = range(8)
+SSN_F32, SSN_BF16 = 0, 1
+ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_DECOMPRESS_MFMA = 0, 1, 2, 3, 5
+ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac",
+              ALGO_DECOMPRESS_MFMA: "decompress_mfma"}
+EPI_NONE, EPI_SILU_GATE = 0, 1
+
+_vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+_SIGS = {
+    "ssn_last_error": ([], ctypes.c_char_p),
+    "ssn_version": ([], _int),
+    "nvfp4_quantize": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
+    "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _vp, _int, _vp], _int),
+    "sp24_prune": ([_vp, _int, _i64, _i64, _vp, _vp], _int),
+    "sp24_check": ([_vp, _i64, _i64, _vp, _vp, _vp], _int),
+    "sp24_compress": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
+    "sp24_decompress": ([_vp, _vp, _i64, _i64, _vp, _vp], _int),
+    "gemm_nvfp4_dense": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp], _int),
+    "gemm_nvfp4_sp24": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp], _int),
+}
+
+_lib = None
+
+
+class SsnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python structured_sparse_nvfp4_amd/build.py` (no CPU fallback exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes, f.restype = args, res
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != SSN_OK:
+        raise SsnError(status, lib().ssn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _wdt(W):
+    if W.dtype == torch.float32:
+        return SSN_F32
+    if W.dtype == torch.bfloat16:
+        return SSN_BF16
+    raise TypeError(f"weights must be float32 or bfloat16, got {W.dtype}")
+
+
+def version() -> int:
+    return lib().ssn_version()
+
+
+def nvfp4_quantize(W, tensor_scale_in=None, codes=None, scales=None, tensor_scale_out=None):
+    """NVFP4-quantise W [N, K] (f32 or bf16). Returns (codes u8 [N,K/2], scales u8 [N,K/16], s_t f32 [1])."""
+    N, K = W.shape
+    _need(W, W.dtype, "W")
+    dev = W.device
+    codes = codes if codes is not None else torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    ts = tensor_scale_out if tensor_scale_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    _need(codes, torch.uint8, "codes", (N, K // 2)); _need(scales, torch.uint8, "scales", (N, K // 16))
+    _need(ts, torch.float32, "tensor_scale_out", (1,))
+    if tensor_scale_in is not None:
+        _need(tensor_scale_in, torch.float32, "tensor_scale_in", (1,))
+    _check(lib().nvfp4_quantize(_ptr(W), _wdt(W), N, K, _ptr(tensor_scale_in), _ptr(codes), _ptr(scales),
+                                _ptr(ts), _stream(dev)))
+    return codes, scales, ts
+
+
+def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, out=None):
+    N, Kh = codes.shape
+    K = 2 * Kh
+    _need(codes, torch.uint8, "codes"); _need(scales, torch.uint8, "scales", (N, K // 16))
+    _need(tensor_scale, torch.float32, "tensor_scale", (1,))
+    out = out if out is not None else torch.empty((N, K), dtype=out_dtype, device=codes.device)
+    dt = SSN_F32 if out.dtype == torch.float32 else SSN_BF16 if out.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("out must be float32 or bfloat16")
+    _need(out, out.dtype, "out", (N, K))
+    _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), N, K, _ptr(out), dt,
+                                  _stream(codes.device)))
+    return out
+
+
+def sp24_prune(W, out=None):
+    """2:4 magnitude prune along K (keep the two largest |w| of every group of four)."""
+    N, K = W.shape
+    _need(W, W.dtype, "W")
+    out = out if out is not None else torch.empty_like(W)
+    _need(out, W.dtype, "out", (N, K))
+    _check(lib().sp24_prune(_ptr(W), _wdt(W), N, K, _ptr(out), _stream(W.device)))
+    return out
+
+
+def sp24_check(codes, bad_groups=None, first_bad=None):
+    """Per-group 2:4 check. Returns device int64 tensors (bad_groups [1], first_bad [1])."""
+    N, Kh = codes.shape
+    _need(codes, torch.uint8, "codes")
+    dev = codes.device
+    bad = bad_groups if bad_groups is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    first = first_bad if first_bad is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    _check(lib().sp24_check(_ptr(codes), N, 2 * Kh, _ptr(bad), _ptr(first), _stream(dev)))
+    return bad, first
+
+
+def sp24_compress(codes, vals=None, meta=None, bad_groups=None, raise_if_bad=False):
+    """2:4 compression. Returns (vals u8 [N,K/4], meta u8 [N,K/8], bad_groups int64 [1] device)."""
+    N, Kh = codes.shape
+    K = 2 * Kh
+    _need(codes, torch.uint8, "codes")
+    dev = codes.device
+    vals = vals if vals is not None else torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    meta = meta if meta is not None else torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
+    bad = bad_groups if bad_groups is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    _need(vals, torch.uint8, "vals", (N, K // 4)); _need(meta, torch.uint8, "meta", (N, K // 8))
+    _check(lib().sp24_compress(_ptr(codes), N, K, _ptr(vals), _ptr(meta), _ptr(bad), _stream(dev)))
+    if raise_if_bad:
+        nb = int(bad.item())
+        if nb:
+            raise ValueError(f"sp24_compress: {nb} group(s) of four have fewer than two zeros")
+    return vals, meta, bad
+
+
+def sp24_decompress(vals, meta, codes=None):
+    N, G = vals.shape
+    K = 4 * G
+    _need(vals, torch.uint8, "vals"); _need(meta, torch.uint8, "meta", (N, K // 8))
+    codes = codes if codes is not None else torch.empty((N, K // 2), dtype=torch.uint8, device=vals.device)
+    _need(codes, torch.uint8, "codes", (N, K // 2))
+    _check(lib().sp24_decompress(_ptr(vals), _ptr(meta), N, K, _ptr(codes), _stream(vals.device)))
+    return codes
+
+
+def _gemm_out(X, N, y_dtype, Y):
+    M = X.shape[0]
+    Y = Y if Y is not None else torch.empty((M, N), dtype=y_dtype, device=X.device)
+    dt = SSN_F32 if Y.dtype == torch.float32 else SSN_BF16 if Y.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("Y must be float32 or bfloat16")
+    _need(Y, Y.dtype, "Y", (M, N))
+    return Y, dt
+
+
+def gemm_nvfp4_dense(X, codes, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None):
+    """Y = X . W_hat^T for dense NVFP4 weights. Returns (Y, algorithm that ran)."""
+    M, K = X.shape
+    N = codes.shape[0]
+    _need(X, torch.bfloat16, "X"); _need(codes, torch.uint8, "codes", (N, K // 2))
+    _need(scales, torch.uint8, "scales", (N, K // 16)); _need(tensor_scale, torch.float32, "tensor_scale", (1,))
+    Y, dt = _gemm_out(X, N, y_dtype, Y)
+    used = ctypes.c_int(-1)
+    _check(lib().gemm_nvfp4_dense(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt,
+                                  algo, ctypes.byref(used), _stream(X.device)))
+    return Y, used.value
+
+
+def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None):
+    """Y = X . W_hat^T from 2:4-compressed NVFP4 weights. Returns (Y, algorithm that ran)."""
+    M, K = X.shape
+    N = vals.shape[0]
+    _need(X, torch.bfloat16, "X"); _need(vals, torch.uint8, "vals", (N, K // 4))
+    _need(meta, torch.uint8, "meta", (N, K // 8)); _need(scales, torch.uint8, "scales", (N, K // 16))
+    _need(tensor_scale, torch.float32, "tensor_scale", (1,))
+    Y, dt = _gemm_out(X, N, y_dtype, Y)
+    used = ctypes.c_int(-1)
+    _check(lib().gemm_nvfp4_sp24(_ptr(X), M, N, K, _ptr(vals), _ptr(meta), _ptr(scales), _ptr(tensor_scale),
+                                 _ptr(Y), dt, algo, ctypes.byref(used), _stream(X.device)))
+    return Y, used.value

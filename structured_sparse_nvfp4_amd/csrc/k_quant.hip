@@ -1,0 +1,240 @@
+// NVFP4 quantisation, decode and 2:4 magnitude pruning on gfx950.
+//
+// Quantisation follows "NVFP4 Without FP4 Hardware" (ai-muninn.com), section "Convert BF16 to
+// NVFP4 yourself": a tensor scale s_t = amax / (6 * 448), one E4M3 scale per 16 values along K
+// and E2M1 values; a group of tensors may share s_t (section "The shared global scale").
+// All rounding decisions are exact: they are taken on float64 quotients and products. w has
+// 24 significant bits and s_t * S at most 28, so a quotient that is not exactly on a grid
+// midpoint is further than half a float64 ulp from it, and comparing |w| against
+// midpoint * s_t * S (an exact float64 product) decides the E2M1 code exactly.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssn {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float load_w(const void* W, int w_bf16, size_t i) {
+  if (w_bf16) return __uint_as_float((uint32_t)((const uint16_t*)W)[i] << 16);
+  return ((const float*)W)[i];
+}
+
+// ---- amax over the tensor: atomic max on the float bit pattern (|w| >= 0 orders as uint) ----
+__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+
+__global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, size_t n, uint32_t* out) {
+  float m = 0.f;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (!w_bf16) {
+    const float* w = (const float*)W;
+    size_t n4 = n / 4;
+    for (size_t j = i; j < n4; j += stride) {
+      f32x4 v = ld_nt((const f32x4*)w + j);
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+    }
+    for (size_t j = n4 * 4 + i; j < n; j += stride) m = fmaxf(m, fabsf(w[j]));
+  } else {
+    const uint16_t* w = (const uint16_t*)W;
+    size_t n8 = n / 8;
+    for (size_t j = i; j < n8; j += stride) {
+      u32x4 v = ld_nt((const u32x4*)w + j);
+      for (int t = 0; t < 4; ++t)
+        m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[t])), fabsf(bf16_hi(v[t]))));
+    }
+    for (size_t j = n8 * 8 + i; j < n; j += stride) m = fmaxf(m, fabsf(load_w(W, 1, j)));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int k = 1; k < kThreads / 64; ++k) r = fmaxf(r, red[k]);
+    atomicMax(out, __float_as_uint(r));
+  }
+}
+
+// s_t = fl32(amax / 2688): float64 division then conversion is the correctly rounded f32
+// quotient (2688 = 2^7 * 21 and 21 is odd, so the quotient is never an f32 midpoint).
+__global__ void k_finalize_scale(const uint32_t* amax_bits, const float* ts_in, float* ts_out) {
+  if (ts_in) { *ts_out = *ts_in; return; }
+  double amax = (double)__uint_as_float(*amax_bits);
+  *ts_out = (float)(amax / 2688.0);
+}
+
+// E4M3 nearest-even of q >= 0, saturating at 448 (0x7E); q is an exactly rounded float64.
+__device__ __forceinline__ uint32_t e4m3_rne(double q) {
+  if (!(q < 448.0)) return 0x7Eu;
+  if (q < 0.015625) {                          // below 2^-6: subnormal spacing 2^-9
+    double m = rint(q * 512.0);                // exact scaling; rint ties to even
+    return (uint32_t)m;                        // 8 -> 0x08 (= 2^-6), still correct
+  }
+  int e = ilogb(q);                            // -6 .. 8
+  double mant = ldexp(q, -e) - 1.0;            // [0, 1), exact
+  double m8 = rint(mant * 8.0);
+  if (m8 >= 8.0) { m8 = 0.0; e += 1; }
+  return (uint32_t)(((e + 7) << 3) | (int)m8);
+}
+
+__device__ __forceinline__ double e4m3_f64(uint32_t b) {
+  int e = (b >> 3) & 15, m = b & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+}
+
+// One thread per block of 16 values: S, then 16 codes packed into 8 bytes.
+__global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16, size_t nblocks,
+                                                       const float* ts, uint8_t* codes, uint8_t* scales) {
+  size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  float w[16];
+  if (!w_bf16) {
+    const f32x4* p = (const f32x4*)((const float*)W + b * 16);
+    for (int t = 0; t < 4; ++t) {
+      f32x4 v = ld_nt(p + t);
+      w[4 * t] = v[0]; w[4 * t + 1] = v[1]; w[4 * t + 2] = v[2]; w[4 * t + 3] = v[3];
+    }
+  } else {
+    const u32x4* p = (const u32x4*)((const uint16_t*)W + b * 16);
+    for (int t = 0; t < 2; ++t) {
+      u32x4 v = ld_nt(p + t);
+      for (int u = 0; u < 4; ++u) { w[8 * t + 2 * u] = bf16_lo(v[u]); w[8 * t + 2 * u + 1] = bf16_hi(v[u]); }
+    }
+  }
+  float amax = 0.f;
+  for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(w[t]));
+  const double st = (double)*ts;
+  uint32_t S = 0;
+  if (st > 0.0) S = e4m3_rne((double)amax / (6.0 * st));
+  const double d = st * e4m3_f64(S);           // exact: <= 24 + 4 significant bits
+  uint32_t lo = 0, hi = 0;
+  if (d > 0.0) {
+    // E2M1 decision thresholds: ties at 0.25, 1.25, 2.5 and 5 go down, at 0.75, 1.75 and 3.5 up
+    const double t025 = 0.25 * d, t075 = 0.75 * d, t125 = 1.25 * d, t175 = 1.75 * d;
+    const double t25 = 2.5 * d, t35 = 3.5 * d, t5 = 5.0 * d;
+    for (int t = 0; t < 16; ++t) {
+      double a = fabs((double)w[t]);
+      uint32_t c = (uint32_t)(a > t025) + (uint32_t)(a >= t075) + (uint32_t)(a > t125) +
+                   (uint32_t)(a >= t175) + (uint32_t)(a > t25) + (uint32_t)(a >= t35) + (uint32_t)(a > t5);
+      c |= (__float_as_uint(w[t]) >> 28) & 8u;  // sign bit -> bit 3 (keeps -0 for tiny negatives)
+      if (t < 8) lo |= c << (4 * t); else hi |= c << (4 * (t - 8));
+    }
+  }
+  u32x2 o; o[0] = lo; o[1] = hi;
+  *(u32x2*)(codes + b * 8) = o;
+  scales[b] = (uint8_t)S;
+}
+
+// double -> f32 rounded to odd: truncate, then set the last bit if anything was dropped. A
+// later rounding to bf16 (16 fewer bits) is then the correctly rounded bf16 of the double.
+__device__ __forceinline__ float to_f32_round_odd(double x) {
+  float t = __double2float_rz(x);
+  if ((double)t != x) t = __uint_as_float(__float_as_uint(t) | 1u);
+  return t;
+}
+
+// Decode: one thread per block of 16. f32 output: the exact product e2m1 * S times s_t, rounded
+// once. bf16 output: the exact float64 product rounded once to bf16 (via round-to-odd f32).
+__global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* codes, const uint8_t* scales,
+                                                         const float* ts, size_t nblocks, void* out,
+                                                         int out_bf16) {
+  size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  u32x2 c = *(const u32x2*)(codes + b * 8);
+  const float s = e4m3_f32(scales[b]);
+  const float st = *ts;
+  float v[16];
+  for (int h = 0; h < 2; ++h) {
+    f32x2 p0 = fp4x2_f32<0>(c[h]), p1 = fp4x2_f32<1>(c[h]), p2 = fp4x2_f32<2>(c[h]), p3 = fp4x2_f32<3>(c[h]);
+    float* o = v + 8 * h;
+    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1]; o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+  }
+  if (!out_bf16) {
+    f32x4* o = (f32x4*)((float*)out + b * 16);
+    for (int t = 0; t < 4; ++t) {
+      f32x4 r;
+      for (int u = 0; u < 4; ++u) r[u] = (v[4 * t + u] * s) * st;  // e2m1*S exact, then one rounding
+      o[t] = r;
+    }
+  } else {
+    u32x4* o = (u32x4*)((uint16_t*)out + b * 16);
+    for (int t = 0; t < 2; ++t) {
+      u32x4 r;
+      for (int u = 0; u < 4; ++u) {
+        float a = to_f32_round_odd((double)(v[8 * t + 2 * u] * s) * (double)st);
+        float c2 = to_f32_round_odd((double)(v[8 * t + 2 * u + 1] * s) * (double)st);
+        r[u] = f32_to_bf16_rne(a) | (f32_to_bf16_rne(c2) << 16);
+      }
+      o[t] = r;
+    }
+  }
+}
+
+// 2:4 magnitude prune: one thread per group of four. Entry i is kept when fewer than two
+// entries outrank it, where j outranks i if |w_j| > |w_i|, or |w_j| == |w_i| and j < i.
+__global__ __launch_bounds__(kThreads) void k_prune(const void* W, int w_bf16, size_t ngroups, void* out) {
+  size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= ngroups) return;
+  float a[4];
+  uint32_t raw[4];
+  if (!w_bf16) {
+    f32x4 v = *((const f32x4*)W + g);
+    for (int i = 0; i < 4; ++i) { raw[i] = __float_as_uint(v[i]); a[i] = fabsf(v[i]); }
+  } else {
+    u32x2 v = *((const u32x2*)W + g);
+    raw[0] = v[0] & 0xFFFFu; raw[1] = v[0] >> 16; raw[2] = v[1] & 0xFFFFu; raw[3] = v[1] >> 16;
+    for (int i = 0; i < 4; ++i) a[i] = fabsf(__uint_as_float(raw[i] << 16));
+  }
+  for (int i = 0; i < 4; ++i) {
+    int outrank = 0;
+    for (int j = 0; j < 4; ++j) outrank += (a[j] > a[i]) || (a[j] == a[i] && j < i);
+    if (outrank >= 2) raw[i] = 0u;
+  }
+  if (!w_bf16) {
+    u32x4 o; o[0] = raw[0]; o[1] = raw[1]; o[2] = raw[2]; o[3] = raw[3];
+    *((u32x4*)out + g) = o;
+  } else {
+    u32x2 o; o[0] = raw[0] | (raw[1] << 16); o[1] = raw[2] | (raw[3] << 16);
+    *((u32x2*)out + g) = o;
+  }
+}
+
+inline unsigned grid_for(size_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
+
+}  // namespace
+
+hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, const float* ts_in,
+                           uint8_t* codes, uint8_t* scales, float* ts_out, hipStream_t s) {
+  const size_t n = (size_t)N * (size_t)K;
+  uint32_t* amax_bits = (uint32_t*)ts_out;  // the output slot doubles as the amax accumulator
+  if (!ts_in) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, amax_bits);
+    unsigned g = (unsigned)std::min<size_t>(grid_for(n / (w_bf16 ? 8 : 4) + 1, kThreads), 4096);
+    hipLaunchKernelGGL(k_amax, dim3(g), dim3(kThreads), 0, s, W, w_bf16, n, amax_bits);
+  }
+  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(1), 0, s, amax_bits, ts_in, ts_out);
+  const size_t nb = n / 16;
+  if (nb)
+    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
+                       (const float*)ts_out, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t N,
+                             int64_t K, void* out, int out_bf16, hipStream_t s) {
+  const size_t nb = (size_t)N * (size_t)K / 16;
+  hipLaunchKernelGGL(k_dequantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, codes, scales, ts,
+                     nb, out, out_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_prune(const void* W, int w_bf16, int64_t N, int64_t K, void* out, hipStream_t s) {
+  const size_t ng = (size_t)N * (size_t)K / 4;
+  hipLaunchKernelGGL(k_prune, dim3(grid_for(ng, kThreads)), dim3(kThreads), 0, s, W, w_bf16, ng, out);
+  return hipGetLastError();
+}
+
+}  // namespace ssn

@@ -1,0 +1,151 @@
+// 2:4 check, compress and decompress of NVFP4 codes on gfx950. HBM-bound streaming kernels:
+// each lane moves 16 B of codes (32 codes = 8 groups of four) per step with a 128-bit load.
+//
+// Rule ("Sparse GPU FLOPS Need the Right Zeros in the Right Places", leviathansystems.co,
+// section "The operation determines which four entries belong together"): a group of four
+// consecutive codes along K is eligible when at least two are zero; a code is zero when its
+// three magnitude bits are 0 (so 0x8, the FP4 negative zero, is zero). The check is per group
+// (same page, section "Two half-zero vectors produce different pattern answers").
+// Compressed form ("NVFP4 vs 2:4 sparse", robertz.co, section "What 2:4 actually is"): the two
+// kept codes plus a 2-bit position each. Kept positions are the nonzero codes first, then the
+// lowest-index zeros, in ascending order; a failing group is written as vals 0x00 with
+// positions (0, 1) and counted.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssn {
+namespace {
+
+constexpr int kThreads = 256;
+
+// bit 4i of the result is set when nibble i of w has zero magnitude bits
+__device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
+  return ~(w | (w >> 1) | (w >> 2)) & 0x11111111u;
+}
+
+__global__ void k_init_counters(int64_t* bad, int64_t* first) {
+  *bad = 0;
+  if (first) *first = -1;  // as uint64 this is the largest value, so atomicMin keeps real indices
+}
+
+// One lane per 16 bytes of codes (8 groups); flat group index = byte offset / 2.
+__global__ __launch_bounds__(kThreads) void k_check(const u32x4* codes, size_t n16, int64_t* bad,
+                                                    int64_t* first) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t nbad = 0;
+  uint64_t fb = ~0ull;
+  if (i < n16) {
+    u32x4 w = ld_nt(codes + i);
+    for (int d = 3; d >= 0; --d) {          // descending so the last write is the smallest index
+      uint32_t z = zero_nibbles(w[d]);
+      uint32_t c0 = __builtin_popcount(z & 0xFFFFu), c1 = __builtin_popcount(z >> 16);
+      if (c1 < 2) { ++nbad; fb = i * 8 + 2 * d + 1; }
+      if (c0 < 2) { ++nbad; fb = i * 8 + 2 * d; }
+    }
+  }
+  // wave reduction, then one atomic per wave
+  for (int off = 32; off > 0; off >>= 1) {
+    nbad += __shfl_xor(nbad, off, 64);
+    uint64_t o = __shfl_xor(fb, off, 64);
+    fb = o < fb ? o : fb;
+  }
+  if ((threadIdx.x & 63) == 0 && nbad) {
+    atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
+    if (first) atomicMin((unsigned long long*)first, (unsigned long long)fb);
+  }
+}
+
+// Compress one group (16-bit word of four codes): returns vals byte | pos nibble << 8 | fail << 12
+__device__ __forceinline__ uint32_t compress_group(uint32_t g) {
+  const uint32_t z = zero_nibbles(g) & 0x1111u;
+  // nonzero mask over the 4 positions
+  const uint32_t nz = (~((z & 1u) | ((z >> 3) & 2u) | ((z >> 6) & 4u) | ((z >> 9) & 8u))) & 0xFu;
+  const uint32_t cnt = __builtin_popcount(nz);
+  if (cnt > 2) return 0x0u | (0x4u << 8) | (1u << 12);
+  uint32_t sel = nz;
+  if (cnt == 1) sel |= (~nz & 0xFu) & (0u - (~nz & 0xFu));   // add the lowest zero position
+  if (cnt == 0) sel = 0x3u;                                    // two lowest zero positions
+  const uint32_t i0 = __builtin_ctz(sel);
+  const uint32_t i1 = 31u - __builtin_clz(sel);
+  const uint32_t c0 = (g >> (4 * i0)) & 0xFu, c1 = (g >> (4 * i1)) & 0xFu;
+  return (c0 | (c1 << 4)) | ((i0 | (i1 << 2)) << 8);
+}
+
+__global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_t n16, u32x2* vals,
+                                                       uint32_t* meta, int64_t* bad) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t nbad = 0;
+  if (i < n16) {
+    u32x4 w = ld_nt(codes + i);
+    uint32_t v[2] = {0u, 0u}, m = 0u;
+    for (int d = 0; d < 4; ++d) {
+      uint32_t r0 = compress_group(w[d] & 0xFFFFu), r1 = compress_group(w[d] >> 16);
+      nbad += (r0 >> 12) + (r1 >> 12);
+      const int g = 2 * d;                   // group index within the 8
+      v[g >> 2] |= ((r0 & 0xFFu) << (8 * (g & 3))) | ((r1 & 0xFFu) << (8 * ((g + 1) & 3)));
+      m |= (((r0 >> 8) & 0xFu) << (4 * g)) | (((r1 >> 8) & 0xFu) << (4 * (g + 1)));
+    }
+    u32x2 vo; vo[0] = v[0]; vo[1] = v[1];
+    vals[i] = vo;
+    meta[i] = m;
+  }
+  for (int off = 32; off > 0; off >>= 1) nbad += __shfl_xor(nbad, off, 64);
+  if ((threadIdx.x & 63) == 0 && nbad) atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
+}
+
+__global__ __launch_bounds__(kThreads) void k_decompress(const u32x2* vals, const uint32_t* meta, size_t n16,
+                                                         u32x4* codes) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n16) return;
+  u32x2 v = vals[i];
+  uint32_t m = meta[i];
+  u32x4 out;
+  for (int d = 0; d < 4; ++d) {
+    uint32_t word = 0;
+    for (int h = 0; h < 2; ++h) {
+      const int g = 2 * d + h;
+      const uint32_t vb = (v[g >> 2] >> (8 * (g & 3))) & 0xFFu;
+      const uint32_t pos = (m >> (4 * g)) & 0xFu;
+      const uint32_t i0 = pos & 3u, i1 = pos >> 2;
+      uint32_t grp = 0;
+      for (uint32_t p = 0; p < 4; ++p) {
+        uint32_t c = (p == i1) ? (vb >> 4) : (p == i0) ? (vb & 0xFu) : 0u;  // i1 wins on a clash
+        grp |= c << (4 * p);
+      }
+      word |= grp << (16 * h);
+    }
+    out[d] = word;
+  }
+  codes[i] = out;
+}
+
+inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+
+}  // namespace
+
+hipError_t launch_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad, int64_t* first,
+                        hipStream_t s) {
+  const size_t n16 = (size_t)N * (size_t)K / 32;  // K % 32 == 0: rows are whole 16-byte chunks
+  hipLaunchKernelGGL(k_init_counters, dim3(1), dim3(1), 0, s, bad, first);
+  if (n16) hipLaunchKernelGGL(k_check, dim3(grid_for(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16, bad, first);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* vals, uint8_t* meta,
+                           int64_t* bad, hipStream_t s) {
+  const size_t n16 = (size_t)N * (size_t)K / 32;
+  hipLaunchKernelGGL(k_init_counters, dim3(1), dim3(1), 0, s, bad, (int64_t*)nullptr);
+  if (n16) hipLaunchKernelGGL(k_compress, dim3(grid_for(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16,
+                              (u32x2*)vals, (uint32_t*)meta, bad);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompress(const uint8_t* vals, const uint8_t* meta, int64_t N, int64_t K, uint8_t* codes,
+                             hipStream_t s) {
+  const size_t n16 = (size_t)N * (size_t)K / 32;
+  if (n16) hipLaunchKernelGGL(k_decompress, dim3(grid_for(n16)), dim3(kThreads), 0, s, (const u32x2*)vals,
+                              (const uint32_t*)meta, n16, (u32x4*)codes);
+  return hipGetLastError();
+}
+
+}  // namespace ssn

@@ -8,3 +8,14 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Print the id of every GPU test (flushed) before it runs, so a run that dies names its case."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield

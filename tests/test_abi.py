@@ -1,0 +1,80 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the header
+declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import structured_sparse_nvfp4_amd as ssn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssnvfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ssn.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ["nvfp4_quantize", "nvfp4_dequantize", "sp24_prune", "sp24_check", "sp24_compress",
+                 "sp24_decompress", "gemm_nvfp4_dense", "gemm_nvfp4_sp24", "ssn_last_error", "ssn_version"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported():
+    L = ctypes.CDLL(ssn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) <= set(ssn._SIGS), "binding misses a declared call"
+
+
+def test_version():
+    assert ssn.lib().ssn_version() >= 100
+
+
+def _bad(ptr=0x1000):
+    return ctypes.c_void_p(ptr)
+
+
+def test_validation_paths_return_codes_without_launching():
+    L = ssn.lib()
+    p, n = _bad(), None
+    # K not a multiple of 32
+    assert L.sp24_check(p, 4, 48, p, p, n) == ssn.SSN_E_SHAPE
+    assert b"multiple of 32" in L.ssn_last_error()
+    assert L.sp24_compress(p, 4, 16, p, p, p, n) == ssn.SSN_E_SHAPE
+    assert L.nvfp4_quantize(p, 0, 4, 40, n, p, p, p, n) == ssn.SSN_E_SHAPE
+    # negative sizes
+    assert L.sp24_decompress(p, p, -1, 32, p, n) == ssn.SSN_E_SHAPE
+    assert L.gemm_nvfp4_dense(p, -2, 4, 32, p, p, p, p, 0, 0, n, n) == ssn.SSN_E_SHAPE
+    # NULL and misaligned pointers
+    assert L.sp24_check(p, 4, 64, n, n, n) == ssn.SSN_E_NULL
+    assert b"bad_groups" in L.ssn_last_error()
+    assert L.sp24_compress(_bad(0x1008), 4, 64, p, p, p, n) == ssn.SSN_E_ALIGN
+    assert L.nvfp4_quantize(p, 0, 4, 64, n, p, p, n, n) == ssn.SSN_E_NULL
+    assert L.gemm_nvfp4_dense(p, 2, 4, 64, n, p, p, p, 0, 0, n, n) == ssn.SSN_E_NULL
+    # dtype and algorithm codes
+    assert L.nvfp4_quantize(p, 7, 4, 64, n, p, p, p, n) == ssn.SSN_E_DTYPE
+    assert L.gemm_nvfp4_dense(p, 2, 4, 64, p, p, p, p, 3, 0, n, n) == ssn.SSN_E_DTYPE
+    assert L.gemm_nvfp4_dense(p, 2, 4, 64, p, p, p, p, 0, 99, n, n) == ssn.SSN_E_ALGO
+    assert L.gemm_nvfp4_dense(p, 2, 4, 64, p, p, p, p, 0, ssn.ALGO_SMFMAC, n, n) == ssn.SSN_E_ALGO
+    assert L.gemm_nvfp4_sp24(p, 2, 4, 64, p, p, p, p, p, 0, ssn.ALGO_MFMA, n, n) == ssn.SSN_E_ALGO
+    # an explicit algorithm that does not fit the shape is refused, not replaced
+    used = ctypes.c_int(-1)
+    assert L.gemm_nvfp4_sp24(p, 2, 4, 96, p, p, p, p, p, 0, ssn.ALGO_SMFMAC, ctypes.byref(used), n) == ssn.SSN_E_ALGO
+    assert b"K % 64" in L.ssn_last_error()
+
+
+def test_empty_problem_is_a_noop():
+    L = ssn.lib()
+    used = ctypes.c_int(-1)
+    assert L.gemm_nvfp4_dense(None, 0, 4, 64, None, None, None, None, 0, 0, ctypes.byref(used), None) == ssn.SSN_OK
+    assert L.gemm_nvfp4_sp24(None, 3, 0, 64, None, None, None, None, None, 0, 0, None, None) == ssn.SSN_OK
+    assert L.sp24_decompress(None, None, 0, 64, None, None) == ssn.SSN_OK
+    assert L.ssn_last_error() == b""

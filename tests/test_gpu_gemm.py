@@ -1,0 +1,124 @@
+"""GPU parity of gemm_nvfp4_dense / gemm_nvfp4_sp24 against the float64 oracle, within
+|err| <= 2e-3 * sum_k |x_k w_k| per element (+ half a bf16 ulp for bf16 outputs)."""
+import numpy as np
+import pytest
+import torch
+
+import structured_sparse_nvfp4_amd as ssn
+import synth
+from oracle import gemm, quant, sp24
+from tests.gpu_util import assert_within_bound, dev, x_dev, y_host
+
+pytestmark = pytest.mark.gpu
+
+DENSE_ALGOS = [ssn.ALGO_AUTO, ssn.ALGO_MFMA, ssn.ALGO_VALU]
+SP24_ALGOS = [ssn.ALGO_AUTO, ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_VALU]
+
+
+def _problem(M, N, K, seed, prune):
+    x = synth.activations(M, K, seed=seed)
+    w = synth.weights(N, K, seed=seed)
+    if prune:
+        w = sp24.prune24(w)
+    c, s, st = quant.quantize(w)
+    return x, c, s, st
+
+
+def _skinny_only(algo, M):
+    return algo in (ssn.ALGO_MFMA, ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA) and M > 16
+
+
+# the small configuration: X [16, 512], W [256, 512], plus ragged and multi-slice shapes
+DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
+               (17, 40, 64), (40, 33, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", DENSE_CASES)
+@pytest.mark.parametrize("algo", DENSE_ALGOS)
+@pytest.mark.parametrize("prune", [False, True])
+def test_dense(M, N, K, algo, prune):
+    if _skinny_only(algo, M):
+        pytest.skip("MFMA dense path covers M <= 16 in this build")
+    x, c, s, st = _problem(M, N, K, seed=M * 7 + N + K, prune=prune)
+    Y, B = gemm.gemm_dense(x, c, s, st)
+    g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
+    assert used != ssn.ALGO_AUTO and (algo == ssn.ALGO_AUTO or used == algo)
+    assert_within_bound(y_host(g), Y, B, what=f"dense algo={used}")
+
+
+SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64, 1024), (4, 48, 4096),
+              (17, 40, 64), (40, 33, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", SP24_CASES)
+@pytest.mark.parametrize("algo", SP24_ALGOS)
+def test_sp24(M, N, K, algo):
+    if _skinny_only(algo, M):
+        pytest.skip("matrix-core 2:4 paths cover M <= 16 in this build")
+    if algo == ssn.ALGO_SMFMAC and K % 64:
+        pytest.skip("SMFMAC needs K % 64 == 0 (refusal is tested on the CPU)")
+    x, c, s, st = _problem(M, N, K, seed=M * 5 + N + K, prune=True)
+    vals, meta, bad = sp24.compress(c)
+    assert bad == 0
+    Y, B = gemm.gemm_sp24(x, vals, meta, s, st)
+    g, used = ssn.gemm_nvfp4_sp24(x_dev(x), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)),
+                                  algo=algo)
+    assert used != ssn.ALGO_AUTO and (algo == ssn.ALGO_AUTO or used == algo)
+    assert_within_bound(y_host(g), Y, B, what=f"sp24 algo={used}")
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_bf16_output(sparse):
+    M, N, K = 8, 96, 512
+    x, c, s, st = _problem(M, N, K, seed=21, prune=sparse)
+    ts = dev(np.array([st], np.float32))
+    if sparse:
+        vals, meta, _ = sp24.compress(c)
+        Y, B = gemm.gemm_sp24(x, vals, meta, s, st)
+        g, _ = ssn.gemm_nvfp4_sp24(x_dev(x), dev(vals), dev(meta), dev(s), ts, y_dtype=torch.bfloat16)
+    else:
+        Y, B = gemm.gemm_dense(x, c, s, st)
+        g, _ = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), ts, y_dtype=torch.bfloat16)
+    assert_within_bound(y_host(g), Y, B, out="bf16", what="bf16 output")
+
+
+@pytest.mark.parametrize("algo", [ssn.ALGO_MFMA, ssn.ALGO_VALU])
+def test_one_hot_rows_extract_weights_dense(algo):
+    # X rows are unit vectors e_k: each output is one decoded weight times the tensor scale,
+    # exact up to the single f32 rounding of the scale product; this pins the operand layouts.
+    N, K = 48, 512
+    ks = np.array([0, 7, 8, 31, 32, 63, 100, 127, 128, 200, 255, 256, 300, 383, 384, 511])
+    x = np.zeros((16, K), np.float32)
+    x[np.arange(16), ks] = 1.0
+    xb = synth.f32_to_bf16_bits(x)
+    _, c, s, st = _problem(1, N, K, seed=4, prune=False)
+    g, _ = ssn.gemm_nvfp4_dense(x_dev(xb), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
+    want = quant.dequantize(c, s, st)[:, ks].T.astype(np.float32)
+    assert np.array_equal(y_host(g).astype(np.float32), want)
+
+
+@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_VALU])
+def test_one_hot_rows_extract_weights_sp24(algo):
+    N, K = 48, 512
+    ks = np.array([0, 1, 2, 3, 17, 63, 64, 100, 127, 128, 200, 255, 256, 301, 383, 510])
+    x = np.zeros((16, K), np.float32)
+    x[np.arange(16), ks] = 1.0
+    xb = synth.f32_to_bf16_bits(x)
+    _, c, s, st = _problem(1, N, K, seed=5, prune=True)
+    vals, meta, _ = sp24.compress(c)
+    g, _ = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)), algo=algo)
+    want = quant.dequantize(sp24.decompress(vals, meta), s, st)[:, ks].T.astype(np.float32)
+    assert np.array_equal(y_host(g).astype(np.float32), want)
+
+
+def test_empty_and_degenerate():
+    ts = dev(np.array([1.0], np.float32))
+    c = torch.zeros((4, 16), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 2), dtype=torch.uint8, device="cuda")
+    x = torch.zeros((0, 32), dtype=torch.bfloat16, device="cuda")
+    y, used = ssn.gemm_nvfp4_dense(x, c, s, ts)
+    assert y.shape == (0, 4)
+    # all-zero weights give exact zeros
+    x1 = torch.ones((2, 32), dtype=torch.bfloat16, device="cuda")
+    y, _ = ssn.gemm_nvfp4_dense(x1, c, s, ts)
+    assert torch.count_nonzero(y).item() == 0
