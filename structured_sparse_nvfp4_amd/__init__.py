@@ -65,6 +65,29 @@ def _check(status: int):
         raise SsnError(status, lib().ssn_last_error().decode())
 
 
+class Prepared:
+    """A call with its arguments already marshalled (tensors, sizes, stream): calling it issues
+    the C entry point with no per-call Python work beyond the ctypes call itself. Used to keep the
+    host ahead of the GPU when timing short kernels. The tensors must stay alive."""
+
+    def __init__(self, fname, cargs, keep):
+        self.f = getattr(lib(), fname)
+        self.cargs = cargs
+        self.keep = keep
+
+    def __call__(self):
+        st = self.f(*self.cargs)
+        if st:
+            _check(st)
+
+
+def _run(fname, cargs, prepare, keep, result):
+    if prepare:
+        return Prepared(fname, cargs, keep), result
+    _check(getattr(lib(), fname)(*cargs))
+    return result
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -99,7 +122,7 @@ def version() -> int:
     return lib().ssn_version()
 
 
-def nvfp4_quantize(W, tensor_scale_in=None, codes=None, scales=None, tensor_scale_out=None):
+def nvfp4_quantize(W, tensor_scale_in=None, codes=None, scales=None, tensor_scale_out=None, prepare=False):
     """NVFP4-quantise W [N, K] (f32 or bf16). Returns (codes u8 [N,K/2], scales u8 [N,K/16], s_t f32 [1])."""
     N, K = W.shape
     _need(W, W.dtype, "W")
@@ -111,9 +134,8 @@ def nvfp4_quantize(W, tensor_scale_in=None, codes=None, scales=None, tensor_scal
     _need(ts, torch.float32, "tensor_scale_out", (1,))
     if tensor_scale_in is not None:
         _need(tensor_scale_in, torch.float32, "tensor_scale_in", (1,))
-    _check(lib().nvfp4_quantize(_ptr(W), _wdt(W), N, K, _ptr(tensor_scale_in), _ptr(codes), _ptr(scales),
-                                _ptr(ts), _stream(dev)))
-    return codes, scales, ts
+    cargs = (_ptr(W), _wdt(W), N, K, _ptr(tensor_scale_in), _ptr(codes), _ptr(scales), _ptr(ts), _stream(dev))
+    return _run("nvfp4_quantize", cargs, prepare, (W, tensor_scale_in), (codes, scales, ts))
 
 
 def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, out=None):
@@ -131,28 +153,28 @@ def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, out=N
     return out
 
 
-def sp24_prune(W, out=None):
+def sp24_prune(W, out=None, prepare=False):
     """2:4 magnitude prune along K (keep the two largest |w| of every group of four)."""
     N, K = W.shape
     _need(W, W.dtype, "W")
     out = out if out is not None else torch.empty_like(W)
     _need(out, W.dtype, "out", (N, K))
-    _check(lib().sp24_prune(_ptr(W), _wdt(W), N, K, _ptr(out), _stream(W.device)))
-    return out
+    cargs = (_ptr(W), _wdt(W), N, K, _ptr(out), _stream(W.device))
+    return _run("sp24_prune", cargs, prepare, (W,), out)
 
 
-def sp24_check(codes, bad_groups=None, first_bad=None):
+def sp24_check(codes, bad_groups=None, first_bad=None, prepare=False):
     """Per-group 2:4 check. Returns device int64 tensors (bad_groups [1], first_bad [1])."""
     N, Kh = codes.shape
     _need(codes, torch.uint8, "codes")
     dev = codes.device
     bad = bad_groups if bad_groups is not None else torch.empty(1, dtype=torch.int64, device=dev)
     first = first_bad if first_bad is not None else torch.empty(1, dtype=torch.int64, device=dev)
-    _check(lib().sp24_check(_ptr(codes), N, 2 * Kh, _ptr(bad), _ptr(first), _stream(dev)))
-    return bad, first
+    cargs = (_ptr(codes), N, 2 * Kh, _ptr(bad), _ptr(first), _stream(dev))
+    return _run("sp24_check", cargs, prepare, (codes,), (bad, first))
 
 
-def sp24_compress(codes, vals=None, meta=None, bad_groups=None, raise_if_bad=False):
+def sp24_compress(codes, vals=None, meta=None, bad_groups=None, raise_if_bad=False, prepare=False):
     """2:4 compression. Returns (vals u8 [N,K/4], meta u8 [N,K/8], bad_groups int64 [1] device)."""
     N, Kh = codes.shape
     K = 2 * Kh
@@ -162,7 +184,10 @@ def sp24_compress(codes, vals=None, meta=None, bad_groups=None, raise_if_bad=Fal
     meta = meta if meta is not None else torch.empty((N, K // 8), dtype=torch.uint8, device=dev)
     bad = bad_groups if bad_groups is not None else torch.empty(1, dtype=torch.int64, device=dev)
     _need(vals, torch.uint8, "vals", (N, K // 4)); _need(meta, torch.uint8, "meta", (N, K // 8))
-    _check(lib().sp24_compress(_ptr(codes), N, K, _ptr(vals), _ptr(meta), _ptr(bad), _stream(dev)))
+    cargs = (_ptr(codes), N, K, _ptr(vals), _ptr(meta), _ptr(bad), _stream(dev))
+    if prepare:
+        return _run("sp24_compress", cargs, True, (codes,), (vals, meta, bad))
+    _check(lib().sp24_compress(*cargs))
     if raise_if_bad:
         nb = int(bad.item())
         if nb:
@@ -190,7 +215,7 @@ def _gemm_out(X, N, y_dtype, Y):
     return Y, dt
 
 
-def gemm_nvfp4_dense(X, codes, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None):
+def gemm_nvfp4_dense(X, codes, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None, prepare=False):
     """Y = X . W_hat^T for dense NVFP4 weights. Returns (Y, algorithm that ran)."""
     M, K = X.shape
     N = codes.shape[0]
@@ -198,12 +223,16 @@ def gemm_nvfp4_dense(X, codes, scales, tensor_scale, y_dtype=torch.float32, algo
     _need(scales, torch.uint8, "scales", (N, K // 16)); _need(tensor_scale, torch.float32, "tensor_scale", (1,))
     Y, dt = _gemm_out(X, N, y_dtype, Y)
     used = ctypes.c_int(-1)
-    _check(lib().gemm_nvfp4_dense(_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt,
-                                  algo, ctypes.byref(used), _stream(X.device)))
+    cargs = (_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt, algo,
+             ctypes.byref(used), _stream(X.device))
+    if prepare:
+        return Prepared("gemm_nvfp4_dense", cargs, (X, codes, scales, tensor_scale, used)), (Y, used)
+    _check(lib().gemm_nvfp4_dense(*cargs))
     return Y, used.value
 
 
-def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None):
+def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None,
+                    prepare=False):
     """Y = X . W_hat^T from 2:4-compressed NVFP4 weights. Returns (Y, algorithm that ran)."""
     M, K = X.shape
     N = vals.shape[0]
@@ -212,6 +241,9 @@ def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, 
     _need(tensor_scale, torch.float32, "tensor_scale", (1,))
     Y, dt = _gemm_out(X, N, y_dtype, Y)
     used = ctypes.c_int(-1)
-    _check(lib().gemm_nvfp4_sp24(_ptr(X), M, N, K, _ptr(vals), _ptr(meta), _ptr(scales), _ptr(tensor_scale),
-                                 _ptr(Y), dt, algo, ctypes.byref(used), _stream(X.device)))
+    cargs = (_ptr(X), M, N, K, _ptr(vals), _ptr(meta), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt, algo,
+             ctypes.byref(used), _stream(X.device))
+    if prepare:
+        return Prepared("gemm_nvfp4_sp24", cargs, (X, vals, meta, scales, tensor_scale, used)), (Y, used)
+    _check(lib().gemm_nvfp4_sp24(*cargs))
     return Y, used.value
