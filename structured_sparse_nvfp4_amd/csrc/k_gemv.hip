@@ -17,6 +17,8 @@
 //                             B: col r, k = 8q..8q+7 then 32+8q..32+8q+7;  D as above.
 // The compressed layout of this library (vals byte = two kept codes, meta nibble = i0 | i1 << 2)
 // is therefore the SMFMAC A operand and index operand as stored: no permutation.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,6 +26,18 @@ namespace ssn {
 namespace {
 
 constexpr int kWaves = 4;
+// 32 zero bytes: activation loads of K-slices outside the problem read here, so that the weights
+// loaded (from a clamped, valid address) for those slices are multiplied by zero.
+__device__ __attribute__((aligned(16))) uint32_t g_zero32[8];
+// Slices in flight per wave (ring depth). Build-time tunables.
+#ifndef SSN_GEMV_DENSE_RING
+#define SSN_GEMV_DENSE_RING 2
+#endif
+#ifndef SSN_GEMV_SPARSE_RING
+#define SSN_GEMV_SPARSE_RING 1
+#endif
+constexpr int kDenseRing = SSN_GEMV_DENSE_RING;    // 128-wide slices (dense)
+constexpr int kSparseRing = SSN_GEMV_SPARSE_RING;  // 256-wide slices (2:4)
 
 __device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
 
@@ -63,11 +77,19 @@ __device__ __forceinline__ void store_tile16(f32x4 acc, float* red, int M, int N
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense, M <= 16. One block = 16 weight rows; the 4 waves split K in 128-wide slices
-// (lane group q takes 32 consecutive k of the slice: 16 B of codes, 2 scale bytes).
+// Dense, M <= 16. One block = 16 weight rows over the whole K; the 4 waves take contiguous
+// quarters of K in 128-wide slices (lane group q takes 32 consecutive k of a slice: 16 B of
+// codes, 2 scale bytes and the 64 B of activations that meet them).
+// The kernel streams the weights once, so it is a software pipeline: a ring of PW slices
+// (weights + activations, in registers) is kept in flight, and the slot just consumed is
+// refilled with the slice PW ahead. Compute then overlaps the loads of later slices instead of
+// waiting for a whole batch. Loads are unconditional with selected addresses only (so the
+// compiler counts outstanding loads exactly); slices past the wave's range read activations
+// from a zero block, so the (clamped, valid) weights loaded for them contribute nothing. Lanes
+// of activation rows >= M read row 0: those output columns are never stored.
 // SRC_SP24: the weights come as vals+meta and are expanded to dense codes in registers first
 // (the decompress-then-dense-MFMA variant of the 2:4 product).
-template <bool SRC_SP24>
+template <bool SRC_SP24, int PW>
 __global__ __launch_bounds__(256) void k_gemv_mfma(const uint16_t* __restrict__ X, int M, int N, int K,
                                                    const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
                                                    const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -77,52 +99,235 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const uint16_t* __restrict__ 
   const int r = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int n = min(n0 + r, N - 1);
-  const bool xv = r < M;
-  const uint16_t* xrow = X + (size_t)(xv ? r : 0) * K;
+  const uint16_t* xrow = X + (size_t)(r < M ? r : 0) * K;
   const uint8_t* srow = scales + (size_t)n * (K / 16);
+  const int S = (K + 127) / 128;
+  const int s_lo = (S * wave) / kWaves, s_hi = (S * (wave + 1)) / kWaves;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nslices = (K + 127) / 128;
-  for (int c = wave; c < nslices; c += kWaves) {
-    const int k = c * 128 + 32 * q;
-    u32x4 cw = zero4();
-    uint32_t sw = 0;
-    u32x4 xw[4] = {zero4(), zero4(), zero4(), zero4()};
-    if (k < K) {
-      if constexpr (!SRC_SP24) {
-        cw = ld_nt((const u32x4*)(w0 + (size_t)n * (K / 2) + k / 2));
-      } else {
-        // 8 groups: 8 vals bytes + 4 meta bytes -> 32 dense codes
-        const u32x2 v = ld_nt((const u32x2*)(w0 + (size_t)n * (K / 4) + k / 4));
-        const uint32_t mt = ld_nt((const uint32_t*)(w1 + (size_t)n * (K / 8) + k / 8));
+
+  struct Slot { u32x4 w; uint32_t sc; u32x4 x[4]; };
+  auto load_slot = [&](int s) -> Slot {
+    Slot o;
+    const bool ok = s < s_hi && s * 128 + 32 * q < K;
+    const int k = ok ? s * 128 + 32 * q : 0;
+    if constexpr (!SRC_SP24) {
+      o.w = ld_nt((const u32x4*)(w0 + (size_t)n * (K / 2) + k / 2));
+    } else {
+      const u32x2 v = ld_nt((const u32x2*)(w0 + (size_t)n * (K / 4) + k / 4));
+      o.w[0] = v[0]; o.w[1] = v[1]; o.w[3] = 0u;
+      o.w[2] = ld_nt((const uint32_t*)(w1 + (size_t)n * (K / 8) + k / 8));
+    }
+    o.sc = ld_nt((const uint16_t*)(srow + k / 16));
+    const u32x4* xp = ok ? (const u32x4*)(xrow + k) : (const u32x4*)g_zero32;
+    const int xs = ok ? 1 : 0;                     // the zero block is 32 B: do not step through it
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.x[j] = xp[j * xs];
+    return o;
+  };
+
+  Slot ring[PW];
+#pragma unroll
+  for (int u = 0; u < PW; ++u) ring[u] = load_slot(s_lo + u);
+  for (int s = s_lo; s < s_hi; s += PW) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const Slot cur = ring[u];
+      ring[u] = load_slot(s + u + PW);             // refill: PW slices ahead
+      u32x4 c = cur.w;
+      if constexpr (SRC_SP24) {
+        // 8 groups: vals bytes in c[0..1], meta nibbles in c[2] -> 32 dense codes
+        const u32x2 v = {c[0], c[1]};
+        const uint32_t mt = c[2];
+        c = zero4();
+#pragma unroll
         for (int g = 0; g < 8; ++g) {
           const uint32_t vb = (v[g >> 2] >> (8 * (g & 3))) & 0xFFu;
           const uint32_t pos = (mt >> (4 * g)) & 0xFu;
           const uint32_t grp = ((vb & 0xFu) << (4 * (pos & 3u))) | ((vb >> 4) << (4 * (pos >> 2)));
-          cw[g >> 1] |= grp << (16 * (g & 1));
+          c[g >> 1] |= grp << (16 * (g & 1));
         }
       }
-      sw = *(const uint16_t*)(srow + k / 16);
-      if (xv) {
-        const u32x4* xp = (const u32x4*)(xrow + k);
-        xw[0] = xp[0]; xw[1] = xp[1]; xw[2] = xp[2]; xw[3] = xp[3];
-      }
-    }
-    const float s0 = e4m3_f32_sel<0>(sw), s1 = e4m3_f32_sel<1>(sw);
+      const float sc0 = e4m3_f32_sel<0>(cur.sc), sc1 = e4m3_f32_sel<1>(cur.sc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4 a = fp4x8_bf16(cw[j], j < 2 ? s0 : s1);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(xw[j]), acc, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 a = fp4x8_bf16(c[j], j < 2 ? sc0 : sc1);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(cur.x[j]), acc, 0, 0, 0);
+      }
     }
   }
   store_tile16(acc, red, M, N, n0, *ts, Y, y_bf16);
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2:4, M <= 16, sparse MFMA. One block = 16 weight rows; waves split K in 256-wide slices.
-// Lane group q of a slice takes 16 consecutive groups (64 k): 16 B vals, 8 B meta, 4 B scales,
-// feeding four v_smfmac_f32_16x16x64_bf16 (j = 0..3). For SMFMAC j the instruction's k index
-// kappa = 16q + t maps to k = slice + 64q + 16j + t, so the B lane (col r, group q) needs the
-// activations at slice + 64(q>>1) + 16j + 8(q&1) (+8 contiguous) and the same +128.
+// Dense, M <= 16, "slab" kernel: one block per CU owns a contiguous slab of R weight rows and
+// streams it once through LDS.
+//  * Weights reach LDS with gfx950 direct-to-LDS loads (global_load_lds_dwordx4, no registers):
+//    every load instruction reads contiguous 256-byte runs of a row (4 rows per instruction), so
+//    HBM sees long runs instead of 16 rows x 64 B per instruction.
+//  * K is streamed in stages of kSK values; kD stages are in flight (a ring of LDS buffers).
+//    Every wave issues the same number of loads per stage (clamped addresses, all lanes active),
+//    so "stage st has landed" is an exact s_waitcnt vmcnt on each wave followed by a barrier.
+//  * Inside a 256-byte row run the 16-byte chunks are stored XOR-swizzled by the row index, so
+//    the MFMA operand reads (16 rows x one chunk) hit 16 different LDS bank groups.
+//  * The activations of the stage (M rows x kSK bf16) are loaded once per block and shared by
+//    its waves.
+// Rows are processed in groups of 64 (four 16-row MFMA tiles); 16 waves: wave w computes tile
+// w & 3 on slice w >> 2 of each stage's four 128-wide slices; the four partial tiles of each row
+// tile are summed at the end.
+constexpr int kSK = 512;                          // K values per stage
+constexpr int kD = 4;                             // stages in flight
+constexpr int kSlabWaves = 16;                    // 4 per SIMD; wave w: tile w & 3, slice w >> 2
+constexpr int kWRow = kSK / 2;                    // code bytes per row per stage (256)
+constexpr int kSRow = kSK / 16;                   // scale bytes per row per stage (32)
+constexpr int kXRow = kSK * 2 + 16;               // activation bytes per row per stage (+ pad)
+constexpr int kWBuf = 64 * kWRow, kSBuf = 64 * kSRow;
+constexpr int kStageBytes = kWBuf + kSBuf + 16 * kXRow;
+constexpr int kSlabLds = kD * kStageBytes;        // 4 x 35 KB: one block per CU
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence would make the
+// compiler drain every outstanding load (vmcnt(0)), including the stages still meant to be in
+// flight. Visibility of a stage is established by the explicit vmcnt wait before this barrier;
+// the empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int L>   // wait until at most `ahead` stages of L loads each are still in flight
+__device__ __forceinline__ void wait_stages(int ahead) {
+  switch (ahead) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<L>(); break;
+    case 2: wait_vmcnt<2 * L>(); break;
+    default: wait_vmcnt<3 * L>(); break;
+  }
+}
+
+template <int XI>   // XI = activation load instructions per wave per stage (M <= kSlabWaves * XI)
+__global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* __restrict__ X, int M, int N, int K,
+                                                               const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ scales,
+                                                               const float* __restrict__ ts, void* __restrict__ Y,
+                                                               int y_bf16, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int kWLoads = 64 * kWRow / 1024 / kSlabWaves;   // 1 KB weight loads per wave per stage
+  constexpr int L = kWLoads + 1 + XI;             // loads per wave per stage: W, scales, X
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
+  const int nst = (K + kSK - 1) / kSK;
+
+  for (int g0 = row_lo; g0 < row_hi; g0 += 64) {
+    // ---- issue the loads of stage st into ring slot st % kD (all lanes, clamped addresses)
+    auto issue = [&](int st) {
+      uint8_t* b = smem + (st % kD) * kStageBytes;
+      const int k0 = st * kSK;
+#pragma unroll
+      for (int i = 0; i < kWLoads; ++i) {           // weights: 4 rows x 256 B per instruction
+        const int rr = (wave * kWLoads + i) * 4 + (lane >> 4);  // row within the group (0..63)
+        const int n = min(g0 + rr, N - 1);
+        const int slot = lane & 15;
+        int cb = k0 / 2 + 16 * (slot ^ (rr & 15));  // swizzled chunk of this row's run
+        cb = min(cb, K / 2 - 16);                   // K tail: clamp (those k meet zero activations)
+        lds_dma16(codes + (size_t)n * (K / 2) + cb, b + (wave * kWLoads + i) * 4 * kWRow);
+      }
+      {                                             // scales: 4 rows x 32 B per wave, lanes 0..7
+        static_assert(kSlabWaves * 4 == 64 && kSRow == 32, "scale staging assumes 4 rows of 32 B per wave");
+        const int rr = wave * 4 + ((lane >> 1) & 3);
+        const int n = min(g0 + rr, N - 1);
+        const int sb = min(k0 / 16 + 16 * (lane & 1), K / 16 - 16);
+        if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + kWBuf + wave * 4 * kSRow);
+      }
+#pragma unroll
+      for (int i = 0; i < XI; ++i) {                // activations: one row x 1 KB per instruction
+        const int m = (wave + i * kSlabWaves) % M;  // rows beyond M reload an existing row
+        const int xe = min(k0 + 8 * lane, K - 8);
+        lds_dma16(X + (size_t)m * K + xe, b + kWBuf + kSBuf + m * kXRow);
+      }
+    };
+
+    const int tile = wave & 3, sl = wave >> 2;      // row tile, slice (128 k) within each stage
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int rt = tile * 16 + r;                   // this lane's A-operand row in the group
+    const int xm = r < M ? r : 0;
+
+#pragma unroll
+    for (int st = 0; st < kD - 1; ++st)
+      if (st < nst) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      wait_stages<L>(min(kD - 2, nst - 1 - st));   // this wave's loads of stage st are in LDS
+      stage_barrier();                              // ... every wave's; slot (st-1)%kD is free
+      if (st + kD - 1 < nst) issue(st + kD - 1);
+      const uint8_t* b = smem + (st % kD) * kStageBytes;
+      const int k0 = st * kSK;
+      {
+        const int c = 4 * sl + q;                   // 16-byte chunk of the row run
+        const bool ok = k0 + sl * 128 + 32 * q < K;
+        const u32x4 cw = *(const u32x4*)(b + rt * kWRow + 16 * (c ^ r));
+        const uint32_t sw = *(const uint16_t*)(b + kWBuf + rt * kSRow + 8 * sl + 2 * q);
+        const uint8_t* xb = b + kWBuf + kSBuf + xm * kXRow + (sl * 128 + 32 * q) * 2;
+        u32x4 x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = *(const u32x4*)(xb + 16 * j);
+        const float s0 = e4m3_f32_sel<0>(sw), s1 = e4m3_f32_sel<1>(sw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 a = fp4x8_bf16(cw[j], j < 2 ? s0 : s1);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(ok ? x[j] : zero4()), acc, 0, 0, 0);
+        }
+      }
+    }
+    // ---- sum the four slice-partials of each row tile, scale, store
+    __syncthreads();                                // all stages consumed: reuse LDS for the sum
+    float* red = (float*)smem;
+    if (sl != 0)
+      for (int i = 0; i < 4; ++i) red[((sl - 1) * 16 + tile * 4 + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (sl == 0) {
+      const float st_ = *ts;
+      f32x4 s;
+      for (int i = 0; i < 4; ++i)
+        s[i] = (acc[i] + red[(0 * 16 + tile * 4 + i) * 64 + lane] + red[(1 * 16 + tile * 4 + i) * 64 + lane] +
+                red[(2 * 16 + tile * 4 + i) * 64 + lane]) * st_;
+      const int m = lane & 15, n = g0 + tile * 16 + 4 * q;
+      if (m < M) {
+        for (int i = 0; i < 4; ++i) {
+          if (n + i < row_hi) {
+            if (!y_bf16) ((float*)Y)[(size_t)m * N + n + i] = s[i];
+            else ((uint16_t*)Y)[(size_t)m * N + n + i] = (uint16_t)f32_to_bf16_rne(s[i]);
+          }
+        }
+      }
+    }
+    __syncthreads();                                // LDS is reused by the next row group
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2:4, M <= 16, sparse MFMA. One block = 16 weight rows; the 4 waves take contiguous quarters of
+// K in 256-wide slices. Lane group q of a slice takes 16 consecutive groups (64 k): 16 B vals,
+// 8 B meta, 4 B scales, feeding four v_smfmac_f32_16x16x64_bf16 (j = 0..3). For SMFMAC j the
+// instruction's k index kappa = 16q + t maps to k = slice + 64q + 16j + t, so the B lane
+// (col r, group q) needs the activations at slice + 64(q>>1) + 16j + 8(q&1) (8 contiguous) and
+// the same + 128. Same ring pipeline as the dense kernel.
+template <int PW>
 __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict__ X, int M, int N, int K,
                                                      const uint8_t* __restrict__ vals, const uint8_t* __restrict__ meta,
                                                      const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -132,39 +337,51 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
   const int r = lane & 15, q = lane >> 4;
   const int n0 = blockIdx.x * 16;
   const int n = min(n0 + r, N - 1);
-  const bool xv = r < M;
-  const uint16_t* xrow = X + (size_t)(xv ? r : 0) * K;
+  const uint16_t* xrow = X + (size_t)(r < M ? r : 0) * K;
+  const int S = (K + 255) / 256;
+  const int s_lo = (S * wave) / kWaves, s_hi = (S * (wave + 1)) / kWaves;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int nslices = (K + 255) / 256;
-  for (int c = wave; c < nslices; c += kWaves) {
-    const int kbase = c * 256;
-    const int k = kbase + 64 * q;                 // this lane's weight k range [k, k+64)
-    u32x4 vw = zero4();
-    u32x2 mw; mw[0] = 0u; mw[1] = 0u;
-    uint32_t sw = 0;
-    if (k < K) {
-      vw = ld_nt((const u32x4*)(vals + (size_t)n * (K / 4) + k / 4));
-      mw = ld_nt((const u32x2*)(meta + (size_t)n * (K / 8) + k / 8));
-      sw = ld_nt((const uint32_t*)(scales + (size_t)n * (K / 16) + k / 16));
-    }
+
+  struct Slot { u32x4 v; u32x2 m; uint32_t sc; u32x4 x[8]; };
+  auto load_slot = [&](int s) -> Slot {
+    Slot o;
+    const bool ok = s < s_hi && s * 256 + 64 * q < K;
+    const int k = ok ? s * 256 + 64 * q : 0;
+    o.v = ld_nt((const u32x4*)(vals + (size_t)n * (K / 4) + k / 4));
+    o.m = ld_nt((const u32x2*)(meta + (size_t)n * (K / 8) + k / 8));
+    o.sc = ld_nt((const uint32_t*)(scales + (size_t)n * (K / 16) + k / 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      u32x8 b;
-      const int kb = kbase + 64 * (q >> 1) + 16 * j + 8 * (q & 1);
-      u32x4 lo = zero4(), hi = zero4();
-      if (xv && kb < K) lo = *(const u32x4*)(xrow + kb);
-      if (xv && kb + 128 < K) hi = *(const u32x4*)(xrow + kb + 128);
-      b[0] = lo[0]; b[1] = lo[1]; b[2] = lo[2]; b[3] = lo[3];
-      b[4] = hi[0]; b[5] = hi[1]; b[6] = hi[2]; b[7] = hi[3];
-      const float s = j == 0 ? e4m3_f32_sel<0>(sw) : j == 1 ? e4m3_f32_sel<1>(sw)
-                    : j == 2 ? e4m3_f32_sel<2>(sw) : e4m3_f32_sel<3>(sw);
-      const u32x4 a = fp4x8_bf16(vw[j], s);
-      if (j < 2)
-        acc = (j == 0) ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, (int)mw[0], 0, 0)
-                       : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, (int)mw[0], 0, 1);
-      else
-        acc = (j == 2) ? __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, (int)mw[1], 0, 0)
-                       : __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, (int)mw[1], 0, 1);
+      const int kb = s * 256 + 64 * (q >> 1) + 16 * j + 8 * (q & 1);
+      const bool ok_lo = s < s_hi && kb < K, ok_hi = s < s_hi && kb + 128 < K;
+      o.x[2 * j] = *(ok_lo ? (const u32x4*)(xrow + kb) : (const u32x4*)g_zero32);
+      o.x[2 * j + 1] = *(ok_hi ? (const u32x4*)(xrow + kb + 128) : (const u32x4*)g_zero32);
+    }
+    return o;
+  };
+
+  Slot ring[PW];
+#pragma unroll
+  for (int u = 0; u < PW; ++u) ring[u] = load_slot(s_lo + u);
+  for (int s = s_lo; s < s_hi; s += PW) {
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const Slot cur = ring[u];
+      ring[u] = load_slot(s + u + PW);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float sc = j == 0 ? e4m3_f32_sel<0>(cur.sc) : j == 1 ? e4m3_f32_sel<1>(cur.sc)
+                       : j == 2 ? e4m3_f32_sel<2>(cur.sc) : e4m3_f32_sel<3>(cur.sc);
+        const u32x4 a = fp4x8_bf16(cur.v[j], sc);
+        u32x8 b;
+        b[0] = cur.x[2 * j][0]; b[1] = cur.x[2 * j][1]; b[2] = cur.x[2 * j][2]; b[3] = cur.x[2 * j][3];
+        b[4] = cur.x[2 * j + 1][0]; b[5] = cur.x[2 * j + 1][1]; b[6] = cur.x[2 * j + 1][2]; b[7] = cur.x[2 * j + 1][3];
+        const int idx = (int)cur.m[j >> 1];
+        if ((j & 1) == 0)
+          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, idx, 0, 0);
+        else
+          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(b), acc, idx, 0, 1);
+      }
     }
   }
   store_tile16(acc, red, M, N, n0, *ts, Y, y_bf16);
@@ -256,20 +473,45 @@ __global__ __launch_bounds__(256) void k_gemm_valu(const uint16_t* __restrict__ 
 
 }  // namespace
 
+int slab_blocks(int64_t N) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int64_t tiles = (N + 15) / 16;
+  return (int)std::min<int64_t>(cus, tiles);
+}
+
 hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemv_mfma<false>, dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
-                     (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kSlabLds);
+    if (e1 != hipSuccess) return e1;
+    attr_set = true;
+  }
+  if (a.K % 64) {   // the slab kernel loads scale rows as dwords: K/16 must be a multiple of 4
+    hipLaunchKernelGGL((k_gemv_mfma<false, kDenseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
+                       (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+    return hipGetLastError();
+  }
+  const int G = slab_blocks(a.N);
+  const int R = (int)((a.N + G - 1) / G);
+  static_assert(kSlabWaves >= 16, "one activation row load per wave must cover M <= 16");
+  hipLaunchKernelGGL(k_gemv_slab<1>, dim3(G), dim3(kSlabWaves * 64), kSlabLds, s, a.X, (int)a.M, (int)a.N, (int)a.K,
+                     a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_sp24_decomp(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemv_mfma<true>, dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
+  hipLaunchKernelGGL((k_gemv_mfma<true, kDenseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
                      (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_gemv_smfmac, dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
+  hipLaunchKernelGGL((k_gemv_smfmac<kSparseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
                      (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
 }

@@ -3,10 +3,11 @@
 // Quantisation follows "NVFP4 Without FP4 Hardware" (ai-muninn.com), section "Convert BF16 to
 // NVFP4 yourself": a tensor scale s_t = amax / (6 * 448), one E4M3 scale per 16 values along K
 // and E2M1 values; a group of tensors may share s_t (section "The shared global scale").
-// All rounding decisions are exact: they are taken on float64 quotients and products. w has
-// 24 significant bits and s_t * S at most 28, so a quotient that is not exactly on a grid
-// midpoint is further than half a float64 ulp from it, and comparing |w| against
-// midpoint * s_t * S (an exact float64 product) decides the E2M1 code exactly.
+// All rounding decisions are exact. The block scale is decided on a float64 quotient: w has 24
+// significant bits and s_t * S at most 28, so a quotient that is not exactly on a grid midpoint
+// is further than half a float64 ulp from it. Each E2M1 code is decided by comparing |w| with
+// the midpoints times s_t * S (exact float64 products), each rounded once to f32 in the
+// direction that preserves the comparison.
 #include <algorithm>
 
 #include "common.hpp"
@@ -32,7 +33,16 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
   if (!w_bf16) {
     const float* w = (const float*)W;
     size_t n4 = n / 4;
-    for (size_t j = i; j < n4; j += stride) {
+    size_t j = i;
+    for (; j + 3 * stride < n4; j += 4 * stride) {     // four 16-byte loads in flight per thread
+      f32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = ld_nt((const f32x4*)w + j + u * stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
+    }
+    for (; j < n4; j += stride) {
       f32x4 v = ld_nt((const f32x4*)w + j);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
@@ -112,13 +122,19 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16
   const double d = st * e4m3_f64(S);           // exact: <= 24 + 4 significant bits
   uint32_t lo = 0, hi = 0;
   if (d > 0.0) {
-    // E2M1 decision thresholds: ties at 0.25, 1.25, 2.5 and 5 go down, at 0.75, 1.75 and 3.5 up
-    const double t025 = 0.25 * d, t075 = 0.75 * d, t125 = 1.25 * d, t175 = 1.75 * d;
-    const double t25 = 2.5 * d, t35 = 3.5 * d, t5 = 5.0 * d;
+    // E2M1 decision thresholds m * d (exact float64 products): ties at 0.25, 1.25, 2.5 and 5 go
+    // down (code = number of thresholds strictly below |w|), at 0.75, 1.75 and 3.5 up (reached
+    // when |w| equals them). For a float x: x > T <=> x > RD(T), and x >= T <=> x >= RU(T), so
+    // rounding each threshold once to f32 (down, resp. up) keeps every decision exact.
+    const float g025 = __double2float_rd(0.25 * d), g125 = __double2float_rd(1.25 * d);
+    const float g25 = __double2float_rd(2.5 * d), g5 = __double2float_rd(5.0 * d);
+    const float e075 = __double2float_ru(0.75 * d), e175 = __double2float_ru(1.75 * d);
+    const float e35 = __double2float_ru(3.5 * d);
+#pragma unroll
     for (int t = 0; t < 16; ++t) {
-      double a = fabs((double)w[t]);
-      uint32_t c = (uint32_t)(a > t025) + (uint32_t)(a >= t075) + (uint32_t)(a > t125) +
-                   (uint32_t)(a >= t175) + (uint32_t)(a > t25) + (uint32_t)(a >= t35) + (uint32_t)(a > t5);
+      const float a = fabsf(w[t]);
+      uint32_t c = (uint32_t)(a > g025) + (uint32_t)(a >= e075) + (uint32_t)(a > g125) +
+                   (uint32_t)(a >= e175) + (uint32_t)(a > g25) + (uint32_t)(a >= e35) + (uint32_t)(a > g5);
       c |= (__float_as_uint(w[t]) >> 28) & 8u;  // sign bit -> bit 3 (keeps -0 for tiny negatives)
       if (t < 8) lo |= c << (4 * t); else hi |= c << (4 * (t - 8));
     }

@@ -28,28 +28,51 @@ __global__ void k_init_counters(int64_t* bad, int64_t* first) {
   if (first) *first = -1;  // as uint64 this is the largest value, so atomicMin keeps real indices
 }
 
-// One lane per 16 bytes of codes (8 groups); flat group index = byte offset / 2.
+// Block-wide sum (and min) of per-thread values; thread 0 gets the result.
+__device__ __forceinline__ void block_reduce(uint32_t& cnt, uint64_t& mn) {
+  for (int off = 32; off > 0; off >>= 1) {
+    cnt += __shfl_xor(cnt, off, 64);
+    const uint64_t o = __shfl_xor(mn, off, 64);
+    mn = o < mn ? o : mn;
+  }
+  __shared__ uint32_t sc[kThreads / 64];
+  __shared__ uint64_t sm[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) { sc[threadIdx.x >> 6] = cnt; sm[threadIdx.x >> 6] = mn; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kThreads / 64; ++w) { cnt += sc[w]; mn = sm[w] < mn ? sm[w] : mn; }
+  }
+}
+
+// Each thread checks kUnroll chunks of 16 bytes (8 groups each), loaded together; chunks of a
+// block are lane-consecutive so every load instruction is coalesced. Flat group index = byte
+// offset / 2. One atomic per block (only when it found failing groups).
+constexpr int kUnroll = 4;
+
 __global__ __launch_bounds__(kThreads) void k_check(const u32x4* codes, size_t n16, int64_t* bad,
                                                     int64_t* first) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t base = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  u32x4 w[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const size_t i = base + (size_t)u * kThreads;
+    w[u] = ld_nt(codes + (i < n16 ? i : 0));
+  }
   uint32_t nbad = 0;
   uint64_t fb = ~0ull;
-  if (i < n16) {
-    u32x4 w = ld_nt(codes + i);
+#pragma unroll
+  for (int u = kUnroll - 1; u >= 0; --u) {
+    const size_t i = base + (size_t)u * kThreads;
+    if (i >= n16) continue;
     for (int d = 3; d >= 0; --d) {          // descending so the last write is the smallest index
-      uint32_t z = zero_nibbles(w[d]);
-      uint32_t c0 = __builtin_popcount(z & 0xFFFFu), c1 = __builtin_popcount(z >> 16);
+      const uint32_t z = zero_nibbles(w[u][d]);
+      const uint32_t c0 = __builtin_popcount(z & 0xFFFFu), c1 = __builtin_popcount(z >> 16);
       if (c1 < 2) { ++nbad; fb = i * 8 + 2 * d + 1; }
       if (c0 < 2) { ++nbad; fb = i * 8 + 2 * d; }
     }
   }
-  // wave reduction, then one atomic per wave
-  for (int off = 32; off > 0; off >>= 1) {
-    nbad += __shfl_xor(nbad, off, 64);
-    uint64_t o = __shfl_xor(fb, off, 64);
-    fb = o < fb ? o : fb;
-  }
-  if ((threadIdx.x & 63) == 0 && nbad) {
+  block_reduce(nbad, fb);
+  if (threadIdx.x == 0 && nbad) {
     atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
     if (first) atomicMin((unsigned long long*)first, (unsigned long long)fb);
   }
@@ -73,13 +96,21 @@ __device__ __forceinline__ uint32_t compress_group(uint32_t g) {
 
 __global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_t n16, u32x2* vals,
                                                        uint32_t* meta, int64_t* bad) {
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t base = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
+  u32x4 w[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const size_t i = base + (size_t)u * kThreads;
+    w[u] = ld_nt(codes + (i < n16 ? i : 0));
+  }
   uint32_t nbad = 0;
-  if (i < n16) {
-    u32x4 w = ld_nt(codes + i);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const size_t i = base + (size_t)u * kThreads;
+    if (i >= n16) continue;
     uint32_t v[2] = {0u, 0u}, m = 0u;
     for (int d = 0; d < 4; ++d) {
-      uint32_t r0 = compress_group(w[d] & 0xFFFFu), r1 = compress_group(w[d] >> 16);
+      const uint32_t r0 = compress_group(w[u][d] & 0xFFFFu), r1 = compress_group(w[u][d] >> 16);
       nbad += (r0 >> 12) + (r1 >> 12);
       const int g = 2 * d;                   // group index within the 8
       v[g >> 2] |= ((r0 & 0xFFu) << (8 * (g & 3))) | ((r1 & 0xFFu) << (8 * ((g + 1) & 3)));
@@ -89,8 +120,9 @@ __global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_
     vals[i] = vo;
     meta[i] = m;
   }
-  for (int off = 32; off > 0; off >>= 1) nbad += __shfl_xor(nbad, off, 64);
-  if ((threadIdx.x & 63) == 0 && nbad) atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
+  uint64_t unused = 0;
+  block_reduce(nbad, unused);
+  if (threadIdx.x == 0 && nbad) atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
 }
 
 __global__ __launch_bounds__(kThreads) void k_decompress(const u32x2* vals, const uint32_t* meta, size_t n16,
@@ -120,6 +152,9 @@ __global__ __launch_bounds__(kThreads) void k_decompress(const u32x2* vals, cons
 }
 
 inline unsigned grid_for(size_t n) { return (unsigned)((n + kThreads - 1) / kThreads); }
+inline unsigned grid_unrolled(size_t n) {
+  return (unsigned)((n + (size_t)kThreads * kUnroll - 1) / ((size_t)kThreads * kUnroll));
+}
 
 }  // namespace
 
@@ -127,7 +162,7 @@ hipError_t launch_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad
                         hipStream_t s) {
   const size_t n16 = (size_t)N * (size_t)K / 32;  // K % 32 == 0: rows are whole 16-byte chunks
   hipLaunchKernelGGL(k_init_counters, dim3(1), dim3(1), 0, s, bad, first);
-  if (n16) hipLaunchKernelGGL(k_check, dim3(grid_for(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16, bad, first);
+  if (n16) hipLaunchKernelGGL(k_check, dim3(grid_unrolled(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16, bad, first);
   return hipGetLastError();
 }
 
@@ -135,7 +170,7 @@ hipError_t launch_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* 
                            int64_t* bad, hipStream_t s) {
   const size_t n16 = (size_t)N * (size_t)K / 32;
   hipLaunchKernelGGL(k_init_counters, dim3(1), dim3(1), 0, s, bad, (int64_t*)nullptr);
-  if (n16) hipLaunchKernelGGL(k_compress, dim3(grid_for(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16,
+  if (n16) hipLaunchKernelGGL(k_compress, dim3(grid_unrolled(n16)), dim3(kThreads), 0, s, (const u32x4*)codes, n16,
                               (u32x2*)vals, (uint32_t*)meta, bad);
   return hipGetLastError();
 }
