@@ -177,12 +177,8 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const uint16_t* __restrict__ 
 constexpr int kSK = 512;                          // K values per stage
 constexpr int kD = 4;                             // stages in flight
 constexpr int kSlabWaves = 16;                    // 4 per SIMD; wave w: tile w & 3, slice w >> 2
-constexpr int kWRow = kSK / 2;                    // code bytes per row per stage (256)
 constexpr int kSRow = kSK / 16;                   // scale bytes per row per stage (32)
 constexpr int kXRow = kSK * 2 + 16;               // activation bytes per row per stage (+ pad)
-constexpr int kWBuf = 64 * kWRow, kSBuf = 64 * kSRow;
-constexpr int kStageBytes = kWBuf + kSBuf + 16 * kXRow;
-constexpr int kSlabLds = kD * kStageBytes;        // 4 x 35 KB: one block per CU
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -220,53 +216,76 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-template <int XI>   // XI = activation load instructions per wave per stage (M <= kSlabWaves * XI)
+// Stage layout of one ring slot (64 rows of the current row group):
+//   dense: codes [64][256 B] (16-byte chunks XOR-swizzled by row & 15), scales [64][32 B]
+//   2:4:   vals  [64][128 B] (16-byte chunks XOR-swizzled by row & 7), meta [64][64 B],
+//          scales [64][32 B]
+//   both:  activations [16][1024 B + 16 B pad] (rows >= M are not read)
+template <bool SP24>
+struct SlabLayout {
+  static constexpr int kA = SP24 ? kSK / 4 : kSK / 2;   // main weight bytes per row per stage
+  static constexpr int kMeta = SP24 ? kSK / 8 : 0;       // position bytes per row per stage
+  static constexpr int kAOff = 0, kMetaOff = 64 * kA, kScOff = kMetaOff + 64 * kMeta;
+  static constexpr int kXOff = kScOff + 64 * kSRow;
+  static constexpr int kBytes = kXOff + 16 * kXRow;
+};
+
+template <bool SP24>
 __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* __restrict__ X, int M, int N, int K,
-                                                               const uint8_t* __restrict__ codes,
+                                                               const uint8_t* __restrict__ w0,
+                                                               const uint8_t* __restrict__ w1,
                                                                const uint8_t* __restrict__ scales,
                                                                const float* __restrict__ ts, void* __restrict__ Y,
                                                                int y_bf16, int R) {
+  using Lay = SlabLayout<SP24>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  constexpr int kWLoads = 64 * kWRow / 1024 / kSlabWaves;   // 1 KB weight loads per wave per stage
-  constexpr int L = kWLoads + 1 + XI;             // loads per wave per stage: W, scales, X
+  // loads per wave per stage: weights (dense: 1 KB = 4 rows; 2:4: vals 512 B + meta 256 B),
+  // scales (128 B), activations (1 KB): every wave issues exactly L, all unconditionally
+  constexpr int L = SP24 ? 4 : 3;
+  static_assert(kSlabWaves == 16 && 64 * (kSK / 2) / 1024 == kSlabWaves, "one 1 KB weight load per wave per stage");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
   const int nst = (K + kSK - 1) / kSK;
+  const int rowA = SP24 ? K / 4 : K / 2;            // bytes per row of the main weight array
 
   for (int g0 = row_lo; g0 < row_hi; g0 += 64) {
-    // ---- issue the loads of stage st into ring slot st % kD (all lanes, clamped addresses)
     auto issue = [&](int st) {
-      uint8_t* b = smem + (st % kD) * kStageBytes;
+      uint8_t* b = smem + (st % kD) * Lay::kBytes;
       const int k0 = st * kSK;
-#pragma unroll
-      for (int i = 0; i < kWLoads; ++i) {           // weights: 4 rows x 256 B per instruction
-        const int rr = (wave * kWLoads + i) * 4 + (lane >> 4);  // row within the group (0..63)
+      if constexpr (!SP24) {                        // codes: 4 rows x 256 B
+        const int rr = wave * 4 + (lane >> 4);
         const int n = min(g0 + rr, N - 1);
-        const int slot = lane & 15;
-        int cb = k0 / 2 + 16 * (slot ^ (rr & 15));  // swizzled chunk of this row's run
-        cb = min(cb, K / 2 - 16);                   // K tail: clamp (those k meet zero activations)
-        lds_dma16(codes + (size_t)n * (K / 2) + cb, b + (wave * kWLoads + i) * 4 * kWRow);
+        const int cb = min(k0 / 2 + 16 * ((lane & 15) ^ (rr & 15)), rowA - 16);  // K tail: clamp
+        lds_dma16(w0 + (size_t)n * rowA + cb, b + Lay::kAOff + wave * 4 * Lay::kA);
+      } else {                                      // vals: 4 rows x 128 B (lanes 0..31)
+        const int rr = wave * 4 + ((lane >> 3) & 3);
+        const int n = min(g0 + rr, N - 1);
+        const int cb = min(k0 / 4 + 16 * ((lane & 7) ^ (rr & 7)), rowA - 16);
+        if (lane < 32) lds_dma16(w0 + (size_t)n * rowA + cb, b + Lay::kAOff + wave * 4 * Lay::kA);
+        // meta: 4 rows x 64 B (lanes 0..15)
+        const int rm = wave * 4 + ((lane >> 2) & 3);
+        const int nm = min(g0 + rm, N - 1);
+        const int mb = min(k0 / 8 + 16 * (lane & 3), K / 8 - 16);
+        if (lane < 16) lds_dma16(w1 + (size_t)nm * (K / 8) + mb, b + Lay::kMetaOff + wave * 4 * Lay::kMeta);
       }
-      {                                             // scales: 4 rows x 32 B per wave, lanes 0..7
-        static_assert(kSlabWaves * 4 == 64 && kSRow == 32, "scale staging assumes 4 rows of 32 B per wave");
+      {                                             // scales: 4 rows x 32 B (lanes 0..7)
         const int rr = wave * 4 + ((lane >> 1) & 3);
         const int n = min(g0 + rr, N - 1);
         const int sb = min(k0 / 16 + 16 * (lane & 1), K / 16 - 16);
-        if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + kWBuf + wave * 4 * kSRow);
+        if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + Lay::kScOff + wave * 4 * kSRow);
       }
-#pragma unroll
-      for (int i = 0; i < XI; ++i) {                // activations: one row x 1 KB per instruction
-        const int m = (wave + i * kSlabWaves) % M;  // rows beyond M reload an existing row
+      {                                             // activations: row wave % M, 1 KB
+        const int m = wave % M;                     // rows loaded twice hold identical bytes
         const int xe = min(k0 + 8 * lane, K - 8);
-        lds_dma16(X + (size_t)m * K + xe, b + kWBuf + kSBuf + m * kXRow);
+        lds_dma16(X + (size_t)m * K + xe, b + Lay::kXOff + m * kXRow);
       }
     };
 
-    const int tile = wave & 3, sl = wave >> 2;      // row tile, slice (128 k) within each stage
+    const int tile = wave & 3, sl = wave >> 2;      // row tile, 128-k slice within each stage
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int rt = tile * 16 + r;                   // this lane's A-operand row in the group
-    const int xm = r < M ? r : 0;
+    const int xm = r < M ? r : 0;                   // B-operand rows >= M: any row, never stored
 
 #pragma unroll
     for (int st = 0; st < kD - 1; ++st)
@@ -275,14 +294,16 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
       wait_stages<L>(min(kD - 2, nst - 1 - st));   // this wave's loads of stage st are in LDS
       stage_barrier();                              // ... every wave's; slot (st-1)%kD is free
       if (st + kD - 1 < nst) issue(st + kD - 1);
-      const uint8_t* b = smem + (st % kD) * kStageBytes;
+      const uint8_t* b = smem + (st % kD) * Lay::kBytes;
       const int k0 = st * kSK;
-      {
+      const uint8_t* xrow = b + Lay::kXOff + xm * kXRow;
+      if constexpr (!SP24) {
+        // four 16x16x32 MFMAs: lane group q takes 32 consecutive k of the slice
         const int c = 4 * sl + q;                   // 16-byte chunk of the row run
         const bool ok = k0 + sl * 128 + 32 * q < K;
-        const u32x4 cw = *(const u32x4*)(b + rt * kWRow + 16 * (c ^ r));
-        const uint32_t sw = *(const uint16_t*)(b + kWBuf + rt * kSRow + 8 * sl + 2 * q);
-        const uint8_t* xb = b + kWBuf + kSBuf + xm * kXRow + (sl * 128 + 32 * q) * 2;
+        const u32x4 cw = *(const u32x4*)(b + Lay::kAOff + rt * Lay::kA + 16 * (c ^ r));
+        const uint32_t sw = *(const uint16_t*)(b + Lay::kScOff + rt * kSRow + 8 * sl + 2 * q);
+        const uint8_t* xb = xrow + (sl * 128 + 32 * q) * 2;
         u32x4 x[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[j] = *(const u32x4*)(xb + 16 * j);
@@ -291,6 +312,29 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
         for (int j = 0; j < 4; ++j) {
           const u32x4 a = fp4x8_bf16(cw[j], j < 2 ? s0 : s1);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(ok ? x[j] : zero4()), acc, 0, 0, 0);
+        }
+      } else {
+        // two 16x16x64 SMFMACs: SMFMAC jj covers k = slice + 64 jj .. +64; lane group q of the
+        // A operand holds its four groups k = slice + 64 jj + 16 q .. +16 (8 kept values, 16 bits
+        // of positions); the B lane (col r, group q) holds k = slice + 64 jj + 8 q (8 values)
+        // and the same + 32.
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int base = sl * 128 + 64 * jj;
+          const bool ok_a = k0 + base + 16 * q < K;
+          const int sidx = (2 * sl + jj) ^ (rt & 7);
+          const uint32_t vw = *(const uint32_t*)(b + Lay::kAOff + rt * Lay::kA + 16 * sidx + 4 * q);
+          const uint32_t mw = *(const uint16_t*)(b + Lay::kMetaOff + rt * Lay::kMeta + base / 8 + 2 * q);
+          const uint32_t sc = *(const uint8_t*)(b + Lay::kScOff + rt * kSRow + base / 16 + q);
+          u32x4 xl = *(const u32x4*)(xrow + (base + 8 * q) * 2);
+          u32x4 xh = *(const u32x4*)(xrow + (base + 32 + 8 * q) * 2);
+          xl = (k0 + base + 8 * q < K) ? xl : zero4();
+          xh = (k0 + base + 32 + 8 * q < K) ? xh : zero4();
+          const u32x4 a = fp4x8_bf16(ok_a ? vw : 0u, e4m3_f32(sc));
+          u32x8 bx;
+          bx[0] = xl[0]; bx[1] = xl[1]; bx[2] = xl[2]; bx[3] = xl[3];
+          bx[4] = xh[0]; bx[5] = xh[1]; bx[6] = xh[2]; bx[7] = xh[3];
+          acc = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(as_bf16x8(a), as_bf16x16(bx), acc, (int)mw, 0, 0);
         }
       }
     }
@@ -487,11 +531,12 @@ int slab_blocks(int64_t N) {
 hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<1>, hipFuncAttributeMaxDynamicSharedMemorySize, kSlabLds);
+    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        kD * SlabLayout<false>::kBytes);
     if (e1 != hipSuccess) return e1;
     attr_set = true;
   }
-  if (a.K % 64) {   // the slab kernel loads scale rows as dwords: K/16 must be a multiple of 4
+  if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
     hipLaunchKernelGGL((k_gemv_mfma<false, kDenseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
@@ -499,8 +544,8 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   const int G = slab_blocks(a.N);
   const int R = (int)((a.N + G - 1) / G);
   static_assert(kSlabWaves >= 16, "one activation row load per wave must cover M <= 16");
-  hipLaunchKernelGGL(k_gemv_slab<1>, dim3(G), dim3(kSlabWaves * 64), kSlabLds, s, a.X, (int)a.M, (int)a.N, (int)a.K,
-                     a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
+  hipLaunchKernelGGL(k_gemv_slab<false>, dim3(G), dim3(kSlabWaves * 64), kD * SlabLayout<false>::kBytes, s, a.X,
+                     (int)a.M, (int)a.N, (int)a.K, a.w0, (const uint8_t*)nullptr, a.scales, a.ts, a.Y, a.y_bf16, R);
   return hipGetLastError();
 }
 
@@ -511,8 +556,22 @@ hipError_t launch_gemv_sp24_decomp(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemv_smfmac<kSparseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X, (int)a.M,
-                     (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        kD * SlabLayout<true>::kBytes);
+    if (e1 != hipSuccess) return e1;
+    attr_set = true;
+  }
+  if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
+    hipLaunchKernelGGL((k_gemv_smfmac<kSparseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
+                       (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+    return hipGetLastError();
+  }
+  const int G = slab_blocks(a.N);
+  const int R = (int)((a.N + G - 1) / G);
+  hipLaunchKernelGGL(k_gemv_slab<true>, dim3(G), dim3(kSlabWaves * 64), kD * SlabLayout<true>::kBytes, s, a.X,
+                     (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
   return hipGetLastError();
 }
 
