@@ -34,10 +34,13 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 #define REQUIRE_OPT_PTR(p) \
   do { if ((p) && !aligned16(p)) return fail(SSN_E_ALIGN, "%s: argument '%s' is not 16-byte aligned", fn, #p); } while (0)
 
+// rows (N, M) are indexed with 32-bit ints inside the kernels, tile origins included
+constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1024;
+
 int check_nk(const char* fn, int64_t N, int64_t K) {
   if (N < 0 || K < 0) return fail(SSN_E_SHAPE, "%s: negative size (N=%lld, K=%lld)", fn, (long long)N, (long long)K);
   if (K % 32) return fail(SSN_E_SHAPE, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
-  if (N > (int64_t)1 << 31 || K > (int64_t)1 << 30)
+  if (N > kMaxRows || K > (int64_t)1 << 30)
     return fail(SSN_E_SHAPE, "%s: size too large (N=%lld, K=%lld)", fn, (long long)N, (long long)K);
   return SSN_OK;
 }
@@ -137,7 +140,7 @@ int gemm_common(const char* fn, const uint16_t* X, int64_t M, int64_t N, int64_t
                 int algo, int* algo_used, void* stream) {
   int st;
   if (M < 0) return fail(SSN_E_SHAPE, "%s: negative M=%lld", fn, (long long)M);
-  if (M > (int64_t)1 << 31) return fail(SSN_E_SHAPE, "%s: M=%lld too large", fn, (long long)M);
+  if (M > kMaxRows) return fail(SSN_E_SHAPE, "%s: M=%lld too large", fn, (long long)M);
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, y_dtype, "y_dtype"))) return st;
   if (algo < SSN_ALGO_AUTO || algo > SSN_ALGO_DECOMPRESS_MFMA || algo == 4)
@@ -151,27 +154,27 @@ int gemm_common(const char* fn, const uint16_t* X, int64_t M, int64_t N, int64_t
   REQUIRE_PTR(X); REQUIRE_PTR(w0); REQUIRE_PTR(scales); REQUIRE_PTR(ts); REQUIRE_PTR(Y);
   if (sp24) REQUIRE_PTR(w1);
 
+  // M <= 16: decode-shaped kernels (weights streamed once); otherwise 256x256 tiles
   const bool skinny = M <= 16;
   int chosen = algo;
   if (algo == SSN_ALGO_AUTO) {
-    if (!sp24) chosen = skinny ? SSN_ALGO_MFMA : SSN_ALGO_VALU;
-    else chosen = (skinny && K % 64 == 0) ? SSN_ALGO_SMFMAC : skinny ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_VALU;
+    if (!sp24) chosen = SSN_ALGO_MFMA;
+    else chosen = (skinny && K % 64) ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_SMFMAC;
   }
   // explicit choices that do not apply to this shape are refused, never replaced
-  if (chosen == SSN_ALGO_SMFMAC && K % 64)
-    return fail(SSN_E_ALGO, "%s: SMFMAC needs K %% 64 == 0 (K=%lld)", fn, (long long)K);
-  if ((chosen == SSN_ALGO_MFMA || chosen == SSN_ALGO_SMFMAC || chosen == SSN_ALGO_DECOMPRESS_MFMA) && !skinny)
-    return fail(SSN_E_ALGO, "%s: algorithm %d is implemented for M <= 16 only in this build (M=%lld)", fn,
-                chosen, (long long)M);
+  if (chosen == SSN_ALGO_SMFMAC && skinny && K % 64)
+    return fail(SSN_E_ALGO, "%s: SMFMAC for M <= 16 needs K %% 64 == 0 (K=%lld)", fn, (long long)K);
 
   ssn::GemmArgs a{X, M, N, K, w0, w1, scales, ts, Y, y_dtype == SSN_BF16};
   hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
   switch (chosen) {
     case SSN_ALGO_VALU: e = sp24 ? ssn::launch_gemm_sp24_valu(a, s) : ssn::launch_gemm_dense_valu(a, s); break;
-    case SSN_ALGO_MFMA: e = ssn::launch_gemv_dense_mfma(a, s); break;
-    case SSN_ALGO_SMFMAC: e = ssn::launch_gemv_sp24_smfmac(a, s); break;
-    case SSN_ALGO_DECOMPRESS_MFMA: e = ssn::launch_gemv_sp24_decomp(a, s); break;
+    case SSN_ALGO_MFMA: e = skinny ? ssn::launch_gemv_dense_mfma(a, s) : ssn::launch_gemm_dense_mfma(a, s); break;
+    case SSN_ALGO_SMFMAC: e = skinny ? ssn::launch_gemv_sp24_smfmac(a, s) : ssn::launch_gemm_sp24_smfmac(a, s); break;
+    case SSN_ALGO_DECOMPRESS_MFMA:
+      e = skinny ? ssn::launch_gemv_sp24_decomp(a, s) : ssn::launch_gemm_sp24_decomp(a, s);
+      break;
   }
   if (algo_used) *algo_used = chosen;
   return hip_status(e, fn);

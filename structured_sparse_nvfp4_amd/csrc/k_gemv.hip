@@ -21,6 +21,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "pipeline.hpp"
 
 namespace ssn {
 namespace {
@@ -179,32 +180,6 @@ constexpr int kD = 4;                             // stages in flight
 constexpr int kSlabWaves = 16;                    // 4 per SIMD; wave w: tile w & 3, slice w >> 2
 constexpr int kSRow = kSK / 16;                   // scale bytes per row per stage (32)
 constexpr int kXRow = kSK * 2 + 16;               // activation bytes per row per stage (+ pad)
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// Workgroup barrier without the memory fence of __syncthreads(): the fence would make the
-// compiler drain every outstanding load (vmcnt(0)), including the stages still meant to be in
-// flight. Visibility of a stage is established by the explicit vmcnt wait before this barrier;
-// the empty asm statements keep the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int L>   // wait until at most `ahead` stages of L loads each are still in flight
 __device__ __forceinline__ void wait_stages(int ahead) {

@@ -39,5 +39,8 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s);    // M <=
 hipError_t launch_gemv_sp24_decomp(const GemmArgs& a, hipStream_t s);    // M <= 16
 hipError_t launch_gemm_dense_valu(const GemmArgs& a, hipStream_t s);     // any M
 hipError_t launch_gemm_sp24_valu(const GemmArgs& a, hipStream_t s);      // any M (skip-and-gather)
+hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s);     // 256x256 tiles, any M
+hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s);    // 256x256 tiles, any M
+hipError_t launch_gemm_sp24_smfmac(const GemmArgs& a, hipStream_t s);    // 256x256 tiles, any M
 
 }  // namespace ssn

@@ -24,21 +24,17 @@ def _problem(M, N, K, seed, prune):
     return x, c, s, st
 
 
-def _skinny_only(algo, M):
-    return algo in (ssn.ALGO_MFMA, ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA) and M > 16
-
-
-# the small configuration: X [16, 512], W [256, 512], plus ragged and multi-slice shapes
+# the small configuration: X [16, 512], W [256, 512], plus ragged and multi-slice shapes; the
+# M > 16 shapes run the 256 x 256 tiles: several tiles in M and N, ragged edges, K tails of 32
 DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
-               (17, 40, 64), (40, 33, 128)]
+               (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
+               (64, 1000, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
 @pytest.mark.parametrize("algo", DENSE_ALGOS)
 @pytest.mark.parametrize("prune", [False, True])
 def test_dense(M, N, K, algo, prune):
-    if _skinny_only(algo, M):
-        pytest.skip("MFMA dense path covers M <= 16 in this build")
     x, c, s, st = _problem(M, N, K, seed=M * 7 + N + K, prune=prune)
     Y, B = gemm.gemm_dense(x, c, s, st)
     g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
@@ -47,16 +43,15 @@ def test_dense(M, N, K, algo, prune):
 
 
 SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64, 1024), (4, 48, 4096),
-              (17, 40, 64), (40, 33, 128)]
+              (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
+              (64, 1000, 2048)]
 
 
 @pytest.mark.parametrize("M,N,K", SP24_CASES)
 @pytest.mark.parametrize("algo", SP24_ALGOS)
 def test_sp24(M, N, K, algo):
-    if _skinny_only(algo, M):
-        pytest.skip("matrix-core 2:4 paths cover M <= 16 in this build")
-    if algo == ssn.ALGO_SMFMAC and K % 64:
-        pytest.skip("SMFMAC needs K % 64 == 0 (refusal is tested on the CPU)")
+    if algo == ssn.ALGO_SMFMAC and K % 64 and M <= 16:
+        pytest.skip("SMFMAC for M <= 16 needs K % 64 == 0 (refusal is tested on the CPU)")
     x, c, s, st = _problem(M, N, K, seed=M * 5 + N + K, prune=True)
     vals, meta, bad = sp24.compress(c)
     assert bad == 0
@@ -67,9 +62,9 @@ def test_sp24(M, N, K, algo):
     assert_within_bound(y_host(g), Y, B, what=f"sp24 algo={used}")
 
 
+@pytest.mark.parametrize("M,N,K", [(8, 96, 512), (270, 300, 320)])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_bf16_output(sparse):
-    M, N, K = 8, 96, 512
+def test_bf16_output(sparse, M, N, K):
     x, c, s, st = _problem(M, N, K, seed=21, prune=sparse)
     ts = dev(np.array([st], np.float32))
     if sparse:
@@ -109,6 +104,37 @@ def test_one_hot_rows_extract_weights_sp24(algo):
     g, _ = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)), algo=algo)
     want = quant.dequantize(sp24.decompress(vals, meta), s, st)[:, ks].T.astype(np.float32)
     assert np.array_equal(y_host(g).astype(np.float32), want)
+
+
+def _one_hot_tiled(M, K, seed):
+    # row m of X is the unit vector e_{k(m)}; k(m) sweeps every position of a 64-wide stage and
+    # both K stages, so each (row block, lane half, MFMA step) operand slot is exercised
+    ks = (np.arange(M) * 37 + 5) % K
+    x = np.zeros((M, K), np.float32)
+    x[np.arange(M), ks] = 1.0
+    return synth.f32_to_bf16_bits(x), ks
+
+
+@pytest.mark.parametrize("algo", [ssn.ALGO_MFMA])
+def test_one_hot_rows_extract_weights_dense_tiled(algo):
+    M, N, K = 300, 290, 160
+    xb, ks = _one_hot_tiled(M, K, 0)
+    _, c, s, st = _problem(1, N, K, seed=6, prune=False)
+    g, used = ssn.gemm_nvfp4_dense(x_dev(xb), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
+    want = quant.dequantize(c, s, st)[:, ks].T.astype(np.float32)
+    assert used == algo and np.array_equal(y_host(g).astype(np.float32), want)
+
+
+@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA])
+def test_one_hot_rows_extract_weights_sp24_tiled(algo):
+    M, N, K = 300, 290, 160
+    xb, ks = _one_hot_tiled(M, K, 1)
+    _, c, s, st = _problem(1, N, K, seed=7, prune=True)
+    vals, meta, _ = sp24.compress(c)
+    g, used = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)),
+                                  algo=algo)
+    want = quant.dequantize(sp24.decompress(vals, meta), s, st)[:, ks].T.astype(np.float32)
+    assert used == algo and np.array_equal(y_host(g).astype(np.float32), want)
 
 
 def test_empty_and_degenerate():

@@ -1,0 +1,100 @@
+"""The square (4096 x 4096 x 4096, f32 out) and prefill (X [8192, 5120], W [27648, 5120] with 1%
+of entries x20 before pruning, bf16 out) products at full size, launched as the benchmark
+launches them, checked against the oracle on sampled outputs (rows and columns that straddle
+tile edges) and by properties that hold at any size."""
+import numpy as np
+import pytest
+import torch
+
+import structured_sparse_nvfp4_amd as ssn
+import synth
+from oracle import gemm, quant, sp24
+from tests.gpu_util import assert_within_bound, dev, host, x_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(n, extra):
+    s = {0, 1, 31, 32, 255, 256, 257, n // 2, n - 257, n - 256, n - 1} | set(extra)
+    return np.array(sorted(i for i in s if 0 <= i < n))
+
+
+def _setup(M, N, K, w):
+    x = synth.activations(M, K)
+    W = dev(w)
+    codes, scales, ts = ssn.nvfp4_quantize(W)
+    Wp = ssn.sp24_prune(W)
+    pc, ps, pts = ssn.nvfp4_quantize(Wp)
+    vals, meta, bad = ssn.sp24_compress(pc)
+    del W, Wp, pc
+    torch.cuda.synchronize()
+    return dict(x=x, X=x_dev(x), codes=codes, scales=scales, ts=ts, vals=vals, meta=meta, ps=ps, pts=pts,
+                bad=bad, st=quant.tensor_scale(w), w=w)
+
+
+@pytest.fixture(scope="module")
+def square():
+    M = N = K = 4096
+    d = _setup(M, N, K, synth.weights(N, K))
+    d.update(M=M, N=N, K=K, ms=_sample(M, [1000, 3001]), ns=_sample(N, [777, 2222]), out="f32")
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+@pytest.fixture(scope="module")
+def prefill():
+    M, N, K = 8192, 27648, 5120
+    w = synth.weight_rows_with_outliers(N, K, 0, N, p=0.01, mult=20.0)
+    d = _setup(M, N, K, w)
+    d.update(M=M, N=N, K=K, ms=_sample(M, [5000]), ns=_sample(N, [13824, 20000]), out="bf16")
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+def _check(d, sparse, algo):
+    x, ms, ns = d["x"], d["ms"], d["ns"]
+    ydt = torch.bfloat16 if d["out"] == "bf16" else torch.float32
+    # pruning keeps the largest magnitude of every group, so the pruned tensor's amax (and scale)
+    # equals the unpruned one's
+    assert host(d["ts"])[0] == d["st"] and host(d["pts"])[0] == d["st"]
+    if sparse:
+        assert int(host(d["bad"])[0]) == 0
+        y, used = ssn.gemm_nvfp4_sp24(d["X"], d["vals"], d["meta"], d["ps"], d["pts"], y_dtype=ydt, algo=algo)
+        c, s, _ = quant.quantize(sp24.prune24(d["w"][ns]), tensor_scale_in=d["st"])
+        v, m, nb = sp24.compress(c)
+        assert nb == 0
+        Y, B = gemm.gemm_sp24(x[ms], v, m, s, d["st"])
+    else:
+        y, used = ssn.gemm_nvfp4_dense(d["X"], d["codes"], d["scales"], d["ts"], y_dtype=ydt, algo=algo)
+        c, s, _ = quant.quantize(d["w"][ns], tensor_scale_in=d["st"])
+        Y, B = gemm.gemm_dense(x[ms], c, s, d["st"])
+    assert used == algo
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(y).all())
+    got = y[torch.from_numpy(ms).cuda()][:, torch.from_numpy(ns).cuda()].float().cpu().numpy().astype(np.float64)
+    assert_within_bound(got, Y, B, out=d["out"], what=f"{'sp24' if sparse else 'dense'} algo={used}")
+    return y
+
+
+@pytest.mark.parametrize("sparse,algo", [(False, ssn.ALGO_MFMA), (True, ssn.ALGO_SMFMAC),
+                                         (True, ssn.ALGO_DECOMPRESS_MFMA)])
+def test_square(square, sparse, algo):
+    _check(square, sparse, algo)
+
+
+@pytest.mark.parametrize("sparse,algo", [(False, ssn.ALGO_MFMA), (True, ssn.ALGO_SMFMAC),
+                                         (True, ssn.ALGO_DECOMPRESS_MFMA)])
+def test_prefill(prefill, sparse, algo):
+    _check(prefill, sparse, algo)
+
+
+def test_square_sparse_variants_agree(square):
+    # the two 2:4 matrix-core paths sum the same exact products in different orders
+    d = square
+    a, _ = ssn.gemm_nvfp4_sp24(d["X"], d["vals"], d["meta"], d["ps"], d["pts"], algo=ssn.ALGO_SMFMAC)
+    b, _ = ssn.gemm_nvfp4_sp24(d["X"], d["vals"], d["meta"], d["ps"], d["pts"], algo=ssn.ALGO_DECOMPRESS_MFMA)
+    torch.cuda.synchronize()
+    scale = float(a.abs().max())
+    assert float((a - b).abs().max()) <= 1e-3 * scale
