@@ -67,15 +67,16 @@ enum { SSN_F32 = 0, SSN_BF16 = 1 };
 
 /* GEMM algorithms. Each call writes the one it ran to *algo_used (host int, nullable).
  * The matrix-core algorithms run decode-shaped kernels for M <= 16 (weights streamed once
- * through LDS) and 256 x 256 output tiles for larger M. AUTO picks MFMA for dense weights and
- * SMFMAC for 2:4 weights (DECOMPRESS_MFMA when M <= 16 and K % 64 != 0). */
+ * through LDS) and 256 x 256 output tiles for larger M; the tiles need K % 64 == 0. AUTO picks
+ * MFMA for dense weights and SMFMAC for 2:4 weights, DECOMPRESS_MFMA when M <= 16 and
+ * K % 64 != 0, and VALU when M > 16 and K % 64 != 0. */
 enum {
   SSN_ALGO_AUTO = 0,             /* let the library choose; the choice is reported */
   SSN_ALGO_VALU = 1,             /* plain vector-ALU kernel, any K % 32 == 0 (dense: FMA per
                                     weight; 2:4: skip-and-gather of x at the stored positions) */
   SSN_ALGO_MFMA = 2,             /* dense: bf16 MFMA on weights decoded in registers */
   SSN_ALGO_SMFMAC = 3,           /* 2:4 only: sparse MFMA (v_smfmac) with the compressed weights
-                                    as the sparse operand; needs K % 64 == 0 when M <= 16 */
+                                    as the sparse operand; needs K % 64 == 0 */
   SSN_ALGO_DECOMPRESS_MFMA = 5   /* 2:4 only: expand vals+meta to a dense tile and run the
                                     dense bf16 MFMA (computes on the zeros) */
 };

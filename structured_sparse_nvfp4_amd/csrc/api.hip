@@ -154,16 +154,21 @@ int gemm_common(const char* fn, const uint16_t* X, int64_t M, int64_t N, int64_t
   REQUIRE_PTR(X); REQUIRE_PTR(w0); REQUIRE_PTR(scales); REQUIRE_PTR(ts); REQUIRE_PTR(Y);
   if (sp24) REQUIRE_PTR(w1);
 
-  // M <= 16: decode-shaped kernels (weights streamed once); otherwise 256x256 tiles
+  // M <= 16: decode-shaped kernels (weights streamed once); otherwise 256x256 tiles, which
+  // take whole 64-wide K stages
   const bool skinny = M <= 16;
   int chosen = algo;
   if (algo == SSN_ALGO_AUTO) {
-    if (!sp24) chosen = SSN_ALGO_MFMA;
+    if (!skinny && K % 64) chosen = SSN_ALGO_VALU;
+    else if (!sp24) chosen = SSN_ALGO_MFMA;
     else chosen = (skinny && K % 64) ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_SMFMAC;
   }
   // explicit choices that do not apply to this shape are refused, never replaced
   if (chosen == SSN_ALGO_SMFMAC && skinny && K % 64)
     return fail(SSN_E_ALGO, "%s: SMFMAC for M <= 16 needs K %% 64 == 0 (K=%lld)", fn, (long long)K);
+  if (chosen != SSN_ALGO_VALU && !skinny && K % 64)
+    return fail(SSN_E_ALGO, "%s: matrix-core algorithm %d for M > 16 needs K %% 64 == 0 (K=%lld)", fn, chosen,
+                (long long)K);
 
   ssn::GemmArgs a{X, M, N, K, w0, w1, scales, ts, Y, y_dtype == SSN_BF16};
   hipStream_t s = as_stream(stream);

@@ -3,13 +3,15 @@
 // The square and prefill shapes are compute-bound ("NVFP4 Without FP4 Hardware", ai-muninn.com,
 // section on prefill: unpacking is extra work on top of the dense product), so the design keeps
 // the matrix cores fed and spends as little vector-ALU time per weight as possible:
-//  - the activation tile [256 rows][64 k] bf16 is copied HBM -> LDS by the direct-to-LDS loads
-//    (three stages in flight), 16-byte chunks XOR-swizzled so that matrix-operand reads are free
-//    of bank conflicts;
-//  - every wave decodes its own weights straight from global memory into matrix operands: a
-//    weight is decoded once per output tile and never written back to LDS.
+//  - every operand of a 64-wide K stage (activation tile [256][64] bf16 and the 4-bit weights
+//    of the 256 output columns with their scales) is copied HBM -> LDS by the direct-to-LDS
+//    loads, three stages in flight; the kernel waits for them with explicit vmcnt counts, and
+//    no register load is left in the loop for the compiler to wait on conservatively;
+//  - 16-byte chunks are XOR-swizzled so that matrix-operand reads are free of bank conflicts;
+//  - every wave decodes its own weights from LDS into matrix operands in registers: a weight is
+//    decoded once per output tile and never written back.
 //
-// Dense and 2:4-decompressed products (v_mfma_f32_32x32x16_bf16, activations = A, weights = B):
+// Dense and 2:4-expanded products (v_mfma_f32_32x32x16_bf16, activations = A, weights = B):
 //   wave w owns all 256 rows x columns [64w, 64w + 64) of the tile: 8 x 2 blocks of 32 x 32.
 //   Lane l (r = l % 32, h = l / 32) feeds k = 8h..8h+7 of each 16-wide MFMA step. The kernel
 //   maps MFMA step s of a 64-wide stage to k = 32h + 8s + j, so one lane's weights for a whole
@@ -21,6 +23,10 @@
 //   8 contiguous vals bytes, 4 meta bytes and 2 scale bytes. The compressed layout of this
 //   library is the SMFMAC A operand and index operand as stored ("NVFP4 vs 2:4 sparse",
 //   robertz.co, section "What 2:4 actually is": two kept values plus a 2-bit index each).
+//
+// K must be a multiple of 64 (whole stages; every per-row weight piece is then aligned).
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
@@ -29,14 +35,31 @@ namespace ssn {
 namespace {
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;   // output tile and K-stage
-constexpr int kStages = 3;                       // activation stages resident in LDS
-constexpr int kXStage = kTM * kTK * 2;           // 32 KiB
+constexpr int kStages = 3;                       // stages resident in LDS
 constexpr int kThreads = 256;
 
-// zero bytes that activation chunks and weight words beyond K are read from
-__device__ __attribute__((aligned(16))) uint32_t g_zero_k[4];
+enum WForm { kDense = 0, kSp24 = 1 };
 
-enum WForm { kDense = 0, kSp24Expand = 1 };
+// Chunk swizzle of the activation tile: eight consecutive rows (one 128-byte bank sweep each)
+// and the eight same-parity rows of any sixteen get distinct chunks, so 16-byte operand reads
+// of 8 or 16 lanes (rows r..r+7 or r..r+15, one chunk each) never share a bank.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// One LDS ring slot (bytes). Rows are tile-local (0..255).
+//   X      [256][128 B]  activation k-chunk c of row r at physical chunk c ^ swz(r)
+//   dense: codes [256][32 B]  half h of row r at physical half h ^ ((r >> 3) & 1)
+//   2:4:   vals  [256][16 B], meta [256][8 B]
+//   scales [256][4 B]   (the four 16-blocks of the stage)
+template <int WF>
+struct Slot {
+  static constexpr int kX = 0;
+  static constexpr int kW = kTM * kTK * 2;
+  static constexpr int kMeta = WF == kDense ? 0 : kW + kTN * 16;
+  static constexpr int kSc = WF == kDense ? kW + kTN * 32 : kMeta + kTN * 8;
+  static constexpr int kBytes = kSc + kTN * 4;
+  // direct loads per wave per stage: activations 8, weights (dense 2 / 2:4 1 + 2), scales 1
+  static constexpr int kLoads = WF == kDense ? 8 + 2 + 1 : 8 + 1 + 2 + 1;
+};
 
 // ---- tile scheduling: consecutive logical tiles share an XCD (workgroups are dealt to the
 // eight XCDs round-robin), and go down GROUP tile rows before moving right, so the
@@ -55,34 +78,91 @@ __device__ __forceinline__ void tile_of(int b, int total, int tiles_m, int tiles
   tn = tin / gsize;
 }
 
-// ---- activation stage: rows [m0, m0+256) x k [k0, k0+64) -> LDS, row r at r * 128 bytes,
-// logical 16-byte chunk c at physical chunk c ^ ((r >> 1) & 7). Eight 1 KiB direct loads per
-// wave; lane l of load i writes tile row 8 * (8 * wave + i) + l / 8, physical chunk l % 8.
-template <bool FULL>   // FULL: the whole stage lies inside K (no zero-block select needed)
-__device__ __forceinline__ void issue_x(const uint16_t* __restrict__ X, int M, int K, int m0, int k0,
-                                        char* slot, int wave, int lane) {
-  const int p = lane & 7;
+// ---- one K stage of operands -> LDS slot. Per-lane byte offsets are computed once; each
+// stage only moves the wave-uniform base pointers, so the loads take a scalar base plus a
+// 32-bit vector offset. Rows beyond M or N are clamped to the last row (their results are not
+// stored). Every boundary issues the same loads (a stage past the end re-reads the last one
+// into a free slot), so the loads a wait must cover are a fixed count.
+template <int WF>
+struct StageSrc {
+  const char* xb;   // activations of rows m0.. at k = 0
+  const char* wb;   // codes (dense) or vals (2:4) of rows n0.. at k = 0
+  const char* mb;   // meta of rows n0.. (2:4)
+  const char* sb;   // scales of rows n0..
+  uint32_t xo[8], wo[2], mo[2], so;
+};
+
+template <int WF>
+__device__ __forceinline__ StageSrc<WF> stage_src(const uint16_t* X, const uint8_t* w0, const uint8_t* w1,
+                                                  const uint8_t* scales, int M, int N, int K, int m0, int n0,
+                                                  int wave, int lane) {
+  StageSrc<WF> o;
+  o.xb = (const char*)(X + (size_t)m0 * K);
+  o.wb = (const char*)w0 + (size_t)n0 * (WF == kDense ? K / 2 : K / 4);
+  o.mb = WF == kDense ? nullptr : (const char*)w1 + (size_t)n0 * (K / 8);
+  o.sb = (const char*)scales + (size_t)n0 * (K / 16);
+  // activations: load i of the wave writes row 8 (8 wave + i) + l / 8, physical chunk l % 8
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = 8 * (8 * wave + i) + (lane >> 3);
-    const int c = p ^ ((r >> 1) & 7);
-    const int k = k0 + 8 * c;
-    const int m = min(m0 + r, M - 1);
-    const void* src = (FULL || k < K) ? (const void*)(X + (size_t)m * K + k) : (const void*)g_zero_k;
-    lds_dma16(src, slot + (8 * wave + i) * 1024);
+    const int c = (lane & 7) ^ swz(r);
+    o.xo[i] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2u;
+  }
+  if constexpr (WF == kDense) {
+    // codes: load i writes row 32 (2 wave + i) + l / 2, physical half l % 2
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 32 * (2 * wave + i) + (lane >> 1);
+      const int hl = (lane & 1) ^ ((r >> 3) & 1);
+      o.wo[i] = (uint32_t)(min(n0 + r, N - 1) - n0) * (uint32_t)(K / 2) + 16u * hl;
+      o.mo[i] = 0u;
+    }
+  } else {
+    // vals: one load of row 64 wave + l (16 B); meta: load i writes row 32 (2 wave + i) + l / 2
+    o.wo[0] = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) - n0) * (uint32_t)(K / 4);
+    o.wo[1] = 0u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 32 * (2 * wave + i) + (lane >> 1);
+      o.mo[i] = (uint32_t)(min(n0 + r, N - 1) - n0) * (uint32_t)(K / 8) + 4u * (lane & 1);
+    }
+  }
+  o.so = (uint32_t)(min(n0 + 64 * wave + lane, N - 1) - n0) * (uint32_t)(K / 16);
+  return o;
+}
+
+template <int WF>
+__device__ __forceinline__ void issue_stage(const StageSrc<WF>& g, int st, char* slot, int wave) {
+  using L = Slot<WF>;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) lds_dma16(g.xb + st * (kTK * 2) + g.xo[i], slot + L::kX + (8 * wave + i) * 1024);
+  if constexpr (WF == kDense) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(g.wb + st * (kTK / 2) + g.wo[i], slot + L::kW + (2 * wave + i) * 1024);
+  } else {
+    lds_dma16(g.wb + st * (kTK / 4) + g.wo[0], slot + L::kW + wave * 1024);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma4(g.mb + st * (kTK / 8) + g.mo[i], slot + L::kMeta + (2 * wave + i) * 256);
+  }
+  lds_dma4(g.sb + st * (kTK / 16) + g.so, slot + L::kSc + wave * 256);
+}
+
+// Scheduling hint for the region just issued: LEAD matrix instructions first, then GROUPS of
+// (one matrix instruction, VALU vector-ALU instructions), so the weight decode fills the
+// matrix pipe's shadow instead of running ahead of or behind it.
+template <int LEAD, int GROUPS, int VALU>
+__device__ __forceinline__ void interleave_mfma_valu() {
+  __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
+#pragma unroll
+  for (int i = 0; i < GROUPS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
 }
 
-__device__ __forceinline__ void issue_x_stage(const uint16_t* __restrict__ X, int M, int K, int m0, int st,
-                                              char* lds, int wave, int lane) {
-  char* slot = lds + (st % kStages) * kXStage;
-  if ((st + 1) * kTK <= K) issue_x<true>(X, M, K, m0, st * kTK, slot, wave, lane);
-  else issue_x<false>(X, M, K, m0, st * kTK, slot, wave, lane);
-}
-
-// 16-byte activation chunk `c` of tile row r (bits 1..3 of r given as `sw`)
-__device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c, int sw) {
-  return *(const u32x4*)(slot + r * 128 + 16 * (c ^ sw));
+// 16-byte activation chunk `c` of tile row r
+__device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c) {
+  return *(const u32x4*)(slot + r * 128 + 16 * (c ^ swz(r)));
 }
 
 // Two kept codes (byte vb) at positions (nib & 3, nib >> 2) of a group of four nibbles.
@@ -90,56 +170,29 @@ __device__ __forceinline__ uint32_t expand_group(uint32_t vb, uint32_t nib) {
   return ((vb & 0xFu) << ((nib & 3u) << 2)) | (((vb >> 4) & 0xFu) << ((nib >> 2) << 2));
 }
 
-// Weights of one lane for one stage (dense: 32 codes; 2:4: 8 groups) and its two scale bytes.
-struct WStage {
-  u32x4 c;        // dense codes, or (vals word 0, vals word 1, meta word, -) for 2:4
-  uint32_t s;     // two E4M3 scale bytes (16-blocks 2h, 2h + 1 of the stage)
-};
-
-template <int WF, bool FULL>
-__device__ __forceinline__ WStage load_w(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
-                                         const uint8_t* __restrict__ scales, int n, int K, int kk) {
-  // kk = first k of this lane's 32-wide slice; a slice at or beyond K reads the zero block
-  const bool ok = FULL || kk < K;
-  WStage o;
-  if constexpr (WF == kDense) {
-    const u32x4* pc = ok ? (const u32x4*)(w0 + (size_t)n * (K / 2) + kk / 2) : (const u32x4*)g_zero_k;
-    o.c = *pc;
-  } else {
-    const u32x2* pv = ok ? (const u32x2*)(w0 + (size_t)n * (K / 4) + kk / 4) : (const u32x2*)g_zero_k;
-    const uint32_t* pm = ok ? (const uint32_t*)(w1 + (size_t)n * (K / 8) + kk / 8) : (const uint32_t*)g_zero_k;
-    const u32x2 v = *pv;
-    o.c[0] = v[0]; o.c[1] = v[1]; o.c[2] = *pm; o.c[3] = 0u;
-  }
-  const uint16_t* ps = ok ? (const uint16_t*)(scales + (size_t)n * (K / 16) + kk / 16) : (const uint16_t*)g_zero_k;
-  o.s = *ps;
-  return o;
-}
-
-// Codes word of MFMA step s (8 codes, k = 8s..8s+7 of the lane's slice)
+// One lane's weights for one stage: dense 32 codes, or 2:4 (vals word 0, vals word 1, meta)
 template <int WF>
-__device__ __forceinline__ uint32_t codes_step(const WStage& w, int s) {
+__device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
+  using L = Slot<WF>;
   if constexpr (WF == kDense) {
-    return w.c[s];
+    return *(const u32x4*)(slot + L::kW + r * 32 + 16 * (h ^ ((r >> 3) & 1)));
   } else {
-    const uint32_t vb = w.c[s >> 1] >> (16 * (s & 1));        // groups 2s, 2s+1: two vals bytes
-    const uint32_t nb = w.c[2] >> (8 * s);                    // their two position nibbles
-    return expand_group(vb & 0xFFu, nb & 0xFu) | (expand_group((vb >> 8) & 0xFFu, (nb >> 4) & 0xFu) << 16);
+    const u32x2 v = *(const u32x2*)(slot + L::kW + r * 16 + 8 * h);
+    u32x4 o;
+    o[0] = v[0]; o[1] = v[1]; o[2] = *(const uint32_t*)(slot + L::kMeta + r * 8 + 4 * h); o[3] = 0u;
+    return o;
   }
 }
 
-// weights of stage st for ROWS rows of this lane (slice k = 64 st + 32 half .. + 31)
-template <int WF, int ROWS>
-__device__ __forceinline__ void load_w_stage(WStage (&w)[ROWS], const uint8_t* __restrict__ w0,
-                                             const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales,
-                                             const int (&nrow)[ROWS], int K, int st, int half) {
-  const int kk = st * kTK + 32 * half;
-  if ((st + 1) * kTK <= K) {
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i) w[i] = load_w<WF, true>(w0, w1, scales, nrow[i], K, kk);
+// Codes word of MFMA step s (8 codes, k = 8s..8s+7 of the lane's 32-wide slice)
+template <int WF>
+__device__ __forceinline__ uint32_t codes_step(const u32x4& w, int s) {
+  if constexpr (WF == kDense) {
+    return w[s];
   } else {
-#pragma unroll
-    for (int i = 0; i < ROWS; ++i) w[i] = load_w<WF, false>(w0, w1, scales, nrow[i], K, kk);
+    const uint32_t vb = w[s >> 1] >> (16 * (s & 1));          // groups 2s, 2s+1: two vals bytes
+    const uint32_t nb = w[2] >> (8 * s);                      // their two position nibbles
+    return expand_group(vb & 0xFFu, nb & 0xFu) | (expand_group((vb >> 8) & 0xFFu, (nb >> 4) & 0xFu) << 16);
   }
 }
 
@@ -148,28 +201,42 @@ __device__ __forceinline__ void store_val(void* Y, int y_bf16, size_t idx, float
   else ((float*)Y)[idx] = v;
 }
 
+// Four consecutive outputs Y[m][n..n+3] (already scaled). `vec`: N % 4 == 0, so the piece is
+// 16-byte (f32) or 8-byte (bf16) aligned; otherwise, and at the right edge, element by element.
+__device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n, f32x4 v, bool vec) {
+  const size_t idx = (size_t)m * N + n;
+  if (vec && n + 3 < N) {
+    if (y_bf16) {
+      u32x2 o;
+      o[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
+      o[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      *(u32x2*)((uint16_t*)Y + idx) = o;
+    } else {
+      *(f32x4*)((float*)Y + idx) = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n + i < N) store_val(Y, y_bf16, idx + i, v[i]);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Dense (or 2:4 expanded to dense) x activations on v_mfma_f32_32x32x16_bf16.
 template <int WF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K,
-                                                        const uint8_t* __restrict__ w0,
-                                                        const uint8_t* __restrict__ w1,
-                                                        const uint8_t* __restrict__ scales,
-                                                        const float* __restrict__ ts, void* __restrict__ Y,
-                                                        int y_bf16) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
+                 const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+                 void* __restrict__ Y, int y_bf16) {
+  using L = Slot<WF>;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kTM, n0 = tn * kTN;
-  const int r32 = lane & 31, h = lane >> 5, sw = (lane >> 1) & 7;
-  const int nst = (K + kTK - 1) / kTK;
-
-  // this lane's two weight rows (clamped; columns beyond N are computed and not stored)
-  int nrow[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) nrow[nt] = min(n0 + 64 * wave + 32 * nt + r32, N - 1);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nst = K / kTK, last = nst - 1;
 
   f32x16 acc[8][2];
 #pragma unroll
@@ -179,94 +246,136 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
-  // Pipeline: activation stages st+1, st+2 and the weights of stage st+1 are in flight while
-  // stage st is computed. Within an iteration the weight loads are issued before the
-  // activation loads, so the register copy of the prefetched weights at the end of the
-  // iteration waits only for them (they were issued a whole stage earlier), never for the
-  // activation stages still meant to be in flight.
-  constexpr int kWL = WF == kDense ? 2 : 3;     // weight loads per weight row per stage
-  WStage wcur[2], wnext[2];
-  issue_x_stage(X, M, K, m0, 0, lds, wave, lane);
-  load_w_stage<WF, 2>(wcur, w0, w1, scales, nrow, K, 0, h);
-  if (nst > 1) issue_x_stage(X, M, K, m0, 1, lds, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
+  // Software pipeline over K stages (ring of three LDS slots). Stage st's loads are issued at
+  // the boundary of stage st - 3 and waited for at the boundary of stage st - 1. The boundary
+  // (wait, barrier, next loads, first operands of the next stage) sits before the last MFMA
+  // step of a stage, so that step's MFMAs cover it.
+  const StageSrc<WF> src = stage_src<WF>(X, w0, w1, scales, M, N, K, m0, n0, wave, lane);
+  issue_stage<WF>(src, 0, lds, wave);
+  issue_stage<WF>(src, min(1, last), lds + L::kBytes, wave);
+  issue_stage<WF>(src, min(2, last), lds + 2 * L::kBytes, wave);
 
-  for (int st = 0; st < nst; ++st) {
-    // issued after activation stage st: weights st (2 kWL) and activation st+1 (8, if any)
-    if (st + 1 < nst) wait_vmcnt<8 + 2 * kWL>();
-    else wait_vmcnt<2 * kWL>();
-    stage_barrier();   // stage st visible to all; every wave is done with slot (st - 1) % 3
-    if (st + 1 < nst) load_w_stage<WF, 2>(wnext, w0, w1, scales, nrow, K, st + 1, h);
-    if (st + 2 < nst) issue_x_stage(X, M, K, m0, st + 2, lds, wave, lane);
+  u32x4 wc[2];          // this stage's weights (per column block) and their scale pair
+  uint32_t wsc[2];
+  u32x4 abuf[2][8];     // activation operands, double-buffered across MFMA steps
+  bf16x8 bcur[2];       // decoded weight operands of the current step
+
+  auto load_w_regs = [&](const char* slot, u32x4 (&c)[2], uint32_t (&sc)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = 64 * wave + 32 * nt + r32;
+      c[nt] = lds_w<WF>(slot, r, h);
+      sc[nt] = *(const uint32_t*)(slot + L::kSc + r * 4) >> (16 * h);   // 16-blocks 2h, 2h + 1
+    }
+  };
+  auto decode = [&](const u32x4 (&c)[2], const uint32_t (&sc)[2], int s, bf16x8 (&b)[2]) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const float f = s < 2 ? e4m3_f32_sel<0>(sc[nt]) : e4m3_f32_sel<1>(sc[nt]);
+      b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(c[nt], s), f));
+    }
+  };
+  auto read_a = [&](const char* slot, int s, u32x4 (&a)[8]) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) a[mt] = lds_x(slot, 32 * mt + r32, 4 * h + s);
+  };
+  auto mfmas = [&](const u32x4 (&a)[8], const bf16x8 (&b)[2]) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      const bf16x8 av = as_bf16x8(a[mt]);
+      acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
+      acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
+    }
+  };
+
+  wait_vmcnt<2 * L::kLoads>();
+  stage_barrier();
+  load_w_regs(lds, wc, wsc);
+  read_a(lds, 0, abuf[0]);
+  decode(wc, wsc, 0, bcur);
+
+  auto stage = [&](auto slot_c, int st) {
+    constexpr int S = decltype(slot_c)::value;
+    const char* slot = lds + S * L::kBytes;
+    const char* next = lds + ((S + 1) % kStages) * L::kBytes;
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      read_a(slot, s + 1, abuf[(s + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);         // operand reads go out first, a whole step ahead
+      bf16x8 bn[2];
+      decode(wc, wsc, s + 1, bn);
+      mfmas(abuf[s & 1], bcur);
+      interleave_mfma_valu<1, 15, 3>();
+      bcur[0] = bn[0]; bcur[1] = bn[1];
+    }
+    // boundary: this wave's reads of slot S are done (their values are in registers) ...
+    __builtin_amdgcn_sched_barrier(0);           // the MFMAs above stay above the barrier
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
+    wait_vmcnt<L::kLoads>();                     // ... and stage st + 1 has landed
+    stage_barrier();
+    issue_stage<WF>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    u32x4 wn[2];
+    uint32_t wsn[2];
+    bf16x8 bn[2];
+    load_w_regs(next, wn, wsn);
+    read_a(next, 0, abuf[0]);
     __builtin_amdgcn_sched_barrier(0);
-
-    // activation operands of MFMA step s+1 are read while step s runs
-    const char* slot = lds + (st % kStages) * kXStage;
-    u32x4 abuf[2][8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) abuf[0][mt] = lds_x(slot, 32 * mt + r32, 4 * h, sw);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) abuf[(s + 1) & 1][mt] = lds_x(slot, 32 * mt + r32, 4 * h + s + 1, sw);
-      }
-      bf16x8 b[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float sc = s < 2 ? e4m3_f32_sel<0>(wcur[nt].s) : e4m3_f32_sel<1>(wcur[nt].s);
-        b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(wcur[nt], s), sc));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        const bf16x8 av = as_bf16x8(abuf[s & 1][mt]);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
-      }
-    }
-    if (st + 1 < nst) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) wcur[nt] = wnext[nt];
-    }
+    decode(wn, wsn, 0, bn);
+    mfmas(abuf[1], bcur);                        // last MFMA step of stage st
+    interleave_mfma_valu<4, 12, 3>();            // the first MFMAs cover the operand reads
+    wc[0] = wn[0]; wc[1] = wn[1]; wsc[0] = wsn[0]; wsc[1] = wsn[1];
+    bcur[0] = bn[0]; bcur[1] = bn[1];
+  };
+  for (int st = 0; st < nst; st += 3) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < nst) stage(std::integral_constant<int, 2>{}, st + 2);
   }
+  wait_vmcnt<0>();   // the duplicate stages past the end have landed before the wave exits
 
-  // epilogue: lane holds rows 8(i/4) + 4h + i%4 of each 32x32 block, column r32
+  // epilogue: lane holds rows 8(i/4) + 4h + i%4 of each 32x32 block, column r32. Each row
+  // block of the wave (32 rows x 64 columns) is staged in LDS and leaves as 16-byte pieces of
+  // a row (four rows of 256 bytes per store instruction).
   const float st_scale = *ts;
+  const bool vec = (N & 3) == 0;
+  __syncthreads();                                  // every wave is done with the ring slots
+  constexpr int kTS = 68;                           // staging row stride (floats): 16-byte aligned, banks shifted
+  float* T = (float*)(lds + wave * (32 * kTS * 4));
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int n = n0 + 64 * wave + 32 * nt + r32;
-    if (n >= N) continue;
+  for (int mt = 0; mt < 8; ++mt) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + 32 * mt + 8 * (i >> 2) + 4 * h + (i & 3);
-        if (m < M) store_val(Y, y_bf16, (size_t)m * N + n, acc[mt][nt][i] * st_scale);
-      }
+      for (int i = 0; i < 16; ++i) T[(8 * (i >> 2) + 4 * h + (i & 3)) * kTS + 32 * nt + r32] = acc[mt][nt][i] * st_scale;
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's stores to T are done
+    const int c4 = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = (lane >> 4) + 4 * j;
+      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
+      const int m = m0 + 32 * mt + r, n = n0 + 64 * wave + 4 * c4;
+      if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);             // reads of T done before the next block overwrites it
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // 2:4 weights on the sparse matrix cores: Y^T tile = W (compressed A) x X^T (B).
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K,
-                                                          const uint8_t* __restrict__ vals,
-                                                          const uint8_t* __restrict__ meta,
-                                                          const uint8_t* __restrict__ scales,
-                                                          const float* __restrict__ ts, void* __restrict__ Y,
-                                                          int y_bf16) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ vals,
+                   const uint8_t* __restrict__ meta, const uint8_t* __restrict__ scales,
+                   const float* __restrict__ ts, void* __restrict__ Y, int y_bf16) {
+  using L = Slot<kSp24>;
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave & 1, wm = wave >> 1;
   const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * kTM, n0 = tn * kTN;
-  const int r32 = lane & 31, q = lane >> 5, sw = (lane >> 1) & 7;
-  const int nst = (K + kTK - 1) / kTK;
-
-  int nrow[4];
-#pragma unroll
-  for (int at = 0; at < 4; ++at) nrow[at] = min(n0 + 128 * wn + 32 * at + r32, N - 1);
+  const int r32 = lane & 31, q = lane >> 5;
+  const int nst = K / kTK, last = nst - 1;
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -276,85 +385,129 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[at][bt][i] = 0.f;
 
-  constexpr int kWL = 4 * 3;   // 4 weight rows x (vals, meta, scales)
-  WStage wcur[4], wnext[4];
-  issue_x_stage(X, M, K, m0, 0, lds, wave, lane);
-  load_w_stage<kSp24Expand, 4>(wcur, vals, meta, scales, nrow, K, 0, q);
-  if (nst > 1) issue_x_stage(X, M, K, m0, 1, lds, wave, lane);
-  __builtin_amdgcn_sched_barrier(0);
+  const StageSrc<kSp24> src = stage_src<kSp24>(X, vals, meta, scales, M, N, K, m0, n0, wave, lane);
+  issue_stage<kSp24>(src, 0, lds, wave);
+  issue_stage<kSp24>(src, min(1, last), lds + L::kBytes, wave);
+  issue_stage<kSp24>(src, min(2, last), lds + 2 * L::kBytes, wave);
 
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) wait_vmcnt<8 + kWL>();
-    else wait_vmcnt<kWL>();
-    stage_barrier();
-    if (st + 1 < nst) load_w_stage<kSp24Expand, 4>(wnext, vals, meta, scales, nrow, K, st + 1, q);
-    if (st + 2 < nst) issue_x_stage(X, M, K, m0, st + 2, lds, wave, lane);
+  u32x4 wa[4];          // this stage's compressed weights (vals, vals, meta) per row block
+  uint32_t wsc[4];
+  u32x8 bx[4];          // activation operands of the current MFMA step
+  bf16x8 acur[4];       // decoded kept weights of the current step
+
+  auto load_w_regs = [&](const char* slot, u32x4 (&c)[4], uint32_t (&sc)[4]) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      const int r = 128 * wn + 32 * at + r32;
+      c[at] = lds_w<kSp24>(slot, r, q);
+      sc[at] = *(const uint32_t*)(slot + L::kSc + r * 4) >> (16 * q);   // 16-blocks 2q, 2q + 1
+    }
+  };
+  // B (activations) of MFMA step t: col r32 of block bt; k = 16t + 8q + j (j < 8) and
+  // 32 + 16t + 8q + j - 8 (j >= 8)
+  auto read_b = [&](const char* slot, int t, u32x8 (&b)[4]) {
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      const int r = 128 * wm + 32 * bt + r32;
+      const u32x4 lo = lds_x(slot, r, 2 * t + q), hi = lds_x(slot, r, 4 + 2 * t + q);
+      b[bt][0] = lo[0]; b[bt][1] = lo[1]; b[bt][2] = lo[2]; b[bt][3] = lo[3];
+      b[bt][4] = hi[0]; b[bt][5] = hi[1]; b[bt][6] = hi[2]; b[bt][7] = hi[3];
+    }
+  };
+  // A (weights): the 8 kept values of 16-block 2q + t
+  auto decode = [&](const u32x4 (&c)[4], const uint32_t (&sc)[4], int t, bf16x8 (&a)[4]) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      const float f = t == 0 ? e4m3_f32_sel<0>(sc[at]) : e4m3_f32_sel<1>(sc[at]);
+      a[at] = as_bf16x8(fp4x8_bf16(c[at][t], f));
+    }
+  };
+  auto mfmas = [&](const bf16x8 (&a)[4], const u32x4 (&c)[4], int t, const u32x8 (&b)[4]) {
+#pragma unroll
+    for (int at = 0; at < 4; ++at) {
+      const int idx = (int)((c[at][2] >> (16 * t)) & 0xFFFFu);   // positions of the 8 kept values
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt)
+        acc[at][bt] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a[at], as_bf16x16(b[bt]), acc[at][bt], idx, 0, 0);
+    }
+  };
+
+  wait_vmcnt<2 * L::kLoads>();
+  stage_barrier();
+  load_w_regs(lds, wa, wsc);
+  read_b(lds, 0, bx);
+  decode(wa, wsc, 0, acur);
+
+  auto stage = [&](auto slot_c, int st) {
+    constexpr int S = decltype(slot_c)::value;
+    const char* slot = lds + S * L::kBytes;
+    const char* next = lds + ((S + 1) % kStages) * L::kBytes;
+    u32x8 b1[4];
+    bf16x8 a1[4];
+    read_b(slot, 1, b1);
     __builtin_amdgcn_sched_barrier(0);
-
-    const char* slot = lds + (st % kStages) * kXStage;
+    decode(wa, wsc, 1, a1);
+    mfmas(acur, wa, 0, bx);
+    interleave_mfma_valu<1, 15, 5>();
+    __builtin_amdgcn_sched_barrier(0);           // the MFMAs above stay above the barrier
+    __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): reads of slot S are in registers
+    wait_vmcnt<L::kLoads>();                     // stage st + 1 has landed
+    stage_barrier();
+    issue_stage<kSp24>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    u32x4 wn[4];
+    uint32_t wsn[4];
+    load_w_regs(next, wn, wsn);
+    read_b(next, 0, bx);
+    __builtin_amdgcn_sched_barrier(0);
+    decode(wn, wsn, 0, acur);
+    mfmas(a1, wa, 1, b1);                        // second MFMA step of stage st
+    interleave_mfma_valu<4, 12, 6>();
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // B (activations): col r32 of block bt; k = 16t + 8q + j (j < 8), 32 + 16t + 8q + j' (j >= 8)
-      u32x8 bx[4];
-#pragma unroll
-      for (int bt = 0; bt < 4; ++bt) {
-        const int r = 128 * wm + 32 * bt + r32;
-        const u32x4 lo = lds_x(slot, r, 2 * t + q, sw), hi = lds_x(slot, r, 4 + 2 * t + q, sw);
-        bx[bt][0] = lo[0]; bx[bt][1] = lo[1]; bx[bt][2] = lo[2]; bx[bt][3] = lo[3];
-        bx[bt][4] = hi[0]; bx[bt][5] = hi[1]; bx[bt][6] = hi[2]; bx[bt][7] = hi[3];
-      }
-#pragma unroll
-      for (int at = 0; at < 4; ++at) {
-        // A (weights): row r32, the 8 kept values of 16-block 2q + t; index bits = its 4 nibbles
-        const float sc = t == 0 ? e4m3_f32_sel<0>(wcur[at].s) : e4m3_f32_sel<1>(wcur[at].s);
-        const bf16x8 a = as_bf16x8(fp4x8_bf16(wcur[at].c[t], sc));
-        const int idx = (int)((wcur[at].c[2] >> (16 * t)) & 0xFFFFu);
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
-          acc[at][bt] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, as_bf16x16(bx[bt]), acc[at][bt], idx, 0, 0);
-      }
-    }
-    if (st + 1 < nst) {
-#pragma unroll
-      for (int at = 0; at < 4; ++at) wcur[at] = wnext[at];
-    }
+    for (int at = 0; at < 4; ++at) { wa[at] = wn[at]; wsc[at] = wsn[at]; }
+  };
+  for (int st = 0; st < nst; st += 3) {
+    stage(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, st + 1);
+    if (st + 2 < nst) stage(std::integral_constant<int, 2>{}, st + 2);
   }
+  wait_vmcnt<0>();
 
-  // epilogue: lane holds weight rows 8(i/4) + 4q + i%4 of each block, activation row r32
+  // epilogue: lane holds weight rows 8(i/4) + 4q + i%4 of each block, activation row r32, i.e.
+  // Y[m][n .. n + 3] for n = 32 at + 8 g + 4 q. Each activation row block of the wave (32 rows x
+  // 128 columns) is staged in LDS and leaves as 16-byte pieces of a row.
   const float st_scale = *ts;
-  const bool vec_ok = (N & 3) == 0;   // 4 consecutive outputs of a row are then 16-B (8-B) aligned
+  const bool vec = (N & 3) == 0;
+  __syncthreads();
+  constexpr int kTS = 132;
+  float* T = (float*)(lds + wave * (32 * kTS * 4));
 #pragma unroll
   for (int bt = 0; bt < 4; ++bt) {
-    const int m = m0 + 128 * wm + 32 * bt + r32;
-    if (m >= M) continue;
 #pragma unroll
     for (int at = 0; at < 4; ++at)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int nb = n0 + 128 * wn + 32 * at + 8 * g + 4 * q;
-        if (vec_ok && nb + 3 < N) {
-          if (y_bf16) {
-            u32x2 o;
-            o[0] = f32_to_bf16_rne(acc[at][bt][4 * g] * st_scale) | (f32_to_bf16_rne(acc[at][bt][4 * g + 1] * st_scale) << 16);
-            o[1] = f32_to_bf16_rne(acc[at][bt][4 * g + 2] * st_scale) | (f32_to_bf16_rne(acc[at][bt][4 * g + 3] * st_scale) << 16);
-            *(u32x2*)((uint16_t*)Y + (size_t)m * N + nb) = o;
-          } else {
-            f32x4 o;
-            for (int i = 0; i < 4; ++i) o[i] = acc[at][bt][4 * g + i] * st_scale;
-            *(f32x4*)((float*)Y + (size_t)m * N + nb) = o;
-          }
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (nb + i < N) store_val(Y, y_bf16, (size_t)m * N + nb + i, acc[at][bt][4 * g + i] * st_scale);
-        }
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[at][bt][4 * g + i] * st_scale;
+        *(f32x4*)(T + r32 * kTS + 32 * at + 8 * g + 4 * q) = v;
       }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const int c4 = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = (lane >> 5) + 2 * j;
+      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
+      const int m = m0 + 128 * wm + 32 * bt + r, n = n0 + 128 * wn + 4 * c4;
+      if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
   }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * kXStage;
+  const int bytes = kStages * Slot<kDense>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kDense>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
@@ -364,17 +517,17 @@ hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * kXStage;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kSp24Expand>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  const int bytes = kStages * Slot<kSp24>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kSp24>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL(k_gemm_mfma<kSp24Expand>, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
+  hipLaunchKernelGGL(k_gemm_mfma<kSp24>, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
                      (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * kXStage;
+  const int bytes = kStages * Slot<kSp24>::kBytes;
   hipError_t e = hipFuncSetAttribute((const void*)k_gemm_smfmac, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));

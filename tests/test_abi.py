@@ -69,6 +69,12 @@ def test_validation_paths_return_codes_without_launching():
     used = ctypes.c_int(-1)
     assert L.gemm_nvfp4_sp24(p, 2, 4, 96, p, p, p, p, p, 0, ssn.ALGO_SMFMAC, ctypes.byref(used), n) == ssn.SSN_E_ALGO
     assert b"K % 64" in L.ssn_last_error()
+    for algo, fn in ((ssn.ALGO_MFMA, "dense"), (ssn.ALGO_DECOMPRESS_MFMA, "sp24"), (ssn.ALGO_SMFMAC, "sp24")):
+        if fn == "dense":
+            st = L.gemm_nvfp4_dense(p, 17, 4, 96, p, p, p, p, 0, algo, ctypes.byref(used), n)
+        else:
+            st = L.gemm_nvfp4_sp24(p, 17, 4, 96, p, p, p, p, p, 0, algo, ctypes.byref(used), n)
+        assert st == ssn.SSN_E_ALGO and b"K % 64" in L.ssn_last_error()
 
 
 def test_empty_problem_is_a_noop():

@@ -28,13 +28,15 @@ def _problem(M, N, K, seed, prune):
 # M > 16 shapes run the 256 x 256 tiles: several tiles in M and N, ragged edges, K tails of 32
 DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
-               (64, 1000, 2048)]
+               (64, 1000, 2048), (257, 300, 128), (513, 257, 1088)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
 @pytest.mark.parametrize("algo", DENSE_ALGOS)
 @pytest.mark.parametrize("prune", [False, True])
 def test_dense(M, N, K, algo, prune):
+    if algo == ssn.ALGO_MFMA and M > 16 and K % 64:
+        pytest.skip("the 256x256 tiles need K % 64 == 0 (refusal is tested on the CPU)")
     x, c, s, st = _problem(M, N, K, seed=M * 7 + N + K, prune=prune)
     Y, B = gemm.gemm_dense(x, c, s, st)
     g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
@@ -44,14 +46,14 @@ def test_dense(M, N, K, algo, prune):
 
 SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64, 1024), (4, 48, 4096),
               (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
-              (64, 1000, 2048)]
+              (64, 1000, 2048), (257, 300, 128), (513, 257, 1088)]
 
 
 @pytest.mark.parametrize("M,N,K", SP24_CASES)
 @pytest.mark.parametrize("algo", SP24_ALGOS)
 def test_sp24(M, N, K, algo):
-    if algo == ssn.ALGO_SMFMAC and K % 64 and M <= 16:
-        pytest.skip("SMFMAC for M <= 16 needs K % 64 == 0 (refusal is tested on the CPU)")
+    if K % 64 and (algo == ssn.ALGO_SMFMAC or (algo == ssn.ALGO_DECOMPRESS_MFMA and M > 16)):
+        pytest.skip("SMFMAC and the 256x256 tiles need K % 64 == 0 (refusal is tested on the CPU)")
     x, c, s, st = _problem(M, N, K, seed=M * 5 + N + K, prune=True)
     vals, meta, bad = sp24.compress(c)
     assert bad == 0
@@ -117,7 +119,7 @@ def _one_hot_tiled(M, K, seed):
 
 @pytest.mark.parametrize("algo", [ssn.ALGO_MFMA])
 def test_one_hot_rows_extract_weights_dense_tiled(algo):
-    M, N, K = 300, 290, 160
+    M, N, K = 300, 290, 192
     xb, ks = _one_hot_tiled(M, K, 0)
     _, c, s, st = _problem(1, N, K, seed=6, prune=False)
     g, used = ssn.gemm_nvfp4_dense(x_dev(xb), dev(c), dev(s), dev(np.array([st], np.float32)), algo=algo)
@@ -127,7 +129,7 @@ def test_one_hot_rows_extract_weights_dense_tiled(algo):
 
 @pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA])
 def test_one_hot_rows_extract_weights_sp24_tiled(algo):
-    M, N, K = 300, 290, 160
+    M, N, K = 300, 290, 192
     xb, ks = _one_hot_tiled(M, K, 1)
     _, c, s, st = _problem(1, N, K, seed=7, prune=True)
     vals, meta, _ = sp24.compress(c)
