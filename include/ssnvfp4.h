@@ -37,7 +37,10 @@
  *    thread-local message.
  *  - Sizes: N, M >= 0 (a zero size is a no-op that returns SSN_OK); K % 32 == 0 for the
  *    NVFP4/2:4 calls (so a 32-bit word of meta covers whole groups and rows of every array
- *    are 2-byte aligned). Device pointers must be 16-byte aligned.
+ *    are 2-byte aligned). Device pointers to tensors (activations, codes, scales, vals, meta,
+ *    outputs) must be 16-byte aligned; pointers to single scalars and to int32/f32 index or
+ *    weight arrays (tensor scales, counters, routing arrays, combine weights) only need the
+ *    alignment of their element type.
  *  - Data-dependent failures (a group that is not 2:4) are reported in device counters, not
  *    in the return code.
  *  - Calls that write the same output buffers and overlap on one stream or across streams race.
@@ -56,7 +59,7 @@ typedef enum {
   SSN_OK = 0,
   SSN_E_NULL = 1,   /* a required pointer is NULL */
   SSN_E_SHAPE = 2,  /* a size is negative, K % 32 != 0, or sizes are inconsistent */
-  SSN_E_ALIGN = 3,  /* a device pointer is not 16-byte aligned */
+  SSN_E_ALIGN = 3,  /* a device pointer is not aligned as required */
   SSN_E_DTYPE = 4,  /* unknown dtype code */
   SSN_E_ALGO = 5,   /* unknown algorithm, or an explicit algorithm that does not apply to the shape */
   SSN_E_HIP = 6,    /* a HIP launch or runtime call failed */
@@ -173,6 +176,81 @@ int gemm_nvfp4_dense(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
 int gemm_nvfp4_sp24(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* vals,
                     const uint8_t* meta, const uint8_t* scales, const float* tensor_scale, void* Y,
                     int y_dtype, int algo, int* algo_used, void* stream);
+
+/* =============================================================================================
+ * Grouped-expert (MoE) path. The pages describe a 512-expert, top-10 mixture whose expert
+ * weights are the thing every step reads ("NVFP4 vs 2:4 sparse", robertz.co, sections
+ * "Concurrency, not sparsity, is the lever" and "The sparsity that does pay is already
+ * running") and note that no grouped 2:4 product exists for it (same page, section "Why it
+ * cannot run on this cluster"). Row space: the T*k (token, slot) entries grouped by expert
+ * (ascending) and, inside an expert, in flat order f = t*k + j. Limits: 1 <= E <= 2048,
+ * 1 <= k <= 64, T*k < 2^31.
+ * ============================================================================================= */
+
+/* moe_route_workspace_bytes — device workspace moe_route needs (0 when T*k == 0). */
+int64_t moe_route_workspace_bytes(int64_t T, int k, int E);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_route — routing bookkeeping: a stable counting sort of the flat entries by expert id.
+ * topk_ids int32 [T, k] (device). Outputs (device, caller-owned): expert_offsets int32 [E+1]
+ * (rows of expert e are [offsets[e], offsets[e+1])), row_token int32 [T*k] and row_slot
+ * int32 [T*k] (the (t, j) of each row), row_of int32 [T*k] (the row of entry t*k + j, or -1).
+ * Entries whose id is outside [0, E) get no row; their count goes to *bad_ids (device int64
+ * [1], nullable) and offsets[E] counts the placed rows. workspace: device, at least
+ * moe_route_workspace_bytes(T, k, E) bytes. Errors: NULL, SHAPE, ALIGN, RANGE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_offsets,
+              int32_t* row_token, int32_t* row_slot, int32_t* row_of, int64_t* bad_ids,
+              void* workspace, int64_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_grouped_gemm_nvfp4 — every expert's product in one launch:
+ *   Y[r, :] = X[src(r), :] . W_hat_e^T  for r in [offsets[e], offsets[e+1]),
+ * src(r) = row_token[r] (gather; nullptr = identity, r itself), W_hat_e as in gemm_nvfp4_dense
+ * with the expert's tensor scale tensor_scales[e].
+ * X bf16 [x_rows, K]; weights per expert, concatenated over e: dense codes [E, N, K/2], or 2:4
+ * (sparse = 1) vals [E, N, K/4] + meta [E, N, K/8]; scales [E, N, K/16]; tensor_scales f32 [E].
+ * epilogue SSN_EPI_NONE: Y [R, N] of y_dtype. SSN_EPI_SILU_GATE: weight rows [0, N/2) are the
+ * gate and [N/2, N) the up projection (W_up [E, 2, I, K] flattened, one shared tensor scale per
+ * expert, "NVFP4 Without FP4 Hardware", ai-muninn.com, section "The shared global scale");
+ * Y [R, N/2] = silu(g) * u with silu(g) = g / (1 + exp(-g)), evaluated in f32 and rounded to
+ * y_dtype. R: rows of Y (offsets are clamped into [0, R]); source rows are clamped into
+ * [0, x_rows). Needs K % 64 == 0 and, for SILU_GATE, N even. algo: AUTO, MFMA (dense) or
+ * DECOMPRESS_MFMA (2:4, expanded to a dense operand in registers). algo_used: host, nullable.
+ * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, RANGE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row_token,
+                           const int32_t* expert_offsets, int E, int64_t R, int64_t N, int64_t K,
+                           int sparse, const uint8_t* w_main, const uint8_t* w_meta,
+                           const uint8_t* w_scales, const float* tensor_scales, int epilogue,
+                           void* Y, int y_dtype, int algo, int* algo_used, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_combine — out[t, :] = sum_j topk_weights[t, j] * Yd[row_of[t*k + j], :], summed in slot
+ * order j = 0..k-1 in f32 (rows outside [0, R) are skipped). Yd [R, D] of yd_dtype; row_of
+ * int32 [T*k]; topk_weights f32 [T, k]; out f32 [T, D]. Errors: NULL, SHAPE, ALIGN, DTYPE,
+ * RANGE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int moe_combine(const void* Yd, int yd_dtype, int64_t R, const int32_t* row_of,
+                const float* topk_weights, int64_t T, int k, int64_t D, float* out, void* stream);
+
+/* moe_ffn_workspace_bytes — device workspace moe_nvfp4_ffn needs. */
+int64_t moe_ffn_workspace_bytes(int64_t T, int k, int E, int64_t I, int64_t D);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_nvfp4_ffn — the whole grouped-expert FFN: route, up (SILU_GATE, H bf16 [T*k, I]),
+ * down (Yd f32 [T*k, D]) and combine into out f32 [T, D]. X bf16 [T, D]; topk_ids int32
+ * [T, k]; topk_weights f32 [T, k]; up weights [E, 2I, D] (+ meta when sparse), up_ts f32 [E];
+ * down weights [E, D, I], down_ts f32 [E]. workspace: device, at least
+ * moe_ffn_workspace_bytes(T, k, E, I, D) bytes (holds the routing arrays, H and Yd).
+ * bad_ids: as in moe_route. Errors: those of the four calls.
+ * ------------------------------------------------------------------------------------------- */
+int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids,
+                  const float* topk_weights, int k, int E, int64_t I, int sparse,
+                  const uint8_t* up_main, const uint8_t* up_meta, const uint8_t* up_scales,
+                  const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
+                  const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids,
+                  void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,14 @@ _SIGS = {
     "sp24_decompress": ([_vp, _vp, _i64, _i64, _vp, _vp], _int),
     "gemm_nvfp4_dense": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp], _int),
     "gemm_nvfp4_sp24": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp], _int),
+    "moe_route_workspace_bytes": ([_i64, _int, _int], _i64),
+    "moe_route": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _int),
+    "moe_grouped_gemm_nvfp4": ([_vp, _i64, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _int,
+                                _vp, _int, _int, _vp, _vp], _int),
+    "moe_combine": ([_vp, _int, _i64, _vp, _vp, _i64, _int, _i64, _vp, _vp], _int),
+    "moe_ffn_workspace_bytes": ([_i64, _int, _int, _i64, _i64], _i64),
+    "moe_nvfp4_ffn": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _vp, _vp, _vp, _vp, _i64, _vp], _int),
 }
 
 _lib = None
@@ -247,3 +255,97 @@ def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, 
         return Prepared("gemm_nvfp4_sp24", cargs, (X, vals, meta, scales, tensor_scale, used)), (Y, used)
     _check(lib().gemm_nvfp4_sp24(*cargs))
     return Y, used.value
+
+
+# ------------------------------------------------------------------------------------------------
+# grouped-expert (MoE) path
+
+
+def moe_route(topk_ids, E, prepare=False):
+    """Routing bookkeeping for topk_ids int32 [T, k]. Returns device tensors
+    (expert_offsets [E+1], row_token [T*k], row_slot [T*k], row_of [T*k], bad_ids [1])."""
+    T, k = topk_ids.shape
+    _need(topk_ids, torch.int32, "topk_ids")
+    dev = topk_ids.device
+    F = T * k
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    row_token = torch.empty(max(F, 1), dtype=torch.int32, device=dev)[:F]
+    row_slot = torch.empty(max(F, 1), dtype=torch.int32, device=dev)[:F]
+    row_of = torch.empty(max(F, 1), dtype=torch.int32, device=dev)[:F]
+    bad = torch.empty(1, dtype=torch.int64, device=dev)
+    nws = lib().moe_route_workspace_bytes(T, k, E)
+    if nws < 0:
+        _check(lib().moe_route(None, T, k, E, None, None, None, None, None, None, 0, None))
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    cargs = (_ptr(topk_ids), T, k, E, _ptr(offsets), _ptr(row_token), _ptr(row_slot), _ptr(row_of), _ptr(bad),
+             _ptr(ws), nws, _stream(dev))
+    return _run("moe_route", cargs, prepare, (topk_ids, ws), (offsets, row_token, row_slot, row_of, bad))
+
+
+def moe_grouped_gemm_nvfp4(X, row_token, expert_offsets, R, w_main, w_scales, tensor_scales, w_meta=None,
+                           epilogue=EPI_NONE, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None, prepare=False):
+    """Every expert's product in one launch. X bf16 [x_rows, K]; row_token int32 [R] or None
+    (identity); expert_offsets int32 [E+1]; dense weights w_main [E, N, K/2] (w_meta None) or
+    2:4 w_main [E, N, K/4] with w_meta [E, N, K/8]; w_scales [E, N, K/16]; tensor_scales f32 [E].
+    Returns (Y [R, N] or [R, N/2] for EPI_SILU_GATE, algorithm that ran)."""
+    x_rows, K = X.shape
+    E, N = w_main.shape[0], w_main.shape[1]
+    sparse = w_meta is not None
+    _need(X, torch.bfloat16, "X"); _need(expert_offsets, torch.int32, "expert_offsets", (E + 1,))
+    if row_token is not None:
+        _need(row_token, torch.int32, "row_token", (R,))
+    _need(w_main, torch.uint8, "w_main", (E, N, K // 4 if sparse else K // 2))
+    if sparse:
+        _need(w_meta, torch.uint8, "w_meta", (E, N, K // 8))
+    _need(w_scales, torch.uint8, "w_scales", (E, N, K // 16)); _need(tensor_scales, torch.float32, "tensor_scales", (E,))
+    ncols = N // 2 if epilogue == EPI_SILU_GATE else N
+    Y = Y if Y is not None else torch.empty((R, ncols), dtype=y_dtype, device=X.device)
+    dt = SSN_F32 if Y.dtype == torch.float32 else SSN_BF16 if Y.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("Y must be float32 or bfloat16")
+    _need(Y, Y.dtype, "Y", (R, ncols))
+    used = ctypes.c_int(-1)
+    cargs = (_ptr(X), x_rows, _ptr(row_token), _ptr(expert_offsets), E, R, N, K, int(sparse), _ptr(w_main),
+             _ptr(w_meta), _ptr(w_scales), _ptr(tensor_scales), epilogue, _ptr(Y), dt, algo, ctypes.byref(used),
+             _stream(X.device))
+    if prepare:
+        return Prepared("moe_grouped_gemm_nvfp4", cargs, (X, row_token, expert_offsets, w_main, w_meta, w_scales,
+                                                          tensor_scales, used)), (Y, used)
+    _check(lib().moe_grouped_gemm_nvfp4(*cargs))
+    return Y, used.value
+
+
+def moe_combine(Yd, row_of, topk_weights, out=None, prepare=False):
+    """out[t] = sum_j topk_weights[t, j] * Yd[row_of[t*k + j]] (f32 [T, D])."""
+    R, D = Yd.shape
+    T, k = topk_weights.shape
+    dt = SSN_F32 if Yd.dtype == torch.float32 else SSN_BF16 if Yd.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("Yd must be float32 or bfloat16")
+    _need(Yd, Yd.dtype, "Yd"); _need(row_of, torch.int32, "row_of", (T * k,))
+    _need(topk_weights, torch.float32, "topk_weights")
+    out = out if out is not None else torch.empty((T, D), dtype=torch.float32, device=Yd.device)
+    _need(out, torch.float32, "out", (T, D))
+    cargs = (_ptr(Yd), dt, R, _ptr(row_of), _ptr(topk_weights), T, k, D, _ptr(out), _stream(Yd.device))
+    return _run("moe_combine", cargs, prepare, (Yd, row_of, topk_weights), out)
+
+
+def moe_nvfp4_ffn(X, topk_ids, topk_weights, E, up, down, out=None, prepare=False):
+    """The whole grouped-expert FFN. up = (main [E, 2I, D/2 or D/4], meta or None, scales
+    [E, 2I, D/16], ts [E]); down = (main [E, D, I/2 or I/4], meta or None, scales [E, D, I/16],
+    ts [E]). Returns (out f32 [T, D], bad_ids int64 [1] device)."""
+    T, D = X.shape
+    _, k = topk_ids.shape
+    I = up[2].shape[1] // 2
+    sparse = up[1] is not None
+    _need(X, torch.bfloat16, "X"); _need(topk_ids, torch.int32, "topk_ids", (T, k))
+    _need(topk_weights, torch.float32, "topk_weights", (T, k))
+    dev = X.device
+    out = out if out is not None else torch.empty((T, D), dtype=torch.float32, device=dev)
+    bad = torch.empty(1, dtype=torch.int64, device=dev)
+    nws = lib().moe_ffn_workspace_bytes(T, k, E, I, D)
+    ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
+    cargs = (_ptr(X), T, D, _ptr(topk_ids), _ptr(topk_weights), k, E, I, int(sparse), _ptr(up[0]), _ptr(up[1]),
+             _ptr(up[2]), _ptr(up[3]), _ptr(down[0]), _ptr(down[1]), _ptr(down[2]), _ptr(down[3]), _ptr(out),
+             _ptr(bad), _ptr(ws), nws, _stream(dev))
+    return _run("moe_nvfp4_ffn", cargs, prepare, (X, topk_ids, topk_weights, up, down, ws), (out, bad))

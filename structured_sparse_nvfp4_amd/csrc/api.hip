@@ -34,6 +34,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 #define REQUIRE_OPT_PTR(p) \
   do { if ((p) && !aligned16(p)) return fail(SSN_E_ALIGN, "%s: argument '%s' is not 16-byte aligned", fn, #p); } while (0)
 
+// scalars and element-wise arrays: the alignment of the element type
+#define REQUIRE_ELEM_PTR(p) \
+  do { if (!(p)) return fail(SSN_E_NULL, "%s: argument '%s' is NULL", fn, #p); \
+       if ((uintptr_t)(p) % alignof(decltype(*(p)))) \
+         return fail(SSN_E_ALIGN, "%s: argument '%s' is not aligned to its element type", fn, #p); } while (0)
+#define REQUIRE_OPT_ELEM_PTR(p) \
+  do { if ((p) && (uintptr_t)(p) % alignof(decltype(*(p)))) \
+         return fail(SSN_E_ALIGN, "%s: argument '%s' is not aligned to its element type", fn, #p); } while (0)
+
 // rows (N, M) are indexed with 32-bit ints inside the kernels, tile origins included
 constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1024;
 
@@ -65,11 +74,10 @@ int nvfp4_quantize(const void* W, int w_dtype, int64_t N, int64_t K, const float
   int st;
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, w_dtype, "w_dtype"))) return st;
-  REQUIRE_PTR(tensor_scale_out);
-  REQUIRE_OPT_PTR(tensor_scale_in);
+  REQUIRE_ELEM_PTR(tensor_scale_out);
+  REQUIRE_OPT_ELEM_PTR(tensor_scale_in);
   if (N == 0 || K == 0) {
     // an empty tensor still has a well-defined scale: zero (or the given shared scale)
-    REQUIRE_PTR(tensor_scale_out);
     return hip_status(ssn::launch_quantize(nullptr, 0, 0, 0, tensor_scale_in, nullptr, nullptr,
                                            tensor_scale_out, as_stream(stream)), fn);
   }
@@ -85,7 +93,7 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, out_dtype, "out_dtype"))) return st;
   if (N == 0 || K == 0) return ok();
-  REQUIRE_PTR(codes); REQUIRE_PTR(scales); REQUIRE_PTR(tensor_scale); REQUIRE_PTR(out);
+  REQUIRE_PTR(codes); REQUIRE_PTR(scales); REQUIRE_ELEM_PTR(tensor_scale); REQUIRE_PTR(out);
   return hip_status(ssn::launch_dequantize(codes, scales, tensor_scale, N, K, out, out_dtype == SSN_BF16,
                                            as_stream(stream)), fn);
 }
@@ -105,8 +113,8 @@ int sp24_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad_groups, 
   const char* fn = "sp24_check";
   int st;
   if ((st = check_nk(fn, N, K))) return st;
-  REQUIRE_PTR(bad_groups);
-  REQUIRE_OPT_PTR(first_bad);
+  REQUIRE_ELEM_PTR(bad_groups);
+  REQUIRE_OPT_ELEM_PTR(first_bad);
   if (N * K > 0) REQUIRE_PTR(codes);
   return hip_status(ssn::launch_check(codes, N, K, bad_groups, first_bad, as_stream(stream)), fn);
 }
@@ -116,7 +124,7 @@ int sp24_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* vals, uin
   const char* fn = "sp24_compress";
   int st;
   if ((st = check_nk(fn, N, K))) return st;
-  REQUIRE_PTR(bad_groups);
+  REQUIRE_ELEM_PTR(bad_groups);
   if (N * K > 0) { REQUIRE_PTR(codes); REQUIRE_PTR(vals); REQUIRE_PTR(meta); }
   return hip_status(ssn::launch_compress(codes, N, K, vals, meta, bad_groups, as_stream(stream)), fn);
 }
@@ -151,7 +159,7 @@ int gemm_common(const char* fn, const uint16_t* X, int64_t M, int64_t N, int64_t
     return fail(SSN_E_ALGO, "%s: use SMFMAC or DECOMPRESS_MFMA for 2:4 weights", fn);
   if (M == 0 || N == 0) { if (algo_used) *algo_used = algo; return ok(); }
   if (K == 0) return fail(SSN_E_SHAPE, "%s: K must be positive when M, N > 0", fn);
-  REQUIRE_PTR(X); REQUIRE_PTR(w0); REQUIRE_PTR(scales); REQUIRE_PTR(ts); REQUIRE_PTR(Y);
+  REQUIRE_PTR(X); REQUIRE_PTR(w0); REQUIRE_PTR(scales); REQUIRE_ELEM_PTR(ts); REQUIRE_PTR(Y);
   if (sp24) REQUIRE_PTR(w1);
 
   // M <= 16: decode-shaped kernels (weights streamed once); otherwise 256x256 tiles, which
@@ -201,6 +209,145 @@ int gemm_nvfp4_sp24(const uint16_t* X, int64_t M, int64_t N, int64_t K, const ui
                     int y_dtype, int algo, int* algo_used, void* stream) {
   return gemm_common("gemm_nvfp4_sp24", X, M, N, K, vals, meta, scales, tensor_scale, Y, y_dtype, true, algo,
                      algo_used, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// grouped-expert path
+namespace {
+
+constexpr int kMaxExperts = 2048, kMaxTopK = 64;
+
+int check_route_shape(const char* fn, int64_t T, int k, int E) {
+  if (T < 0) return fail(SSN_E_SHAPE, "%s: negative T=%lld", fn, (long long)T);
+  if (k < 1 || k > kMaxTopK) return fail(SSN_E_RANGE, "%s: k=%d outside [1, %d]", fn, k, kMaxTopK);
+  if (E < 1 || E > kMaxExperts) return fail(SSN_E_RANGE, "%s: E=%d outside [1, %d]", fn, E, kMaxExperts);
+  if (T * k >= ((int64_t)1 << 31) - 1024) return fail(SSN_E_SHAPE, "%s: T*k=%lld too large", fn, (long long)(T * k));
+  return SSN_OK;
+}
+
+int64_t route_ws(int64_t T, int k, int E) { return (int64_t)ssn::moe_route_workspace(T * k, E); }
+
+int64_t align256(int64_t n) { return (n + 255) & ~(int64_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_route_workspace_bytes(int64_t T, int k, int E) {
+  if (check_route_shape("moe_route_workspace_bytes", T, k, E)) return -1;
+  return route_ws(T, k, E);
+}
+
+int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_offsets, int32_t* row_token,
+              int32_t* row_slot, int32_t* row_of, int64_t* bad_ids, void* workspace, int64_t workspace_bytes,
+              void* stream) {
+  const char* fn = "moe_route";
+  int st;
+  if ((st = check_route_shape(fn, T, k, E))) return st;
+  REQUIRE_ELEM_PTR(expert_offsets);
+  REQUIRE_OPT_ELEM_PTR(bad_ids);
+  const int64_t need = route_ws(T, k, E);
+  if (T > 0) {
+    REQUIRE_ELEM_PTR(topk_ids); REQUIRE_ELEM_PTR(row_token); REQUIRE_ELEM_PTR(row_slot); REQUIRE_ELEM_PTR(row_of);
+    REQUIRE_PTR(workspace);
+  }
+  if (workspace_bytes < need)
+    return fail(SSN_E_RANGE, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                (long long)need);
+  return hip_status(ssn::launch_moe_route(topk_ids, T, k, E, expert_offsets, row_token, row_slot, row_of, bad_ids,
+                                          workspace, as_stream(stream)), fn);
+}
+
+int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row_token, const int32_t* expert_offsets,
+                           int E, int64_t R, int64_t N, int64_t K, int sparse, const uint8_t* w_main,
+                           const uint8_t* w_meta, const uint8_t* w_scales, const float* tensor_scales, int epilogue,
+                           void* Y, int y_dtype, int algo, int* algo_used, void* stream) {
+  const char* fn = "moe_grouped_gemm_nvfp4";
+  int st;
+  if (E < 1 || E > kMaxExperts) return fail(SSN_E_RANGE, "%s: E=%d outside [1, %d]", fn, E, kMaxExperts);
+  if (R < 0 || R > kMaxRows || x_rows < 0 || x_rows > kMaxRows)
+    return fail(SSN_E_SHAPE, "%s: bad row counts (R=%lld, x_rows=%lld)", fn, (long long)R, (long long)x_rows);
+  if ((st = check_nk(fn, N, K))) return st;
+  if ((st = check_dtype(fn, y_dtype, "y_dtype"))) return st;
+  if (sparse != 0 && sparse != 1) return fail(SSN_E_RANGE, "%s: sparse=%d must be 0 or 1", fn, sparse);
+  if (epilogue != SSN_EPI_NONE && epilogue != SSN_EPI_SILU_GATE)
+    return fail(SSN_E_RANGE, "%s: unknown epilogue %d", fn, epilogue);
+  if (epilogue == SSN_EPI_SILU_GATE && N % 2) return fail(SSN_E_SHAPE, "%s: SILU_GATE needs N even (N=%lld)", fn, (long long)N);
+  const int chosen = algo == SSN_ALGO_AUTO ? (sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA) : algo;
+  if (chosen != (sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA))
+    return fail(SSN_E_ALGO, "%s: algorithm %d is not available for %s expert weights", fn, algo,
+                sparse ? "2:4" : "dense");
+  if (algo_used) *algo_used = chosen;
+  if (R == 0 || N == 0) return ok();
+  if (K == 0 || K % 64) return fail(SSN_E_SHAPE, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
+  if (x_rows == 0) return fail(SSN_E_SHAPE, "%s: x_rows must be positive when R > 0", fn);
+  if (N * (K / 2) * (int64_t)E > ((int64_t)1 << 40)) return fail(SSN_E_SHAPE, "%s: expert weights too large", fn);
+  REQUIRE_PTR(X); REQUIRE_OPT_ELEM_PTR(row_token); REQUIRE_ELEM_PTR(expert_offsets); REQUIRE_PTR(w_main);
+  REQUIRE_PTR(w_scales); REQUIRE_ELEM_PTR(tensor_scales); REQUIRE_PTR(Y);
+  if (sparse) REQUIRE_PTR(w_meta);
+  ssn::MoeGemmArgs a{X, x_rows, K, row_token, expert_offsets, E, R, N, w_main, sparse ? w_meta : nullptr, w_scales,
+                     tensor_scales, Y, y_dtype == SSN_BF16, sparse, epilogue == SSN_EPI_SILU_GATE};
+  return hip_status(ssn::launch_moe_gemm(a, as_stream(stream)), fn);
+}
+
+int moe_combine(const void* Yd, int yd_dtype, int64_t R, const int32_t* row_of, const float* topk_weights, int64_t T,
+                int k, int64_t D, float* out, void* stream) {
+  const char* fn = "moe_combine";
+  int st;
+  if (T < 0 || D < 0 || R < 0 || R > kMaxRows || T > kMaxRows || D > ((int64_t)1 << 30))
+    return fail(SSN_E_SHAPE, "%s: bad sizes (T=%lld, D=%lld, R=%lld)", fn, (long long)T, (long long)D, (long long)R);
+  if (k < 1 || k > kMaxTopK) return fail(SSN_E_RANGE, "%s: k=%d outside [1, %d]", fn, k, kMaxTopK);
+  if ((st = check_dtype(fn, yd_dtype, "yd_dtype"))) return st;
+  if (T == 0 || D == 0) return ok();
+  REQUIRE_ELEM_PTR(row_of); REQUIRE_ELEM_PTR(topk_weights); REQUIRE_PTR(out);
+  if (R > 0) REQUIRE_PTR(Yd);
+  return hip_status(ssn::launch_moe_combine(Yd, yd_dtype == SSN_BF16, R, row_of, topk_weights, T, k, D, out,
+                                            as_stream(stream)), fn);
+}
+
+int64_t moe_ffn_workspace_bytes(int64_t T, int k, int E, int64_t I, int64_t D) {
+  if (check_route_shape("moe_ffn_workspace_bytes", T, k, E) || I < 0 || D < 0) return -1;
+  const int64_t F = T * k;
+  return align256((E + 1) * 4) + 3 * align256(F * 4) + align256(route_ws(T, k, E)) + align256(F * I * 2) +
+         align256(F * D * 4);
+}
+
+int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids, const float* topk_weights, int k,
+                  int E, int64_t I, int sparse, const uint8_t* up_main, const uint8_t* up_meta,
+                  const uint8_t* up_scales, const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
+                  const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids, void* workspace,
+                  int64_t workspace_bytes, void* stream) {
+  const char* fn = "moe_nvfp4_ffn";
+  int st;
+  if ((st = check_route_shape(fn, T, k, E))) return st;
+  if (I <= 0 || D <= 0 || I % 64 || D % 64)
+    return fail(SSN_E_SHAPE, "%s: I=%lld and D=%lld must be positive multiples of 64", fn, (long long)I, (long long)D);
+  const int64_t need = moe_ffn_workspace_bytes(T, k, E, I, D);
+  if (T > 0) REQUIRE_PTR(workspace);
+  if (workspace_bytes < need)
+    return fail(SSN_E_RANGE, "%s: workspace of %lld bytes, %lld needed", fn, (long long)workspace_bytes,
+                (long long)need);
+  if (T == 0) return ok();
+  const int64_t F = T * k;
+  char* w = (char*)workspace;
+  int32_t* offsets = (int32_t*)w; w += align256((E + 1) * 4);
+  int32_t* row_token = (int32_t*)w; w += align256(F * 4);
+  int32_t* row_slot = (int32_t*)w; w += align256(F * 4);
+  int32_t* row_of = (int32_t*)w; w += align256(F * 4);
+  void* rws = w; w += align256(route_ws(T, k, E));
+  uint16_t* H = (uint16_t*)w; w += align256(F * I * 2);
+  float* Yd = (float*)w;
+  if ((st = moe_route(topk_ids, T, k, E, offsets, row_token, row_slot, row_of, bad_ids, rws, route_ws(T, k, E), stream)))
+    return st;
+  if ((st = moe_grouped_gemm_nvfp4(X, T, row_token, offsets, E, F, 2 * I, D, sparse, up_main, up_meta, up_scales, up_ts,
+                                   SSN_EPI_SILU_GATE, H, SSN_BF16, SSN_ALGO_AUTO, nullptr, stream)))
+    return st;
+  if ((st = moe_grouped_gemm_nvfp4(H, F, nullptr, offsets, E, F, D, I, sparse, down_main, down_meta, down_scales,
+                                   down_ts, SSN_EPI_NONE, Yd, SSN_F32, SSN_ALGO_AUTO, nullptr, stream)))
+    return st;
+  return moe_combine(Yd, SSN_F32, F, row_of, topk_weights, T, k, D, out, stream);
 }
 
 }  // extern "C"

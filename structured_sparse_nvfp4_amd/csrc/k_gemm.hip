@@ -30,6 +30,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
+#include "tile.hpp"
 
 namespace ssn {
 namespace {
@@ -37,13 +38,6 @@ namespace {
 constexpr int kTM = 256, kTN = 256, kTK = 64;   // output tile and K-stage
 constexpr int kStages = 3;                       // stages resident in LDS
 constexpr int kThreads = 256;
-
-enum WForm { kDense = 0, kSp24 = 1 };
-
-// Chunk swizzle of the activation tile: eight consecutive rows (one 128-byte bank sweep each)
-// and the eight same-parity rows of any sixteen get distinct chunks, so 16-byte operand reads
-// of 8 or 16 lanes (rows r..r+7 or r..r+15, one chunk each) never share a bank.
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
 // One LDS ring slot (bytes). Rows are tile-local (0..255).
 //   X      [256][128 B]  activation k-chunk c of row r at physical chunk c ^ swz(r)
@@ -147,27 +141,9 @@ __device__ __forceinline__ void issue_stage(const StageSrc<WF>& g, int st, char*
   lds_dma4(g.sb + st * (kTK / 16) + g.so, slot + L::kSc + wave * 256);
 }
 
-// Scheduling hint for the region just issued: LEAD matrix instructions first, then GROUPS of
-// (one matrix instruction, VALU vector-ALU instructions), so the weight decode fills the
-// matrix pipe's shadow instead of running ahead of or behind it.
-template <int LEAD, int GROUPS, int VALU>
-__device__ __forceinline__ void interleave_mfma_valu() {
-  __builtin_amdgcn_sched_group_barrier(0x008, LEAD, 0);
-#pragma unroll
-  for (int i = 0; i < GROUPS; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
-}
-
 // 16-byte activation chunk `c` of tile row r
 __device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c) {
   return *(const u32x4*)(slot + r * 128 + 16 * (c ^ swz(r)));
-}
-
-// Two kept codes (byte vb) at positions (nib & 3, nib >> 2) of a group of four nibbles.
-__device__ __forceinline__ uint32_t expand_group(uint32_t vb, uint32_t nib) {
-  return ((vb & 0xFu) << ((nib & 3u) << 2)) | (((vb >> 4) & 0xFu) << ((nib >> 2) << 2));
 }
 
 // One lane's weights for one stage: dense 32 codes, or 2:4 (vals word 0, vals word 1, meta)
@@ -181,43 +157,6 @@ __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
     u32x4 o;
     o[0] = v[0]; o[1] = v[1]; o[2] = *(const uint32_t*)(slot + L::kMeta + r * 8 + 4 * h); o[3] = 0u;
     return o;
-  }
-}
-
-// Codes word of MFMA step s (8 codes, k = 8s..8s+7 of the lane's 32-wide slice)
-template <int WF>
-__device__ __forceinline__ uint32_t codes_step(const u32x4& w, int s) {
-  if constexpr (WF == kDense) {
-    return w[s];
-  } else {
-    const uint32_t vb = w[s >> 1] >> (16 * (s & 1));          // groups 2s, 2s+1: two vals bytes
-    const uint32_t nb = w[2] >> (8 * s);                      // their two position nibbles
-    return expand_group(vb & 0xFFu, nb & 0xFu) | (expand_group((vb >> 8) & 0xFFu, (nb >> 4) & 0xFu) << 16);
-  }
-}
-
-__device__ __forceinline__ void store_val(void* Y, int y_bf16, size_t idx, float v) {
-  if (y_bf16) ((uint16_t*)Y)[idx] = (uint16_t)f32_to_bf16_rne(v);
-  else ((float*)Y)[idx] = v;
-}
-
-// Four consecutive outputs Y[m][n..n+3] (already scaled). `vec`: N % 4 == 0, so the piece is
-// 16-byte (f32) or 8-byte (bf16) aligned; otherwise, and at the right edge, element by element.
-__device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n, f32x4 v, bool vec) {
-  const size_t idx = (size_t)m * N + n;
-  if (vec && n + 3 < N) {
-    if (y_bf16) {
-      u32x2 o;
-      o[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      o[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
-      *(u32x2*)((uint16_t*)Y + idx) = o;
-    } else {
-      *(f32x4*)((float*)Y + idx) = v;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (n + i < N) store_val(Y, y_bf16, idx + i, v[i]);
   }
 }
 

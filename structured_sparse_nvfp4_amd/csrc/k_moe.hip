@@ -1,0 +1,511 @@
+// Grouped-expert (MoE) path: routing bookkeeping, grouped NVFP4 products (dense or 2:4) with the
+// SiLU-gate epilogue, and the weighted combine.
+//
+// The pages describe a 512-expert, top-10 mixture whose expert weights are the thing every step
+// reads ("NVFP4 vs 2:4 sparse", robertz.co, sections "Concurrency, not sparsity, is the lever"
+// and "The sparsity that does pay is already running") and note that no grouped 2:4 product
+// exists for it (same page, section "Why it cannot run on this cluster"). Here every expert's
+// rows are a contiguous range of an expert-major row space (built by the routing kernels), and
+// one launch runs every (expert, 64-row tile, 256-column tile) of a projection:
+//  - rows per expert range from a handful to thousands, so the row tile is 64: small experts
+//    waste little matrix-core work and the product stays bound by the expert weight read;
+//  - the activation rows of a tile are gathered by row id straight into LDS by direct loads,
+//    the expert's weights follow the same three-stage LDS pipeline as the square tiles;
+//  - gate and up projections of one expert share a tile (128 gate + 128 up columns), so the
+//    SiLU-gate product is formed in the epilogue and only H = bf16(silu(g) * u) is written.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "pipeline.hpp"
+#include "tile.hpp"
+
+namespace ssn {
+namespace {
+
+// ------------------------------------------------------------------------------ routing
+// Rows are grouped by expert (ascending) and, inside an expert, follow the flat order
+// f = t * k + j of the (token, slot) entries: a stable counting sort by expert id.
+constexpr int kRouteChunk = 1024;   // flat entries per block
+constexpr int kRouteThreads = 256;
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_hist(const int32_t* __restrict__ ids, int F, int E,
+                                                              int32_t* __restrict__ hist) {
+  extern __shared__ int32_t h[];   // [E]
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) h[e] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kRouteChunk;
+  for (int i = threadIdx.x; i < kRouteChunk; i += kRouteThreads) {
+    const int f = base + i;
+    if (f < F) {
+      const int e = ids[f];
+      if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = hist + (size_t)blockIdx.x * E;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) out[e] = h[e];
+}
+
+// Exclusive scan of one value per thread over a block of 1024 threads.
+__device__ __forceinline__ int block_excl_scan_1024(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? wsum[lane] : 0;
+    for (int d = 1; d < 16; d <<= 1) {
+      const int t = __shfl_up(w, d, 64);
+      if (lane >= d) w += t;
+    }
+    if (lane < 16) wsum[16 + lane] = w;   // inclusive sums of the wave totals
+  }
+  __syncthreads();
+  return inc - v + (wave > 0 ? wsum[16 + wave - 1] : 0);
+}
+
+// One block: per-expert totals, expert offsets, and the absolute first row of every
+// (chunk, expert) pair (written over the histogram).
+__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist, int B, int E, int F,
+                                                     int32_t* __restrict__ offsets, int64_t* __restrict__ bad) {
+  extern __shared__ int32_t tot[];   // [E]
+  __shared__ int wsum[32];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int run = 0;
+    for (int b = 0; b < B; ++b) {
+      const int c = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  const int per = (E + 1023) / 1024;
+  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += tot[e];
+  int ex = block_excl_scan_1024(s, wsum);
+  for (int e = e0; e < e1; ++e) { const int c = tot[e]; tot[e] = ex; ex += c; }
+  if (threadIdx.x == 1023) {
+    offsets[E] = ex;                        // rows with a valid expert id
+    if (bad) *bad = (int64_t)F - ex;        // entries whose id is outside [0, E)
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    const int o = tot[e];
+    offsets[e] = o;
+    for (int b = 0; b < B; ++b) hist[(size_t)b * E + e] += o;
+  }
+}
+
+// Stable placement inside a chunk: four rounds of 256 entries; inside a wave the rank among
+// equal ids comes from ballots, across the round's waves from per-wave counts in LDS.
+__global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ ids, int F, int k,
+                                                                 int E, const int32_t* __restrict__ hist,
+                                                                 int32_t* __restrict__ row_token,
+                                                                 int32_t* __restrict__ row_slot,
+                                                                 int32_t* __restrict__ row_of) {
+  extern __shared__ int32_t sm[];
+  int32_t* cur = sm;            // [E]   next output row of each expert
+  int32_t* wc = sm + E;         // [4][E] per-wave counts of the current round
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    cur[e] = hist[(size_t)blockIdx.x * E + e];
+    for (int w = 0; w < 4; ++w) wc[w * E + e] = 0;
+  }
+  __syncthreads();
+  for (int round = 0; round < kRouteChunk / kRouteThreads; ++round) {
+    const int f = blockIdx.x * kRouteChunk + round * kRouteThreads + threadIdx.x;
+    const int e = f < F ? ids[f] : -1;
+    const bool valid = f < F && e >= 0 && e < E;
+    unsigned long long active = __ballot(valid);
+    int rank = 0, cnt = 0;
+    while (active) {
+      const int leader = __ffsll((long long)active) - 1;
+      const int el = __shfl(e, leader, 64);
+      const unsigned long long m = __ballot(valid && e == el);
+      if (valid && e == el) {
+        rank = __popcll(m & ((1ull << lane) - 1ull));
+        cnt = __popcll(m);
+      }
+      active &= ~m;
+    }
+    if (valid && rank == 0) wc[wave * E + e] = cnt;
+    __syncthreads();
+    if (valid) {
+      int pos = cur[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
+      row_token[pos] = f / k;
+      row_slot[pos] = f % k;
+      row_of[f] = pos;
+    } else if (f < F) {
+      row_of[f] = -1;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < E; x += kRouteThreads) {
+      cur[x] += wc[x] + wc[E + x] + wc[2 * E + x] + wc[3 * E + x];
+      wc[x] = 0; wc[E + x] = 0; wc[2 * E + x] = 0; wc[3 * E + x] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------------ grouped product
+constexpr int kBM = 64, kBN = 256, kBK = 64;
+constexpr int kStages = 3;
+constexpr int kThreads = 256;
+constexpr int kEpiNone = 0, kEpiSilu = 1;
+
+// One LDS ring slot (bytes): activations [64][128 B] (chunk swizzle), weights of the 256
+// tile columns (dense codes [256][32 B] with half swizzle, or 2:4 vals [256][16 B] + meta
+// [256][8 B]), scales [256][4 B].
+template <int WF>
+struct MSlot {
+  static constexpr int kX = 0;
+  static constexpr int kW = kBM * kBK * 2;
+  static constexpr int kMeta = WF == kDense ? 0 : kW + kBN * 16;
+  static constexpr int kSc = WF == kDense ? kW + kBN * 32 : kMeta + kBN * 8;
+  static constexpr int kBytes = kSc + kBN * 4;
+  static constexpr int kLoads = WF == kDense ? 2 + 2 + 1 : 2 + 1 + 2 + 1;   // per wave per stage
+};
+// epilogue staging needs: row blocks of 32 x 64 f32 per wave, or the 64 x 128 up tile
+constexpr int kStageStrideNone = 68, kStageStrideSilu = 132;
+template <int WF>
+constexpr int moe_lds_bytes() {
+  constexpr int ring = kStages * MSlot<WF>::kBytes;
+  constexpr int a = 4 * 32 * kStageStrideNone * 4, b = kBM * kStageStrideSilu * 4;
+  return ring > a ? (ring > b ? ring : b) : (a > b ? a : b);
+}
+
+// Expert e and tile j (of 64 rows) of linear tile index bx; false when bx is past the last
+// tile. Expert ranges are clamped into [0, R] so that inconsistent offsets cannot address
+// rows outside Y.
+__device__ __forceinline__ void expert_range(const int32_t* off, int e, int R, int& o0, int& o1) {
+  o0 = min(max(off[e], 0), R);
+  o1 = min(max(off[e + 1], o0), R);
+}
+
+__device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx, int& e_out, int& j_out) {
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;
+  int my = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = lane * per + i;
+    if (e < E) {
+      int o0, o1;
+      expert_range(off, e, R, o0, o1);
+      my += (o1 - o0 + kBM - 1) / kBM;
+    }
+  }
+  int inc = my;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  const int total = __shfl(inc, 63, 64);
+  if (bx >= total) return false;
+  const unsigned long long m = __ballot(bx < inc);
+  const int L = __ffsll((long long)m) - 1;
+  int acc = __shfl(inc - my, L, 64);
+  for (int i = 0; i < per; ++i) {
+    const int e = L * per + i;
+    if (e >= E) break;
+    int o0, o1;
+    expert_range(off, e, R, o0, o1);
+    const int t = (o1 - o0 + kBM - 1) / kBM;
+    if (bx < acc + t) { e_out = e; j_out = bx - acc; return true; }
+    acc += t;
+  }
+  return false;
+}
+
+template <int WF, int EPI>
+__global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __restrict__ X, int x_rows, int K,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ off, int E, int R, int N,
+                                                          const uint8_t* __restrict__ w0,
+                                                          const uint8_t* __restrict__ w1,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ ts, void* __restrict__ Y,
+                                                          int y_bf16) {
+  using L = MSlot<WF>;
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int e = 0, j = 0;
+  if (!find_tile(off, E, R, blockIdx.x, e, j)) return;
+  e = __builtin_amdgcn_readfirstlane(e);
+  j = __builtin_amdgcn_readfirstlane(j);
+  int o0, o1;
+  expert_range(off, e, R, o0, o1);
+  const int r0 = o0 + kBM * j, cnt = min(kBM, o1 - r0);
+  const int tn = blockIdx.y;
+  const int I = N / 2;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int nst = K / kBK;
+
+  // weight row of tile column tc (0..255); clamped rows are computed and never stored
+  auto wrow = [&](int tc) -> int {
+    if constexpr (EPI == kEpiSilu) return (tc >> 7) * I + min(128 * tn + (tc & 127), I - 1);
+    else return min(kBN * tn + tc, N - 1);
+  };
+
+  // per-lane sources of the direct loads
+  const uint8_t* wb = w0 + (size_t)e * N * (WF == kDense ? K / 2 : K / 4);
+  const uint8_t* mb = WF == kDense ? nullptr : w1 + (size_t)e * N * (K / 8);
+  const uint8_t* sb = scales + (size_t)e * N * (K / 16);
+  const char* xsrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 8 * (2 * wave + i) + (lane >> 3);
+    const int rr = r0 + min(r, cnt - 1);
+    int src = row_token ? row_token[rr] : rr;
+    src = min(max(src, 0), x_rows - 1);
+    const int c = (lane & 7) ^ swz(r);
+    xsrc[i] = (const char*)(X + (size_t)src * K + 8 * c);
+  }
+  const uint8_t* wsrc[2];
+  const uint8_t* msrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if constexpr (WF == kDense) {
+      const int tc = 32 * (2 * wave + i) + (lane >> 1);
+      const int hl = (lane & 1) ^ ((tc >> 3) & 1);
+      wsrc[i] = wb + (size_t)wrow(tc) * (K / 2) + 16 * hl;
+      msrc[i] = nullptr;
+    } else {
+      wsrc[i] = i == 0 ? wb + (size_t)wrow(64 * wave + lane) * (K / 4) : nullptr;
+      const int tc = 32 * (2 * wave + i) + (lane >> 1);
+      msrc[i] = mb + (size_t)wrow(tc) * (K / 8) + 4 * (lane & 1);
+    }
+  }
+  const uint8_t* ssrc = sb + (size_t)wrow(64 * wave + lane) * (K / 16);
+
+  auto issue = [&](int st, char* slot) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + st * (kBK * 2), slot + L::kX + (2 * wave + i) * 1024);
+    if constexpr (WF == kDense) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16(wsrc[i] + st * (kBK / 2), slot + L::kW + (2 * wave + i) * 1024);
+    } else {
+      lds_dma16(wsrc[0] + st * (kBK / 4), slot + L::kW + wave * 1024);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma4(msrc[i] + st * (kBK / 8), slot + L::kMeta + (2 * wave + i) * 256);
+    }
+    lds_dma4(ssrc + st * (kBK / 16), slot + L::kSc + wave * 256);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
+
+  const int last = nst - 1;
+  issue(0, lds);
+  issue(min(1, last), lds + L::kBytes);
+  for (int st = 0; st < nst; ++st) {
+    wait_vmcnt<L::kLoads>();    // stage st has landed (st + 1 may be in flight)
+    stage_barrier();            // ... for every wave; slot (st - 1) % 3 is no longer read
+    issue(min(st + 2, last), lds + ((st + 2) % kStages) * L::kBytes);
+    const char* slot = lds + (st % kStages) * L::kBytes;
+    u32x4 wc[2];
+    uint32_t wsc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int tc = 64 * wave + 32 * nt + r32;
+      if constexpr (WF == kDense) {
+        wc[nt] = *(const u32x4*)(slot + L::kW + tc * 32 + 16 * (h ^ ((tc >> 3) & 1)));
+      } else {
+        const u32x2 v = *(const u32x2*)(slot + L::kW + tc * 16 + 8 * h);
+        wc[nt][0] = v[0]; wc[nt][1] = v[1];
+        wc[nt][2] = *(const uint32_t*)(slot + L::kMeta + tc * 8 + 4 * h);
+        wc[nt][3] = 0u;
+      }
+      wsc[nt] = *(const uint32_t*)(slot + L::kSc + tc * 4) >> (16 * h);
+    }
+    u32x4 a[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int r = 32 * mt + r32;
+        a[s][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h + s) ^ swz(r)));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float f = s < 2 ? e4m3_f32_sel<0>(wsc[nt]) : e4m3_f32_sel<1>(wsc[nt]);
+        b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(wc[nt], s), f));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 av = as_bf16x8(a[s][mt]);
+        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
+        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
+      }
+    }
+  }
+  wait_vmcnt<0>();
+  __syncthreads();   // ring slots are free for the epilogue staging
+
+  // lane holds rows 8(i/4) + 4h + i%4 of each 32-row block mt, tile column 64 wave + 32 nt + r32
+  const float sc = ts[e];
+  if constexpr (EPI == kEpiNone) {
+    const bool vec = (N & 3) == 0;
+    float* T = (float*)(lds + wave * (32 * kStageStrideNone * 4));
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          T[(8 * (i >> 2) + 4 * h + (i & 3)) * kStageStrideNone + 32 * nt + r32] = acc[mt][nt][i] * sc;
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int c4 = lane & 15;
+#pragma unroll
+      for (int jr = 0; jr < 8; ++jr) {
+        const int r = (lane >> 4) + 4 * jr;
+        const int row = 32 * mt + r;
+        const f32x4 v = *(const f32x4*)(T + r * kStageStrideNone + 4 * c4);
+        const int n = kBN * tn + 64 * wave + 4 * c4;
+        if (row < cnt) store4(Y, y_bf16, N, r0 + row, n, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
+  } else {
+    // U [64 rows][128 columns]: the up projection (waves 2, 3), then H in place
+    float* U = (float*)lds;
+    constexpr int S = kStageStrideSilu;
+    if (wave >= 2) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            U[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * S + 64 * (wave - 2) + 32 * nt + r32] = acc[mt][nt][i] * sc;
+    }
+    __syncthreads();
+    if (wave < 2) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float* p = U + (32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * S + 64 * wave + 32 * nt + r32;
+            const float g = acc[mt][nt][i] * sc;
+            *p = g / (1.0f + expf(-g)) * *p;      // silu(g) * u
+          }
+    }
+    __syncthreads();
+    const bool vec = (I & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = threadIdx.x + kThreads * i;
+      const int row = p >> 5, c4 = p & 31;
+      const int jc = 128 * tn + 4 * c4;
+      const f32x4 v = *(const f32x4*)(U + row * S + 4 * c4);
+      if (row < cnt && jc < I) store4(Y, y_bf16, I, r0 + row, jc, v, vec);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ combine
+// out[t, :] = sum_j w[t, j] * Yd[row_of[t, j], :]; one block per token, j in slot order.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd, int R,
+                                                     const int32_t* __restrict__ row_of,
+                                                     const float* __restrict__ w, int k, int D,
+                                                     float* __restrict__ out) {
+  const int t = blockIdx.x;
+  for (int d0 = 4 * threadIdx.x; d0 < D; d0 += 4 * 256) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const bool full = d0 + 3 < D && (D & 3) == 0;
+    for (int jj = 0; jj < k; ++jj) {
+      const int r = row_of[(size_t)t * k + jj];
+      if (r < 0 || r >= R) continue;
+      const float wt = w[(size_t)t * k + jj];
+      if (BF16) {
+        const uint16_t* y = (const uint16_t*)Yd + (size_t)r * D;
+        for (int i = 0; i < 4; ++i)
+          if (d0 + i < D) acc[i] += wt * __uint_as_float((uint32_t)y[d0 + i] << 16);
+      } else {
+        const float* y = (const float*)Yd + (size_t)r * D;
+        if (full) {
+          const f32x4 v = *(const f32x4*)(y + d0);
+          for (int i = 0; i < 4; ++i) acc[i] += wt * v[i];
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (d0 + i < D) acc[i] += wt * y[d0 + i];
+        }
+      }
+    }
+    if (full) *(f32x4*)(out + (size_t)t * D + d0) = acc;
+    else
+      for (int i = 0; i < 4; ++i)
+        if (d0 + i < D) out[(size_t)t * D + d0 + i] = acc[i];
+  }
+}
+
+template <int WF, int EPI>
+hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
+  constexpr int bytes = moe_lds_bytes<WF>();
+  hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     bytes);
+  if (e != hipSuccess) return e;
+  // upper bound of the tile count: sum over experts of ceil(rows / 64) <= R / 64 + min(E, R)
+  const long tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
+  const int ntiles = EPI == kEpiSilu ? (int)((a.N / 2 + 127) / 128) : (int)((a.N + kBN - 1) / kBN);
+  hipLaunchKernelGGL((k_moe_gemm<WF, EPI>), dim3((unsigned)tiles, (unsigned)ntiles), dim3(kThreads), bytes, s,
+                     a.X, (int)a.x_rows, (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1,
+                     a.scales, a.ts, a.Y, a.y_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t moe_route_workspace(int64_t F, int E) {
+  const size_t B = (size_t)((F + kRouteChunk - 1) / kRouteChunk);
+  return B * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
+                            int32_t* row_slot, int32_t* row_of, int64_t* bad, void* ws, hipStream_t s) {
+  const int F = (int)(T * k);
+  const int B = (F + kRouteChunk - 1) / kRouteChunk;
+  int32_t* hist = (int32_t*)ws;
+  if (B > 0)
+    hipLaunchKernelGGL(k_route_hist, dim3(B), dim3(kRouteThreads), E * sizeof(int32_t), s, ids, F, E, hist);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), E * sizeof(int32_t), s, hist, B, E, F, offsets, bad);
+  if (B > 0)
+    hipLaunchKernelGGL(k_route_scatter, dim3(B), dim3(kRouteThreads), 5 * E * sizeof(int32_t), s, ids, F, k, E,
+                       hist, row_token, row_slot, row_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s) {
+  if (a.sparse) return a.silu ? launch_moe_gemm_t<kSp24, kEpiSilu>(a, s) : launch_moe_gemm_t<kSp24, kEpiNone>(a, s);
+  return a.silu ? launch_moe_gemm_t<kDense, kEpiSilu>(a, s) : launch_moe_gemm_t<kDense, kEpiNone>(a, s);
+}
+
+hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,
+                              int64_t T, int k, int64_t D, float* out, hipStream_t s) {
+  if (yd_bf16)
+    hipLaunchKernelGGL(k_moe_combine<true>, dim3((unsigned)T), dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out);
+  else
+    hipLaunchKernelGGL(k_moe_combine<false>, dim3((unsigned)T), dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out);
+  return hipGetLastError();
+}
+
+}  // namespace ssn

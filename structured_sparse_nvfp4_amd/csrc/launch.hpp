@@ -43,4 +43,27 @@ hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s);     // 256x
 hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s);    // 256x256 tiles, any M
 hipError_t launch_gemm_sp24_smfmac(const GemmArgs& a, hipStream_t s);    // 256x256 tiles, any M
 
+// grouped-expert (MoE) path
+struct MoeGemmArgs {
+  const uint16_t* X;        // activations [x_rows, K] bf16
+  int64_t x_rows, K;
+  const int32_t* row_token; // [R] source row of each expert-ordered row, or nullptr (identity)
+  const int32_t* offsets;   // [E + 1] device
+  int E;
+  int64_t R, N;             // rows of Y; weight rows per expert (2I for the SiLU-gate form)
+  const uint8_t* w0;        // codes [E, N, K/2] or vals [E, N, K/4]
+  const uint8_t* w1;        // meta [E, N, K/8] or nullptr
+  const uint8_t* scales;    // [E, N, K/16]
+  const float* ts;          // [E]
+  void* Y;                  // [R, N] (or [R, N/2] for the SiLU-gate form)
+  int y_bf16, sparse, silu;
+};
+
+size_t moe_route_workspace(int64_t F, int E);
+hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
+                            int32_t* row_slot, int32_t* row_of, int64_t* bad, void* ws, hipStream_t s);
+hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s);
+hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,
+                              int64_t T, int k, int64_t D, float* out, hipStream_t s);
+
 }  // namespace ssn

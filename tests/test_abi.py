@@ -84,3 +84,35 @@ def test_empty_problem_is_a_noop():
     assert L.gemm_nvfp4_sp24(None, 3, 0, 64, None, None, None, None, None, 0, 0, None, None) == ssn.SSN_OK
     assert L.sp24_decompress(None, None, 0, 64, None, None) == ssn.SSN_OK
     assert L.ssn_last_error() == b""
+
+
+def test_moe_validation_without_launch():
+    L = ssn.lib()
+    p = ctypes.c_void_p(16)
+    n = None
+    assert L.moe_route_workspace_bytes(10, 0, 8) == -1
+    assert L.moe_route_workspace_bytes(10, 2, 4096) == -1
+    assert L.moe_route_workspace_bytes(0, 2, 8) == 0
+    # top-k and expert count outside their ranges
+    assert L.moe_route(p, 10, 0, 8, p, p, p, p, n, p, 1 << 20, n) == ssn.SSN_E_RANGE
+    assert L.moe_route(p, 10, 2, 0, p, p, p, p, n, p, 1 << 20, n) == ssn.SSN_E_RANGE
+    # too small a workspace is refused before any launch
+    need = L.moe_route_workspace_bytes(5000, 10, 512)
+    assert need > 0
+    assert L.moe_route(p, 5000, 10, 512, p, p, p, p, n, p, need - 1, n) == ssn.SSN_E_RANGE
+    assert b"workspace" in L.ssn_last_error()
+    # grouped product: odd N with the SiLU gate, K not a multiple of 64, unknown epilogue and algorithms
+    used = ctypes.c_int(-1)
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 33, 64, 0, p, n, p, p, 1, p, 1, 0, n, n) == ssn.SSN_E_SHAPE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 96, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_SHAPE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, p, n, p, p, 5, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, p, n, p, p, 0, p, 0, ssn.ALGO_SMFMAC,
+                                    ctypes.byref(used), n) == ssn.SSN_E_ALGO
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 1, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_NULL
+    assert L.moe_grouped_gemm_nvfp4(p, 8, n, p, 9999, 8, 32, 64, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    # empty problems are no-ops
+    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 32, 64, 0, n, n, n, n, 0, n, 0, 0, ctypes.byref(used), n) == ssn.SSN_OK
+    assert used.value == ssn.ALGO_MFMA
+    assert L.moe_combine(n, 0, 0, n, n, 0, 4, 16, n, n) == ssn.SSN_OK
+    assert L.moe_combine(p, 7, 4, p, p, 2, 2, 16, p, n) == ssn.SSN_E_DTYPE
+    assert L.moe_ffn_workspace_bytes(4096, 10, 512, 512, 2048) > 4096 * 10 * 2048 * 4
