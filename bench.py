@@ -1,10 +1,10 @@
 """Benchmark of the NVFP4 / 2:4 weight-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|square|prefill|tiny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,prefill,moe]
 
-Prints ONE JSON line. A step is one pass of the whole hot path over one batch of synthetic
-input at the chosen workload. For the default decode workload (X [M, 5120] bf16 for
-M in {1, 4, 8}; W [13824, 5120] float32 ~ N(0, 0.02)) a step is:
+Prints ONE JSON line. ``value`` / ``ms_per_step`` / ``roofline`` / ``cpu_baseline`` describe the
+decode workload, where a step is one pass of the whole hot path over one batch of synthetic
+input (X [M, 5120] bf16 for M in {1, 4, 8}; W [13824, 5120] float32 ~ N(0, 0.02)):
 
     nvfp4_quantize(W)                        dense NVFP4 weights
     sp24_prune(W) -> nvfp4_quantize          2:4-pruned NVFP4 weights
@@ -12,15 +12,23 @@ M in {1, 4, 8}; W [13824, 5120] float32 ~ N(0, 0.02)) a step is:
     gemm_nvfp4_dense  at M = 1, 4, 8         decode GEMVs on dense weights
     gemm_nvfp4_sp24   at M = 1, 4, 8         decode GEMVs on compressed weights
 
-Inputs are resident in HBM before timing starts. The GEMVs read weight copies that were
-written several steps earlier (a ring of copies larger than the 256 MB Infinity Cache), so
-they are measured from HBM, not from cache. Every kernel is bracketed by HIP events on the
-stream it runs on; ``value`` is the algorithmic bytes of the whole step divided by the step
-time. ``roofline`` describes the kernel with the largest share of the step time.
+Inputs are resident in HBM before timing starts. The K timed steps run call by call: all K
+quantisations, then all K prunes, and so on (every step has its own ring slot of outputs, so
+the work is the same as K steps in order); HIP events on the launch stream bracket each batch,
+which gives every kernel's average duration over back-to-back launches. The GEMVs read weight
+copies written many calls earlier (a ring larger than the 256 MB Infinity Cache), so they read
+HBM. ``value`` is the algorithmic bytes of the whole step divided by the step time;
+``roofline`` describes the kernel with the largest share of the step.
+
+``workloads`` adds the other shapes, each timed the same way: the square (4096^3, f32 out) and
+prefill (8192 x 27648 x 5120, 1% outliers x20, bf16 out) products for dense MFMA, 2:4 SMFMAC
+and 2:4 expanded-to-dense MFMA, and the grouped-expert FFN (4096 tokens, 512 experts, top-10
+Zipf(1.1), D = 2048, I = 512) stage by stage, dense and 2:4.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,7 +40,9 @@ sys.path.insert(0, ROOT)
 METRIC = "NVFP4 GEMM TFLOP/s & HBM GB/s, 2:4 vs dense, % of MI355X roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 matrix peak
+SPARSE_BF16_PEAK_TFLOPS = 5000.0  # the same with 2:4 structured sparsity (dense-equivalent)
 RING = 16                       # weight copies rotated by the GEMVs (16 x 40 MB > 2 x 256 MB cache)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
@@ -40,9 +50,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode", choices=["decode"])
+    p.add_argument("--workloads", default="decode,square,prefill,moe",
+                   help="comma list; decode is always run (it defines the step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=6912, help="weight rows of the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=13824, help="weight rows of the oracle sample")
     return p.parse_args()
 
 
@@ -64,48 +75,47 @@ def bytes_compress(N, K):
     return N * K // 2 + N * K // 4 + N * K // 8
 
 
-def bytes_gemv_dense(M, N, K, y_bytes=4):
-    return N * K // 2 + N * K // 16 + M * K * 2 + M * N * y_bytes
+def bytes_w_dense(N, K):
+    return N * K // 2 + N * K // 16
 
 
-def bytes_gemv_sp24(M, N, K, y_bytes=4):
-    return N * K // 4 + N * K // 8 + N * K // 16 + M * K * 2 + M * N * y_bytes
+def bytes_w_sp24(N, K):
+    return N * K // 4 + N * K // 8 + N * K // 16
 
 
-class Timer:
-    """Per-name HIP event pairs recorded on the current stream, which is also the stream the
-    prepared calls launch on. Events are created up front so recording costs one call each."""
+def bytes_gemm(M, N, K, sparse, y_bytes):
+    return (bytes_w_sp24(N, K) if sparse else bytes_w_dense(N, K)) + M * K * 2 + M * N * y_bytes
 
-    def __init__(self, torch, pool=4096):
+
+class Batches:
+    """Event pairs around batches of back-to-back launches on the current stream (the stream
+    the prepared calls launch on)."""
+
+    def __init__(self, torch):
         self.torch = torch
-        self.free = [torch.cuda.Event(enable_timing=True) for _ in range(pool)]
         self.ev = {}
 
-    def __call__(self, name, fn):
-        a, b = self.free.pop(), self.free.pop()
+    def run(self, name, fns):
+        a = self.torch.cuda.Event(enable_timing=True)
+        b = self.torch.cuda.Event(enable_timing=True)
         a.record()
-        fn()
+        for f in fns:
+            f()
         b.record()
-        self.ev.setdefault(name, []).append((a, b))
+        self.ev[name] = (a, b, len(fns))
 
-    def mean_ms(self, name):
-        pairs = self.ev[name]
-        return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
-
-    def reset(self):
-        for pairs in self.ev.values():
-            for a, b in pairs:
-                self.free += [a, b]
-        self.ev = {}
+    def us(self, name):
+        a, b, n = self.ev[name]
+        return a.elapsed_time(b) * 1e3 / n
 
 
 def hbm_probe(torch, ssn):
     """Measured bandwidth on this GPU: a 2 GiB device copy and a 2 GiB streaming read
-    (sp24_check over 2 GiB of codes reads every byte once and writes two counters)."""
+    (sp24_check over 2 GiB of zero codes reads every byte once; every group passes, so the
+    counters are never touched)."""
     n = 1 << 31
-    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src = torch.zeros(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
-    src.fill_(0x11)
     codes = src.view(1 << 16, n >> 16)
     for _ in range(2):
         dst.copy_(src)
@@ -126,6 +136,22 @@ def hbm_probe(torch, ssn):
     return res
 
 
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, only if the kernel's
+    source is unchanged since the counters were taken (else None)."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(kernel)
+        if not t:
+            return None
+        with open(os.path.join(ROOT, t["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
+                return None
+        return int(t["fetch_bytes"] + t["write_bytes"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 # ------------------------------------------------------------------------------------------
 def run_decode(args, torch, ssn, synth):
     N, K, Ms = 13824, 5120, (1, 4, 8)
@@ -134,8 +160,8 @@ def run_decode(args, torch, ssn, synth):
     w = synth.weights(N, K)
     X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
     W = torch.from_numpy(w).to(dev)
-    Wp = torch.empty_like(W)
     u8 = dict(dtype=torch.uint8, device=dev)
+    wps = [torch.empty_like(W) for _ in range(2)]   # pruned copies, alternating
     dense = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8),
                   ts=torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(RING)]
     sparse = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8),
@@ -145,69 +171,62 @@ def run_decode(args, torch, ssn, synth):
     Yd = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
     Ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
     Xm = {M: X[:M].contiguous() for M in Ms}
-    T = Timer(torch)
-    # every call of the step, marshalled once per ring slot
-    calls = []
-    for j in range(RING):
-        d, sp = dense[j], sparse[j]
-        rd, rs = dense[(j + RING // 2) % RING], sparse[(j + RING // 2) % RING]
-        c = [("quantize", ssn.nvfp4_quantize(W, codes=d["codes"], scales=d["scales"], tensor_scale_out=d["ts"],
-                                             prepare=True)[0]),
-             ("prune", ssn.sp24_prune(W, out=Wp, prepare=True)[0]),
-             ("quantize_pruned", ssn.nvfp4_quantize(Wp, codes=sp["codes"], scales=sp["scales"],
-                                                    tensor_scale_out=sp["ts"], prepare=True)[0]),
-             ("check", ssn.sp24_check(sp["codes"], bad_groups=sp["bad"], first_bad=sp["first"], prepare=True)[0]),
-             ("compress", ssn.sp24_compress(sp["codes"], vals=sp["vals"], meta=sp["meta"], bad_groups=sp["bad"],
-                                            prepare=True)[0])]
-        for M in Ms:
-            c.append((f"gemv_dense_M{M}", ssn.gemm_nvfp4_dense(Xm[M], rd["codes"], rd["scales"], rd["ts"], Y=Yd[M],
-                                                               prepare=True)))
-        for M in Ms:
-            c.append((f"gemv_sp24_M{M}", ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"],
-                                                             Y=Ys[M], prepare=True)))
-        calls.append(c)
+    names = ["quantize", "prune", "quantize_pruned", "check", "compress"] + \
+            [f"gemv_dense_M{M}" for M in Ms] + [f"gemv_sp24_M{M}" for M in Ms]
+    calls = {n: [] for n in names}
     used = {}
+    for j in range(RING):
+        d, sp, wp = dense[j], sparse[j], wps[j % 2]
+        rd, rs = dense[(j + RING // 2) % RING], sparse[(j + RING // 2) % RING]
+        calls["quantize"].append(ssn.nvfp4_quantize(W, codes=d["codes"], scales=d["scales"], tensor_scale_out=d["ts"],
+                                                    prepare=True)[0])
+        calls["prune"].append(ssn.sp24_prune(W, out=wp, prepare=True)[0])
+        calls["quantize_pruned"].append(ssn.nvfp4_quantize(wp, codes=sp["codes"], scales=sp["scales"],
+                                                           tensor_scale_out=sp["ts"], prepare=True)[0])
+        calls["check"].append(ssn.sp24_check(sp["codes"], bad_groups=sp["bad"], first_bad=sp["first"],
+                                             prepare=True)[0])
+        calls["compress"].append(ssn.sp24_compress(sp["codes"], vals=sp["vals"], meta=sp["meta"],
+                                                   bad_groups=sp["bad"], prepare=True)[0])
+        for M in Ms:
+            p, (_, u) = ssn.gemm_nvfp4_dense(Xm[M], rd["codes"], rd["scales"], rd["ts"], Y=Yd[M], prepare=True)
+            calls[f"gemv_dense_M{M}"].append(p)
+            used[f"gemv_dense_M{M}"] = u
+            p, (_, u) = ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"], Y=Ys[M],
+                                            prepare=True)
+            calls[f"gemv_sp24_M{M}"].append(p)
+            used[f"gemv_sp24_M{M}"] = u
+    B = Batches(torch)
 
-    def step(i):
-        for name, call in calls[i % RING]:
-            if isinstance(call, tuple):            # GEMMs return (prepared, (Y, algo_used))
-                T(name, call[0])
-                used[name] = call[1][1]
-            else:
-                T(name, call)
+    def steps(count):
+        # `count` steps, call by call; step i uses ring slot i % RING
+        for n in names:
+            B.run(n, [calls[n][i % RING] for i in range(count)])
 
-    # fill every ring slot once so the GEMVs always read valid weights
-    for i in range(RING):
-        step(i)
+    steps(RING)                        # every ring slot holds valid weights
     torch.cuda.synchronize()
-    T.reset()
-    for i in range(args.warmup):
-        step(i)
+    steps(args.warmup)
     torch.cuda.synchronize()
-    T.reset()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
+    steps(args.steps)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
 
     kb = {"quantize": bytes_quantize(N, K), "prune": bytes_prune(N, K), "quantize_pruned": bytes_quantize(N, K),
           "check": bytes_check(N, K), "compress": bytes_compress(N, K)}
     for M in Ms:
-        kb[f"gemv_dense_M{M}"] = bytes_gemv_dense(M, N, K)
-        kb[f"gemv_sp24_M{M}"] = bytes_gemv_sp24(M, N, K)
+        kb[f"gemv_dense_M{M}"] = bytes_gemm(M, N, K, False, 4)
+        kb[f"gemv_sp24_M{M}"] = bytes_gemm(M, N, K, True, 4)
     kernels = {}
     for name, b in kb.items():
-        ms = T.mean_ms(name)
-        e = {"us": round(ms * 1e3, 2), "alg_bytes": b, "GBps": round(b / (ms * 1e-3) / 1e9, 1),
-             "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        us = B.us(name)
+        e = {"us": round(us, 2), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
+             "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
         if name.startswith("gemv"):
             M = int(name.split("_M")[1])
             flops = 2 * M * N * K
-            e["tflops_dense_equiv"] = round(flops / (ms * 1e-3) / 1e12, 3)
+            e["tflops_dense_equiv"] = round(flops / (us * 1e-6) / 1e12, 3)
             if "sp24" in name:
-                e["tflops_actual"] = round(flops / 2 / (ms * 1e-3) / 1e12, 3)
+                e["tflops_actual"] = round(flops / 2 / (us * 1e-6) / 1e12, 3)
             e["algo"] = ssn.ALGO_NAMES.get(used[name].value, "?")
         kernels[name] = e
     for M in Ms:
@@ -217,7 +236,7 @@ def run_decode(args, torch, ssn, synth):
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dominant]
     roof = {"kernel": dominant, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": None}
+            "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dominant)}
     result = {
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(ms_step, 4),
         "dtype": "bf16",
@@ -229,9 +248,139 @@ def run_decode(args, torch, ssn, synth):
     return result, (w, x)
 
 
+# ------------------------------------------------------------------------------------------
+def _gpu_weights(ssn, W):
+    """Dense and 2:4 NVFP4 forms of W (device float32) made on the GPU."""
+    codes, scales, ts = ssn.nvfp4_quantize(W)
+    Wp = ssn.sp24_prune(W)
+    pc, ps, pts = ssn.nvfp4_quantize(Wp)
+    vals, meta, _ = ssn.sp24_compress(pc)
+    del Wp, pc
+    return (codes, scales, ts), (vals, meta, ps, pts)
+
+
+def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
+    x = synth.activations(M, K)
+    w = synth.weight_rows_with_outliers(N, K, 0, N, 0.01, 20.0) if outliers else synth.weights(N, K)
+    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    W = torch.from_numpy(w).cuda()
+    del w, x
+    dn, sp = _gpu_weights(ssn, W)
+    del W
+    Y = torch.empty((M, N), dtype=y_dtype, device="cuda")
+    yb = 2 if y_dtype == torch.bfloat16 else 4
+    variants = [("dense_mfma", False, ssn.ALGO_MFMA), ("sp24_smfmac", True, ssn.ALGO_SMFMAC),
+                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA)]
+    B = Batches(torch)
+    preps = {}
+    for vname, sparse, algo in variants:
+        if sparse:
+            p, _ = ssn.gemm_nvfp4_sp24(X, sp[0], sp[1], sp[2], sp[3], y_dtype=y_dtype, algo=algo, Y=Y, prepare=True)
+        else:
+            p, _ = ssn.gemm_nvfp4_dense(X, dn[0], dn[1], dn[2], y_dtype=y_dtype, algo=algo, Y=Y, prepare=True)
+        preps[vname] = p
+    for vname in preps:                      # warm-up
+        B.run(vname, [preps[vname]] * 2)
+    torch.cuda.synchronize()
+    for vname in preps:
+        B.run(vname, [preps[vname]] * reps)
+    torch.cuda.synchronize()
+    flops = 2.0 * M * N * K
+    out = {"shape": {"M": M, "N": N, "K": K, "y": "bf16" if yb == 2 else "f32", "outliers": outliers},
+           "flops_dense_equiv": flops}
+    for vname, sparse, algo in variants:
+        us = B.us(vname)
+        b = bytes_gemm(M, N, K, sparse, yb)
+        e = {"us": round(us, 1), "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
+             "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1)}
+        if sparse:
+            e["tflops_actual"] = round(flops / 2 / (us * 1e-6) / 1e12, 1)
+            e["mfma_frac_actual_vs_bf16_peak"] = round(e["tflops_actual"] / BF16_PEAK_TFLOPS, 4)
+            if algo == ssn.ALGO_SMFMAC:
+                e["mfma_frac_vs_sparse_peak"] = round(e["tflops_dense_equiv"] / SPARSE_BF16_PEAK_TFLOPS, 4)
+        else:
+            e["mfma_frac"] = round(e["tflops_dense_equiv"] / BF16_PEAK_TFLOPS, 4)
+        out[vname] = e
+    for vname in ("sp24_smfmac", "sp24_decompress_mfma"):
+        out[vname]["speedup_vs_dense"] = round(out["dense_mfma"]["us"] / out[vname]["us"], 3)
+    del X, Y, dn, sp, preps
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_moe(torch, ssn, synth, reps):
+    import numpy as np
+    T, E, k, D, I = 4096, 512, 10, 2048, 512
+    ids, wts = synth.routing(T, E, k, 1.1)
+    x = synth.activations(T, D)
+    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    dids, dw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+
+    def build(rows, cols, sparse):
+        c = torch.empty((E, rows, cols // (4 if sparse else 2)), dtype=torch.uint8, device="cuda")
+        m = torch.empty((E, rows, cols // 8), dtype=torch.uint8, device="cuda") if sparse else None
+        s = torch.empty((E, rows, cols // 16), dtype=torch.uint8, device="cuda")
+        ts = torch.empty(E, dtype=torch.float32, device="cuda")
+        for e in range(E):
+            Wf = torch.randn(rows, cols, device="cuda", generator=g) * 0.02
+            if sparse:
+                Wf = ssn.sp24_prune(Wf)
+                codes, _, _ = ssn.nvfp4_quantize(Wf, scales=s[e], tensor_scale_out=ts[e:e + 1])
+                ssn.sp24_compress(codes, vals=c[e], meta=m[e])
+            else:
+                ssn.nvfp4_quantize(Wf, codes=c[e], scales=s[e], tensor_scale_out=ts[e:e + 1])
+        return c, m, s, ts
+
+    R = T * k
+    flops = 2.0 * R * D * 2 * I + 2.0 * R * I * D
+    counts = np.bincount(ids.ravel(), minlength=E)
+    out = {"shape": {"T": T, "E": E, "top_k": k, "D": D, "I": I, "rows": R, "zipf_s": 1.1,
+                     "experts_touched": int((counts > 0).sum()), "max_rows": int(counts.max()),
+                     "median_rows": float(np.median(counts))},
+           "flops_dense_equiv": flops,
+           "note": "expert weights ~N(0, 0.02) drawn on the GPU (torch generator, seed 0); routing and X from the "
+                   "seeded synthetic generators"}
+    for sparse in (False, True):
+        up, down = build(2 * I, D, sparse), build(D, I, sparse)
+        H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+        Yd = torch.empty((R, D), dtype=torch.float32, device="cuda")
+        off, rt, rs, ro, bad = ssn.moe_route(dids, E)
+        p_route, _ = ssn.moe_route(dids, E, prepare=True)
+        p_up, _ = ssn.moe_grouped_gemm_nvfp4(X, rt, off, R, up[0], up[2], up[3], w_meta=up[1],
+                                             epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, Y=H, prepare=True)
+        p_down, _ = ssn.moe_grouped_gemm_nvfp4(H, None, off, R, down[0], down[2], down[3], w_meta=down[1], Y=Yd,
+                                               prepare=True)
+        p_comb, _ = ssn.moe_combine(Yd, ro, dw, prepare=True)
+        p_ffn, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up, down, prepare=True)
+        B = Batches(torch)
+        stages = [("route", p_route), ("up_silu_gate", p_up), ("down", p_down), ("combine", p_comb), ("ffn", p_ffn)]
+        for n, p in stages:
+            B.run(n, [p] * 2)
+        torch.cuda.synchronize()
+        for n, p in stages:
+            B.run(n, [p] * reps)
+        torch.cuda.synchronize()
+        wbytes = sum(t.numel() for t in (up[0], up[1], up[2], down[0], down[1], down[2]) if t is not None)
+        ffn_bytes = wbytes + T * D * 2 + 2 * R * I * 2 + T * D * 4
+        res = {n: {"us": round(B.us(n), 1)} for n, _ in stages}
+        us = res["ffn"]["us"]
+        t_roof = max(flops / (2 if sparse else 1) / (BF16_PEAK_TFLOPS * 1e12), ffn_bytes / (HBM_PEAK_GBPS * 1e9))
+        res["ffn"].update({"weight_bytes": wbytes, "alg_bytes": ffn_bytes,
+                           "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
+                           "GBps_alg": round(ffn_bytes / (us * 1e-6) / 1e9, 1),
+                           "t_roof_us": round(t_roof * 1e6, 1), "frac_of_t_roof": round(t_roof / (us * 1e-6), 4)})
+        out["sp24" if sparse else "dense"] = res
+        del up, down, H, Yd
+        torch.cuda.empty_cache()
+    out["sp24"]["ffn"]["speedup_vs_dense"] = round(out["dense"]["ffn"]["us"] / out["sp24"]["ffn"]["us"], 3)
+    return out
+
+
+# ------------------------------------------------------------------------------------------
 def cpu_baseline_decode(w, x, rows):
     """The oracle (unchanged) on the host: the decode step's calls over a sample of weight rows."""
-    import numpy as np
     from oracle import gemm, quant, sp24
     try:
         from threadpoolctl import threadpool_info
@@ -255,7 +404,7 @@ def cpu_baseline_decode(w, x, rows):
         gemm.gemm_sp24(x[:M], v, m, ps, stp)
     sec = time.perf_counter() - t0
     b = (2 * bytes_quantize(rows, K) + bytes_prune(rows, K) + bytes_check(rows, K) + bytes_compress(rows, K)
-         + sum(bytes_gemv_dense(M, rows, K) + bytes_gemv_sp24(M, rows, K) for M in (1, 4, 8)))
+         + sum(bytes_gemm(M, rows, K, False, 4) + bytes_gemm(M, rows, K, True, 4) for M in (1, 4, 8)))
     return {"value": round(b / sec / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"the decode step's calls on weight rows [0, {rows}) of {N} (K={K}), M in {{1,4,8}}; "
                       f"{sec:.1f} s on host cores; NumPy float64 oracle",
@@ -275,15 +424,30 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     ssn.lib()
+    wl = set(args.workloads.split(","))
     hbm = hbm_probe(torch, ssn)
+    print(f"[bench] hbm probe {hbm}", file=sys.stderr, flush=True)
     res, (w, x) = run_decode(args, torch, ssn, synth)
+    print(f"[bench] decode done: {res['ms_per_step']} ms/step", file=sys.stderr, flush=True)
     out = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": res["config"],
-           "roofline": res["roofline"], "hbm_measured": hbm}
-    out["kernels"] = res["kernels"]
+           "roofline": res["roofline"], "hbm_measured": hbm, "mfma_peak_bf16_TFLOPs": BF16_PEAK_TFLOPS,
+           "kernels": res["kernels"]}
+    work = {}
+    if "square" in wl:
+        work["square"] = run_gemm_shape(torch, ssn, synth, 4096, 4096, 4096, torch.float32, False, 10)
+        print("[bench] square done", file=sys.stderr, flush=True)
+    if "prefill" in wl:
+        work["prefill"] = run_gemm_shape(torch, ssn, synth, 8192, 27648, 5120, torch.bfloat16, True, 5)
+        print("[bench] prefill done", file=sys.stderr, flush=True)
+    if "moe" in wl:
+        work["moe"] = run_moe(torch, ssn, synth, 5)
+        print("[bench] moe done", file=sys.stderr, flush=True)
+    out["workloads"] = work
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_decode(w, x, args.cpu_rows)
+        print("[bench] cpu baseline done", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

@@ -156,93 +156,113 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
 }
 
 // ------------------------------------------------------------------------------ grouped product
-constexpr int kBM = 64, kBN = 256, kBK = 64;
+// With kSplitBig, rows of an expert are cut into full 256-row tiles (run by the BM = 256 form,
+// which decodes each weight once per 256 rows) and a remainder of at most 255 rows in 64-row
+// tiles (BM = 64 form). Measured on the 512-expert top-10 workload, the split was slower than
+// 64-row tiles throughout (the 256-row launch has too few tiles to fill the chip), so it is
+// off; the 256-row form stays available for routings with many rows per expert.
+constexpr int kBigRows = 256;
+constexpr bool kSplitBig = false;
+constexpr int kBN = 256, kBK = 64;
 constexpr int kStages = 3;
 constexpr int kThreads = 256;
 constexpr int kEpiNone = 0, kEpiSilu = 1;
 
-// One LDS ring slot (bytes): activations [64][128 B] (chunk swizzle), weights of the 256
-// tile columns (dense codes [256][32 B] with half swizzle, or 2:4 vals [256][16 B] + meta
+// One LDS ring slot (bytes): activations [BM][128 B] (chunk swizzle), weights of the 256 tile
+// columns (dense codes [256][32 B] with half swizzle, or 2:4 vals [256][16 B] + meta
 // [256][8 B]), scales [256][4 B].
-template <int WF>
+template <int WF, int BM>
 struct MSlot {
   static constexpr int kX = 0;
-  static constexpr int kW = kBM * kBK * 2;
+  static constexpr int kW = BM * kBK * 2;
   static constexpr int kMeta = WF == kDense ? 0 : kW + kBN * 16;
   static constexpr int kSc = WF == kDense ? kW + kBN * 32 : kMeta + kBN * 8;
   static constexpr int kBytes = kSc + kBN * 4;
-  static constexpr int kLoads = WF == kDense ? 2 + 2 + 1 : 2 + 1 + 2 + 1;   // per wave per stage
+  static constexpr int kXLoads = BM / 32;                                    // per wave per stage
+  static constexpr int kLoads = kXLoads + (WF == kDense ? 2 : 1 + 2) + 1;
 };
-// epilogue staging needs: row blocks of 32 x 64 f32 per wave, or the 64 x 128 up tile
+// epilogue staging: row blocks of 32 x 64 f32 per wave, or the BM x 128 up tile
 constexpr int kStageStrideNone = 68, kStageStrideSilu = 132;
-template <int WF>
+template <int WF, int BM>
 constexpr int moe_lds_bytes() {
-  constexpr int ring = kStages * MSlot<WF>::kBytes;
-  constexpr int a = 4 * 32 * kStageStrideNone * 4, b = kBM * kStageStrideSilu * 4;
+  constexpr int ring = kStages * MSlot<WF, BM>::kBytes;
+  constexpr int a = 4 * 32 * kStageStrideNone * 4, b = BM * kStageStrideSilu * 4;
   return ring > a ? (ring > b ? ring : b) : (a > b ? a : b);
 }
 
-// Expert e and tile j (of 64 rows) of linear tile index bx; false when bx is past the last
-// tile. Expert ranges are clamped into [0, R] so that inconsistent offsets cannot address
-// rows outside Y.
-__device__ __forceinline__ void expert_range(const int32_t* off, int e, int R, int& o0, int& o1) {
-  o0 = min(max(off[e], 0), R);
-  o1 = min(max(off[e + 1], o0), R);
+// Rows [o0, o1) of expert e, clamped into [0, R] so that inconsistent offsets cannot address
+// rows outside Y; then the part a tile form covers: full 256-row tiles (BIG) or the rest.
+template <bool BIG>
+__device__ __forceinline__ void expert_part(const int32_t* off, int e, int R, int& a, int& b) {
+  const int o0 = min(max(off[e], 0), R);
+  const int o1 = min(max(off[e + 1], o0), R);
+  const int full = kSplitBig ? o0 + (o1 - o0) / kBigRows * kBigRows : o0;
+  a = BIG ? o0 : full;
+  b = BIG ? full : o1;
 }
 
-__device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx, int& e_out, int& j_out) {
-  const int lane = threadIdx.x & 63;
-  const int per = (E + 63) / 64;
-  int my = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = lane * per + i;
-    if (e < E) {
-      int o0, o1;
-      expert_range(off, e, R, o0, o1);
-      my += (o1 - o0 + kBM - 1) / kBM;
+// Expert, first row and row count of linear tile bx (all threads of the block take part:
+// every thread sums the tiles of E / 256 experts, a block scan finds the owner). False when
+// bx is past the last tile (uniformly for the block).
+template <int BM, bool BIG>
+__device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx, int& e_out, int& r0_out,
+                          int& cnt_out) {
+  __shared__ int sm[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (E + kThreads - 1) / kThreads;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int t = 0;
+  for (int e = e0; e < e1; ++e) {
+    int a, b;
+    expert_part<BIG>(off, e, R, a, b);
+    t += (b - a + BM - 1) / BM;
+  }
+  int inc = t;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += v;
+  }
+  if (lane == 63) sm[wave] = inc;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sm[w];
+  const int total = sm[0] + sm[1] + sm[2] + sm[3];
+  const int excl = before + inc - t;
+  if (bx >= total) return false;
+  if (bx >= excl && bx < excl + t) {
+    int acc = excl;
+    for (int e = e0; e < e1; ++e) {
+      int a, b;
+      expert_part<BIG>(off, e, R, a, b);
+      const int nt = (b - a + BM - 1) / BM;
+      if (bx < acc + nt) {
+        const int r0 = a + BM * (bx - acc);
+        sm[4] = e; sm[5] = r0; sm[6] = min(BM, b - r0);
+        break;
+      }
+      acc += nt;
     }
   }
-  int inc = my;
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += t;
-  }
-  const int total = __shfl(inc, 63, 64);
-  if (bx >= total) return false;
-  const unsigned long long m = __ballot(bx < inc);
-  const int L = __ffsll((long long)m) - 1;
-  int acc = __shfl(inc - my, L, 64);
-  for (int i = 0; i < per; ++i) {
-    const int e = L * per + i;
-    if (e >= E) break;
-    int o0, o1;
-    expert_range(off, e, R, o0, o1);
-    const int t = (o1 - o0 + kBM - 1) / kBM;
-    if (bx < acc + t) { e_out = e; j_out = bx - acc; return true; }
-    acc += t;
-  }
-  return false;
+  __syncthreads();
+  e_out = sm[4]; r0_out = sm[5]; cnt_out = sm[6];
+  return true;
 }
 
-template <int WF, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __restrict__ X, int x_rows, int K,
-                                                          const int32_t* __restrict__ row_token,
-                                                          const int32_t* __restrict__ off, int E, int R, int N,
-                                                          const uint8_t* __restrict__ w0,
-                                                          const uint8_t* __restrict__ w1,
-                                                          const uint8_t* __restrict__ scales,
-                                                          const float* __restrict__ ts, void* __restrict__ Y,
-                                                          int y_bf16) {
-  using L = MSlot<WF>;
+template <int WF, int EPI, int BM>
+__global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
+    const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
+    const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+    void* __restrict__ Y, int y_bf16) {
+  using L = MSlot<WF, BM>;
+  constexpr int MT = BM / 32;   // 32-row blocks per wave
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int e = 0, j = 0;
-  if (!find_tile(off, E, R, blockIdx.x, e, j)) return;
+  int e, r0, cnt;
+  if (!find_tile<BM, BM == kBigRows>(off, E, R, blockIdx.x, e, r0, cnt)) return;
   e = __builtin_amdgcn_readfirstlane(e);
-  j = __builtin_amdgcn_readfirstlane(j);
-  int o0, o1;
-  expert_range(off, e, R, o0, o1);
-  const int r0 = o0 + kBM * j, cnt = min(kBM, o1 - r0);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  cnt = __builtin_amdgcn_readfirstlane(cnt);
   const int tn = blockIdx.y;
   const int I = N / 2;
   const int r32 = lane & 31, h = lane >> 5;
@@ -258,10 +278,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
   const uint8_t* wb = w0 + (size_t)e * N * (WF == kDense ? K / 2 : K / 4);
   const uint8_t* mb = WF == kDense ? nullptr : w1 + (size_t)e * N * (K / 8);
   const uint8_t* sb = scales + (size_t)e * N * (K / 16);
-  const char* xsrc[2];
+  const char* xsrc[L::kXLoads];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 8 * (2 * wave + i) + (lane >> 3);
+  for (int i = 0; i < L::kXLoads; ++i) {
+    const int r = 8 * (L::kXLoads * wave + i) + (lane >> 3);
     const int rr = r0 + min(r, cnt - 1);
     int src = row_token ? row_token[rr] : rr;
     src = min(max(src, 0), x_rows - 1);
@@ -287,7 +307,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
 
   auto issue = [&](int st, char* slot) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(xsrc[i] + st * (kBK * 2), slot + L::kX + (2 * wave + i) * 1024);
+    for (int i = 0; i < L::kXLoads; ++i)
+      lds_dma16(xsrc[i] + st * (kBK * 2), slot + L::kX + (L::kXLoads * wave + i) * 1024);
     if constexpr (WF == kDense) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) lds_dma16(wsrc[i] + st * (kBK / 2), slot + L::kW + (2 * wave + i) * 1024);
@@ -299,9 +320,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
     lds_dma4(ssrc + st * (kBK / 16), slot + L::kSc + wave * 256);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[MT][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -330,17 +351,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
       }
       wsc[nt] = *(const uint32_t*)(slot + L::kSc + tc * 4) >> (16 * h);
     }
-    u32x4 a[4][2];
+    // activation operands of MFMA step s + 1 are read while step s runs
+    u32x4 a[2][MT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int r = 32 * mt + r32;
-        a[s][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h + s) ^ swz(r)));
-      }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = 32 * mt + r32;
+      a[0][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h) ^ swz(r)));
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int r = 32 * mt + r32;
+          a[(s + 1) & 1][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h + s + 1) ^ swz(r)));
+        }
+      }
       bf16x8 b[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -348,8 +374,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
         b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(wc[nt], s), f));
       }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 av = as_bf16x8(a[s][mt]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 av = as_bf16x8(a[s & 1][mt]);
         acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
         acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
       }
@@ -364,7 +390,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
     const bool vec = (N & 3) == 0;
     float* T = (float*)(lds + wave * (32 * kStageStrideNone * 4));
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -383,12 +409,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
       __builtin_amdgcn_s_waitcnt(0xC07F);
     }
   } else {
-    // U [64 rows][128 columns]: the up projection (waves 2, 3), then H in place
+    // U [BM rows][128 columns]: the up projection (waves 2, 3), then H in place
     float* U = (float*)lds;
     constexpr int S = kStageStrideSilu;
     if (wave >= 2) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -398,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
     __syncthreads();
     if (wave < 2) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -411,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(const uint16_t* __rest
     __syncthreads();
     const bool vec = (I & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < BM * 32 / kThreads; ++i) {
       const int p = threadIdx.x + kThreads * i;
       const int row = p >> 5, c4 = p & 31;
       const int jc = 128 * tn + 4 * c4;
@@ -458,19 +484,30 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd
   }
 }
 
-template <int WF, int EPI>
+template <int WF, int EPI, int BM>
 hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
-  constexpr int bytes = moe_lds_bytes<WF>();
-  hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     bytes);
+  constexpr int bytes = moe_lds_bytes<WF, BM>();
+  hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  // upper bound of the tile count: sum over experts of ceil(rows / 64) <= R / 64 + min(E, R)
-  const long tiles = (a.R + kBM - 1) / kBM + (a.E < a.R ? a.E : a.R);
+  // upper bound of the tile count: full 256-row tiles <= R / 256; remainders (< 256 rows per
+  // expert) in 64-row tiles <= R / 64 + min(E, R)
+  const long tiles = BM == kBigRows ? a.R / kBigRows : (a.R + BM - 1) / BM + (a.E < a.R ? a.E : a.R);
+  if (tiles == 0) return hipSuccess;
   const int ntiles = EPI == kEpiSilu ? (int)((a.N / 2 + 127) / 128) : (int)((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((k_moe_gemm<WF, EPI>), dim3((unsigned)tiles, (unsigned)ntiles), dim3(kThreads), bytes, s,
+  hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM>), dim3((unsigned)tiles, (unsigned)ntiles), dim3(kThreads), bytes, s,
                      a.X, (int)a.x_rows, (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1,
                      a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
+}
+
+template <int WF, int EPI>
+hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
+  if (kSplitBig) {
+    hipError_t e = launch_moe_gemm_t<WF, EPI, kBigRows>(a, s);
+    if (e != hipSuccess) return e;
+  }
+  return launch_moe_gemm_t<WF, EPI, 64>(a, s);
 }
 
 }  // namespace
@@ -495,8 +532,8 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
 }
 
 hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s) {
-  if (a.sparse) return a.silu ? launch_moe_gemm_t<kSp24, kEpiSilu>(a, s) : launch_moe_gemm_t<kSp24, kEpiNone>(a, s);
-  return a.silu ? launch_moe_gemm_t<kDense, kEpiSilu>(a, s) : launch_moe_gemm_t<kDense, kEpiNone>(a, s);
+  if (a.sparse) return a.silu ? launch_moe_gemm_both<kSp24, kEpiSilu>(a, s) : launch_moe_gemm_both<kSp24, kEpiNone>(a, s);
+  return a.silu ? launch_moe_gemm_both<kDense, kEpiSilu>(a, s) : launch_moe_gemm_both<kDense, kEpiNone>(a, s);
 }
 
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,

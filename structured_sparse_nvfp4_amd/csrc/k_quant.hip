@@ -26,6 +26,10 @@ __device__ __forceinline__ float load_w(const void* W, int w_bf16, size_t i) {
 // ---- amax over the tensor: atomic max on the float bit pattern (|w| >= 0 orders as uint) ----
 __global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
 
+// Plain (not non-temporal) loads: the quantisation pass that follows re-reads W, and the part of
+// W still in the Infinity Cache then comes from there (that pass walks W in reverse order).
+constexpr int kAmaxUnroll = 8;
+
 __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, size_t n, uint32_t* out) {
   float m = 0.f;
   size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -34,16 +38,16 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
     const float* w = (const float*)W;
     size_t n4 = n / 4;
     size_t j = i;
-    for (; j + 3 * stride < n4; j += 4 * stride) {     // four 16-byte loads in flight per thread
-      f32x4 v[4];
+    for (; j + (kAmaxUnroll - 1) * stride < n4; j += kAmaxUnroll * stride) {   // 8 loads in flight
+      f32x4 v[kAmaxUnroll];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = ld_nt((const f32x4*)w + j + u * stride);
+      for (int u = 0; u < kAmaxUnroll; ++u) v[u] = *((const f32x4*)w + j + u * stride);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kAmaxUnroll; ++u)
         m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
     }
     for (; j < n4; j += stride) {
-      f32x4 v = ld_nt((const f32x4*)w + j);
+      f32x4 v = *((const f32x4*)w + j);
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
     }
     for (size_t j = n4 * 4 + i; j < n; j += stride) m = fmaxf(m, fabsf(w[j]));
@@ -51,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
     const uint16_t* w = (const uint16_t*)W;
     size_t n8 = n / 8;
     for (size_t j = i; j < n8; j += stride) {
-      u32x4 v = ld_nt((const u32x4*)w + j);
+      u32x4 v = *((const u32x4*)w + j);
       for (int t = 0; t < 4; ++t)
         m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[t])), fabsf(bf16_hi(v[t]))));
     }
@@ -95,32 +99,34 @@ __device__ __forceinline__ double e4m3_f64(uint32_t b) {
   return e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
 }
 
-// One thread per block of 16 values: S, then 16 codes packed into 8 bytes.
+// Four lanes per block of 16 values (a wave reads 1 KiB of f32 weights per load, lane-contiguous):
+// each lane holds 4 values, the block maximum comes from two lane shuffles, every lane of the
+// quad derives the same S and thresholds, and writes its 4 codes (2 bytes). Blocks are visited
+// from the end of W backwards, so the tail that the amax pass left in the Infinity Cache is
+// read first.
 __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16, size_t nblocks,
                                                        const float* ts, uint8_t* codes, uint8_t* scales) {
-  size_t b = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  float w[16];
+  const size_t gq = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t q = gq >> 2;                    // quad index
+  const int part = (int)(gq & 3);
+  if (q >= nblocks) return;                    // quads are whole: lanes of a quad exit together
+  const size_t b = nblocks - 1 - q;
+  float w[4];
   if (!w_bf16) {
-    const f32x4* p = (const f32x4*)((const float*)W + b * 16);
-    for (int t = 0; t < 4; ++t) {
-      f32x4 v = ld_nt(p + t);
-      w[4 * t] = v[0]; w[4 * t + 1] = v[1]; w[4 * t + 2] = v[2]; w[4 * t + 3] = v[3];
-    }
+    const f32x4 v = ld_nt((const f32x4*)((const float*)W + b * 16) + part);
+    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
   } else {
-    const u32x4* p = (const u32x4*)((const uint16_t*)W + b * 16);
-    for (int t = 0; t < 2; ++t) {
-      u32x4 v = ld_nt(p + t);
-      for (int u = 0; u < 4; ++u) { w[8 * t + 2 * u] = bf16_lo(v[u]); w[8 * t + 2 * u + 1] = bf16_hi(v[u]); }
-    }
+    const u32x2 v = ld_nt((const u32x2*)((const uint16_t*)W + b * 16) + part);
+    w[0] = bf16_lo(v[0]); w[1] = bf16_hi(v[0]); w[2] = bf16_lo(v[1]); w[3] = bf16_hi(v[1]);
   }
-  float amax = 0.f;
-  for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(w[t]));
+  float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const double st = (double)*ts;
   uint32_t S = 0;
   if (st > 0.0) S = e4m3_rne((double)amax / (6.0 * st));
   const double d = st * e4m3_f64(S);           // exact: <= 24 + 4 significant bits
-  uint32_t lo = 0, hi = 0;
+  uint32_t out = 0;                            // a block whose scale is zero stores code 0x0 throughout
   if (d > 0.0) {
     // E2M1 decision thresholds m * d (exact float64 products): ties at 0.25, 1.25, 2.5 and 5 go
     // down (code = number of thresholds strictly below |w|), at 0.75, 1.75 and 3.5 up (reached
@@ -131,17 +137,16 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16
     const float e075 = __double2float_ru(0.75 * d), e175 = __double2float_ru(1.75 * d);
     const float e35 = __double2float_ru(3.5 * d);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < 4; ++t) {
       const float a = fabsf(w[t]);
       uint32_t c = (uint32_t)(a > g025) + (uint32_t)(a >= e075) + (uint32_t)(a > g125) +
                    (uint32_t)(a >= e175) + (uint32_t)(a > g25) + (uint32_t)(a >= e35) + (uint32_t)(a > g5);
       c |= (__float_as_uint(w[t]) >> 28) & 8u;  // sign bit -> bit 3 (keeps -0 for tiny negatives)
-      if (t < 8) lo |= c << (4 * t); else hi |= c << (4 * (t - 8));
+      out |= c << (4 * t);
     }
   }
-  u32x2 o; o[0] = lo; o[1] = hi;
-  *(u32x2*)(codes + b * 8) = o;
-  scales[b] = (uint8_t)S;
+  *((uint16_t*)(codes + b * 8) + part) = (uint16_t)out;
+  if (part == 0) scales[b] = (uint8_t)S;
 }
 
 // double -> f32 rounded to odd: truncate, then set the last bit if anything was dropped. A
@@ -228,13 +233,13 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
   uint32_t* amax_bits = (uint32_t*)ts_out;  // the output slot doubles as the amax accumulator
   if (!ts_in) {
     hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, amax_bits);
-    unsigned g = (unsigned)std::min<size_t>(grid_for(n / (w_bf16 ? 8 : 4) + 1, kThreads), 4096);
+    unsigned g = (unsigned)std::min<size_t>(grid_for(n / (w_bf16 ? 8 : 4) + 1, kThreads), 2048);
     hipLaunchKernelGGL(k_amax, dim3(g), dim3(kThreads), 0, s, W, w_bf16, n, amax_bits);
   }
   hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(1), 0, s, amax_bits, ts_in, ts_out);
   const size_t nb = n / 16;
   if (nb)
-    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
+    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb * 4, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
                        (const float*)ts_out, codes, scales);
   return hipGetLastError();
 }
