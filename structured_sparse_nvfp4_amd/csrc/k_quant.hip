@@ -99,54 +99,70 @@ __device__ __forceinline__ double e4m3_f64(uint32_t b) {
   return e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
 }
 
-// Four lanes per block of 16 values (a wave reads 1 KiB of f32 weights per load, lane-contiguous):
-// each lane holds 4 values, the block maximum comes from two lane shuffles, every lane of the
-// quad derives the same S and thresholds, and writes its 4 codes (2 bytes). Blocks are visited
+// One lane per block of 16 values: S, then 16 codes packed into 8 bytes. Blocks are visited
 // from the end of W backwards, so the tail that the amax pass left in the Infinity Cache is
 // read first.
+//
+// E2M1 decision thresholds m * d (exact float64 products): ties at 0.25, 1.25, 2.5 and 5 go
+// down, at 0.75, 1.75 and 3.5 up, so code = [a > 0.25d] + [a >= 0.75d] + [a > 1.25d] +
+// [a >= 1.75d] + [a > 2.5d] + [a >= 3.5d] + [a > 5d]. For a float x: x > T <=> x > RD(T), and
+// x >= T <=> x >= RU(T), so rounding each threshold once to f32 (down, resp. up) keeps every
+// decision exact. The seven tests are evaluated as a three-level search: bit 2 of the code is
+// [a >= 1.75d], bit 1 is [a >= 0.75d] or [a >= 3.5d], bit 0 the remaining test of that quarter.
+struct Thresholds {
+  float e175, e075, e35, g025, g125, g25, g5;
+};
+
+__device__ __forceinline__ uint32_t e2m1_code(float a, const Thresholds& t) {
+  const bool b2 = a >= t.e175;
+  const bool b1 = a >= (b2 ? t.e35 : t.e075);
+  const float tl = b2 ? (b1 ? t.g5 : t.g25) : (b1 ? t.g125 : t.g025);
+  const bool b0 = a > tl;
+  return ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
+}
+
 __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16, size_t nblocks,
                                                        const float* ts, uint8_t* codes, uint8_t* scales) {
-  const size_t gq = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t q = gq >> 2;                    // quad index
-  const int part = (int)(gq & 3);
-  if (q >= nblocks) return;                    // quads are whole: lanes of a quad exit together
+  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (q >= nblocks) return;
   const size_t b = nblocks - 1 - q;
-  float w[4];
+  float w[16];
   if (!w_bf16) {
-    const f32x4 v = ld_nt((const f32x4*)((const float*)W + b * 16) + part);
-    w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    const f32x4* p = (const f32x4*)((const float*)W + b * 16);
+    for (int t = 0; t < 4; ++t) {
+      f32x4 v = ld_nt(p + t);
+      w[4 * t] = v[0]; w[4 * t + 1] = v[1]; w[4 * t + 2] = v[2]; w[4 * t + 3] = v[3];
+    }
   } else {
-    const u32x2 v = ld_nt((const u32x2*)((const uint16_t*)W + b * 16) + part);
-    w[0] = bf16_lo(v[0]); w[1] = bf16_hi(v[0]); w[2] = bf16_lo(v[1]); w[3] = bf16_hi(v[1]);
+    const u32x4* p = (const u32x4*)((const uint16_t*)W + b * 16);
+    for (int t = 0; t < 2; ++t) {
+      u32x4 v = ld_nt(p + t);
+      for (int u = 0; u < 4; ++u) { w[8 * t + 2 * u] = bf16_lo(v[u]); w[8 * t + 2 * u + 1] = bf16_hi(v[u]); }
+    }
   }
-  float amax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
-  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  float amax = 0.f;
+  for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(w[t]));
   const double st = (double)*ts;
   uint32_t S = 0;
   if (st > 0.0) S = e4m3_rne((double)amax / (6.0 * st));
   const double d = st * e4m3_f64(S);           // exact: <= 24 + 4 significant bits
-  uint32_t out = 0;                            // a block whose scale is zero stores code 0x0 throughout
+  uint32_t lo = 0, hi = 0;                     // a block whose scale is zero stores code 0x0
   if (d > 0.0) {
-    // E2M1 decision thresholds m * d (exact float64 products): ties at 0.25, 1.25, 2.5 and 5 go
-    // down (code = number of thresholds strictly below |w|), at 0.75, 1.75 and 3.5 up (reached
-    // when |w| equals them). For a float x: x > T <=> x > RD(T), and x >= T <=> x >= RU(T), so
-    // rounding each threshold once to f32 (down, resp. up) keeps every decision exact.
-    const float g025 = __double2float_rd(0.25 * d), g125 = __double2float_rd(1.25 * d);
-    const float g25 = __double2float_rd(2.5 * d), g5 = __double2float_rd(5.0 * d);
-    const float e075 = __double2float_ru(0.75 * d), e175 = __double2float_ru(1.75 * d);
-    const float e35 = __double2float_ru(3.5 * d);
+    Thresholds th;
+    th.g025 = __double2float_rd(0.25 * d); th.g125 = __double2float_rd(1.25 * d);
+    th.g25 = __double2float_rd(2.5 * d);   th.g5 = __double2float_rd(5.0 * d);
+    th.e075 = __double2float_ru(0.75 * d); th.e175 = __double2float_ru(1.75 * d);
+    th.e35 = __double2float_ru(3.5 * d);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float a = fabsf(w[t]);
-      uint32_t c = (uint32_t)(a > g025) + (uint32_t)(a >= e075) + (uint32_t)(a > g125) +
-                   (uint32_t)(a >= e175) + (uint32_t)(a > g25) + (uint32_t)(a >= e35) + (uint32_t)(a > g5);
+    for (int t = 0; t < 16; ++t) {
+      uint32_t c = e2m1_code(fabsf(w[t]), th);
       c |= (__float_as_uint(w[t]) >> 28) & 8u;  // sign bit -> bit 3 (keeps -0 for tiny negatives)
-      out |= c << (4 * t);
+      if (t < 8) lo |= c << (4 * t); else hi |= c << (4 * (t - 8));
     }
   }
-  *((uint16_t*)(codes + b * 8) + part) = (uint16_t)out;
-  if (part == 0) scales[b] = (uint8_t)S;
+  u32x2 o; o[0] = lo; o[1] = hi;
+  *(u32x2*)(codes + b * 8) = o;
+  scales[b] = (uint8_t)S;
 }
 
 // double -> f32 rounded to odd: truncate, then set the last bit if anything was dropped. A
@@ -239,7 +255,7 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
   hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(1), 0, s, amax_bits, ts_in, ts_out);
   const size_t nb = n / 16;
   if (nb)
-    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb * 4, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
+    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
                        (const float*)ts_out, codes, scales);
   return hipGetLastError();
 }
