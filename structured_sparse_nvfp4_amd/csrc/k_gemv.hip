@@ -166,12 +166,13 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(const uint16_t* __restrict__ 
 //    every load instruction reads contiguous 256-byte runs of a row (4 rows per instruction), so
 //    HBM sees long runs instead of 16 rows x 64 B per instruction.
 //  * K is streamed in stages of kSK values; kD stages are in flight (a ring of LDS buffers).
-//    Every wave issues the same number of loads per stage (clamped addresses, all lanes active),
-//    so "stage st has landed" is an exact s_waitcnt vmcnt on each wave followed by a barrier.
+//    Every wave issues a fixed number of loads per stage (clamped addresses), so "stage st has
+//    landed" is an exact s_waitcnt vmcnt on each wave followed by a barrier. Rows past the
+//    block's own range repeat its last row, so no other block's rows are read.
 //  * Inside a 256-byte row run the 16-byte chunks are stored XOR-swizzled by the row index, so
 //    the MFMA operand reads (16 rows x one chunk) hit 16 different LDS bank groups.
-//  * The activations of the stage (M rows x kSK bf16) are loaded once per block and shared by
-//    its waves.
+//  * The activations of the stage (M rows x kSK bf16) are loaded once per block (wave m loads
+//    row m) and shared by its waves.
 // Rows are processed in groups of 64 (four 16-row MFMA tiles); 16 waves: wave w computes tile
 // w & 3 on slice w >> 2 of each stage's four 128-wide slices; the four partial tiles of each row
 // tile are summed at the end.
@@ -215,7 +216,9 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
   using Lay = SlabLayout<SP24>;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // loads per wave per stage: weights (dense: 1 KB = 4 rows; 2:4: vals 512 B + meta 256 B),
-  // scales (128 B), activations (1 KB): every wave issues exactly L, all unconditionally
+  // scales (128 B), and for waves m < M the activation row m (1 KB): L loads, or L - 1 for waves
+  // without an activation row; rows past this block's range repeat its last row (no HBM traffic
+  // outside the block's own rows)
   constexpr int L = SP24 ? 4 : 3;
   static_assert(kSlabWaves == 16 && 64 * (kSK / 2) / 1024 == kSlabWaves, "one 1 KB weight load per wave per stage");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -230,30 +233,29 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
       const int k0 = st * kSK;
       if constexpr (!SP24) {                        // codes: 4 rows x 256 B
         const int rr = wave * 4 + (lane >> 4);
-        const int n = min(g0 + rr, N - 1);
+        const int n = min(g0 + rr, row_hi - 1);
         const int cb = min(k0 / 2 + 16 * ((lane & 15) ^ (rr & 15)), rowA - 16);  // K tail: clamp
         lds_dma16(w0 + (size_t)n * rowA + cb, b + Lay::kAOff + wave * 4 * Lay::kA);
       } else {                                      // vals: 4 rows x 128 B (lanes 0..31)
         const int rr = wave * 4 + ((lane >> 3) & 3);
-        const int n = min(g0 + rr, N - 1);
+        const int n = min(g0 + rr, row_hi - 1);
         const int cb = min(k0 / 4 + 16 * ((lane & 7) ^ (rr & 7)), rowA - 16);
         if (lane < 32) lds_dma16(w0 + (size_t)n * rowA + cb, b + Lay::kAOff + wave * 4 * Lay::kA);
         // meta: 4 rows x 64 B (lanes 0..15)
         const int rm = wave * 4 + ((lane >> 2) & 3);
-        const int nm = min(g0 + rm, N - 1);
+        const int nm = min(g0 + rm, row_hi - 1);
         const int mb = min(k0 / 8 + 16 * (lane & 3), K / 8 - 16);
         if (lane < 16) lds_dma16(w1 + (size_t)nm * (K / 8) + mb, b + Lay::kMetaOff + wave * 4 * Lay::kMeta);
       }
       {                                             // scales: 4 rows x 32 B (lanes 0..7)
         const int rr = wave * 4 + ((lane >> 1) & 3);
-        const int n = min(g0 + rr, N - 1);
+        const int n = min(g0 + rr, row_hi - 1);
         const int sb = min(k0 / 16 + 16 * (lane & 1), K / 16 - 16);
         if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + Lay::kScOff + wave * 4 * kSRow);
       }
-      {                                             // activations: row wave % M, 1 KB
-        const int m = wave % M;                     // rows loaded twice hold identical bytes
+      if (wave < M) {                               // activations: wave m < M loads row m, 1 KB
         const int xe = min(k0 + 8 * lane, K - 8);
-        lds_dma16(X + (size_t)m * K + xe, b + Lay::kXOff + m * kXRow);
+        lds_dma16(X + (size_t)wave * K + xe, b + Lay::kXOff + wave * kXRow);
       }
     };
 
@@ -266,7 +268,8 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
     for (int st = 0; st < kD - 1; ++st)
       if (st < nst) issue(st);
     for (int st = 0; st < nst; ++st) {
-      wait_stages<L>(min(kD - 2, nst - 1 - st));   // this wave's loads of stage st are in LDS
+      if (wave < M) wait_stages<L>(min(kD - 2, nst - 1 - st));   // this wave's loads of stage st
+      else wait_stages<L - 1>(min(kD - 2, nst - 1 - st));        // are in LDS
       stage_barrier();                              // ... every wave's; slot (st-1)%kD is free
       if (st + kD - 1 < nst) issue(st + kD - 1);
       const uint8_t* b = smem + (st % kD) * Lay::kBytes;
