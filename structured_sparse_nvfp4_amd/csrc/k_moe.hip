@@ -26,7 +26,7 @@ namespace {
 // ------------------------------------------------------------------------------ routing
 // Rows are grouped by expert (ascending) and, inside an expert, follow the flat order
 // f = t * k + j of the (token, slot) entries: a stable counting sort by expert id.
-constexpr int kRouteChunk = 1024;   // flat entries per block
+constexpr int kRouteChunk = 256;    // flat entries per block (one 256-thread round)
 constexpr int kRouteThreads = 256;
 
 __global__ __launch_bounds__(kRouteThreads) void k_route_hist(const int32_t* __restrict__ ids, int F, int E,
@@ -70,17 +70,21 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* wsum) {
 }
 
 // One block: per-expert totals, expert offsets, and the absolute first row of every
-// (chunk, expert) pair (written over the histogram).
+// (chunk, expert) pair (written over the histogram). The chunk counts of an expert are read in
+// batches of 8 independent loads, so a pass over B chunks costs B / 8 memory round trips.
+constexpr int kScanBatch = 8;
 __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist, int B, int E, int F,
                                                      int32_t* __restrict__ offsets, int64_t* __restrict__ bad) {
   extern __shared__ int32_t tot[];   // [E]
   __shared__ int wsum[32];
   for (int e = threadIdx.x; e < E; e += 1024) {
     int run = 0;
-    for (int b = 0; b < B; ++b) {
-      const int c = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < B; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < B ? hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) run += c[j];
     }
     tot[e] = run;
   }
@@ -97,13 +101,22 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 1024) {
-    const int o = tot[e];
-    offsets[e] = o;
-    for (int b = 0; b < B; ++b) hist[(size_t)b * E + e] += o;
+    int run = tot[e];
+    offsets[e] = run;
+    for (int b0 = 0; b0 < B; b0 += kScanBatch) {
+      int c[kScanBatch];
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < B ? hist[(size_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kScanBatch; ++j) {
+        if (b0 + j < B) hist[(size_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
+    }
   }
 }
 
-// Stable placement inside a chunk: four rounds of 256 entries; inside a wave the rank among
+// Stable placement inside a chunk, in rounds of 256 entries; inside a wave the rank among
 // equal ids comes from ballots, across the round's waves from per-wave counts in LDS.
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ ids, int F, int k,
                                                                  int E, const int32_t* __restrict__ hist,
@@ -164,7 +177,13 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
 constexpr int kBigRows = 256;
 constexpr bool kSplitBig = false;
 constexpr int kBN = 256, kBK = 64;
-constexpr int kStages = 3;
+#ifndef SSN_MOE_STAGES
+#define SSN_MOE_STAGES 3
+#endif
+// ring slots (kStages - 1 stages in flight): deeper for the 64-row form, which runs two
+// workgroups per CU; the 256-row form fits three slots
+template <int BM>
+constexpr int moe_stages() { return BM == 64 ? SSN_MOE_STAGES : 3; }
 constexpr int kThreads = 256;
 constexpr int kEpiNone = 0, kEpiSilu = 1;
 
@@ -185,9 +204,18 @@ struct MSlot {
 constexpr int kStageStrideNone = 68, kStageStrideSilu = 132;
 template <int WF, int BM>
 constexpr int moe_lds_bytes() {
-  constexpr int ring = kStages * MSlot<WF, BM>::kBytes;
+  constexpr int ring = moe_stages<BM>() * MSlot<WF, BM>::kBytes;
   constexpr int a = 4 * 32 * kStageStrideNone * 4, b = BM * kStageStrideSilu * 4;
   return ring > a ? (ring > b ? ring : b) : (a > b ? a : b);
+}
+
+// Item index of workgroup b of `total`: XCD b % 8 takes the contiguous run of items
+// [x * per + min(x, extra), ...) in dispatch order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int b, int total) {
+  const int per = total / kXcds, extra = total % kXcds;
+  const int x = b % kXcds, idx = b / kXcds;
+  return x * per + min(x, extra) + idx;
 }
 
 // Rows [o0, o1) of expert e, clamped into [0, R] so that inconsistent offsets cannot address
@@ -253,17 +281,23 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
-    void* __restrict__ Y, int y_bf16) {
+    void* __restrict__ Y, int y_bf16, int ncols) {
   using L = MSlot<WF, BM>;
+  constexpr int kStages = moe_stages<BM>();
   constexpr int MT = BM / 32;   // 32-row blocks per wave
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Work item t = (row tile, column tile), row-tile major. Workgroups are dealt to the eight
+  // XCDs round-robin; each XCD takes a contiguous run of items, so the column tiles of a row
+  // tile (same gathered activations) and consecutive row tiles of an expert (same weights) meet
+  // in one XCD's L2.
   int e, r0, cnt;
-  if (!find_tile<BM, BM == kBigRows>(off, E, R, blockIdx.x, e, r0, cnt)) return;
+  const int t = xcd_contiguous(blockIdx.x, gridDim.x);
+  const int tn = t % ncols;
+  if (!find_tile<BM, BM == kBigRows>(off, E, R, t / ncols, e, r0, cnt)) return;
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   cnt = __builtin_amdgcn_readfirstlane(cnt);
-  const int tn = blockIdx.y;
   const int I = N / 2;
   const int r32 = lane & 31, h = lane >> 5;
   const int nst = K / kBK;
@@ -329,12 +363,12 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
   const int last = nst - 1;
-  issue(0, lds);
-  issue(min(1, last), lds + L::kBytes);
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) issue(min(i, last), lds + i * L::kBytes);
   for (int st = 0; st < nst; ++st) {
-    wait_vmcnt<L::kLoads>();    // stage st has landed (st + 1 may be in flight)
-    stage_barrier();            // ... for every wave; slot (st - 1) % 3 is no longer read
-    issue(min(st + 2, last), lds + ((st + 2) % kStages) * L::kBytes);
+    wait_vmcnt<(kStages - 2) * L::kLoads>();   // stage st has landed (later ones may be in flight)
+    stage_barrier();            // ... for every wave; slot (st - 1) % kStages is no longer read
+    issue(min(st + kStages - 1, last), lds + ((st + kStages - 1) % kStages) * L::kBytes);
     const char* slot = lds + (st % kStages) * L::kBytes;
     u32x4 wc[2];
     uint32_t wsc[2];
@@ -487,6 +521,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd
 template <int WF, int EPI, int BM>
 hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   constexpr int bytes = moe_lds_bytes<WF, BM>();
+  static_assert(bytes <= 160 * 1024 && (BM != 64 || 2 * bytes <= 160 * 1024), "LDS budget: 64-row tiles run two workgroups per CU");
   hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
@@ -495,9 +530,10 @@ hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   const long tiles = BM == kBigRows ? a.R / kBigRows : (a.R + BM - 1) / BM + (a.E < a.R ? a.E : a.R);
   if (tiles == 0) return hipSuccess;
   const int ntiles = EPI == kEpiSilu ? (int)((a.N / 2 + 127) / 128) : (int)((a.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM>), dim3((unsigned)tiles, (unsigned)ntiles), dim3(kThreads), bytes, s,
+  if (tiles * ntiles > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM>), dim3((unsigned)(tiles * ntiles)), dim3(kThreads), bytes, s,
                      a.X, (int)a.x_rows, (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1,
-                     a.scales, a.ts, a.Y, a.y_bf16);
+                     a.scales, a.ts, a.Y, a.y_bf16, ntiles);
   return hipGetLastError();
 }
 
