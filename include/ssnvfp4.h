@@ -85,6 +85,8 @@ enum {
 };
 
 enum { SSN_EPI_NONE = 0, SSN_EPI_SILU_GATE = 1 };
+/* Weight layouts of the grouped-expert calls (see moe_pack_ktiles). */
+enum { SSN_WLAYOUT_ROWS = 0, SSN_WLAYOUT_KTILE64 = 1 };
 
 /* Thread-local message describing the last non-OK return on this thread ("" if none). */
 const char* ssn_last_error(void);
@@ -215,15 +217,31 @@ int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_
  * expert, "NVFP4 Without FP4 Hardware", ai-muninn.com, section "The shared global scale");
  * Y [R, N/2] = silu(g) * u with silu(g) = g / (1 + exp(-g)), evaluated in f32 and rounded to
  * y_dtype. R: rows of Y (offsets are clamped into [0, R]); source rows are clamped into
- * [0, x_rows). Needs K % 64 == 0 and, for SILU_GATE, N even. algo: AUTO, MFMA (dense) or
- * DECOMPRESS_MFMA (2:4, expanded to a dense operand in registers). algo_used: host, nullable.
+ * [0, x_rows). Needs K % 64 == 0 and, for SILU_GATE, N even. w_layout: SSN_WLAYOUT_ROWS (the
+ * arrays as above, as nvfp4_quantize / sp24_compress write them) or SSN_WLAYOUT_KTILE64 (all
+ * three arrays as moe_pack_ktiles writes them). algo: AUTO, MFMA (dense) or DECOMPRESS_MFMA
+ * (2:4, expanded to a dense operand in registers). algo_used: host, nullable.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, RANGE, HIP.
  * ------------------------------------------------------------------------------------------- */
 int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row_token,
                            const int32_t* expert_offsets, int E, int64_t R, int64_t N, int64_t K,
-                           int sparse, const uint8_t* w_main, const uint8_t* w_meta,
+                           int sparse, int w_layout, const uint8_t* w_main, const uint8_t* w_meta,
                            const uint8_t* w_scales, const float* tensor_scales, int epilogue,
                            void* Y, int y_dtype, int algo, int* algo_used, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * moe_pack_ktiles — the 64-k tiled layout of one expert weight array, for the grouped products.
+ * Every step of the grouped path reads all expert weights ("NVFP4 vs 2:4 sparse", robertz.co,
+ * section "Concurrency, not sparsity, is the lever"); a product tile consumes them 64 k at a
+ * time, so this layout stores, per expert, the 64-k pieces of consecutive rows next to each
+ * other: dst[e][kt][n][0:P] = src[e][n][kt*P : (kt+1)*P], kt < row_bytes / P. The bytes are
+ * unchanged (a permutation). src, dst: device, [E, N, row_bytes], caller-owned, not
+ * overlapping. piece_bytes P per 64 k: codes 32, vals 16, meta 8, scales 4 (row_bytes =
+ * K/2, K/4, K/8, K/16). Pack all three arrays of a weight set (main, meta, scales) before
+ * passing SSN_WLAYOUT_KTILE64. Errors: NULL, SHAPE, ALIGN, RANGE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece_bytes,
+                    uint8_t* dst, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * moe_combine — out[t, :] = sum_j topk_weights[t, j] * Yd[row_of[t*k + j], :], summed in slot
@@ -241,12 +259,13 @@ int64_t moe_ffn_workspace_bytes(int64_t T, int k, int E, int64_t I, int64_t D);
  * moe_nvfp4_ffn — the whole grouped-expert FFN: route, up (SILU_GATE, H bf16 [T*k, I]),
  * down (Yd f32 [T*k, D]) and combine into out f32 [T, D]. X bf16 [T, D]; topk_ids int32
  * [T, k]; topk_weights f32 [T, k]; up weights [E, 2I, D] (+ meta when sparse), up_ts f32 [E];
- * down weights [E, D, I], down_ts f32 [E]. workspace: device, at least
- * moe_ffn_workspace_bytes(T, k, E, I, D) bytes (holds the routing arrays, H and Yd).
- * bad_ids: as in moe_route. Errors: those of the four calls.
+ * down weights [E, D, I], down_ts f32 [E]; w_layout (both weight sets) as in
+ * moe_grouped_gemm_nvfp4. workspace: device, at least moe_ffn_workspace_bytes(T, k, E, I, D)
+ * bytes (holds the routing arrays, H and Yd). bad_ids: as in moe_route. Errors: those of the
+ * four calls.
  * ------------------------------------------------------------------------------------------- */
 int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids,
-                  const float* topk_weights, int k, int E, int64_t I, int sparse,
+                  const float* topk_weights, int k, int E, int64_t I, int sparse, int w_layout,
                   const uint8_t* up_main, const uint8_t* up_meta, const uint8_t* up_scales,
                   const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
                   const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids,

@@ -21,6 +21,7 @@ ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_DECOMPRESS_MFMA = 0, 1, 2, 3,
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac",
               ALGO_DECOMPRESS_MFMA: "decompress_mfma"}
 EPI_NONE, EPI_SILU_GATE = 0, 1
+WLAYOUT_ROWS, WLAYOUT_KTILE64 = 0, 1
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGS = {
@@ -36,12 +37,13 @@ _SIGS = {
     "gemm_nvfp4_sp24": ([_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _int, _int, _vp, _vp], _int),
     "moe_route_workspace_bytes": ([_i64, _int, _int], _i64),
     "moe_route": ([_vp, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp], _int),
-    "moe_grouped_gemm_nvfp4": ([_vp, _i64, _vp, _vp, _int, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp, _int,
-                                _vp, _int, _int, _vp, _vp], _int),
+    "moe_grouped_gemm_nvfp4": ([_vp, _i64, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _vp, _vp, _vp,
+                                _int, _vp, _int, _int, _vp, _vp], _int),
+    "moe_pack_ktiles": ([_vp, _i64, _i64, _i64, _i64, _vp, _vp], _int),
     "moe_combine": ([_vp, _int, _i64, _vp, _vp, _i64, _int, _i64, _vp, _vp], _int),
     "moe_ffn_workspace_bytes": ([_i64, _int, _int, _i64, _i64], _i64),
-    "moe_nvfp4_ffn": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                       _vp, _vp, _vp, _vp, _i64, _vp], _int),
+    "moe_nvfp4_ffn": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp,
+                       _vp, _vp, _vp, _vp, _vp, _i64, _vp], _int),
 }
 
 _lib = None
@@ -283,10 +285,12 @@ def moe_route(topk_ids, E, prepare=False):
 
 
 def moe_grouped_gemm_nvfp4(X, row_token, expert_offsets, R, w_main, w_scales, tensor_scales, w_meta=None,
-                           epilogue=EPI_NONE, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None, prepare=False):
+                           epilogue=EPI_NONE, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None, prepare=False,
+                           w_layout=WLAYOUT_ROWS):
     """Every expert's product in one launch. X bf16 [x_rows, K]; row_token int32 [R] or None
     (identity); expert_offsets int32 [E+1]; dense weights w_main [E, N, K/2] (w_meta None) or
     2:4 w_main [E, N, K/4] with w_meta [E, N, K/8]; w_scales [E, N, K/16]; tensor_scales f32 [E].
+    w_layout WLAYOUT_KTILE64 when the weight arrays come from moe_pack_weights.
     Returns (Y [R, N] or [R, N/2] for EPI_SILU_GATE, algorithm that ran)."""
     x_rows, K = X.shape
     E, N = w_main.shape[0], w_main.shape[1]
@@ -305,14 +309,37 @@ def moe_grouped_gemm_nvfp4(X, row_token, expert_offsets, R, w_main, w_scales, te
         raise TypeError("Y must be float32 or bfloat16")
     _need(Y, Y.dtype, "Y", (R, ncols))
     used = ctypes.c_int(-1)
-    cargs = (_ptr(X), x_rows, _ptr(row_token), _ptr(expert_offsets), E, R, N, K, int(sparse), _ptr(w_main),
-             _ptr(w_meta), _ptr(w_scales), _ptr(tensor_scales), epilogue, _ptr(Y), dt, algo, ctypes.byref(used),
-             _stream(X.device))
+    cargs = (_ptr(X), x_rows, _ptr(row_token), _ptr(expert_offsets), E, R, N, K, int(sparse), int(w_layout),
+             _ptr(w_main), _ptr(w_meta), _ptr(w_scales), _ptr(tensor_scales), epilogue, _ptr(Y), dt, algo,
+             ctypes.byref(used), _stream(X.device))
     if prepare:
         return Prepared("moe_grouped_gemm_nvfp4", cargs, (X, row_token, expert_offsets, w_main, w_meta, w_scales,
                                                           tensor_scales, used)), (Y, used)
     _check(lib().moe_grouped_gemm_nvfp4(*cargs))
     return Y, used.value
+
+
+def moe_pack_ktiles(src, piece_bytes, out=None, prepare=False):
+    """64-k tiled copy of one expert weight array [E, N, row_bytes] (uint8): out[e][kt][n] =
+    src[e][n][kt*P:(kt+1)*P] with P = piece_bytes (codes 32, vals 16, meta 8, scales 4). The
+    result keeps the shape [E, N, row_bytes]; only the byte order inside each expert changes."""
+    _need(src, torch.uint8, "src")
+    if src.dim() != 3:
+        raise ValueError("src must be [E, N, row_bytes]")
+    E, N, rb = src.shape
+    out = out if out is not None else torch.empty_like(src)
+    _need(out, torch.uint8, "out", (E, N, rb))
+    cargs = (_ptr(src), E, N, rb, int(piece_bytes), _ptr(out), _stream(src.device))
+    return _run("moe_pack_ktiles", cargs, prepare, (src,), out)
+
+
+def moe_pack_weights(w):
+    """(main, meta or None, scales, ts) in the row layout -> the same tuple in the 64-k tiled
+    layout (WLAYOUT_KTILE64)."""
+    main, meta, scales, ts = w
+    sparse = meta is not None
+    return (moe_pack_ktiles(main, 16 if sparse else 32), moe_pack_ktiles(meta, 8) if sparse else None,
+            moe_pack_ktiles(scales, 4), ts)
 
 
 def moe_combine(Yd, row_of, topk_weights, out=None, prepare=False):
@@ -330,10 +357,11 @@ def moe_combine(Yd, row_of, topk_weights, out=None, prepare=False):
     return _run("moe_combine", cargs, prepare, (Yd, row_of, topk_weights), out)
 
 
-def moe_nvfp4_ffn(X, topk_ids, topk_weights, E, up, down, out=None, prepare=False):
+def moe_nvfp4_ffn(X, topk_ids, topk_weights, E, up, down, out=None, prepare=False, w_layout=WLAYOUT_ROWS):
     """The whole grouped-expert FFN. up = (main [E, 2I, D/2 or D/4], meta or None, scales
     [E, 2I, D/16], ts [E]); down = (main [E, D, I/2 or I/4], meta or None, scales [E, D, I/16],
-    ts [E]). Returns (out f32 [T, D], bad_ids int64 [1] device)."""
+    ts [E]); w_layout WLAYOUT_KTILE64 when both come from moe_pack_weights.
+    Returns (out f32 [T, D], bad_ids int64 [1] device)."""
     T, D = X.shape
     _, k = topk_ids.shape
     I = up[2].shape[1] // 2
@@ -345,7 +373,8 @@ def moe_nvfp4_ffn(X, topk_ids, topk_weights, E, up, down, out=None, prepare=Fals
     bad = torch.empty(1, dtype=torch.int64, device=dev)
     nws = lib().moe_ffn_workspace_bytes(T, k, E, I, D)
     ws = torch.empty(max(nws, 16), dtype=torch.uint8, device=dev)
-    cargs = (_ptr(X), T, D, _ptr(topk_ids), _ptr(topk_weights), k, E, I, int(sparse), _ptr(up[0]), _ptr(up[1]),
+    cargs = (_ptr(X), T, D, _ptr(topk_ids), _ptr(topk_weights), k, E, I, int(sparse), int(w_layout), _ptr(up[0]),
+             _ptr(up[1]),
              _ptr(up[2]), _ptr(up[3]), _ptr(down[0]), _ptr(down[1]), _ptr(down[2]), _ptr(down[3]), _ptr(out),
              _ptr(bad), _ptr(ws), nws, _stream(dev))
     return _run("moe_nvfp4_ffn", cargs, prepare, (X, topk_ids, topk_weights, up, down, ws), (out, bad))

@@ -261,7 +261,7 @@ int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_
 }
 
 int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row_token, const int32_t* expert_offsets,
-                           int E, int64_t R, int64_t N, int64_t K, int sparse, const uint8_t* w_main,
+                           int E, int64_t R, int64_t N, int64_t K, int sparse, int w_layout, const uint8_t* w_main,
                            const uint8_t* w_meta, const uint8_t* w_scales, const float* tensor_scales, int epilogue,
                            void* Y, int y_dtype, int algo, int* algo_used, void* stream) {
   const char* fn = "moe_grouped_gemm_nvfp4";
@@ -272,6 +272,8 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, y_dtype, "y_dtype"))) return st;
   if (sparse != 0 && sparse != 1) return fail(SSN_E_RANGE, "%s: sparse=%d must be 0 or 1", fn, sparse);
+  if (w_layout != SSN_WLAYOUT_ROWS && w_layout != SSN_WLAYOUT_KTILE64)
+    return fail(SSN_E_RANGE, "%s: unknown weight layout %d", fn, w_layout);
   if (epilogue != SSN_EPI_NONE && epilogue != SSN_EPI_SILU_GATE)
     return fail(SSN_E_RANGE, "%s: unknown epilogue %d", fn, epilogue);
   if (epilogue == SSN_EPI_SILU_GATE && N % 2) return fail(SSN_E_SHAPE, "%s: SILU_GATE needs N even (N=%lld)", fn, (long long)N);
@@ -288,8 +290,27 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   REQUIRE_PTR(w_scales); REQUIRE_ELEM_PTR(tensor_scales); REQUIRE_PTR(Y);
   if (sparse) REQUIRE_PTR(w_meta);
   ssn::MoeGemmArgs a{X, x_rows, K, row_token, expert_offsets, E, R, N, w_main, sparse ? w_meta : nullptr, w_scales,
-                     tensor_scales, Y, y_dtype == SSN_BF16, sparse, epilogue == SSN_EPI_SILU_GATE};
+                     tensor_scales, Y, y_dtype == SSN_BF16, sparse, epilogue == SSN_EPI_SILU_GATE,
+                     w_layout == SSN_WLAYOUT_KTILE64};
   return hip_status(ssn::launch_moe_gemm(a, as_stream(stream)), fn);
+}
+
+int moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece_bytes, uint8_t* dst,
+                    void* stream) {
+  const char* fn = "moe_pack_ktiles";
+  if (E < 0 || N < 0 || row_bytes < 0 || E > kMaxExperts)
+    return fail(SSN_E_SHAPE, "%s: bad sizes (E=%lld, N=%lld, row_bytes=%lld)", fn, (long long)E, (long long)N,
+                (long long)row_bytes);
+  if (piece_bytes != 4 && piece_bytes != 8 && piece_bytes != 16 && piece_bytes != 32)
+    return fail(SSN_E_RANGE, "%s: piece_bytes=%lld must be 4, 8, 16 or 32", fn, (long long)piece_bytes);
+  if (row_bytes % piece_bytes) return fail(SSN_E_SHAPE, "%s: row_bytes=%lld is not a multiple of piece_bytes=%lld", fn,
+                                           (long long)row_bytes, (long long)piece_bytes);
+  if (E * N * row_bytes > ((int64_t)1 << 40)) return fail(SSN_E_SHAPE, "%s: array too large", fn);
+  if (E * N * row_bytes == 0) return ok();
+  REQUIRE_PTR(src); REQUIRE_PTR(dst);
+  if ((const uint8_t*)dst < src + E * N * row_bytes && src < (const uint8_t*)dst + E * N * row_bytes)
+    return fail(SSN_E_RANGE, "%s: src and dst overlap", fn);
+  return hip_status(ssn::launch_moe_pack_ktiles(src, E, N, row_bytes, piece_bytes, dst, as_stream(stream)), fn);
 }
 
 int moe_combine(const void* Yd, int yd_dtype, int64_t R, const int32_t* row_of, const float* topk_weights, int64_t T,
@@ -315,7 +336,7 @@ int64_t moe_ffn_workspace_bytes(int64_t T, int k, int E, int64_t I, int64_t D) {
 }
 
 int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids, const float* topk_weights, int k,
-                  int E, int64_t I, int sparse, const uint8_t* up_main, const uint8_t* up_meta,
+                  int E, int64_t I, int sparse, int w_layout, const uint8_t* up_main, const uint8_t* up_meta,
                   const uint8_t* up_scales, const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
                   const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids, void* workspace,
                   int64_t workspace_bytes, void* stream) {
@@ -341,10 +362,12 @@ int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_i
   float* Yd = (float*)w;
   if ((st = moe_route(topk_ids, T, k, E, offsets, row_token, row_slot, row_of, bad_ids, rws, route_ws(T, k, E), stream)))
     return st;
-  if ((st = moe_grouped_gemm_nvfp4(X, T, row_token, offsets, E, F, 2 * I, D, sparse, up_main, up_meta, up_scales, up_ts,
+  if ((st = moe_grouped_gemm_nvfp4(X, T, row_token, offsets, E, F, 2 * I, D, sparse, w_layout, up_main, up_meta,
+                                   up_scales, up_ts,
                                    SSN_EPI_SILU_GATE, H, SSN_BF16, SSN_ALGO_AUTO, nullptr, stream)))
     return st;
-  if ((st = moe_grouped_gemm_nvfp4(H, F, nullptr, offsets, E, F, D, I, sparse, down_main, down_meta, down_scales,
+  if ((st = moe_grouped_gemm_nvfp4(H, F, nullptr, offsets, E, F, D, I, sparse, w_layout, down_main, down_meta,
+                                   down_scales,
                                    down_ts, SSN_EPI_NONE, Yd, SSN_F32, SSN_ALGO_AUTO, nullptr, stream)))
     return st;
   return moe_combine(Yd, SSN_F32, F, row_of, topk_weights, T, k, D, out, stream);

@@ -13,6 +13,7 @@
 //    the expert's weights follow the same three-stage LDS pipeline as the square tiles;
 //  - gate and up projections of one expert share a tile (128 gate + 128 up columns), so the
 //    SiLU-gate product is formed in the epilogue and only H = bf16(silu(g) * u) is written.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
-    void* __restrict__ Y, int y_bf16, int ncols) {
+    void* __restrict__ Y, int y_bf16, int ncols, int ktiled) {
   using L = MSlot<WF, BM>;
   constexpr int kStages = moe_stages<BM>();
   constexpr int MT = BM / 32;   // 32-row blocks per wave
@@ -322,6 +323,14 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
     const int c = (lane & 7) ^ swz(r);
     xsrc[i] = (const char*)(X + (size_t)src * K + 8 * c);
   }
+  // Weight sources. Row-major layout: piece kt of row n at n * row_bytes + kt * piece. 64-k tiled
+  // layout: at (kt * N + n) * piece, so a stage's pieces of consecutive rows are contiguous and
+  // every load instruction reads whole cache lines.
+  const int pw = WF == kDense ? kBK / 2 : kBK / 4, pm = kBK / 8, ps = kBK / 16;   // piece bytes
+  const size_t wrs = ktiled ? pw : (size_t)K * pw / kBK, mrs = ktiled ? pm : (size_t)K * pm / kBK,
+               srs = ktiled ? ps : (size_t)K * ps / kBK;                          // row strides
+  const size_t wst = ktiled ? (size_t)N * pw : pw, mst = ktiled ? (size_t)N * pm : pm,
+               sst = ktiled ? (size_t)N * ps : ps;                                // stage strides
   const uint8_t* wsrc[2];
   const uint8_t* msrc[2];
 #pragma unroll
@@ -329,15 +338,15 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
     if constexpr (WF == kDense) {
       const int tc = 32 * (2 * wave + i) + (lane >> 1);
       const int hl = (lane & 1) ^ ((tc >> 3) & 1);
-      wsrc[i] = wb + (size_t)wrow(tc) * (K / 2) + 16 * hl;
+      wsrc[i] = wb + (size_t)wrow(tc) * wrs + 16 * hl;
       msrc[i] = nullptr;
     } else {
-      wsrc[i] = i == 0 ? wb + (size_t)wrow(64 * wave + lane) * (K / 4) : nullptr;
+      wsrc[i] = i == 0 ? wb + (size_t)wrow(64 * wave + lane) * wrs : nullptr;
       const int tc = 32 * (2 * wave + i) + (lane >> 1);
-      msrc[i] = mb + (size_t)wrow(tc) * (K / 8) + 4 * (lane & 1);
+      msrc[i] = mb + (size_t)wrow(tc) * mrs + 4 * (lane & 1);
     }
   }
-  const uint8_t* ssrc = sb + (size_t)wrow(64 * wave + lane) * (K / 16);
+  const uint8_t* ssrc = sb + (size_t)wrow(64 * wave + lane) * srs;
 
   auto issue = [&](int st, char* slot) {
 #pragma unroll
@@ -345,13 +354,13 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
       lds_dma16(xsrc[i] + st * (kBK * 2), slot + L::kX + (L::kXLoads * wave + i) * 1024);
     if constexpr (WF == kDense) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma16(wsrc[i] + st * (kBK / 2), slot + L::kW + (2 * wave + i) * 1024);
+      for (int i = 0; i < 2; ++i) lds_dma16(wsrc[i] + st * wst, slot + L::kW + (2 * wave + i) * 1024);
     } else {
-      lds_dma16(wsrc[0] + st * (kBK / 4), slot + L::kW + wave * 1024);
+      lds_dma16(wsrc[0] + st * wst, slot + L::kW + wave * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma4(msrc[i] + st * (kBK / 8), slot + L::kMeta + (2 * wave + i) * 256);
+      for (int i = 0; i < 2; ++i) lds_dma4(msrc[i] + st * mst, slot + L::kMeta + (2 * wave + i) * 256);
     }
-    lds_dma4(ssrc + st * (kBK / 16), slot + L::kSc + wave * 256);
+    lds_dma4(ssrc + st * sst, slot + L::kSc + wave * 256);
   };
 
   f32x16 acc[MT][2];
@@ -481,6 +490,21 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
   }
 }
 
+// ------------------------------------------------------------------------------ weight layout
+// 64-k tiled copy of one weight array: dst[e][kt][n][0:P] = src[e][n][kt P : (kt + 1) P], one
+// 4-byte word per thread (P is 4, 8, 16 or 32 bytes; row_bytes = (K / 64) P).
+__global__ __launch_bounds__(256) void k_pack_ktiles(const uint32_t* __restrict__ src, int64_t E, int64_t N,
+                                                     int64_t row_words, int64_t piece_words,
+                                                     uint32_t* __restrict__ dst) {
+  const int64_t per_e = N * row_words, total = E * per_e;
+  for (int64_t o = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; o < total; o += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = o / per_e, rem = o - e * per_e;
+    const int64_t kt = rem / (N * piece_words), rem2 = rem - kt * (N * piece_words);
+    const int64_t n = rem2 / piece_words, b = rem2 - n * piece_words;
+    dst[o] = src[e * per_e + n * row_words + kt * piece_words + b];
+  }
+}
+
 // ------------------------------------------------------------------------------ combine
 // out[t, :] = sum_j w[t, j] * Yd[row_of[t, j], :]; one block per token, j in slot order.
 template <bool BF16>
@@ -533,7 +557,7 @@ hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   if (tiles * ntiles > 0x7fffffffL) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM>), dim3((unsigned)(tiles * ntiles)), dim3(kThreads), bytes, s,
                      a.X, (int)a.x_rows, (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1,
-                     a.scales, a.ts, a.Y, a.y_bf16, ntiles);
+                     a.scales, a.ts, a.Y, a.y_bf16, ntiles, a.ktiled);
   return hipGetLastError();
 }
 
@@ -570,6 +594,16 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
 hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s) {
   if (a.sparse) return a.silu ? launch_moe_gemm_both<kSp24, kEpiSilu>(a, s) : launch_moe_gemm_both<kSp24, kEpiNone>(a, s);
   return a.silu ? launch_moe_gemm_both<kDense, kEpiSilu>(a, s) : launch_moe_gemm_both<kDense, kEpiNone>(a, s);
+}
+
+hipError_t launch_moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece,
+                                  uint8_t* dst, hipStream_t s) {
+  const int64_t words = E * N * (row_bytes / 4);
+  if (words == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((words + 255) / 256, 16384);
+  hipLaunchKernelGGL(k_pack_ktiles, dim3((unsigned)blocks), dim3(256), 0, s, (const uint32_t*)src, E, N, row_bytes / 4,
+                     piece / 4, (uint32_t*)dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,

@@ -57,12 +57,15 @@ struct MoeGemmArgs {
   const float* ts;          // [E]
   void* Y;                  // [R, N] (or [R, N/2] for the SiLU-gate form)
   int y_bf16, sparse, silu;
+  int ktiled;               // weights (all three arrays) in the 64-k tiled layout [E][K/64][N][piece]
 };
 
 size_t moe_route_workspace(int64_t F, int E);
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
                             int32_t* row_slot, int32_t* row_of, int64_t* bad, void* ws, hipStream_t s);
 hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s);
+hipError_t launch_moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece,
+                                  uint8_t* dst, hipStream_t s);
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,
                               int64_t T, int k, int64_t D, float* out, hipStream_t s);
 

@@ -90,6 +90,7 @@ def test_moe_validation_without_launch():
     L = ssn.lib()
     p = ctypes.c_void_p(16)
     n = None
+    p2 = ctypes.c_void_p(1 << 20)   # a second, non-overlapping fake device address
     assert L.moe_route_workspace_bytes(10, 0, 8) == -1
     assert L.moe_route_workspace_bytes(10, 2, 4096) == -1
     assert L.moe_route_workspace_bytes(0, 2, 8) == 0
@@ -103,16 +104,24 @@ def test_moe_validation_without_launch():
     assert b"workspace" in L.ssn_last_error()
     # grouped product: odd N with the SiLU gate, K not a multiple of 64, unknown epilogue and algorithms
     used = ctypes.c_int(-1)
-    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 33, 64, 0, p, n, p, p, 1, p, 1, 0, n, n) == ssn.SSN_E_SHAPE
-    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 96, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_SHAPE
-    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, p, n, p, p, 5, p, 0, 0, n, n) == ssn.SSN_E_RANGE
-    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, p, n, p, p, 0, p, 0, ssn.ALGO_SMFMAC,
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 33, 64, 0, 0, p, n, p, p, 1, p, 1, 0, n, n) == ssn.SSN_E_SHAPE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 96, 0, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_SHAPE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, 0, p, n, p, p, 5, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, 0, p, n, p, p, 0, p, 0, ssn.ALGO_SMFMAC,
                                     ctypes.byref(used), n) == ssn.SSN_E_ALGO
-    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 1, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_NULL
-    assert L.moe_grouped_gemm_nvfp4(p, 8, n, p, 9999, 8, 32, 64, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 1, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_NULL
+    assert L.moe_grouped_gemm_nvfp4(p, 8, n, p, 9999, 8, 32, 64, 0, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
     # empty problems are no-ops
-    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 32, 64, 0, n, n, n, n, 0, n, 0, 0, ctypes.byref(used), n) == ssn.SSN_OK
+    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 32, 64, 0, 0, n, n, n, n, 0, n, 0, 0, ctypes.byref(used), n) == ssn.SSN_OK
     assert used.value == ssn.ALGO_MFMA
+    # unknown weight layout
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, 7, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    # 64-k tiling of a weight array: piece sizes, divisibility, overlap, NULL, empty
+    assert L.moe_pack_ktiles(p, 2, 8, 32, 12, p2, n) == ssn.SSN_E_RANGE
+    assert L.moe_pack_ktiles(p, 2, 8, 48, 32, p2, n) == ssn.SSN_E_SHAPE
+    assert L.moe_pack_ktiles(p, 2, 8, 32, 32, p, n) == ssn.SSN_E_RANGE
+    assert L.moe_pack_ktiles(n, 2, 8, 32, 32, p2, n) == ssn.SSN_E_NULL
+    assert L.moe_pack_ktiles(n, 0, 8, 32, 32, n, n) == ssn.SSN_OK
     assert L.moe_combine(n, 0, 0, n, n, 0, 4, 16, n, n) == ssn.SSN_OK
     assert L.moe_combine(p, 7, 4, p, p, 2, 2, 16, p, n) == ssn.SSN_E_DTYPE
     assert L.moe_ffn_workspace_bytes(4096, 10, 512, 512, 2048) > 4096 * 10 * 2048 * 4

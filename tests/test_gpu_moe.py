@@ -90,9 +90,25 @@ def _product(x, q, rows=None):
     return gemm.gemm_sp24(x, q[1], q[2], q[3], q[4], rows=rows)
 
 
+def _ktiles(a, piece):
+    """The 64-k tiled layout by its definition: dst[e][kt][n] = src[e][n][kt*P:(kt+1)*P]."""
+    E, N, rb = a.shape
+    return np.ascontiguousarray(a.reshape(E, N, rb // piece, piece).transpose(0, 2, 1, 3)).reshape(E, N, rb)
+
+
+@pytest.mark.parametrize("piece", [4, 8, 16, 32])
+def test_pack_ktiles_matches_definition(piece):
+    rng = np.random.default_rng(piece)
+    for E, N, rb in [(1, 1, piece), (3, 37, 8 * piece), (5, 256, 32 * piece)]:
+        a = rng.integers(0, 256, size=(E, N, rb), dtype=np.uint8)
+        got = host(ssn.moe_pack_ktiles(dev(a), piece))
+        assert np.array_equal(got, _ktiles(a, piece))
+
+
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
 @pytest.mark.parametrize("gather", [True, False])
-def test_grouped_product_rows(sparse, gather):
+def test_grouped_product_rows(sparse, gather, layout):
     T, E, k, N, K = 90, 6, 3, 320, 192
     x = synth.activations(T, K, seed=11)
     ids = np.random.default_rng(3).integers(0, E, size=(T, k)).astype(np.int32)
@@ -108,7 +124,9 @@ def test_grouped_product_rows(sparse, gather):
     else:                                           # identity rows: X already in expert order
         X, rtok, src = x_dev(x[rts]), None, np.arange(R)
         x = x[rts]
-    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta)
+    if layout == ssn.WLAYOUT_KTILE64:
+        dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
+    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta, w_layout=layout)
     assert used == (ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA)
     yh = y_host(y)
     for e in range(E):
@@ -119,8 +137,9 @@ def test_grouped_product_rows(sparse, gather):
         assert_within_bound(yh[r0:r1], Y, B, what=f"expert {e}")
 
 
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_grouped_silu_gate(sparse):
+def test_grouped_silu_gate(sparse, layout):
     T, E, k, D, I = 70, 5, 2, 128, 160
     x = synth.activations(T, D, seed=12)
     ids = np.random.default_rng(4).integers(0, E, size=(T, k)).astype(np.int32)
@@ -128,8 +147,10 @@ def test_grouped_silu_gate(sparse):
     qs, dm, dmeta, dsc, dts = _quant_experts(ws, sparse)
     off, rt, _, _, _ = ssn.moe_route(dev(ids), E)
     R = T * k
+    if layout == ssn.WLAYOUT_KTILE64:
+        dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
     H, _ = ssn.moe_grouped_gemm_nvfp4(x_dev(x), rt, off, R, dm, dsc, dts, w_meta=dmeta,
-                                      epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16)
+                                      epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, w_layout=layout)
     Hh = y_host(H)
     offs, rts = host(off).astype(np.int64), host(rt).astype(np.int64)
     for e in range(E):
@@ -164,13 +185,16 @@ def _ffn_weights(E, I, D, sparse):
     return qu, qd, (um, umeta, usc, uts), (dm, dmeta, dsc, dts)
 
 
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_ffn_reduced_config(sparse):
+def test_ffn_reduced_config(sparse, layout):
     T, E, k, D, I = 256, 16, 4, 256, 128
     x = synth.activations(T, D, seed=13)
     ids, w = synth.routing(T, E, k, 1.1, seed=14)
     qu, qd, up, down = _ffn_weights(E, I, D, sparse)
-    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down)
+    if layout == ssn.WLAYOUT_KTILE64:
+        up, down = ssn.moe_pack_weights(up), ssn.moe_pack_weights(down)
+    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down, w_layout=layout)
     ref, tol, _ = moe.moe_ffn(x, ids, w, lambda e: qu[e], lambda e: qd[e], E, I)
     assert int(host(bad)[0]) == 0
     err = np.abs(y_host(out) - ref)
@@ -198,13 +222,16 @@ def _full_gpu_weights(E, I, D, sparse):
     return up, down
 
 
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_ffn_full_config_sampled_tokens(sparse):
+def test_ffn_full_config_sampled_tokens(sparse, layout):
     T, E, k, D, I = 4096, 512, 10, 2048, 512
     x = synth.activations(T, D)
     ids, w = synth.routing(T, E, k, 1.1)
     up, down = _full_gpu_weights(E, I, D, sparse)
-    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down)
+    if layout == ssn.WLAYOUT_KTILE64:
+        up, down = ssn.moe_pack_weights(up), ssn.moe_pack_weights(down)
+    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down, w_layout=layout)
     tokens = np.array([0, 4095])
 
     def q(gen, e):
