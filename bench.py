@@ -343,19 +343,25 @@ def run_moe(torch, ssn, synth, reps):
            "note": "expert weights ~N(0, 0.02) drawn on the GPU (torch generator, seed 0); routing and X from the "
                    "seeded synthetic generators"}
     for sparse in (False, True):
-        up, down = build(2 * I, D, sparse), build(D, I, sparse)
+        up_rows, down_rows = build(2 * I, D, sparse), build(D, I, sparse)
+        # weight preparation, once: the 64-k tiled layout of the grouped products
+        up, down = ssn.moe_pack_weights(up_rows), ssn.moe_pack_weights(down_rows)
+        kt = ssn.WLAYOUT_KTILE64
         H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
         Yd = torch.empty((R, D), dtype=torch.float32, device="cuda")
         off, rt, rs, ro, bad = ssn.moe_route(dids, E)
         p_route, _ = ssn.moe_route(dids, E, prepare=True)
         p_up, _ = ssn.moe_grouped_gemm_nvfp4(X, rt, off, R, up[0], up[2], up[3], w_meta=up[1],
-                                             epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, Y=H, prepare=True)
+                                             epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, Y=H, prepare=True,
+                                             w_layout=kt)
         p_down, _ = ssn.moe_grouped_gemm_nvfp4(H, None, off, R, down[0], down[2], down[3], w_meta=down[1], Y=Yd,
-                                               prepare=True)
+                                               prepare=True, w_layout=kt)
         p_comb, _ = ssn.moe_combine(Yd, ro, dw, prepare=True)
-        p_ffn, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up, down, prepare=True)
+        p_ffn, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up, down, prepare=True, w_layout=kt)
+        p_ffn_rows, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up_rows, down_rows, prepare=True)
         B = Batches(torch)
-        stages = [("route", p_route), ("up_silu_gate", p_up), ("down", p_down), ("combine", p_comb), ("ffn", p_ffn)]
+        stages = [("route", p_route), ("up_silu_gate", p_up), ("down", p_down), ("combine", p_comb), ("ffn", p_ffn),
+                  ("ffn_row_layout", p_ffn_rows)]
         for n, p in stages:
             B.run(n, [p] * 2)
         torch.cuda.synchronize()
@@ -367,12 +373,12 @@ def run_moe(torch, ssn, synth, reps):
         res = {n: {"us": round(B.us(n), 1)} for n, _ in stages}
         us = res["ffn"]["us"]
         t_roof = max(flops / (2 if sparse else 1) / (BF16_PEAK_TFLOPS * 1e12), ffn_bytes / (HBM_PEAK_GBPS * 1e9))
-        res["ffn"].update({"weight_bytes": wbytes, "alg_bytes": ffn_bytes,
+        res["ffn"].update({"weight_layout": "ktile64", "weight_bytes": wbytes, "alg_bytes": ffn_bytes,
                            "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
                            "GBps_alg": round(ffn_bytes / (us * 1e-6) / 1e9, 1),
                            "t_roof_us": round(t_roof * 1e6, 1), "frac_of_t_roof": round(t_roof / (us * 1e-6), 4)})
         out["sp24" if sparse else "dense"] = res
-        del up, down, H, Yd
+        del up, down, up_rows, down_rows, H, Yd
         torch.cuda.empty_cache()
     out["sp24"]["ffn"]["speedup_vs_dense"] = round(out["dense"]["ffn"]["us"] / out["sp24"]["ffn"]["us"], 3)
     return out
