@@ -23,44 +23,46 @@ __device__ __forceinline__ float load_w(const void* W, int w_bf16, size_t i) {
   return ((const float*)W)[i];
 }
 
-// ---- amax over the tensor: atomic max on the float bit pattern (|w| >= 0 orders as uint) ----
-__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+// ---- amax over the tensor: one pass of one-shot blocks, each reading a contiguous run of
+// kThreads * kAmaxUnroll 16-byte pieces and writing its block maximum to a partial slot; the
+// scale kernel reduces the partials. No accumulator has to be cleared first.
+#ifndef SSN_AMAX_UNROLL
+#define SSN_AMAX_UNROLL 8
+#endif
+#ifndef SSN_AMAX_NT
+#define SSN_AMAX_NT 0
+#endif
+constexpr int kAmaxUnroll = SSN_AMAX_UNROLL;
+constexpr size_t kAmaxPiece = (size_t)kThreads * kAmaxUnroll;   // 16-byte pieces per block
 
-// Plain (not non-temporal) loads: the quantisation pass that follows re-reads W, and the part of
-// W still in the Infinity Cache then comes from there (that pass walks W in reverse order).
-constexpr int kAmaxUnroll = 8;
-
-__global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, size_t n, uint32_t* out) {
+__device__ __forceinline__ float absmax4(f32x4 v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+__device__ __forceinline__ float absmax_bf16x8(u32x4 v) {
   float m = 0.f;
-  size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (!w_bf16) {
-    const float* w = (const float*)W;
-    size_t n4 = n / 4;
-    size_t j = i;
-    for (; j + (kAmaxUnroll - 1) * stride < n4; j += kAmaxUnroll * stride) {   // 8 loads in flight
-      f32x4 v[kAmaxUnroll];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u) v[u] = *((const f32x4*)w + j + u * stride);
+  for (int t = 0; t < 4; ++t) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[t])), fabsf(bf16_hi(v[t]))));
+  return m;
+}
+
+__global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, size_t n, float* part) {
+  const size_t per16 = w_bf16 ? 8 : 4;                       // values per 16-byte piece
+  const size_t n16 = n / per16;
+  const size_t base = (size_t)blockIdx.x * kAmaxPiece + threadIdx.x;
+  const u32x4* p = (const u32x4*)W;
+  u32x4 v[kAmaxUnroll];
 #pragma unroll
-      for (int u = 0; u < kAmaxUnroll; ++u)
-        m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3]))));
-    }
-    for (; j < n4; j += stride) {
-      f32x4 v = *((const f32x4*)w + j);
-      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
-    }
-    for (size_t j = n4 * 4 + i; j < n; j += stride) m = fmaxf(m, fabsf(w[j]));
-  } else {
-    const uint16_t* w = (const uint16_t*)W;
-    size_t n8 = n / 8;
-    for (size_t j = i; j < n8; j += stride) {
-      u32x4 v = *((const u32x4*)w + j);
-      for (int t = 0; t < 4; ++t)
-        m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[t])), fabsf(bf16_hi(v[t]))));
-    }
-    for (size_t j = n8 * 8 + i; j < n; j += stride) m = fmaxf(m, fabsf(load_w(W, 1, j)));
+  for (int u = 0; u < kAmaxUnroll; ++u) {
+    const size_t i = base + (size_t)u * kThreads;
+    const u32x4* q = p + (i < n16 ? i : 0);                  // piece 0 again past the end: harmless for a max
+    v[u] = SSN_AMAX_NT ? ld_nt(q) : *q;
   }
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < kAmaxUnroll; ++u)
+    m = fmaxf(m, w_bf16 ? absmax_bf16x8(v[u]) : absmax4(__builtin_bit_cast(f32x4, v[u])));
+  if (blockIdx.x == gridDim.x - 1)                           // values after the last whole piece
+    for (size_t j = n16 * per16 + threadIdx.x; j < n; j += kThreads) m = fmaxf(m, fabsf(load_w(W, w_bf16, j)));
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float red[kThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -68,16 +70,35 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
   if (threadIdx.x == 0) {
     float r = red[0];
     for (int k = 1; k < kThreads / 64; ++k) r = fmaxf(r, red[k]);
-    atomicMax(out, __float_as_uint(r));
+    part[blockIdx.x] = r;
   }
 }
 
 // s_t = fl32(amax / 2688): float64 division then conversion is the correctly rounded f32
 // quotient (2688 = 2^7 * 21 and 21 is odd, so the quotient is never an f32 midpoint).
-__global__ void k_finalize_scale(const uint32_t* amax_bits, const float* ts_in, float* ts_out) {
-  if (ts_in) { *ts_out = *ts_in; return; }
-  double amax = (double)__uint_as_float(*amax_bits);
-  *ts_out = (float)(amax / 2688.0);
+// One block: the maximum of the nparts block maxima, or ts_in when the caller gives s_t.
+constexpr int kFinThreads = 1024;
+__global__ __launch_bounds__(kFinThreads) void k_finalize_scale(const float* part, unsigned nparts, const float* ts_in,
+                                                                float* ts_out) {
+  if (ts_in) {
+    if (threadIdx.x == 0) *ts_out = *ts_in;
+    return;
+  }
+  float m = 0.f;
+  unsigned i = threadIdx.x;
+  for (; i + 3 * kFinThreads < nparts; i += 4 * kFinThreads)   // four loads in flight per thread
+    m = fmaxf(fmaxf(m, fmaxf(part[i], part[i + kFinThreads])),
+              fmaxf(part[i + 2 * kFinThreads], part[i + 3 * kFinThreads]));
+  for (; i < nparts; i += kFinThreads) m = fmaxf(m, part[i]);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float red[kFinThreads / 64];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int k = 1; k < kFinThreads / 64; ++k) r = fmaxf(r, red[k]);
+    *ts_out = (float)((double)r / 2688.0);
+  }
 }
 
 // E4M3 nearest-even of q >= 0, saturating at 448 (0x7E); q is an exactly rounded float64.
@@ -246,13 +267,16 @@ inline unsigned grid_for(size_t n, int per_block) { return (unsigned)((n + per_b
 hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, const float* ts_in,
                            uint8_t* codes, uint8_t* scales, float* ts_out, hipStream_t s) {
   const size_t n = (size_t)N * (size_t)K;
-  uint32_t* amax_bits = (uint32_t*)ts_out;  // the output slot doubles as the amax accumulator
+  // The block maxima are parked in the codes output (N*K/2 bytes >= 4 bytes per amax block for
+  // any K % 16 == 0 tensor); the quantisation kernel overwrites them afterwards.
+  float* part = (float*)codes;
+  unsigned nparts = 0;
   if (!ts_in) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, amax_bits);
-    unsigned g = (unsigned)std::min<size_t>(grid_for(n / (w_bf16 ? 8 : 4) + 1, kThreads), 2048);
-    hipLaunchKernelGGL(k_amax, dim3(g), dim3(kThreads), 0, s, W, w_bf16, n, amax_bits);
+    const size_t n16 = n / (w_bf16 ? 8 : 4);
+    nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece - 1) / kAmaxPiece);
+    hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
   }
-  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(1), 0, s, amax_bits, ts_in, ts_out);
+  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
   const size_t nb = n / 16;
   if (nb)
     hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
