@@ -410,6 +410,120 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
+// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. Two 8-wave workgroups per CU, each owning a
+// contiguous range of weight rows (32-row groups), stream the rows through a 3-deep LDS ring of
+// 512-wide K stages with direct-to-LDS loads (as the slab kernel above). The E4M3 block scale is
+// applied after the matrix product instead of before it: one v_mfma_f32_32x32x16_bf16 per
+// 16-wide scale block takes the E2M1 codes converted to bf16 unscaled (one
+// v_cvt_scalef32_pk_bf16_fp4 per two codes, exact) and the activations, and its 32x32 result is
+// accumulated with one f32 FMA per needed output row, times the block's scale. That costs about
+// 0.6 vector instructions per weight instead of two. Operands: A = activations (row m = lane % 32,
+// rows >= M read row 0 and are never stored), B = weights (column = weight row lane % 32); lane
+// half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
+// every stage; the eight partial sums of a row are added at the end.
+constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
+constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
+constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
+constexpr int kPsBytes = kPsXOff + kPsMaxM * kPsXRow;          // one ring slot
+
+template <int F>   // output rows per lane: M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4
+__global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
+                                                           const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           const float* __restrict__ ts, void* __restrict__ Y,
+                                                           int y_bf16, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
+  const int nst = K / kSK;
+  const int h = lane >> 5, nl = lane & 31;
+  const int xm = nl < M ? nl : 0;
+  for (int g0 = row_lo; g0 < row_hi; g0 += kPsRows) {
+    // per wave per stage: codes of rows 4w..4w+3 (1 KB), their scales, and for w < M activation
+    // row w (1 KB); rows past the block's range repeat its last row
+    auto issue = [&](int st) {
+      uint8_t* b = smem + (st % kPsStages) * kPsBytes;
+      const int k0 = st * kSK;
+      {
+        const int rr = wave * 4 + (lane >> 4);
+        const int n = min(g0 + rr, row_hi - 1);
+        const int cb = k0 / 2 + 16 * ((lane & 15) ^ (rr & 15));
+        lds_dma16(codes + (size_t)n * (K / 2) + cb, b + kPsAOff + wave * 4 * (kSK / 2));
+      }
+      {
+        const int rr = wave * 4 + ((lane >> 1) & 3);
+        const int n = min(g0 + rr, row_hi - 1);
+        const int sb = k0 / 16 + 16 * (lane & 1);
+        if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + kPsScOff + wave * 4 * kSRow);
+      }
+      if (wave < M) lds_dma16(X + (size_t)wave * K + k0 + 8 * lane, b + kPsXOff + wave * kPsXRow);
+    };
+    float acc[F];
+#pragma unroll
+    for (int i = 0; i < F; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int st = 0; st < kPsStages - 1; ++st)
+      if (st < nst) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // this wave's loads of stage st have landed (stage st + 1 may be in flight), then every wave's
+      const bool ahead = st + 1 < nst;
+      if (wave < M) { if (ahead) wait_vmcnt<3>(); else wait_vmcnt<0>(); }
+      else { if (ahead) wait_vmcnt<2>(); else wait_vmcnt<0>(); }
+      stage_barrier();
+      if (st + kPsStages - 1 < nst) issue(st + kPsStages - 1);
+      const uint8_t* b = smem + (st % kPsStages) * kPsBytes;
+      // codes words of blocks 4w..4w+3 for this lane's half: 16-byte chunk c of the row run sits
+      // at chunk c ^ (row & 15) (the slab's swizzle); block j's half h is word 2 (j & 1) + h
+      const uint8_t* arow = b + kPsAOff + nl * (kSK / 2);
+      uint32_t w[4];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint8_t* p = arow + 16 * ((2 * wave + jj) ^ (nl & 15)) + 4 * h;
+        w[2 * jj] = *(const uint32_t*)p;
+        w[2 * jj + 1] = *(const uint32_t*)(p + 8);
+      }
+      const uint32_t sw = *(const uint32_t*)(b + kPsScOff + nl * kSRow + 4 * wave);
+      const uint8_t* xr = b + kPsXOff + xm * kPsXRow;
+      f32x16 d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 xv = *(const u32x4*)(xr + 2 * (16 * (4 * wave + j) + 8 * h));
+        u32x4 bw;
+        bw[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 0));
+        bw[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 1));
+        bw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 2));
+        bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 3));
+        f32x16 z = {};
+        d[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv), as_bf16x8(bw), z, 0, 0, 0);
+      }
+      const float s0 = e4m3_f32_sel<0>(sw), s1 = e4m3_f32_sel<1>(sw), s2 = e4m3_f32_sel<2>(sw),
+                  s3 = e4m3_f32_sel<3>(sw);
+#pragma unroll
+      for (int i = 0; i < F; ++i)      // result row 4h + i (i < 4) of the 32x32 tile, column nl
+        acc[i] = fmaf(s3, d[3][i], fmaf(s2, d[2][i], fmaf(s1, d[1][i], fmaf(s0, d[0][i], acc[i]))));
+    }
+    __syncthreads();                               // every stage consumed: LDS holds the partial sums
+    float* red = (float*)smem;
+    if (wave != 0)
+      for (int i = 0; i < F; ++i) red[((wave - 1) * F + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (wave == 0) {
+      const float st_ = *ts;
+      for (int i = 0; i < F; ++i) {
+        float v = acc[i];
+        for (int q = 0; q < kPsWaves - 1; ++q) v += red[(q * F + i) * 64 + lane];
+        const int m = 4 * h + i, n = g0 + nl;
+        if (m < M && n < row_hi) {
+          if (!y_bf16) ((float*)Y)[(size_t)m * N + n] = v * st_;
+          else ((uint16_t*)Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * st_);
+        }
+      }
+    }
+    __syncthreads();                               // LDS is reused by the next row group
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // Vector-ALU products, any M, K % 32 == 0. One wave per weight row n and block of 16
 // activation rows; lanes stride over 32-wide K chunks; f32 FMAs; a wave reduction at the end.
 // Dense: every weight is multiplied. 2:4 (skip-and-gather): only the two kept values of each
@@ -495,15 +609,19 @@ __global__ __launch_bounds__(256) void k_gemm_valu(const uint16_t* __restrict__ 
 
 }  // namespace
 
-int slab_blocks(int64_t N) {
+static int cu_count() {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       cus = 256;
   }
+  return cus;
+}
+
+int slab_blocks(int64_t N) {
   const int64_t tiles = (N + 15) / 16;
-  return (int)std::min<int64_t>(cus, tiles);
+  return (int)std::min<int64_t>(cu_count(), tiles);
 }
 
 hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
@@ -517,6 +635,22 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
     hipLaunchKernelGGL((k_gemv_mfma<false, kDenseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+    return hipGetLastError();
+  }
+  if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab: two workgroups per CU
+    static bool ps_set = false;
+    if (!ps_set) {
+      for (const void* f : {(const void*)k_gemv_ps<1>, (const void*)k_gemv_ps<2>, (const void*)k_gemv_ps<4>}) {
+        hipError_t e2 = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kPsStages * kPsBytes);
+        if (e2 != hipSuccess) return e2;
+      }
+      ps_set = true;
+    }
+    const int G = (int)std::min<int64_t>(2 * (int64_t)cu_count(), (a.N + kPsRows - 1) / kPsRows);
+    const int R = (int)((a.N + G - 1) / G);
+    auto k = a.M == 1 ? k_gemv_ps<1> : a.M == 2 ? k_gemv_ps<2> : k_gemv_ps<4>;
+    hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), kPsStages * kPsBytes, s, a.X, (int)a.M, (int)a.N, (int)a.K,
+                       a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
   const int G = slab_blocks(a.N);
