@@ -192,42 +192,44 @@ __device__ __forceinline__ void wait_stages(int ahead) {
   }
 }
 
-// Stage layout of one ring slot (64 rows of the current row group):
-//   dense: codes [64][256 B] (16-byte chunks XOR-swizzled by row & 15), scales [64][32 B]
-//   2:4:   vals  [64][128 B] (16-byte chunks XOR-swizzled by row & 7), meta [64][64 B],
-//          scales [64][32 B]
-//   both:  activations [16][1024 B + 16 B pad] (rows >= M are not read)
-template <bool SP24>
+// Stage layout of one ring slot (G = 4 W rows of the current row group, W waves):
+//   dense: codes [G][256 B] (16-byte chunks XOR-swizzled by row & 15), scales [G][32 B]
+//   2:4:   vals  [G][128 B] (16-byte chunks XOR-swizzled by row & 7), meta [G][64 B],
+//          scales [G][32 B]
+//   both:  activations [W][1024 B + 16 B pad] (rows >= M are not read; M <= W)
+template <bool SP24, int W>
 struct SlabLayout {
+  static constexpr int kG = 4 * W;                       // weight rows per group
   static constexpr int kA = SP24 ? kSK / 4 : kSK / 2;   // main weight bytes per row per stage
   static constexpr int kMeta = SP24 ? kSK / 8 : 0;       // position bytes per row per stage
-  static constexpr int kAOff = 0, kMetaOff = 64 * kA, kScOff = kMetaOff + 64 * kMeta;
-  static constexpr int kXOff = kScOff + 64 * kSRow;
-  static constexpr int kBytes = kXOff + 16 * kXRow;
+  static constexpr int kAOff = 0, kMetaOff = kG * kA, kScOff = kMetaOff + kG * kMeta;
+  static constexpr int kXOff = kScOff + kG * kSRow;
+  static constexpr int kBytes = kXOff + W * kXRow;
 };
 
-template <bool SP24>
-__global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* __restrict__ X, int M, int N, int K,
+template <bool SP24, int W>
+__global__ __launch_bounds__(W * 64) void k_gemv_slab(const uint16_t* __restrict__ X, int M, int N, int K,
                                                                const uint8_t* __restrict__ w0,
                                                                const uint8_t* __restrict__ w1,
                                                                const uint8_t* __restrict__ scales,
                                                                const float* __restrict__ ts, void* __restrict__ Y,
                                                                int y_bf16, int R) {
-  using Lay = SlabLayout<SP24>;
+  using Lay = SlabLayout<SP24, W>;
+  constexpr int NT = W / 4;                        // 16-row MFMA tiles per group
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   // loads per wave per stage: weights (dense: 1 KB = 4 rows; 2:4: vals 512 B + meta 256 B),
   // scales (128 B), and for waves m < M the activation row m (1 KB): L loads, or L - 1 for waves
   // without an activation row; rows past this block's range repeat its last row (no HBM traffic
   // outside the block's own rows)
   constexpr int L = SP24 ? 4 : 3;
-  static_assert(kSlabWaves == 16 && 64 * (kSK / 2) / 1024 == kSlabWaves, "one 1 KB weight load per wave per stage");
+  static_assert((W == 8 || W == 16) && Lay::kG * (kSK / 2) / 1024 == W, "one 1 KB weight load per wave per stage");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
   const int nst = (K + kSK - 1) / kSK;
   const int rowA = SP24 ? K / 4 : K / 2;            // bytes per row of the main weight array
 
-  for (int g0 = row_lo; g0 < row_hi; g0 += 64) {
+  for (int g0 = row_lo; g0 < row_hi; g0 += Lay::kG) {
     auto issue = [&](int st) {
       uint8_t* b = smem + (st % kD) * Lay::kBytes;
       const int k0 = st * kSK;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
       }
     };
 
-    const int tile = wave & 3, sl = wave >> 2;      // row tile, 128-k slice within each stage
+    const int tile = wave % NT, sl = wave / NT;     // row tile, 128-k slice within each stage
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int rt = tile * 16 + r;                   // this lane's A-operand row in the group
     const int xm = r < M ? r : 0;                   // B-operand rows >= M: any row, never stored
@@ -320,14 +322,14 @@ __global__ __launch_bounds__(kSlabWaves * 64) void k_gemv_slab(const uint16_t* _
     __syncthreads();                                // all stages consumed: reuse LDS for the sum
     float* red = (float*)smem;
     if (sl != 0)
-      for (int i = 0; i < 4; ++i) red[((sl - 1) * 16 + tile * 4 + i) * 64 + lane] = acc[i];
+      for (int i = 0; i < 4; ++i) red[((sl - 1) * 4 * NT + tile * 4 + i) * 64 + lane] = acc[i];
     __syncthreads();
     if (sl == 0) {
       const float st_ = *ts;
       f32x4 s;
       for (int i = 0; i < 4; ++i)
-        s[i] = (acc[i] + red[(0 * 16 + tile * 4 + i) * 64 + lane] + red[(1 * 16 + tile * 4 + i) * 64 + lane] +
-                red[(2 * 16 + tile * 4 + i) * 64 + lane]) * st_;
+        s[i] = (acc[i] + red[(0 * 4 * NT + tile * 4 + i) * 64 + lane] + red[(1 * 4 * NT + tile * 4 + i) * 64 + lane] +
+                red[(2 * 4 * NT + tile * 4 + i) * 64 + lane]) * st_;
       const int m = lane & 15, n = g0 + tile * 16 + 4 * q;
       if (m < M) {
         for (int i = 0; i < 4; ++i) {
@@ -627,8 +629,8 @@ int slab_blocks(int64_t N) {
 hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        kD * SlabLayout<false>::kBytes);
+    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<false, kSlabWaves>,
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, kD * SlabLayout<false, kSlabWaves>::kBytes);
     if (e1 != hipSuccess) return e1;
     attr_set = true;
   }
@@ -656,7 +658,8 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   const int G = slab_blocks(a.N);
   const int R = (int)((a.N + G - 1) / G);
   static_assert(kSlabWaves >= 16, "one activation row load per wave must cover M <= 16");
-  hipLaunchKernelGGL(k_gemv_slab<false>, dim3(G), dim3(kSlabWaves * 64), kD * SlabLayout<false>::kBytes, s, a.X,
+  constexpr int lds16 = kD * SlabLayout<false, kSlabWaves>::kBytes;
+  hipLaunchKernelGGL((k_gemv_slab<false, kSlabWaves>), dim3(G), dim3(kSlabWaves * 64), lds16, s, a.X,
                      (int)a.M, (int)a.N, (int)a.K, a.w0, (const uint8_t*)nullptr, a.scales, a.ts, a.Y, a.y_bf16, R);
   return hipGetLastError();
 }
@@ -670,9 +673,11 @@ hipError_t launch_gemv_sp24_decomp(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        kD * SlabLayout<true>::kBytes);
-    if (e1 != hipSuccess) return e1;
+    for (const void* f : {(const void*)k_gemv_slab<true, 8>, (const void*)k_gemv_slab<true, kSlabWaves>}) {
+      hipError_t e1 = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          kD * SlabLayout<true, kSlabWaves>::kBytes);
+      if (e1 != hipSuccess) return e1;
+    }
     attr_set = true;
   }
   if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
@@ -680,9 +685,18 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
+  if (a.M <= 8) {    // two 8-wave workgroups per CU, 32-row groups
+    const int G = (int)std::min<int64_t>(2 * (int64_t)cu_count(), (a.N + 31) / 32);
+    const int R = (int)((a.N + G - 1) / G);
+    constexpr int lds8 = kD * SlabLayout<true, 8>::kBytes;
+    hipLaunchKernelGGL((k_gemv_slab<true, 8>), dim3(G), dim3(8 * 64), lds8, s, a.X,
+                       (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
+    return hipGetLastError();
+  }
   const int G = slab_blocks(a.N);
   const int R = (int)((a.N + G - 1) / G);
-  hipLaunchKernelGGL(k_gemv_slab<true>, dim3(G), dim3(kSlabWaves * 64), kD * SlabLayout<true>::kBytes, s, a.X,
+  constexpr int lds16 = kD * SlabLayout<true, kSlabWaves>::kBytes;
+  hipLaunchKernelGGL((k_gemv_slab<true, kSlabWaves>), dim3(G), dim3(kSlabWaves * 64), lds16, s, a.X,
                      (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
   return hipGetLastError();
 }
