@@ -70,50 +70,43 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* wsum) {
   return inc - v + (wave > 0 ? wsum[16 + wave - 1] : 0);
 }
 
-// One block: per-expert totals, expert offsets, and the absolute first row of every
-// (chunk, expert) pair (written over the histogram). The chunk counts of an expert are read in
-// batches of 8 independent loads, so a pass over B chunks costs B / 8 memory round trips.
-constexpr int kScanBatch = 8;
-__global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist, int B, int E, int F,
-                                                     int32_t* __restrict__ offsets, int64_t* __restrict__ bad) {
-  extern __shared__ int32_t tot[];   // [E]
-  __shared__ int wsum[32];
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int run = 0;
-    for (int b0 = 0; b0 < B; b0 += kScanBatch) {
-      int c[kScanBatch];
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < B ? hist[(size_t)(b0 + j) * E + e] : 0;
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) run += c[j];
+// Column scan, one wave per expert: the exclusive prefix of the expert's per-chunk counts over
+// the chunks (written over the histogram) and its total. Lane l takes chunks l, l + 64, ...
+__global__ __launch_bounds__(kRouteThreads) void k_route_colscan(int32_t* __restrict__ hist, int B, int E,
+                                                                 int32_t* __restrict__ tot) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kRouteThreads / 64) + (threadIdx.x >> 6);
+  if (e >= E) return;                               // uniform per wave
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int c = b < B ? hist[(size_t)b * E + e] : 0;
+    int inc = c;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += t;
     }
-    tot[e] = run;
+    if (b < B) hist[(size_t)b * E + e] = carry + inc - c;
+    carry += __shfl(inc, 63, 64);
   }
-  __syncthreads();
+  if (lane == 0) tot[e] = carry;
+}
+
+// One block: expert offsets (exclusive scan of the totals), the placed-row count and the count
+// of entries whose id is out of range. Null totals stand for all zero (no entries).
+__global__ __launch_bounds__(1024) void k_route_scan(const int32_t* __restrict__ tot, int E, int F,
+                                                     int32_t* __restrict__ offsets, int64_t* __restrict__ bad) {
+  __shared__ int wsum[32];
   const int per = (E + 1023) / 1024;
   const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
   int s = 0;
-  for (int e = e0; e < e1; ++e) s += tot[e];
+  if (tot)
+    for (int e = e0; e < e1; ++e) s += tot[e];
   int ex = block_excl_scan_1024(s, wsum);
-  for (int e = e0; e < e1; ++e) { const int c = tot[e]; tot[e] = ex; ex += c; }
+  for (int e = e0; e < e1; ++e) { offsets[e] = ex; ex += tot ? tot[e] : 0; }
   if (threadIdx.x == 1023) {
     offsets[E] = ex;                        // rows with a valid expert id
     if (bad) *bad = (int64_t)F - ex;        // entries whose id is outside [0, E)
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int run = tot[e];
-    offsets[e] = run;
-    for (int b0 = 0; b0 < B; b0 += kScanBatch) {
-      int c[kScanBatch];
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) c[j] = b0 + j < B ? hist[(size_t)(b0 + j) * E + e] : 0;
-#pragma unroll
-      for (int j = 0; j < kScanBatch; ++j) {
-        if (b0 + j < B) hist[(size_t)(b0 + j) * E + e] = run;
-        run += c[j];
-      }
-    }
   }
 }
 
@@ -121,6 +114,7 @@ __global__ __launch_bounds__(1024) void k_route_scan(int32_t* __restrict__ hist,
 // equal ids comes from ballots, across the round's waves from per-wave counts in LDS.
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ ids, int F, int k,
                                                                  int E, const int32_t* __restrict__ hist,
+                                                                 const int32_t* __restrict__ offsets,
                                                                  int32_t* __restrict__ row_token,
                                                                  int32_t* __restrict__ row_slot,
                                                                  int32_t* __restrict__ row_of) {
@@ -129,7 +123,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
   int32_t* wc = sm + E;         // [4][E] per-wave counts of the current round
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    cur[e] = hist[(size_t)blockIdx.x * E + e];
+    cur[e] = offsets[e] + hist[(size_t)blockIdx.x * E + e];
     for (int w = 0; w < 4; ++w) wc[w * E + e] = 0;
   }
   __syncthreads();
@@ -573,21 +567,27 @@ hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
 }  // namespace
 
 size_t moe_route_workspace(int64_t F, int E) {
+  if (F == 0) return 0;
   const size_t B = (size_t)((F + kRouteChunk - 1) / kRouteChunk);
-  return B * (size_t)E * sizeof(int32_t);
+  return (B + 1) * (size_t)E * sizeof(int32_t);      // histogram [B][E], then totals [E]
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
                             int32_t* row_slot, int32_t* row_of, int64_t* bad, void* ws, hipStream_t s) {
   const int F = (int)(T * k);
   const int B = (F + kRouteChunk - 1) / kRouteChunk;
+  if (B == 0) {   // nothing to place: every offset and the bad count are zero
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, (const int32_t*)nullptr, E, 0, offsets, bad);
+    return hipGetLastError();
+  }
   int32_t* hist = (int32_t*)ws;
-  if (B > 0)
-    hipLaunchKernelGGL(k_route_hist, dim3(B), dim3(kRouteThreads), E * sizeof(int32_t), s, ids, F, E, hist);
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), E * sizeof(int32_t), s, hist, B, E, F, offsets, bad);
-  if (B > 0)
-    hipLaunchKernelGGL(k_route_scatter, dim3(B), dim3(kRouteThreads), 5 * E * sizeof(int32_t), s, ids, F, k, E,
-                       hist, row_token, row_slot, row_of);
+  int32_t* tot = hist + (size_t)B * E;
+  hipLaunchKernelGGL(k_route_hist, dim3(B), dim3(kRouteThreads), E * sizeof(int32_t), s, ids, F, E, hist);
+  hipLaunchKernelGGL(k_route_colscan, dim3((E + kRouteThreads / 64 - 1) / (kRouteThreads / 64)), dim3(kRouteThreads), 0,
+                     s, hist, B, E, tot);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, (const int32_t*)tot, E, F, offsets, bad);
+  hipLaunchKernelGGL(k_route_scatter, dim3(B), dim3(kRouteThreads), 5 * E * sizeof(int32_t), s, ids, F, k, E,
+                     (const int32_t*)hist, (const int32_t*)offsets, row_token, row_slot, row_of);
   return hipGetLastError();
 }
 
