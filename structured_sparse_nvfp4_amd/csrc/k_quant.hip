@@ -32,8 +32,11 @@ __device__ __forceinline__ float load_w(const void* W, int w_bf16, size_t i) {
 #ifndef SSN_AMAX_NT
 #define SSN_AMAX_NT 0
 #endif
-constexpr int kAmaxUnroll = SSN_AMAX_UNROLL;
-constexpr size_t kAmaxPiece = (size_t)kThreads * kAmaxUnroll;   // 16-byte pieces per block
+#ifndef SSN_AMAX_ITERS
+#define SSN_AMAX_ITERS 1
+#endif
+constexpr int kAmaxUnroll = SSN_AMAX_UNROLL, kAmaxIters = SSN_AMAX_ITERS;
+constexpr size_t kAmaxPiece = (size_t)kThreads * kAmaxUnroll;   // 16-byte pieces per span; a block reads kAmaxIters spans
 
 __device__ __forceinline__ float absmax4(f32x4 v) {
   return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
@@ -48,19 +51,21 @@ __device__ __forceinline__ float absmax_bf16x8(u32x4 v) {
 __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, size_t n, float* part) {
   const size_t per16 = w_bf16 ? 8 : 4;                       // values per 16-byte piece
   const size_t n16 = n / per16;
-  const size_t base = (size_t)blockIdx.x * kAmaxPiece + threadIdx.x;
   const u32x4* p = (const u32x4*)W;
-  u32x4 v[kAmaxUnroll];
-#pragma unroll
-  for (int u = 0; u < kAmaxUnroll; ++u) {
-    const size_t i = base + (size_t)u * kThreads;
-    const u32x4* q = p + (i < n16 ? i : 0);                  // piece 0 again past the end: harmless for a max
-    v[u] = SSN_AMAX_NT ? ld_nt(q) : *q;
-  }
   float m = 0.f;
+  for (int it = 0; it < kAmaxIters; ++it) {
+    const size_t base = ((size_t)blockIdx.x * kAmaxIters + it) * kAmaxPiece + threadIdx.x;
+    u32x4 v[kAmaxUnroll];
 #pragma unroll
-  for (int u = 0; u < kAmaxUnroll; ++u)
-    m = fmaxf(m, w_bf16 ? absmax_bf16x8(v[u]) : absmax4(__builtin_bit_cast(f32x4, v[u])));
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const size_t i = base + (size_t)u * kThreads;
+      const u32x4* q = p + (i < n16 ? i : 0);                // piece 0 again past the end: harmless for a max
+      v[u] = SSN_AMAX_NT ? ld_nt(q) : *q;
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u)
+      m = fmaxf(m, w_bf16 ? absmax_bf16x8(v[u]) : absmax4(__builtin_bit_cast(f32x4, v[u])));
+  }
   if (blockIdx.x == gridDim.x - 1)                           // values after the last whole piece
     for (size_t j = n16 * per16 + threadIdx.x; j < n; j += kThreads) m = fmaxf(m, fabsf(load_w(W, w_bf16, j)));
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
 // s_t = fl32(amax / 2688): float64 division then conversion is the correctly rounded f32
 // quotient (2688 = 2^7 * 21 and 21 is odd, so the quotient is never an f32 midpoint).
 // One block: the maximum of the nparts block maxima, or ts_in when the caller gives s_t.
-constexpr int kFinThreads = 1024;
+constexpr int kFinThreads = 1024, kFinBatch = 8;
 __global__ __launch_bounds__(kFinThreads) void k_finalize_scale(const float* part, unsigned nparts, const float* ts_in,
                                                                 float* ts_out) {
   if (ts_in) {
@@ -85,11 +90,16 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize_scale(const float* par
     return;
   }
   float m = 0.f;
-  unsigned i = threadIdx.x;
-  for (; i + 3 * kFinThreads < nparts; i += 4 * kFinThreads)   // four loads in flight per thread
-    m = fmaxf(fmaxf(m, fmaxf(part[i], part[i + kFinThreads])),
-              fmaxf(part[i + 2 * kFinThreads], part[i + 3 * kFinThreads]));
-  for (; i < nparts; i += kFinThreads) m = fmaxf(m, part[i]);
+  for (unsigned i0 = 0; i0 < nparts; i0 += kFinBatch * kFinThreads) {   // one batch of loads in flight
+    float v[kFinBatch];
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) {
+      const unsigned i = i0 + j * kFinThreads + threadIdx.x;
+      v[j] = i < nparts ? part[i] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < kFinBatch; ++j) m = fmaxf(m, v[j]);
+  }
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   __shared__ float red[kFinThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -120,9 +130,7 @@ __device__ __forceinline__ double e4m3_f64(uint32_t b) {
   return e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
 }
 
-// One lane per block of 16 values: S, then 16 codes packed into 8 bytes. Blocks are visited
-// from the end of W backwards, so the tail that the amax pass left in the Infinity Cache is
-// read first.
+// Per block of 16 values: S, then 16 codes packed into 8 bytes.
 //
 // E2M1 decision thresholds m * d (exact float64 products): ties at 0.25, 1.25, 2.5 and 5 go
 // down, at 0.75, 1.75 and 3.5 up, so code = [a > 0.25d] + [a >= 0.75d] + [a > 1.25d] +
@@ -134,37 +142,25 @@ struct Thresholds {
   float e175, e075, e35, g025, g125, g25, g5;
 };
 
-__device__ __forceinline__ uint32_t e2m1_code(float a, const Thresholds& t) {
-  const bool b2 = a >= t.e175;
-  const bool b1 = a >= (b2 ? t.e35 : t.e075);
-  const float tl = b2 ? (b1 ? t.g5 : t.g25) : (b1 ? t.g125 : t.g025);
-  const bool b0 = a > tl;
+// The thresholds are passed by value so that they stay in registers: the quarter's threshold is
+// picked with two selects, not by indexing a spilled copy of the struct.
+__device__ __forceinline__ uint32_t e2m1_code(float a, float e175, float e075, float e35, float g025, float g125,
+                                              float g25, float g5) {
+  const bool b2 = a >= e175;
+  const float t1 = b2 ? e35 : e075;
+  const bool b1 = a >= t1;
+  const float lo = b1 ? g125 : g025;
+  const float hi = b1 ? g5 : g25;
+  const bool b0 = a > (b2 ? hi : lo);
   return ((uint32_t)b2 << 2) | ((uint32_t)b1 << 1) | (uint32_t)b0;
 }
 
-__global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16, size_t nblocks,
-                                                       const float* ts, uint8_t* codes, uint8_t* scales) {
-  const size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (q >= nblocks) return;
-  const size_t b = nblocks - 1 - q;
-  float w[16];
-  if (!w_bf16) {
-    const f32x4* p = (const f32x4*)((const float*)W + b * 16);
-    for (int t = 0; t < 4; ++t) {
-      f32x4 v = ld_nt(p + t);
-      w[4 * t] = v[0]; w[4 * t + 1] = v[1]; w[4 * t + 2] = v[2]; w[4 * t + 3] = v[3];
-    }
-  } else {
-    const u32x4* p = (const u32x4*)((const uint16_t*)W + b * 16);
-    for (int t = 0; t < 2; ++t) {
-      u32x4 v = ld_nt(p + t);
-      for (int u = 0; u < 4; ++u) { w[8 * t + 2 * u] = bf16_lo(v[u]); w[8 * t + 2 * u + 1] = bf16_hi(v[u]); }
-    }
-  }
+// S and the 16 codes of one block.
+__device__ __forceinline__ void quantize_block(const float (&w)[16], double st, u32x2& code, uint32_t& S) {
   float amax = 0.f;
+#pragma unroll
   for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(w[t]));
-  const double st = (double)*ts;
-  uint32_t S = 0;
+  S = 0;
   if (st > 0.0) S = e4m3_rne((double)amax / (6.0 * st));
   const double d = st * e4m3_f64(S);           // exact: <= 24 + 4 significant bits
   uint32_t lo = 0, hi = 0;                     // a block whose scale is zero stores code 0x0
@@ -176,14 +172,78 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, int w_bf16
     th.e35 = __double2float_ru(3.5 * d);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      uint32_t c = e2m1_code(fabsf(w[t]), th);
+      uint32_t c = e2m1_code(fabsf(w[t]), th.e175, th.e075, th.e35, th.g025, th.g125, th.g25, th.g5);
       c |= (__float_as_uint(w[t]) >> 28) & 8u;  // sign bit -> bit 3 (keeps -0 for tiny negatives)
       if (t < 8) lo |= c << (4 * t); else hi |= c << (4 * (t - 8));
     }
   }
-  u32x2 o; o[0] = lo; o[1] = hi;
-  *(u32x2*)(codes + b * 8) = o;
-  scales[b] = (uint8_t)S;
+  code[0] = lo; code[1] = hi;
+}
+
+// A wave takes chunks of 64 blocks (4 KB of f32, 2 KB of bf16). Its loads are contiguous: load
+// u of lane l reads 16-byte piece 64u + l of the chunk. An LDS transpose then hands lane b the
+// whole block b, so codes (8 bytes) and scales (1 byte) leave as contiguous runs. The pieces of a
+// block sit at swizzled slots x ^ sw(b), which keeps both the writes and the reads free of bank
+// conflicts. Chunks are visited from the end of W backwards, so the tail that the amax pass left
+// in the Infinity Cache is read first.
+constexpr int kQBlocks = 64;     // blocks per wave-chunk
+#ifndef SSN_Q_ITER
+#define SSN_Q_ITER 4
+#endif
+constexpr int kQIter = SSN_Q_ITER;   // chunks per wave
+
+template <int BF16>
+__device__ __forceinline__ int q_swz(int b) {
+  return BF16 ? (((b >> 2) ^ (b >> 3)) & 1) : (((b >> 1) ^ (b >> 3)) & 3);
+}
+
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nblocks, const float* ts,
+                                                       uint8_t* codes, uint8_t* scales) {
+  constexpr int P = BF16 ? 2 : 4;              // 16-byte pieces per block
+  __shared__ u32x4 tr[kThreads / 64][kQBlocks * P];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4* t = tr[wave];
+  const size_t nchunks = (nblocks + kQBlocks - 1) / kQBlocks;
+  const size_t c0 = ((size_t)blockIdx.x * (kThreads / 64) + wave) * kQIter;
+  const double st = (double)*ts;
+  for (int it = 0; it < kQIter; ++it) {
+    if (c0 + it >= nchunks) break;                               // uniform per wave
+    const size_t b0 = (nchunks - 1 - (c0 + it)) * kQBlocks;      // first block of the chunk
+    const u32x4* src = (const u32x4*)W + b0 * P;
+    u32x4 v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int p = 64 * u + lane;
+      v[u] = b0 + p / P < nblocks ? ld_nt(src + p) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int p = 64 * u + lane, b = p / P;
+      t[b * P + ((p % P) ^ q_swz<BF16>(b))] = v[u];
+    }
+    __asm__ volatile("" ::: "memory");          // this wave's LDS reads stay after its writes
+    float w[16];
+#pragma unroll
+    for (int x = 0; x < P; ++x) {
+      const u32x4 r = t[lane * P + (x ^ q_swz<BF16>(lane))];
+      if (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { w[8 * x + 2 * e] = bf16_lo(r[e]); w[8 * x + 2 * e + 1] = bf16_hi(r[e]); }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * x + e] = __uint_as_float(r[e]);
+      }
+    }
+    __asm__ volatile("" ::: "memory");          // ... and before the next chunk's writes
+    if (b0 + lane < nblocks) {
+      u32x2 code;
+      uint32_t S;
+      quantize_block(w, st, code, S);
+      *(u32x2*)(codes + (b0 + lane) * 8) = code;
+      scales[b0 + lane] = (uint8_t)S;
+    }
+  }
 }
 
 // double -> f32 rounded to odd: truncate, then set the last bit if anything was dropped. A
@@ -273,14 +333,19 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
   unsigned nparts = 0;
   if (!ts_in) {
     const size_t n16 = n / (w_bf16 ? 8 : 4);
-    nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece - 1) / kAmaxPiece);
+    nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece * kAmaxIters - 1) / (kAmaxPiece * kAmaxIters));
     hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
   }
   hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
   const size_t nb = n / 16;
-  if (nb)
-    hipLaunchKernelGGL(k_quantize, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, s, W, w_bf16, nb,
-                       (const float*)ts_out, codes, scales);
+  if (nb) {
+    const size_t waves = ((nb + kQBlocks - 1) / kQBlocks + kQIter - 1) / kQIter;
+    const dim3 grid(grid_for(waves, kThreads / 64));
+    if (w_bf16)
+      hipLaunchKernelGGL(k_quantize<1>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
+    else
+      hipLaunchKernelGGL(k_quantize<0>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
+  }
   return hipGetLastError();
 }
 
