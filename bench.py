@@ -23,7 +23,8 @@ HBM. ``value`` is the algorithmic bytes of the whole step divided by the step ti
 ``workloads`` adds the other shapes, each timed the same way: the square (4096^3, f32 out) and
 prefill (8192 x 27648 x 5120, 1% outliers x20, bf16 out) products for dense MFMA, 2:4 SMFMAC
 and 2:4 expanded-to-dense MFMA, and the grouped-expert FFN (4096 tokens, 512 experts, top-10
-Zipf(1.1), D = 2048, I = 512) stage by stage, dense and 2:4.
+Zipf(1.1), D = 2048, I = 512) stage by stage, dense and 2:4, plus the same FFN at decode sizes
+(1, 4, 16, 32 tokens) against the full expert set, on the weight-streaming grouped kernels.
 """
 from __future__ import annotations
 
@@ -378,10 +379,89 @@ def run_moe(torch, ssn, synth, reps):
                            "GBps_alg": round(ffn_bytes / (us * 1e-6) / 1e9, 1),
                            "t_roof_us": round(t_roof * 1e6, 1), "frac_of_t_roof": round(t_roof / (us * 1e-6), 4)})
         out["sp24" if sparse else "dense"] = res
-        del up, down, up_rows, down_rows, H, Yd
+        del H, Yd, up_rows, down_rows
+        torch.cuda.empty_cache()
+        out["decode_" + ("sp24" if sparse else "dense")] = run_moe_decode(torch, ssn, synth, x, up, down, sparse,
+                                                                          E, k, D, I)
+        del up, down
         torch.cuda.empty_cache()
     out["sp24"]["ffn"]["speedup_vs_dense"] = round(out["dense"]["ffn"]["us"] / out["sp24"]["ffn"]["us"], 3)
+    for T in MOE_DECODE_TOKENS:
+        d, s_ = out["decode_dense"][f"T{T}"], out["decode_sp24"][f"T{T}"]
+        s_["ffn_speedup_vs_dense"] = round(d["ffn_us"] / s_["ffn_us"], 3)
     return out
+
+
+MOE_DECODE_TOKENS = (1, 4, 16, 32)
+MOE_RING = 20      # weight copies x routings rotated (20 x 17.7 MB at one token > the 256 MB cache)
+
+
+def run_moe_decode(torch, ssn, synth, x, up, down, sparse, E, k, D, I):
+    """Decode-sized routings (1..32 tokens) on the full expert set: every call reads the touched
+    experts' weights. Calls rotate over MOE_RING weight copies and as many routing draws, so
+    the weights come from HBM, not from the Infinity Cache of an earlier call."""
+    import numpy as np
+    ups = [up] + [tuple(t.clone() if t is not None else None for t in up) for _ in range(MOE_RING - 1)]
+    downs = [down] + [tuple(t.clone() if t is not None else None for t in down) for _ in range(MOE_RING - 1)]
+    kt = ssn.WLAYOUT_KTILE64
+    per_expert = sum(t[0].numel() for t in (up[0], up[2], down[0], down[2])) + \
+        (sum(t[0].numel() for t in (up[1], down[1])) if sparse else 0)
+    res = {"weight_copies": MOE_RING, "weight_layout": "ktile64",
+           "note": "stages timed over back-to-back calls, each on its own weight copy and routing draw (seeds "
+                   "100..119)"}
+    tiles = ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
+    for T in MOE_DECODE_TOKENS:
+        R = T * k
+        X = torch.from_numpy(x[:T].view("int16")).view(torch.bfloat16).cuda()
+        stages = {n: [] for n in ("route", "up", "down", "combine", "ffn", "up_tiles", "down_tiles")}
+        touched, used = [], []
+        for j in range(MOE_RING):
+            ids, wts = synth.routing(T, E, k, 1.1, seed=100 + j)
+            touched.append(len(np.unique(ids)))
+            dids, dw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+            u, d = ups[j], downs[j]
+            off, rt, rs, ro, bad = ssn.moe_route(dids, E)
+            H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
+            Yd = torch.empty((R, D), dtype=torch.float32, device="cuda")
+            stages["route"].append(ssn.moe_route(dids, E, prepare=True)[0])
+            p, (_, a) = ssn.moe_grouped_gemm_nvfp4(X, rt, off, R, u[0], u[2], u[3], w_meta=u[1],
+                                                   epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, Y=H,
+                                                   prepare=True, w_layout=kt)
+            stages["up"].append(p)
+            used.append(a)
+            p, (_, a) = ssn.moe_grouped_gemm_nvfp4(H, None, off, R, d[0], d[2], d[3], w_meta=d[1], Y=Yd, prepare=True,
+                                                   w_layout=kt)
+            stages["down"].append(p)
+            used.append(a)
+            stages["combine"].append(ssn.moe_combine(Yd, ro, dw, prepare=True)[0])
+            stages["ffn"].append(ssn.moe_nvfp4_ffn(X, dids, dw, E, u, d, prepare=True, w_layout=kt)[0])
+            stages["up_tiles"].append(ssn.moe_grouped_gemm_nvfp4(
+                X, rt, off, R, u[0], u[2], u[3], w_meta=u[1], epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16,
+                Y=torch.empty_like(H), prepare=True, w_layout=kt, algo=tiles)[0])
+            stages["down_tiles"].append(ssn.moe_grouped_gemm_nvfp4(
+                H, None, off, R, d[0], d[2], d[3], w_meta=d[1], Y=torch.empty_like(Yd), prepare=True, w_layout=kt,
+                algo=tiles)[0])
+        B = Batches(torch)
+        for n, ps in stages.items():
+            B.run(n, ps)
+        torch.cuda.synchronize()
+        for n, ps in stages.items():
+            B.run(n, ps + ps)
+        torch.cuda.synchronize()
+        t = {n: B.us(n) for n in stages}
+        wb = float(np.mean(touched)) * per_expert
+        e = {"tokens": T, "rows": R, "experts_touched_mean": round(float(np.mean(touched)), 1),
+             "weight_bytes_touched": int(wb), "algo": "+".join(sorted({ssn.ALGO_NAMES.get(a.value, "?") for a in used})),
+             "route_us": round(t["route"], 1), "up_us": round(t["up"], 1), "down_us": round(t["down"], 1),
+             "combine_us": round(t["combine"], 1), "ffn_us": round(t["ffn"], 1),
+             "up_tiles_us": round(t["up_tiles"], 1), "down_tiles_us": round(t["down_tiles"], 1),
+             "GBps_up_down": round(wb / ((t["up"] + t["down"]) * 1e-6) / 1e9, 1),
+             "GBps_ffn": round(wb / (t["ffn"] * 1e-6) / 1e9, 1)}
+        e["hbm_frac_up_down"] = round(e["GBps_up_down"] / HBM_PEAK_GBPS, 4)
+        e["stream_speedup_vs_tiles"] = round((t["up_tiles"] + t["down_tiles"]) / (t["up"] + t["down"]), 3)
+        res[f"T{T}"] = e
+    del ups, downs
+    return res
 
 
 # ------------------------------------------------------------------------------------------

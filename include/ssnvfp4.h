@@ -80,8 +80,11 @@ enum {
   SSN_ALGO_MFMA = 2,             /* dense: bf16 MFMA on weights decoded in registers */
   SSN_ALGO_SMFMAC = 3,           /* 2:4 only: sparse MFMA (v_smfmac) with the compressed weights
                                     as the sparse operand; needs K % 64 == 0 */
-  SSN_ALGO_DECOMPRESS_MFMA = 5   /* 2:4 only: expand vals+meta to a dense tile and run the
+  SSN_ALGO_DECOMPRESS_MFMA = 5,  /* 2:4 only: expand vals+meta to a dense tile and run the
                                     dense bf16 MFMA (computes on the zeros) */
+  SSN_ALGO_STREAM = 6            /* grouped-expert calls only: one wave streams 32 weight rows
+                                    of an expert for up to 32 of its routed rows (decode-sized
+                                    routings); dense on MFMA, 2:4 on SMFMAC; needs N % 32 == 0 */
 };
 
 enum { SSN_EPI_NONE = 0, SSN_EPI_SILU_GATE = 1 };
@@ -219,8 +222,14 @@ int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_
  * y_dtype. R: rows of Y (offsets are clamped into [0, R]); source rows are clamped into
  * [0, x_rows). Needs K % 64 == 0 and, for SILU_GATE, N even. w_layout: SSN_WLAYOUT_ROWS (the
  * arrays as above, as nvfp4_quantize / sp24_compress write them) or SSN_WLAYOUT_KTILE64 (all
- * three arrays as moe_pack_ktiles writes them). algo: AUTO, MFMA (dense) or DECOMPRESS_MFMA
- * (2:4, expanded to a dense operand in registers). algo_used: host, nullable.
+ * three arrays as moe_pack_ktiles writes them). algo: MFMA (dense) or DECOMPRESS_MFMA (2:4,
+ * expanded to a dense operand in registers) run 64-row x 256-column output tiles; STREAM (dense
+ * or 2:4, N % 32 == 0) cuts the work along the weight rows instead, one wave per (expert, 32
+ * weight rows, up to 32 routed rows), for routings with few rows per expert ("NVFP4 vs 2:4
+ * sparse", robertz.co, section "Where a decode step actually spends itself": the expert weight
+ * read is the cost). AUTO picks STREAM when N % 32 == 0 and R <= 4 E (dense) or R <= 10 E (2:4),
+ * else the tiles.
+ * algo_used: host, nullable.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, RANGE, HIP.
  * ------------------------------------------------------------------------------------------- */
 int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row_token,

@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libssnvfp4.so")
 
 SSN_OK, SSN_E_NULL, SSN_E_SHAPE, SSN_E_ALIGN, SSN_E_DTYPE, SSN_E_ALGO, SSN_E_HIP, SSN_E_RANGE = range(8)
 SSN_F32, SSN_BF16 = 0, 1
-ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_DECOMPRESS_MFMA = 0, 1, 2, 3, 5
+ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_DECOMPRESS_MFMA, ALGO_STREAM = 0, 1, 2, 3, 5, 6
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac",
-              ALGO_DECOMPRESS_MFMA: "decompress_mfma"}
+              ALGO_DECOMPRESS_MFMA: "decompress_mfma", ALGO_STREAM: "stream"}
 EPI_NONE, EPI_SILU_GATE = 0, 1
 WLAYOUT_ROWS, WLAYOUT_KTILE64 = 0, 1
 
@@ -92,8 +92,8 @@ class Prepared:
 
 
 def _run(fname, cargs, prepare, keep, result):
-    if prepare:
-        return Prepared(fname, cargs, keep), result
+    if prepare:   # the prepared call holds its outputs too: they must outlive every later call
+        return Prepared(fname, cargs, (keep, result)), result
     _check(getattr(lib(), fname)(*cargs))
     return result
 
@@ -236,7 +236,7 @@ def gemm_nvfp4_dense(X, codes, scales, tensor_scale, y_dtype=torch.float32, algo
     cargs = (_ptr(X), M, N, K, _ptr(codes), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt, algo,
              ctypes.byref(used), _stream(X.device))
     if prepare:
-        return Prepared("gemm_nvfp4_dense", cargs, (X, codes, scales, tensor_scale, used)), (Y, used)
+        return Prepared("gemm_nvfp4_dense", cargs, (X, codes, scales, tensor_scale, used, Y)), (Y, used)
     _check(lib().gemm_nvfp4_dense(*cargs))
     return Y, used.value
 
@@ -254,7 +254,7 @@ def gemm_nvfp4_sp24(X, vals, meta, scales, tensor_scale, y_dtype=torch.float32, 
     cargs = (_ptr(X), M, N, K, _ptr(vals), _ptr(meta), _ptr(scales), _ptr(tensor_scale), _ptr(Y), dt, algo,
              ctypes.byref(used), _stream(X.device))
     if prepare:
-        return Prepared("gemm_nvfp4_sp24", cargs, (X, vals, meta, scales, tensor_scale, used)), (Y, used)
+        return Prepared("gemm_nvfp4_sp24", cargs, (X, vals, meta, scales, tensor_scale, used, Y)), (Y, used)
     _check(lib().gemm_nvfp4_sp24(*cargs))
     return Y, used.value
 
@@ -314,7 +314,7 @@ def moe_grouped_gemm_nvfp4(X, row_token, expert_offsets, R, w_main, w_scales, te
              ctypes.byref(used), _stream(X.device))
     if prepare:
         return Prepared("moe_grouped_gemm_nvfp4", cargs, (X, row_token, expert_offsets, w_main, w_meta, w_scales,
-                                                          tensor_scales, used)), (Y, used)
+                                                          tensor_scales, used, Y)), (Y, used)
     _check(lib().moe_grouped_gemm_nvfp4(*cargs))
     return Y, used.value
 

@@ -277,10 +277,17 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   if (epilogue != SSN_EPI_NONE && epilogue != SSN_EPI_SILU_GATE)
     return fail(SSN_E_RANGE, "%s: unknown epilogue %d", fn, epilogue);
   if (epilogue == SSN_EPI_SILU_GATE && N % 2) return fail(SSN_E_SHAPE, "%s: SILU_GATE needs N even (N=%lld)", fn, (long long)N);
-  const int chosen = algo == SSN_ALGO_AUTO ? (sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA) : algo;
-  if (chosen != (sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA))
+  const int tiles = sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA;
+  const bool can_stream = N % 32 == 0;
+  // measured crossover (512 experts, D = 2048, I = 512): streaming wins up to ~4 rows per expert
+  // for dense weights and ~10 for 2:4 weights
+  const int64_t stream_max = (sparse ? 10 : 4) * (int64_t)E;
+  const int chosen = algo == SSN_ALGO_AUTO ? (can_stream && R <= stream_max ? SSN_ALGO_STREAM : tiles) : algo;
+  if (chosen != tiles && chosen != SSN_ALGO_STREAM)
     return fail(SSN_E_ALGO, "%s: algorithm %d is not available for %s expert weights", fn, algo,
                 sparse ? "2:4" : "dense");
+  if (chosen == SSN_ALGO_STREAM && !can_stream)
+    return fail(SSN_E_ALGO, "%s: STREAM needs N %% 32 == 0 (N=%lld)", fn, (long long)N);
   if (algo_used) *algo_used = chosen;
   if (R == 0 || N == 0) return ok();
   if (K == 0 || K % 64) return fail(SSN_E_SHAPE, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);
@@ -292,7 +299,8 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   ssn::MoeGemmArgs a{X, x_rows, K, row_token, expert_offsets, E, R, N, w_main, sparse ? w_meta : nullptr, w_scales,
                      tensor_scales, Y, y_dtype == SSN_BF16, sparse, epilogue == SSN_EPI_SILU_GATE,
                      w_layout == SSN_WLAYOUT_KTILE64};
-  return hip_status(ssn::launch_moe_gemm(a, as_stream(stream)), fn);
+  return hip_status(chosen == SSN_ALGO_STREAM ? ssn::launch_moe_stream(a, as_stream(stream))
+                                              : ssn::launch_moe_gemm(a, as_stream(stream)), fn);
 }
 
 int moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece_bytes, uint8_t* dst,

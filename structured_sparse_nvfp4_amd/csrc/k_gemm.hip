@@ -38,21 +38,30 @@ namespace {
 constexpr int kTM = 256, kTN = 256, kTK = 64;   // output tile and K-stage
 constexpr int kStages = 3;                       // stages resident in LDS
 constexpr int kThreads = 256;
+#ifndef SSN_GEMM_WGM
+#define SSN_GEMM_WGM 2
+#endif
+constexpr int kGemmWGM = SSN_GEMM_WGM;   // waves along M in the dense tile (1 or 2)
+#ifndef SSN_GEMM_TM
+#define SSN_GEMM_TM 256
+#endif
+constexpr int kGemmTM = SSN_GEMM_TM;     // activation rows of the dense tile (256: one block per CU, 128: two)
 
-// One LDS ring slot (bytes). Rows are tile-local (0..255).
-//   X      [256][128 B]  activation k-chunk c of row r at physical chunk c ^ swz(r)
+// One LDS ring slot (bytes) of a tile with TM activation rows and 256 weight rows (tile-local).
+//   X      [TM][128 B]   activation k-chunk c of row r at physical chunk c ^ swz(r)
 //   dense: codes [256][32 B]  half h of row r at physical half h ^ ((r >> 3) & 1)
 //   2:4:   vals  [256][16 B], meta [256][8 B]
 //   scales [256][4 B]   (the four 16-blocks of the stage)
-template <int WF>
+template <int WF, int TM = kTM>
 struct Slot {
   static constexpr int kX = 0;
-  static constexpr int kW = kTM * kTK * 2;
+  static constexpr int kW = TM * kTK * 2;
   static constexpr int kMeta = WF == kDense ? 0 : kW + kTN * 16;
   static constexpr int kSc = WF == kDense ? kW + kTN * 32 : kMeta + kTN * 8;
   static constexpr int kBytes = kSc + kTN * 4;
-  // direct loads per wave per stage: activations 8, weights (dense 2 / 2:4 1 + 2), scales 1
-  static constexpr int kLoads = WF == kDense ? 8 + 2 + 1 : 8 + 1 + 2 + 1;
+  // direct loads per wave per stage: activations TM / 32, weights (dense 2 / 2:4 1 + 2), scales 1
+  static constexpr int kXLoads = TM / 32;
+  static constexpr int kLoads = WF == kDense ? kXLoads + 2 + 1 : kXLoads + 1 + 2 + 1;
 };
 
 // ---- tile scheduling: consecutive logical tiles share an XCD (workgroups are dealt to the
@@ -77,28 +86,28 @@ __device__ __forceinline__ void tile_of(int b, int total, int tiles_m, int tiles
 // 32-bit vector offset. Rows beyond M or N are clamped to the last row (their results are not
 // stored). Every boundary issues the same loads (a stage past the end re-reads the last one
 // into a free slot), so the loads a wait must cover are a fixed count.
-template <int WF>
+template <int WF, int TM = kTM>
 struct StageSrc {
   const char* xb;   // activations of rows m0.. at k = 0
   const char* wb;   // codes (dense) or vals (2:4) of rows n0.. at k = 0
   const char* mb;   // meta of rows n0.. (2:4)
   const char* sb;   // scales of rows n0..
-  uint32_t xo[8], wo[2], mo[2], so;
+  uint32_t xo[TM / 32], wo[2], mo[2], so;
 };
 
-template <int WF>
-__device__ __forceinline__ StageSrc<WF> stage_src(const uint16_t* X, const uint8_t* w0, const uint8_t* w1,
+template <int WF, int TM = kTM>
+__device__ __forceinline__ StageSrc<WF, TM> stage_src(const uint16_t* X, const uint8_t* w0, const uint8_t* w1,
                                                   const uint8_t* scales, int M, int N, int K, int m0, int n0,
                                                   int wave, int lane) {
-  StageSrc<WF> o;
+  StageSrc<WF, TM> o;
   o.xb = (const char*)(X + (size_t)m0 * K);
   o.wb = (const char*)w0 + (size_t)n0 * (WF == kDense ? K / 2 : K / 4);
   o.mb = WF == kDense ? nullptr : (const char*)w1 + (size_t)n0 * (K / 8);
   o.sb = (const char*)scales + (size_t)n0 * (K / 16);
-  // activations: load i of the wave writes row 8 (8 wave + i) + l / 8, physical chunk l % 8
+  // activations: load i of the wave writes row 8 (TM / 32 wave + i) + l / 8, physical chunk l % 8
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 8 * (8 * wave + i) + (lane >> 3);
+  for (int i = 0; i < TM / 32; ++i) {
+    const int r = 8 * (TM / 32 * wave + i) + (lane >> 3);
     const int c = (lane & 7) ^ swz(r);
     o.xo[i] = (uint32_t)((min(m0 + r, M - 1) - m0) * K + 8 * c) * 2u;
   }
@@ -125,20 +134,22 @@ __device__ __forceinline__ StageSrc<WF> stage_src(const uint16_t* X, const uint8
   return o;
 }
 
-template <int WF>
-__device__ __forceinline__ void issue_stage(const StageSrc<WF>& g, int st, char* slot, int wave) {
-  using L = Slot<WF>;
+template <int WF, int TM = kTM>
+__device__ __forceinline__ void issue_stage(const StageSrc<WF, TM>& g, int st, char* slot, int wave) {
+  using L = Slot<WF, TM>;
+  const auto xr = buf_rsrc(g.xb), wr = buf_rsrc(g.wb), sr = buf_rsrc(g.sb);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) lds_dma16(g.xb + st * (kTK * 2) + g.xo[i], slot + L::kX + (8 * wave + i) * 1024);
+  for (int i = 0; i < TM / 32; ++i) lds_dma16(xr, g.xo[i], st * (kTK * 2), slot + L::kX + (TM / 32 * wave + i) * 1024);
   if constexpr (WF == kDense) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma16(g.wb + st * (kTK / 2) + g.wo[i], slot + L::kW + (2 * wave + i) * 1024);
+    for (int i = 0; i < 2; ++i) lds_dma16(wr, g.wo[i], st * (kTK / 2), slot + L::kW + (2 * wave + i) * 1024);
   } else {
-    lds_dma16(g.wb + st * (kTK / 4) + g.wo[0], slot + L::kW + wave * 1024);
+    const auto mr = buf_rsrc(g.mb);
+    lds_dma16(wr, g.wo[0], st * (kTK / 4), slot + L::kW + wave * 1024);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_dma4(g.mb + st * (kTK / 8) + g.mo[i], slot + L::kMeta + (2 * wave + i) * 256);
+    for (int i = 0; i < 2; ++i) lds_dma4(mr, g.mo[i], st * (kTK / 8), slot + L::kMeta + (2 * wave + i) * 256);
   }
-  lds_dma4(g.sb + st * (kTK / 16) + g.so, slot + L::kSc + wave * 256);
+  lds_dma4(sr, g.so, st * (kTK / 16), slot + L::kSc + wave * 256);
 }
 
 // 16-byte activation chunk `c` of tile row r
@@ -147,9 +158,9 @@ __device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c) {
 }
 
 // One lane's weights for one stage: dense 32 codes, or 2:4 (vals word 0, vals word 1, meta)
-template <int WF>
+template <int WF, int TM = kTM>
 __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
-  using L = Slot<WF>;
+  using L = Slot<WF, TM>;
   if constexpr (WF == kDense) {
     return *(const u32x4*)(slot + L::kW + r * 32 + 16 * (h ^ ((r >> 3) & 1)));
   } else {
@@ -162,26 +173,34 @@ __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
 
 // ---------------------------------------------------------------------------------------------
 // Dense (or 2:4 expanded to dense) x activations on v_mfma_f32_32x32x16_bf16.
-template <int WF>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// WGM x (4 / WGM) waves: wave (wm, wn) owns activation rows [256/WGM * wm, +256/WGM) and
+// weight rows [64 WGM * wn, +64 WGM) of the tile, MB x NB blocks of 32 x 32. With WGM = 2 each
+// activation operand read from LDS feeds four MFMAs instead of two (half the LDS read traffic
+// of WGM = 1), and each weight is decoded by two waves instead of one.
+template <int WF, int WGM, int TM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(256 / TM, 256 / TM)))
 void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
                  const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
                  void* __restrict__ Y, int y_bf16) {
-  using L = Slot<WF>;
+  using L = Slot<WF, TM>;
+  constexpr int MB = TM / 32 / WGM, NB = 2 * WGM;       // 32 x 32 blocks per wave along M and N
+  constexpr int VS = NB == 2 ? 3 : 5, VB = NB == 2 ? 3 : 6;   // decode instructions per MFMA slot
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kTN - 1) / kTN;
+  const int wn = wave % (4 / WGM), wm = wave / (4 / WGM);
+  const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + kTN - 1) / kTN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * kTM, n0 = tn * kTN;
+  const int m0 = tm * TM, n0 = tn * kTN;
   const int r32 = lane & 31, h = lane >> 5;
   const int nst = K / kTK, last = nst - 1;
+  const int am = 32 * MB * wm, bn0 = 32 * NB * wn;  // first activation / weight row of the wave
 
-  f32x16 acc[8][2];
+  f32x16 acc[MB][NB];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][nt][i] = 0.f;
 
@@ -189,41 +208,42 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   // the boundary of stage st - 3 and waited for at the boundary of stage st - 1. The boundary
   // (wait, barrier, next loads, first operands of the next stage) sits before the last MFMA
   // step of a stage, so that step's MFMAs cover it.
-  const StageSrc<WF> src = stage_src<WF>(X, w0, w1, scales, M, N, K, m0, n0, wave, lane);
-  issue_stage<WF>(src, 0, lds, wave);
-  issue_stage<WF>(src, min(1, last), lds + L::kBytes, wave);
-  issue_stage<WF>(src, min(2, last), lds + 2 * L::kBytes, wave);
+  const StageSrc<WF, TM> src = stage_src<WF, TM>(X, w0, w1, scales, M, N, K, m0, n0, wave, lane);
+  issue_stage<WF, TM>(src, 0, lds, wave);
+  issue_stage<WF, TM>(src, min(1, last), lds + L::kBytes, wave);
+  issue_stage<WF, TM>(src, min(2, last), lds + 2 * L::kBytes, wave);
 
-  u32x4 wc[2];          // this stage's weights (per column block) and their scale pair
-  uint32_t wsc[2];
-  u32x4 abuf[2][8];     // activation operands, double-buffered across MFMA steps
-  bf16x8 bcur[2];       // decoded weight operands of the current step
+  u32x4 wc[NB];         // this stage's weights (per column block) and their scale pair
+  uint32_t wsc[NB];
+  u32x4 abuf[2][MB];    // activation operands, double-buffered across MFMA steps
+  bf16x8 bcur[NB];      // decoded weight operands of the current step
 
-  auto load_w_regs = [&](const char* slot, u32x4 (&c)[2], uint32_t (&sc)[2]) {
+  auto load_w_regs = [&](const char* slot, u32x4 (&c)[NB], uint32_t (&sc)[NB]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int r = 64 * wave + 32 * nt + r32;
-      c[nt] = lds_w<WF>(slot, r, h);
+    for (int nt = 0; nt < NB; ++nt) {
+      const int r = bn0 + 32 * nt + r32;
+      c[nt] = lds_w<WF, TM>(slot, r, h);
       sc[nt] = *(const uint32_t*)(slot + L::kSc + r * 4) >> (16 * h);   // 16-blocks 2h, 2h + 1
     }
   };
-  auto decode = [&](const u32x4 (&c)[2], const uint32_t (&sc)[2], int s, bf16x8 (&b)[2]) {
+  auto decode = [&](const u32x4 (&c)[NB], const uint32_t (&sc)[NB], int s, bf16x8 (&b)[NB]) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NB; ++nt) {
       const float f = s < 2 ? e4m3_f32_sel<0>(sc[nt]) : e4m3_f32_sel<1>(sc[nt]);
       b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(c[nt], s), f));
     }
   };
-  auto read_a = [&](const char* slot, int s, u32x4 (&a)[8]) {
+  auto read_a = [&](const char* slot, int s, u32x4 (&a)[MB]) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) a[mt] = lds_x(slot, 32 * mt + r32, 4 * h + s);
+    for (int mt = 0; mt < MB; ++mt) a[mt] = lds_x(slot, am + 32 * mt + r32, 4 * h + s);
   };
-  auto mfmas = [&](const u32x4 (&a)[8], const bf16x8 (&b)[2]) {
+  auto mfmas = [&](const u32x4 (&a)[MB], const bf16x8 (&b)[NB]) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
+    for (int mt = 0; mt < MB; ++mt) {
       const bf16x8 av = as_bf16x8(a[mt]);
-      acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
-      acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NB; ++nt)
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[nt], acc[mt][nt], 0, 0, 0);
     }
   };
 
@@ -241,29 +261,31 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     for (int s = 0; s < 3; ++s) {
       read_a(slot, s + 1, abuf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);         // operand reads go out first, a whole step ahead
-      bf16x8 bn[2];
+      bf16x8 bn[NB];
       decode(wc, wsc, s + 1, bn);
       mfmas(abuf[s & 1], bcur);
-      interleave_mfma_valu<1, 15, 3>();
-      bcur[0] = bn[0]; bcur[1] = bn[1];
+      interleave_mfma_valu<1, MB * NB - 1, VS>();
+#pragma unroll
+      for (int nt = 0; nt < NB; ++nt) bcur[nt] = bn[nt];
     }
     // boundary: this wave's reads of slot S are done (their values are in registers) ...
     __builtin_amdgcn_sched_barrier(0);           // the MFMAs above stay above the barrier
     __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
     wait_vmcnt<L::kLoads>();                     // ... and stage st + 1 has landed
     stage_barrier();
-    issue_stage<WF>(src, min(st + 3, last), lds + S * L::kBytes, wave);
-    u32x4 wn[2];
-    uint32_t wsn[2];
-    bf16x8 bn[2];
-    load_w_regs(next, wn, wsn);
+    issue_stage<WF, TM>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    u32x4 wn_[NB];
+    uint32_t wsn[NB];
+    bf16x8 bn[NB];
+    load_w_regs(next, wn_, wsn);
+    __builtin_amdgcn_sched_barrier(0);           // the weights go out first: the decode below waits only for them
     read_a(next, 0, abuf[0]);
     __builtin_amdgcn_sched_barrier(0);
-    decode(wn, wsn, 0, bn);
+    decode(wn_, wsn, 0, bn);
     mfmas(abuf[1], bcur);                        // last MFMA step of stage st
-    interleave_mfma_valu<4, 12, 3>();            // the first MFMAs cover the operand reads
-    wc[0] = wn[0]; wc[1] = wn[1]; wsc[0] = wsn[0]; wsc[1] = wsn[1];
-    bcur[0] = bn[0]; bcur[1] = bn[1];
+    interleave_mfma_valu<4, MB * NB - 4, VB>();  // the first MFMAs cover the operand reads
+#pragma unroll
+    for (int nt = 0; nt < NB; ++nt) { wc[nt] = wn_[nt]; wsc[nt] = wsn[nt]; bcur[nt] = bn[nt]; }
   };
   for (int st = 0; st < nst; st += 3) {
     stage(std::integral_constant<int, 0>{}, st);
@@ -273,26 +295,27 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   wait_vmcnt<0>();   // the duplicate stages past the end have landed before the wave exits
 
   // epilogue: lane holds rows 8(i/4) + 4h + i%4 of each 32x32 block, column r32. Each row
-  // block of the wave (32 rows x 64 columns) is staged in LDS and leaves as 16-byte pieces of
-  // a row (four rows of 256 bytes per store instruction).
+  // block of the wave (32 rows x 32 NB columns) is staged in LDS and leaves as 16-byte pieces
+  // of a row.
   const float st_scale = *ts;
   const bool vec = (N & 3) == 0;
   __syncthreads();                                  // every wave is done with the ring slots
-  constexpr int kTS = 68;                           // staging row stride (floats): 16-byte aligned, banks shifted
+  constexpr int kTS = 32 * NB + 4;                  // staging row stride (floats): 16-byte aligned, banks shifted
+  constexpr int kPR = 8 * NB;                       // 16-byte pieces per staged row
   float* T = (float*)(lds + wave * (32 * kTS * 4));
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
+  for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) T[(8 * (i >> 2) + 4 * h + (i & 3)) * kTS + 32 * nt + r32] = acc[mt][nt][i] * st_scale;
     __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's stores to T are done
-    const int c4 = lane & 15;
+    const int c4 = lane % kPR;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = (lane >> 4) + 4 * j;
+    for (int j = 0; j < 32 * kPR / 64; ++j) {
+      const int r = lane / kPR + (64 / kPR) * j;
       const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
-      const int m = m0 + 32 * mt + r, n = n0 + 64 * wave + 4 * c4;
+      const int m = m0 + am + 32 * mt + r, n = n0 + bn0 + 4 * c4;
       if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);             // reads of T done before the next block overwrites it
@@ -396,6 +419,7 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
     u32x4 wn[4];
     uint32_t wsn[4];
     load_w_regs(next, wn, wsn);
+    __builtin_amdgcn_sched_barrier(0);
     read_b(next, 0, bx);
     __builtin_amdgcn_sched_barrier(0);
     decode(wn, wsn, 0, acur);
@@ -443,27 +467,26 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
   }
 }
 
+
+
+template <int WF>
+hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
+  constexpr int TM = kGemmTM;
+  const int bytes = kStages * Slot<WF, TM>::kBytes;
+  const void* fn = (const void*)k_gemm_mfma<WF, kGemmWGM, TM>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  const unsigned tiles = (unsigned)(((a.M + TM - 1) / TM) * ((a.N + kTN - 1) / kTN));
+  hipLaunchKernelGGL((k_gemm_mfma<WF, kGemmWGM, TM>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
+                     (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * Slot<kDense>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kDense>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL(k_gemm_mfma<kDense>, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
-                     (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
-  return hipGetLastError();
-}
+hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) { return launch_mfma_tiles<kDense>(a, s); }
 
-hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * Slot<kSp24>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_mfma<kSp24>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL(k_gemm_mfma<kSp24>, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
-                     (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
-  return hipGetLastError();
-}
+hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s) { return launch_mfma_tiles<kSp24>(a, s); }
 
 hipError_t launch_gemm_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   const int bytes = kStages * Slot<kSp24>::kBytes;

@@ -110,8 +110,49 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t* __restrict__
   }
 }
 
-// Stable placement inside a chunk, in rounds of 256 entries; inside a wave the rank among
-// equal ids comes from ballots, across the round's waves from per-wave counts in LDS.
+// Stable placement of the 256 entries [f0, f0 + 256): inside a wave the rank among equal ids
+// comes from ballots, across the four waves from per-wave counts wc[4][E] (zero on entry and on
+// return); cur[e] (next output row of expert e) advances past the round's rows.
+__device__ __forceinline__ void route_place_round(const int32_t* __restrict__ ids, int F, int k, int E, int f0,
+                                                  int32_t* cur, int32_t* wc, int32_t* __restrict__ row_token,
+                                                  int32_t* __restrict__ row_slot, int32_t* __restrict__ row_of) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int f = f0 + threadIdx.x;
+  const int e = f < F ? ids[f] : -1;
+  const bool valid = f < F && e >= 0 && e < E;
+  unsigned long long active = __ballot(valid);
+  int rank = 0, cnt = 0;
+  while (active) {
+    const int leader = __ffsll((long long)active) - 1;
+    const int el = __shfl(e, leader, 64);
+    const unsigned long long m = __ballot(valid && e == el);
+    if (valid && e == el) {
+      rank = __popcll(m & ((1ull << lane) - 1ull));
+      cnt = __popcll(m);
+    }
+    active &= ~m;
+  }
+  if (valid && rank == 0) wc[wave * E + e] = cnt;
+  __syncthreads();
+  if (valid) {
+    int pos = cur[e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
+    row_token[pos] = f / k;
+    row_slot[pos] = f % k;
+    row_of[f] = pos;
+  } else if (f < F) {
+    row_of[f] = -1;
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < E; x += kRouteThreads) {
+    cur[x] += wc[x] + wc[E + x] + wc[2 * E + x] + wc[3 * E + x];
+    wc[x] = 0; wc[E + x] = 0; wc[2 * E + x] = 0; wc[3 * E + x] = 0;
+  }
+  __syncthreads();
+}
+
+// One chunk per block; the chunk's first row of each expert comes from the offsets and the
+// column-scanned histogram.
 __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* __restrict__ ids, int F, int k,
                                                                  int E, const int32_t* __restrict__ hist,
                                                                  const int32_t* __restrict__ offsets,
@@ -121,46 +162,68 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_scatter(const int32_t* 
   extern __shared__ int32_t sm[];
   int32_t* cur = sm;            // [E]   next output row of each expert
   int32_t* wc = sm + E;         // [4][E] per-wave counts of the current round
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int e = threadIdx.x; e < E; e += kRouteThreads) {
     cur[e] = offsets[e] + hist[(size_t)blockIdx.x * E + e];
     for (int w = 0; w < 4; ++w) wc[w * E + e] = 0;
   }
   __syncthreads();
-  for (int round = 0; round < kRouteChunk / kRouteThreads; ++round) {
-    const int f = blockIdx.x * kRouteChunk + round * kRouteThreads + threadIdx.x;
-    const int e = f < F ? ids[f] : -1;
-    const bool valid = f < F && e >= 0 && e < E;
-    unsigned long long active = __ballot(valid);
-    int rank = 0, cnt = 0;
-    while (active) {
-      const int leader = __ffsll((long long)active) - 1;
-      const int el = __shfl(e, leader, 64);
-      const unsigned long long m = __ballot(valid && e == el);
-      if (valid && e == el) {
-        rank = __popcll(m & ((1ull << lane) - 1ull));
-        cnt = __popcll(m);
-      }
-      active &= ~m;
-    }
-    if (valid && rank == 0) wc[wave * E + e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int pos = cur[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wc[w * E + e];
-      row_token[pos] = f / k;
-      row_slot[pos] = f % k;
-      row_of[f] = pos;
-    } else if (f < F) {
-      row_of[f] = -1;
-    }
-    __syncthreads();
-    for (int x = threadIdx.x; x < E; x += kRouteThreads) {
-      cur[x] += wc[x] + wc[E + x] + wc[2 * E + x] + wc[3 * E + x];
-      wc[x] = 0; wc[E + x] = 0; wc[2 * E + x] = 0; wc[3 * E + x] = 0;
-    }
-    __syncthreads();
+  for (int round = 0; round < kRouteChunk / kRouteThreads; ++round)
+    route_place_round(ids, F, k, E, blockIdx.x * kRouteChunk + round * kRouteThreads, cur, wc, row_token, row_slot,
+                      row_of);
+}
+
+// Small routings (decode: a few tokens) in one block and one launch: histogram, offsets and
+// stable placement, the same results as the four kernels above.
+constexpr int kRouteSmallMax = 4 * kRouteChunk;    // entries (one block is slower beyond)
+
+__global__ __launch_bounds__(kRouteThreads) void k_route_small(const int32_t* __restrict__ ids, int F, int k, int E,
+                                                               int32_t* __restrict__ offsets, int64_t* __restrict__ bad,
+                                                               int32_t* __restrict__ row_token,
+                                                               int32_t* __restrict__ row_slot,
+                                                               int32_t* __restrict__ row_of) {
+  extern __shared__ int32_t sm[];
+  int32_t* cur = sm;            // [E] counts, then the next output row of each expert
+  int32_t* wc = sm + E;         // [4][E]
+  __shared__ int wsum[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    cur[e] = 0;
+    for (int w = 0; w < 4; ++w) wc[w * E + e] = 0;
   }
+  __syncthreads();
+  for (int f = threadIdx.x; f < F; f += kRouteThreads) {
+    const int e = ids[f];
+    if (e >= 0 && e < E) atomicAdd(&cur[e], 1);
+  }
+  __syncthreads();
+  // exclusive scan of the counts: thread t takes experts [t per, (t + 1) per)
+  const int per = (E + kRouteThreads - 1) / kRouteThreads;
+  const int e0 = min(E, (int)threadIdx.x * per), e1 = min(E, e0 + per);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += cur[e];
+  int inc = sum;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int ex = inc - sum;
+  for (int w = 0; w < wave; ++w) ex += wsum[w];
+  const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();                                  // every count is read before it is replaced
+  for (int e = e0; e < e1; ++e) {
+    const int c = cur[e];
+    offsets[e] = ex;
+    cur[e] = ex;
+    ex += c;
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = total;                             // rows with a valid expert id
+    if (bad) *bad = (int64_t)F - total;             // entries whose id is outside [0, E)
+  }
+  __syncthreads();
+  for (int f0 = 0; f0 < F; f0 += kRouteThreads) route_place_round(ids, F, k, E, f0, cur, wc, row_token, row_slot, row_of);
 }
 
 // ------------------------------------------------------------------------------ grouped product
@@ -484,6 +547,208 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
   }
 }
 
+// ------------------------------------------------------------------------------ weight streaming
+// Decode-sized routings (a few routed rows per touched expert): every touched expert's weights
+// must still be read once, so the work is cut along the weight rows and along K until every CU
+// has loads in flight. A work item is (expert e, group g of 32 weight rows, chunk of up to 32
+// routed rows of e) and runs on one workgroup of KS waves; wave w takes the w-th share of the
+// 64-wide K chunks (KS > 1 only when there are too few items to keep every CU's loads in flight), reads its 32 rows straight into registers (a ring of kSwRing chunks in
+// flight) and multiplies them on the matrix cores with the weights as the 32-row A operand:
+//  - dense: v_mfma_f32_32x32x16_bf16; lane (n = l % 32, h = l / 32) holds codes k = 32h..32h+31
+//    of each 64-k chunk (16 contiguous bytes) and feeds k = 32h + 8s + j to MFMA step s;
+//  - 2:4: v_smfmac_f32_32x32x32_bf16 with the stored vals/meta as the compressed A operand and
+//    its index operand (the two 16-k halves of step t are the 16-blocks 2h + t of the chunk).
+// The activations are the B operand (routed row m = l % 32; rows past the chunk read a zero
+// block). Weights are decoded with their E4M3 scale folded in (exact in bf16), so any k order
+// inside a chunk is valid as long as both operands use it. With KS > 1 the waves' partial sums
+// meet in LDS; wave 0 applies the tensor scale and the epilogue. Items run expert-major, weight group
+// next, routed-row chunk fastest, so workgroups that share weight rows run side by side.
+// For the SiLU-gate form the 32 rows of group g are gate rows 16g..16g+15 and up rows
+// I + 16g..I + 16g + 15; D row n of lane m holds gate row n and up row n + 16 at i and i + 8.
+constexpr int kSwRows = 32, kSwM = 32;
+#ifndef SSN_SW_RING
+#define SSN_SW_RING 4
+#endif
+constexpr int kSwRing = SSN_SW_RING;
+__device__ __attribute__((aligned(16))) uint32_t g_sw_zero[16];   // 64 zero bytes
+
+template <int WF>
+struct SwChunk {
+  u32x4 w;        // dense: 32 codes; 2:4: vals words 0, 1 and the meta word in w[2]
+  uint32_t sc;    // two E4M3 scale bytes (16-blocks 2h, 2h + 1 of the chunk)
+  u32x4 x[4];     // activation pieces (dense: k = 32h + 8s; 2:4: 16t + 8h and 32 + 16t + 8h)
+};
+
+template <int WF, int EPI, int KS>
+__global__ __launch_bounds__(KS * 64) void k_moe_stream(
+    const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
+    const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+    void* __restrict__ Y, int y_bf16, int ktiled) {
+  // LDS: clamped offsets co[E + 1], first item of each expert pre[E + 1], partial sums
+  extern __shared__ int lds_i[];
+  const int stride = (E + 4) & ~3;
+  int* co = lds_i;
+  int* pre = lds_i + stride;
+  float* red = (float*)(lds_i + 2 * stride);               // [KS - 1][16][64]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = N / kSwRows;        // weight-row groups per expert
+  // offsets clamped into [0, R] (one independent load per entry); the rows of expert e are
+  // [co[e], max(co[e + 1], co[e]))
+  for (int i = threadIdx.x; i <= E; i += KS * 64) co[i] = min(max(off[i], 0), R);
+  __syncthreads();
+  if (wave == 0) {                  // item counts per expert and their exclusive prefix
+    const int per = (E + 63) / 64;
+    const int e0 = min(E, lane * per), e1 = min(E, e0 + per);
+    int t = 0;
+    for (int e = e0; e < e1; ++e) t += G * ((max(co[e + 1] - co[e], 0) + kSwM - 1) / kSwM);
+    int inc = t;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += v;
+    }
+    int acc = inc - t;
+    for (int e = e0; e < e1; ++e) {
+      pre[e] = acc;
+      acc += G * ((max(co[e + 1] - co[e], 0) + kSwM - 1) / kSwM);
+    }
+    if (lane == 63) pre[E] = inc;
+  }
+  __syncthreads();
+  const int total = pre[E];
+  const int n = lane & 31, h = lane >> 5;
+  const int nch = K / 64;
+  const int c_lo = nch * wave / KS, c_hi = nch * (wave + 1) / KS;   // this wave's chunks
+  const size_t rowA = WF == kDense ? K / 2 : K / 4;        // main bytes per weight row
+  for (int it = blockIdx.x; it < total; it += gridDim.x) {
+    int lo = 0, hi = E;                                      // last e with pre[e] <= it
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (pre[mid] <= it) lo = mid; else hi = mid;
+    }
+    const int e = __builtin_amdgcn_readfirstlane(lo);
+    const int o0 = co[e], o1 = max(co[e + 1], o0);
+    const int mcs = (o1 - o0 + kSwM - 1) / kSwM;
+    const int local = it - pre[e];
+    const int g = local / mcs, mc = local % mcs;
+    const int r0 = o0 + kSwM * mc, cnt = min(kSwM, o1 - r0);
+    // this lane's weight row (A row n) and activation row (B column n)
+    const int wrow = EPI == kEpiSilu ? (n < 16 ? 16 * g + n : N / 2 + 16 * g + n - 16) : kSwRows * g + n;
+    const size_t er = (size_t)e * N + wrow;                 // row in the [E * N] row space
+    const uint8_t* pa;                                      // main weights of chunk 0
+    const uint8_t* pm = nullptr;                            // meta of chunk 0
+    const uint8_t* ps;                                      // scales of chunk 0
+    size_t sa, sm = 0, ss;                                  // byte steps per chunk
+    if (!ktiled) {
+      pa = w0 + er * rowA + (WF == kDense ? 16 : 8) * h; sa = WF == kDense ? 32 : 16;
+      if (WF == kSp24) { pm = w1 + er * (K / 8) + 4 * h; sm = 8; }
+      ps = scales + er * (K / 16) + 2 * h; ss = 4;
+    } else {                                                // piece (e, c, n) at ((e * nch + c) * N + n) * P
+      const size_t base = (size_t)e * nch * N + wrow;
+      pa = w0 + base * (WF == kDense ? 32 : 16) + (WF == kDense ? 16 : 8) * h; sa = (size_t)N * (WF == kDense ? 32 : 16);
+      if (WF == kSp24) { pm = w1 + base * 8 + 4 * h; sm = (size_t)N * 8; }
+      ps = scales + base * 4 + 2 * h; ss = (size_t)N * 4;
+    }
+    const bool xok = n < cnt;
+    int tok = r0 + n;
+    if (xok && row_token) tok = min(max(row_token[r0 + n], 0), x_rows - 1);
+    const uint16_t* xrow = xok ? X + (size_t)tok * K : (const uint16_t*)g_sw_zero;
+
+    auto load = [&](int c) -> SwChunk<WF> {
+      SwChunk<WF> o;
+      const bool in = c < c_hi;
+      const int cc = in ? c : c_lo;                          // past the share: its first chunk again, times zero
+      if constexpr (WF == kDense) {
+        o.w = *(const u32x4*)(pa + cc * sa);
+      } else {
+        const u32x2 v = *(const u32x2*)(pa + cc * sa);
+        o.w[0] = v[0]; o.w[1] = v[1]; o.w[2] = *(const uint32_t*)(pm + cc * sm); o.w[3] = 0u;
+      }
+      o.sc = *(const uint16_t*)(ps + cc * ss);
+      const bool live = xok && in;
+      const uint16_t* xp = live ? xrow + 64 * c : (const uint16_t*)g_sw_zero;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kx = WF == kDense ? 32 * h + 8 * j : 32 * (j >> 1) + 16 * (j & 1) + 8 * h;
+        o.x[j] = *(const u32x4*)(xp + (live ? kx : 0));
+      }
+      return o;
+    };
+
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    if (c_lo < c_hi) {
+      SwChunk<WF> ring[kSwRing];
+#pragma unroll
+      for (int u = 0; u < kSwRing; ++u) ring[u] = load(c_lo + u);
+      for (int c = c_lo; c < c_hi; c += kSwRing) {
+#pragma unroll
+        for (int u = 0; u < kSwRing; ++u) {
+          const SwChunk<WF> cur = ring[u];
+          ring[u] = load(c + u + kSwRing);
+          const float f0 = e4m3_f32_sel<0>(cur.sc), f1 = e4m3_f32_sel<1>(cur.sc);
+          if constexpr (WF == kDense) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+              const u32x4 a = fp4x8_bf16(cur.w[s], s < 2 ? f0 : f1);
+              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(cur.x[s]), acc, 0, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+              const u32x4 a = fp4x8_bf16(cur.w[t], t == 0 ? f0 : f1);
+              u32x8 b;
+              b[0] = cur.x[t][0]; b[1] = cur.x[t][1]; b[2] = cur.x[t][2]; b[3] = cur.x[t][3];
+              b[4] = cur.x[2 + t][0]; b[5] = cur.x[2 + t][1]; b[6] = cur.x[2 + t][2]; b[7] = cur.x[2 + t][3];
+              const int idx = (int)((cur.w[2] >> (16 * t)) & 0xFFFFu);
+              acc = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a), as_bf16x16(b), acc, idx, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    // the K shares meet in LDS; wave 0 holds D[8(i/4) + 4h + i%4][n] for routed row r0 + n
+    if (KS > 1) {
+      if (wave != 0)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[i];
+      __syncthreads();
+    }
+    if (wave == 0) {
+#pragma unroll
+      for (int w = 1; w < KS; ++w)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] += red[((w - 1) * 16 + i) * 64 + lane];
+      if (n < cnt) {
+        const float sc = ts[e];
+        if constexpr (EPI == kEpiSilu) {
+          const int I = N / 2;
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gt = acc[4 * b + i] * sc, up = acc[8 + 4 * b + i] * sc;
+              v[i] = gt / (1.0f + expf(-gt)) * up;     // silu(g) * u
+            }
+            store4(Y, y_bf16, I, r0 + n, 16 * g + 8 * b + 4 * h, v, (I & 3) == 0);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[4 * b + i] * sc;
+            store4(Y, y_bf16, N, r0 + n, kSwRows * g + 8 * b + 4 * h, v, (N & 3) == 0);
+          }
+        }
+      }
+    }
+    if (KS > 1) __syncthreads();                            // red is reused by the next item
+  }
+}
+
 // ------------------------------------------------------------------------------ weight layout
 // 64-k tiled copy of one weight array: dst[e][kt][n][0:P] = src[e][n][kt P : (kt + 1) P], one
 // 4-byte word per thread (P is 4, 8, 16 or 32 bytes; row_bytes = (K / 64) P).
@@ -564,6 +829,31 @@ hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
   return launch_moe_gemm_t<WF, EPI, 64>(a, s);
 }
 
+template <int WF, int EPI>
+hipError_t launch_moe_stream_t(const MoeGemmArgs& a, hipStream_t s) {
+  const int G = (int)(a.N / kSwRows);
+  // items <= G * (touched experts + R / 32) <= G * (min(E, R) + R / 32); extra workgroups exit
+  // after the item scan, and a workgroup loops over items when the grid is capped
+  const long touched = a.E < a.R ? a.E : a.R;
+  const long items = (long)G * (touched + a.R / kSwM);
+  if (items == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<long>(items, 4096);
+  const size_t stride = (size_t)((a.E + 4) & ~3);
+  // Few items and a long K: split K over four waves per item so that enough loads are in flight
+  if ((long)G * touched < 2048 && a.K / 64 >= 16) {
+    const size_t lds = 2 * stride * sizeof(int) + 3 * 16 * 64 * sizeof(float);
+    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 4>), dim3(grid), dim3(4 * 64), lds, s, a.X, (int)a.x_rows, (int)a.K,
+                       a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16,
+                       a.ktiled);
+  } else {
+    const size_t lds = 2 * stride * sizeof(int);
+    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 1>), dim3(grid), dim3(64), lds, s, a.X, (int)a.x_rows, (int)a.K,
+                       a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16,
+                       a.ktiled);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t moe_route_workspace(int64_t F, int E) {
@@ -580,6 +870,11 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
     hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), 0, s, (const int32_t*)nullptr, E, 0, offsets, bad);
     return hipGetLastError();
   }
+  if (F <= kRouteSmallMax) {
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(kRouteThreads), 5 * E * sizeof(int32_t), s, ids, F, k, E, offsets,
+                       bad, row_token, row_slot, row_of);
+    return hipGetLastError();
+  }
   int32_t* hist = (int32_t*)ws;
   int32_t* tot = hist + (size_t)B * E;
   hipLaunchKernelGGL(k_route_hist, dim3(B), dim3(kRouteThreads), E * sizeof(int32_t), s, ids, F, E, hist);
@@ -589,6 +884,11 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t
   hipLaunchKernelGGL(k_route_scatter, dim3(B), dim3(kRouteThreads), 5 * E * sizeof(int32_t), s, ids, F, k, E,
                      (const int32_t*)hist, (const int32_t*)offsets, row_token, row_slot, row_of);
   return hipGetLastError();
+}
+
+hipError_t launch_moe_stream(const MoeGemmArgs& a, hipStream_t s) {
+  if (a.sparse) return a.silu ? launch_moe_stream_t<kSp24, kEpiSilu>(a, s) : launch_moe_stream_t<kSp24, kEpiNone>(a, s);
+  return a.silu ? launch_moe_stream_t<kDense, kEpiSilu>(a, s) : launch_moe_stream_t<kDense, kEpiNone>(a, s);
 }
 
 hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s) {

@@ -64,6 +64,8 @@ size_t moe_route_workspace(int64_t F, int E);
 hipError_t launch_moe_route(const int32_t* ids, int64_t T, int k, int E, int32_t* offsets, int32_t* row_token,
                             int32_t* row_slot, int32_t* row_of, int64_t* bad, void* ws, hipStream_t s);
 hipError_t launch_moe_gemm(const MoeGemmArgs& a, hipStream_t s);
+// one wave per (expert, 32 weight rows, <= 32 routed rows); N % 32 == 0, K % 64 == 0
+hipError_t launch_moe_stream(const MoeGemmArgs& a, hipStream_t s);
 hipError_t launch_moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int64_t row_bytes, int64_t piece,
                                   uint8_t* dst, hipStream_t s);
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,

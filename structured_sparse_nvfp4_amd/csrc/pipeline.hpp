@@ -16,6 +16,21 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)l, 4, 0, 0);
 }
 
+// The same copies issued as buffer loads (MUBUF with the LDS bit) through a raw buffer resource:
+// base address `base` (wave-uniform), no bounds clamp, 32-bit byte offsets (per lane `voff`,
+// wave-uniform `soff`). The compiler's wait insertion treats the FLAT-encoded global form as an
+// access that may complete out of order with LDS reads, so every wait for an LDS read in a
+// kernel that holds one becomes lgkmcnt(0); with the buffer form it keeps exact counts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 4, voff, soff, 0, 0);
+}
+
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left unconstrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

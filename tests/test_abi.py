@@ -113,7 +113,13 @@ def test_moe_validation_without_launch():
     assert L.moe_grouped_gemm_nvfp4(p, 8, n, p, 9999, 8, 32, 64, 0, 0, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
     # empty problems are no-ops
     assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 32, 64, 0, 0, n, n, n, n, 0, n, 0, 0, ctypes.byref(used), n) == ssn.SSN_OK
-    assert used.value == ssn.ALGO_MFMA
+    assert used.value == ssn.ALGO_STREAM       # AUTO: few rows per expert and N % 32 == 0
+    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 40, 64, 0, 0, n, n, n, n, 0, n, 0, 0, ctypes.byref(used), n) == ssn.SSN_OK
+    assert used.value == ssn.ALGO_MFMA         # N % 32 != 0: the tiles
+    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 40, 64, 0, 0, n, n, n, n, 0, n, 0, ssn.ALGO_STREAM,
+                                    ctypes.byref(used), n) == ssn.SSN_E_ALGO
+    assert L.moe_grouped_gemm_nvfp4(n, 0, n, n, 4, 0, 32, 64, 1, 0, n, n, n, n, 0, n, 0, ssn.ALGO_STREAM,
+                                    ctypes.byref(used), n) == ssn.SSN_OK and used.value == ssn.ALGO_STREAM
     # unknown weight layout
     assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, 7, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
     # 64-k tiling of a weight array: piece sizes, divisibility, overlap, NULL, empty

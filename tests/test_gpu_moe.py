@@ -105,10 +105,11 @@ def test_pack_ktiles_matches_definition(piece):
         assert np.array_equal(got, _ktiles(a, piece))
 
 
+@pytest.mark.parametrize("algo", ["tiles", "stream"])
 @pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
 @pytest.mark.parametrize("gather", [True, False])
-def test_grouped_product_rows(sparse, gather, layout):
+def test_grouped_product_rows(sparse, gather, layout, algo):
     T, E, k, N, K = 90, 6, 3, 320, 192
     x = synth.activations(T, K, seed=11)
     ids = np.random.default_rng(3).integers(0, E, size=(T, k)).astype(np.int32)
@@ -126,8 +127,10 @@ def test_grouped_product_rows(sparse, gather, layout):
         x = x[rts]
     if layout == ssn.WLAYOUT_KTILE64:
         dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
-    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta, w_layout=layout)
-    assert used == (ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA)
+    want = ssn.ALGO_STREAM if algo == "stream" else ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
+    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta, w_layout=layout,
+                                         algo=ssn.ALGO_STREAM if algo == "stream" else ssn.ALGO_AUTO)
+    assert used == want
     yh = y_host(y)
     for e in range(E):
         r0, r1 = offs[e], offs[e + 1]
@@ -137,9 +140,10 @@ def test_grouped_product_rows(sparse, gather, layout):
         assert_within_bound(yh[r0:r1], Y, B, what=f"expert {e}")
 
 
+@pytest.mark.parametrize("algo", ["tiles", "stream"])
 @pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
-def test_grouped_silu_gate(sparse, layout):
+def test_grouped_silu_gate(sparse, layout, algo):
     T, E, k, D, I = 70, 5, 2, 128, 160
     x = synth.activations(T, D, seed=12)
     ids = np.random.default_rng(4).integers(0, E, size=(T, k)).astype(np.int32)
@@ -149,8 +153,11 @@ def test_grouped_silu_gate(sparse, layout):
     R = T * k
     if layout == ssn.WLAYOUT_KTILE64:
         dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
-    H, _ = ssn.moe_grouped_gemm_nvfp4(x_dev(x), rt, off, R, dm, dsc, dts, w_meta=dmeta,
-                                      epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, w_layout=layout)
+    tiles = ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
+    al = ssn.ALGO_STREAM if algo == "stream" else tiles
+    H, used = ssn.moe_grouped_gemm_nvfp4(x_dev(x), rt, off, R, dm, dsc, dts, w_meta=dmeta,
+                                         epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, w_layout=layout, algo=al)
+    assert used == al
     Hh = y_host(H)
     offs, rts = host(off).astype(np.int64), host(rt).astype(np.int64)
     for e in range(E):
@@ -161,6 +168,46 @@ def test_grouped_silu_gate(sparse, layout):
         err = np.abs(Hh[r0:r1] - st["H"])
         bound = moe.h_bound(st)
         assert np.all(err <= bound), f"expert {e}: max excess {float((err - bound).max())}"
+
+
+@pytest.mark.parametrize("sparse", [False, True])
+def test_stream_k_split_and_edges(sparse):
+    """Few items and a long K (the four-wave K split), an expert with more than 32 routed rows
+    (several routed-row chunks), and K not a multiple of the chunk ring."""
+    E, D, I = 6, 1088, 96                          # up: K = 1088 (17 chunks), N = 192
+    x = synth.activations(40, D, seed=21)
+    ids = np.array([[1, 4]] * 3 + [[4, 2]] * 37, np.int32)   # expert 4: 40 rows, 1: 3, 2: 37
+    ws = [synth.expert_up(e, I, D, seed=8) for e in range(E)]
+    qs, dm, dmeta, dsc, dts = _quant_experts(ws, sparse)
+    off, rt, _, _, _ = ssn.moe_route(dev(ids), E)
+    R = ids.size
+    H, used = ssn.moe_grouped_gemm_nvfp4(x_dev(x), rt, off, R, dm, dsc, dts, w_meta=dmeta,
+                                         epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.float32, algo=ssn.ALGO_STREAM)
+    assert used == ssn.ALGO_STREAM
+    Hh = y_host(H)
+    offs, rts = host(off).astype(np.int64), host(rt).astype(np.int64)
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 == r0:
+            continue
+        st = moe.up_stage(x[rts[r0:r1]], qs[e], I)
+        # f32 output: compare the unrounded silu(g) * u with the GEMM bound propagated through silu
+        err = np.abs(Hh[r0:r1] - st["h"])
+        bound = moe.h_bound(st)
+        assert np.all(err <= bound), f"expert {e}: max excess {float((err - bound).max())}"
+
+
+def test_stream_rejects_unaligned_n():
+    E, K, N = 2, 64, 48                            # N % 32 != 0
+    X = torch.zeros((4, K), dtype=torch.bfloat16, device="cuda")
+    off = torch.tensor([0, 2, 4], dtype=torch.int32, device="cuda")
+    w = torch.zeros((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((E, N, K // 16), dtype=torch.uint8, device="cuda")
+    ts = torch.ones(E, dtype=torch.float32, device="cuda")
+    with pytest.raises(ssn.SsnError):
+        ssn.moe_grouped_gemm_nvfp4(X, None, off, 4, w, sc, ts, algo=ssn.ALGO_STREAM)
+    _, used = ssn.moe_grouped_gemm_nvfp4(X, None, off, 4, w, sc, ts)   # AUTO: the tiles
+    assert used == ssn.ALGO_MFMA
 
 
 def test_combine_weighted_sum():
@@ -262,3 +309,34 @@ def test_ffn_full_config_sampled_tokens(sparse, layout):
     err = np.abs(got - ref)
     assert np.all(err <= tol), f"max excess {float((err - tol).max())}"
     assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_ffn_full_config_decode_tokens(sparse, layout):
+    """Decode-sized routing on the full expert set (512 experts, top-10, D = 2048, I = 512): two
+    tokens, every output checked. AUTO runs the routing in one block and both projections on the
+    weight-streaming kernel (the up projection with its K split over four waves)."""
+    T, E, k, D, I = 2, 512, 10, 2048, 512
+    x = synth.activations(T, D, seed=31)
+    ids, w = synth.routing(T, E, k, 1.1, seed=32)
+    up, down = _full_gpu_weights(E, I, D, sparse)
+    if layout == ssn.WLAYOUT_KTILE64:
+        up, down = ssn.moe_pack_weights(up), ssn.moe_pack_weights(down)
+    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down, w_layout=layout)
+
+    def q(gen, e):
+        wt = gen(e)
+        if sparse:
+            wt = sp24.prune24(wt)
+        c, s, st = quant.quantize(wt)
+        if sparse:
+            v, m, _ = sp24.compress(c)
+            return ("sp24", v, m, s, st)
+        return ("dense", c, s, st)
+
+    ref, tol, _ = moe.moe_ffn(x, ids, w, lambda e: q(lambda i: synth.expert_up(i, I, D), e),
+                              lambda e: q(lambda i: synth.expert_down(i, I, D), e), E, I)
+    assert int(host(bad)[0]) == 0
+    err = np.abs(y_host(out) - ref)
+    assert np.all(err <= tol), f"max excess {float((err - tol).max())}"
