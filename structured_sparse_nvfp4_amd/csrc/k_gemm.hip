@@ -39,7 +39,7 @@ constexpr int kTM = 256, kTN = 256, kTK = 64;   // output tile and K-stage
 constexpr int kStages = 3;                       // stages resident in LDS
 constexpr int kThreads = 256;
 #ifndef SSN_GEMM_WGM
-#define SSN_GEMM_WGM 2
+#define SSN_GEMM_WGM 1
 #endif
 constexpr int kGemmWGM = SSN_GEMM_WGM;   // waves along M in the dense tile (1 or 2)
 #ifndef SSN_GEMM_TM
