@@ -423,7 +423,11 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // rows >= M read row 0 and are never stored), B = weights (column = weight row lane % 32); lane
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
-constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
+#ifndef SSN_PS_STAGES
+#define SSN_PS_STAGES 3
+#endif
+constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = SSN_PS_STAGES, kPsMaxM = 8;
+static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
 constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
 constexpr int kPsBytes = kPsXOff + kPsMaxM * kPsXRow;          // one ring slot
@@ -467,10 +471,10 @@ __global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __res
     for (int st = 0; st < kPsStages - 1; ++st)
       if (st < nst) issue(st);
     for (int st = 0; st < nst; ++st) {
-      // this wave's loads of stage st have landed (stage st + 1 may be in flight), then every wave's
-      const bool ahead = st + 1 < nst;
-      if (wave < M) { if (ahead) wait_vmcnt<3>(); else wait_vmcnt<0>(); }
-      else { if (ahead) wait_vmcnt<2>(); else wait_vmcnt<0>(); }
+      // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
+      const int ahead = min(kPsStages - 2, nst - 1 - st);
+      if (wave < M) wait_stages<3>(ahead);
+      else wait_stages<2>(ahead);
       stage_barrier();
       if (st + kPsStages - 1 < nst) issue(st + kPsStages - 1);
       const uint8_t* b = smem + (st % kPsStages) * kPsBytes;
@@ -519,6 +523,127 @@ __global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __res
           if (!y_bf16) ((float*)Y)[(size_t)m * N + n] = v * st_;
           else ((uint16_t*)Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * st_);
         }
+      }
+    }
+    __syncthreads();                               // LDS is reused by the next row group
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (two 8-wave workgroups per
+// CU, 32-row groups, 512-wide K stages in a ring of kP4Stages LDS slots), with every direct load
+// a full 1 KB instruction: waves 0-3 load the vals of rows 8w..8w+7 (128 B each), waves 4-5 the
+// meta of rows 16(w-4)..+15 (64 B each), wave 6 the scales of all 32 rows (32 B each), and wave
+// m < M activation row m. Wave w then multiplies the 64-wide K chunk w of the stage for all 32
+// rows: two v_smfmac_f32_32x32x32_bf16 with the stored vals/meta as the compressed A operand and
+// its index operand (lane (n = l % 32, h = l / 32) holds the 8 kept values of 16-blocks 2h and
+// 2h + 1 of the chunk; step t takes block 2h + t), the kept values decoded with their E4M3 scale
+// (exact in bf16). The activations are the B operand (row m = l % 32, rows >= M read row 0 and
+// are never stored). The eight chunk partials of a row meet in LDS at the end.
+// LDS slot: vals [32][128 B] (16-byte piece p of row r holds global piece p ^ (r & 7)), meta
+// [32][64 B] (piece p holds global piece p ^ ((r >> 1) & 3)), scales [32][32 B], activations
+// [8][1 KB + 16 B].
+#ifndef SSN_P4_STAGES
+#define SSN_P4_STAGES 3
+#endif
+constexpr int kP4Stages = SSN_P4_STAGES;
+static_assert(kP4Stages >= 2 && kP4Stages <= 5, "wait_stages covers up to three stages in flight");
+constexpr int kP4VOff = 0, kP4MOff = kPsRows * (kSK / 4), kP4SOff = kP4MOff + kPsRows * (kSK / 8);
+constexpr int kP4XOff = kP4SOff + kPsRows * kSRow;
+constexpr int kP4Bytes = kP4XOff + kPsMaxM * kPsXRow;
+
+__global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
+                                                             const uint8_t* __restrict__ vals,
+                                                             const uint8_t* __restrict__ meta,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ ts, void* __restrict__ Y,
+                                                             int y_bf16, int R) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
+  const int nst = K / kSK;
+  const int h = lane >> 5, nl = lane & 31;
+  const int xm = nl < M ? nl : 0;
+  // direct loads of this wave per stage
+  const int nload = (wave < 7 ? 1 : 0) + (wave < M ? 1 : 0);
+  for (int g0 = row_lo; g0 < row_hi; g0 += kPsRows) {
+    auto issue = [&](int st) {
+      uint8_t* b = smem + (st % kP4Stages) * kP4Bytes;
+      const int k0 = st * kSK;
+      if (wave < 4) {                              // vals: rows 8w + l/8, piece l % 8
+        const int r = 8 * wave + (lane >> 3);
+        const int n = min(g0 + r, row_hi - 1);
+        const int q = (lane & 7) ^ (r & 7);
+        lds_dma16(vals + (size_t)n * (K / 4) + k0 / 4 + 16 * q, b + kP4VOff + wave * 1024);
+      } else if (wave < 6) {                       // meta: rows 16(w - 4) + l/4, piece l % 4
+        const int r = 16 * (wave - 4) + (lane >> 2);
+        const int n = min(g0 + r, row_hi - 1);
+        const int q = (lane & 3) ^ ((r >> 1) & 3);
+        lds_dma16(meta + (size_t)n * (K / 8) + k0 / 8 + 16 * q, b + kP4MOff + (wave - 4) * 1024);
+      } else if (wave == 6) {                      // scales: rows l/2, piece l % 2
+        const int r = lane >> 1;
+        const int n = min(g0 + r, row_hi - 1);
+        lds_dma16(scales + (size_t)n * (K / 16) + k0 / 16 + 16 * (lane & 1), b + kP4SOff);
+      }
+      if (wave < M) lds_dma16(X + (size_t)wave * K + k0 + 8 * lane, b + kP4XOff + wave * kPsXRow);
+    };
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int st = 0; st < kP4Stages - 1; ++st)
+      if (st < nst) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
+      const int ahead = min(kP4Stages - 2, nst - 1 - st);
+      if (nload == 2) wait_stages<2>(ahead);
+      else if (nload == 1) wait_stages<1>(ahead);
+      else wait_vmcnt<0>();
+      stage_barrier();
+      if (st + kP4Stages - 1 < nst) issue(st + kP4Stages - 1);
+      const uint8_t* b = smem + (st % kP4Stages) * kP4Bytes;
+      const u32x2 v = *(const u32x2*)(b + kP4VOff + nl * (kSK / 4) + 16 * (wave ^ (nl & 7)) + 8 * h);
+      const uint32_t mw = *(const uint32_t*)(b + kP4MOff + nl * (kSK / 8) + 16 * ((wave >> 1) ^ ((nl >> 1) & 3)) +
+                                             8 * (wave & 1) + 4 * h);
+      const uint32_t sw = *(const uint16_t*)(b + kP4SOff + nl * kSRow + 4 * wave + 2 * h);
+      const uint8_t* xr = b + kP4XOff + xm * kPsXRow + 2 * (64 * wave + 8 * h);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 lo = *(const u32x4*)(xr + 2 * (16 * t));
+        const u32x4 hi = *(const u32x4*)(xr + 2 * (32 + 16 * t));
+        u32x8 bx;
+        bx[0] = lo[0]; bx[1] = lo[1]; bx[2] = lo[2]; bx[3] = lo[3];
+        bx[4] = hi[0]; bx[5] = hi[1]; bx[6] = hi[2]; bx[7] = hi[3];
+        const u32x4 a = fp4x8_bf16(v[t], t == 0 ? e4m3_f32_sel<0>(sw) : e4m3_f32_sel<1>(sw));
+        acc = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(as_bf16x8(a), as_bf16x16(bx), acc, (int)((mw >> (16 * t)) & 0xFFFFu),
+                                                        0, 0);
+      }
+    }
+    __syncthreads();                               // every stage consumed: LDS holds the partial sums
+    float* red = (float*)smem;
+    if (wave != 0)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[i];
+    __syncthreads();
+    if (wave == 0 && nl < M) {
+      // lane holds D[8(i/4) + 4h + i%4][nl]: weight rows of the group for activation row nl
+      const float st_ = *ts;
+#pragma unroll
+      for (int b4 = 0; b4 < 4; ++b4) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc[4 * b4 + i];
+          for (int q = 0; q < kPsWaves - 1; ++q) v += red[(q * 16 + 4 * b4 + i) * 64 + lane];
+          o[i] = v * st_;
+        }
+        const int n = g0 + 8 * b4 + 4 * h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < row_hi) {
+            if (!y_bf16) ((float*)Y)[(size_t)nl * N + n + i] = o[i];
+            else ((uint16_t*)Y)[(size_t)nl * N + n + i] = (uint16_t)f32_to_bf16_rne(o[i]);
+          }
       }
     }
     __syncthreads();                               // LDS is reused by the next row group
@@ -683,6 +808,20 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
     hipLaunchKernelGGL((k_gemv_smfmac<kSparseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+    return hipGetLastError();
+  }
+  if (a.M <= kPsMaxM && a.K % kSK == 0) {   // full-width loads, 32x32x32 sparse MFMA per 64-k chunk
+    static bool p4_set = false;
+    if (!p4_set) {
+      hipError_t e2 = hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          kP4Stages * kP4Bytes);
+      if (e2 != hipSuccess) return e2;
+      p4_set = true;
+    }
+    const int G = (int)std::min<int64_t>(2 * (int64_t)cu_count(), (a.N + kPsRows - 1) / kPsRows);
+    const int R = (int)((a.N + G - 1) / G);
+    hipLaunchKernelGGL(k_gemv_ps24, dim3(G), dim3(kPsWaves * 64), kP4Stages * kP4Bytes, s, a.X, (int)a.M, (int)a.N,
+                       (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
   if (a.M <= 8) {    // two 8-wave workgroups per CU, 32-row groups

@@ -46,7 +46,10 @@ def test_dense(M, N, K, algo, prune):
 
 SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64, 1024), (4, 48, 4096),
               (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
-              (64, 1000, 2048), (257, 300, 128), (513, 257, 1088)]
+              (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
+              # M <= 8, K % 512 == 0 (full-width-load decode kernel): ragged row groups, several
+              # row groups per workgroup (N > 512 x 32), every M
+              (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", SP24_CASES)
@@ -94,18 +97,22 @@ def test_one_hot_rows_extract_weights_dense(algo):
     assert np.array_equal(y_host(g).astype(np.float32), want)
 
 
+@pytest.mark.parametrize("rows", [16, 8])
 @pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_VALU])
-def test_one_hot_rows_extract_weights_sp24(algo):
+def test_one_hot_rows_extract_weights_sp24(algo, rows):
     N, K = 48, 512
-    ks = np.array([0, 1, 2, 3, 17, 63, 64, 100, 127, 128, 200, 255, 256, 301, 383, 510])
-    x = np.zeros((16, K), np.float32)
-    x[np.arange(16), ks] = 1.0
-    xb = synth.f32_to_bf16_bits(x)
+    ks_all = np.array([0, 1, 2, 3, 17, 63, 64, 100, 127, 128, 200, 255, 256, 301, 383, 510])
     _, c, s, st = _problem(1, N, K, seed=5, prune=True)
     vals, meta, _ = sp24.compress(c)
-    g, _ = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)), algo=algo)
-    want = quant.dequantize(sp24.decompress(vals, meta), s, st)[:, ks].T.astype(np.float32)
-    assert np.array_equal(y_host(g).astype(np.float32), want)
+    for ks in (ks_all[:rows], ks_all[rows:]):
+        if ks.size == 0:
+            continue
+        x = np.zeros((ks.size, K), np.float32)
+        x[np.arange(ks.size), ks] = 1.0
+        xb = synth.f32_to_bf16_bits(x)
+        g, _ = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)), algo=algo)
+        want = quant.dequantize(sp24.decompress(vals, meta), s, st)[:, ks].T.astype(np.float32)
+        assert np.array_equal(y_host(g).astype(np.float32), want)
 
 
 def _one_hot_tiled(M, K, seed):
