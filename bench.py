@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 / 2:4 weight-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,prefill,moe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,prefill,head,moe]
 
 Prints ONE JSON line. ``value`` / ``ms_per_step`` / ``roofline`` / ``cpu_baseline`` describe the
 decode workload, where a step is one pass of the whole hot path over one batch of synthetic
@@ -22,7 +22,8 @@ HBM. ``value`` is the algorithmic bytes of the whole step divided by the step ti
 
 ``workloads`` adds the other shapes, each timed the same way: the square (4096^3, f32 out) and
 prefill (8192 x 27648 x 5120, 1% outliers x20, bf16 out) products for dense MFMA, 2:4 SMFMAC
-and 2:4 expanded-to-dense MFMA, and the grouped-expert FFN (4096 tokens, 512 experts, top-10
+and 2:4 expanded-to-dense MFMA, an output-head-shaped GEMV (N = 131072, K = 5120, M = 1, 8, 9),
+and the grouped-expert FFN (4096 tokens, 512 experts, top-10
 Zipf(1.1), D = 2048, I = 512) stage by stage, dense and 2:4, plus the same FFN at decode sizes
 (1, 4, 16, 32 tokens) against the full expert set, on the weight-streaming grouped kernels.
 """
@@ -51,7 +52,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workloads", default="decode,square,prefill,moe",
+    p.add_argument("--workloads", default="decode,square,prefill,head,moe",
                    help="comma list; decode is always run (it defines the step)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=13824, help="weight rows of the oracle sample")
@@ -309,6 +310,55 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
     return out
 
 
+HEAD_N, HEAD_K, HEAD_MS = 131072, 5120, (1, 8, 9)
+
+
+def run_head(torch, ssn, synth, reps):
+    """Output-head-shaped GEMV (vocabulary-sized N = 131072, K = 5120; M = 1, and 8 and 9 rows as
+    in speculative verification): weights of 377 MB (dense) / 294 MB (2:4), larger than the
+    Infinity Cache; two weight copies alternate so every call reads HBM."""
+    N, K = HEAD_N, HEAD_K
+    x = synth.activations(max(HEAD_MS), K)
+    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    W = torch.from_numpy(synth.weights(N, K)).cuda()
+    dn, sp = _gpu_weights(ssn, W)
+    del W
+    torch.cuda.empty_cache()
+    dns = [dn, tuple(t.clone() for t in dn)]
+    sps = [sp, tuple(t.clone() for t in sp)]
+    out = {"shape": {"N": N, "K": K, "M": list(HEAD_MS), "y": "f32"}, "weight_copies": 2}
+    for M in HEAD_MS:
+        Xm = X[:M].contiguous()
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        pd, ps, used = [], [], {}
+        for d, s_ in zip(dns, sps):
+            p, (_, ud) = ssn.gemm_nvfp4_dense(Xm, d[0], d[1], d[2], Y=Y, prepare=True)
+            pd.append(p)
+            p, (_, us_) = ssn.gemm_nvfp4_sp24(Xm, s_[0], s_[1], s_[2], s_[3], Y=Y, prepare=True)
+            ps.append(p)
+            used = {"dense": ud, "sp24": us_}
+        B = Batches(torch)
+        for n, calls in (("dense", pd), ("sp24", ps)):
+            B.run(n, calls)
+        torch.cuda.synchronize()
+        for n, calls in (("dense", pd), ("sp24", ps)):
+            B.run(n, calls * reps)
+        torch.cuda.synchronize()
+        e = {}
+        for n in ("dense", "sp24"):
+            us = B.us(n)
+            b = bytes_gemm(M, N, K, n == "sp24", 4)
+            e[n] = {"us": round(us, 1), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "tflops_dense_equiv": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2),
+                    "algo": ssn.ALGO_NAMES.get(used[n].value, "?")}
+        e["sp24"]["speedup_vs_dense"] = round(e["dense"]["us"] / e["sp24"]["us"], 3)
+        out[f"M{M}"] = e
+    del dns, sps, dn, sp, X
+    torch.cuda.empty_cache()
+    return out
+
+
 def run_moe(torch, ssn, synth, reps):
     import numpy as np
     T, E, k, D, I = 4096, 512, 10, 2048, 512
@@ -527,6 +577,9 @@ def main():
     if "prefill" in wl:
         work["prefill"] = run_gemm_shape(torch, ssn, synth, 8192, 27648, 5120, torch.bfloat16, True, 5)
         print("[bench] prefill done", file=sys.stderr, flush=True)
+    if "head" in wl:
+        work["head"] = run_head(torch, ssn, synth, 10)
+        print("[bench] head done", file=sys.stderr, flush=True)
     if "moe" in wl:
         work["moe"] = run_moe(torch, ssn, synth, 5)
         print("[bench] moe done", file=sys.stderr, flush=True)

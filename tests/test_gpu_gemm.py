@@ -28,7 +28,8 @@ def _problem(M, N, K, seed, prune):
 # M > 16 shapes run the 256 x 256 tiles: several tiles in M and N, ragged edges, K tails of 32
 DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
-               (64, 1000, 2048), (257, 300, 128), (513, 257, 1088)]
+               (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
+               (3, 17000, 512)]                   # several row groups per decode workgroup
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
