@@ -151,6 +151,25 @@ int sp24_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad_groups, 
 int sp24_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* vals, uint8_t* meta,
                   int64_t* bad_groups, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * nvfp4_sp24_produce — the 2:4 weight producer in one pass over W: the result of sp24_prune,
+ * then nvfp4_quantize, then sp24_compress, bit for bit ("NVFP4 vs 2:4 sparse", robertz.co,
+ * section on what the ecosystem supports: the tool that pruned and packed 2:4 checkpoints was
+ * withdrawn; "NVFP4 Without FP4 Hardware", ai-muninn.com, sections "Convert BF16 to NVFP4
+ * yourself" and "The shared global scale").
+ * Pruning keeps the two largest |w| of each group of four along K (ties to the lower index) and
+ * sets the others to +0.0; because the largest entry of every block and of the tensor is kept,
+ * s_t and the block scales are those of W itself (s_t = *tensor_scale_in when given).
+ * W: f32 or bf16 (w_dtype) [N, K], finite; outputs (device, caller-owned): vals [N, K/4],
+ * meta [N, K/8], scales [N, K/16], tensor_scale_out f32 [1], codes [N, K/2] (nullable: the
+ * pruned tensor's NVFP4 codes, for the dense product on pruned weights), bad_groups int64 [1]
+ * (groups with fewer than two zero codes: always 0 after pruning, kept for the compress
+ * contract). Errors: NULL, SHAPE (K % 32), ALIGN, DTYPE, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int nvfp4_sp24_produce(const void* W, int w_dtype, int64_t N, int64_t K, const float* tensor_scale_in,
+                       uint8_t* vals, uint8_t* meta, uint8_t* scales, float* tensor_scale_out,
+                       uint8_t* codes, int64_t* bad_groups, void* stream);
+
 /* sp24_decompress — inverse of sp24_compress: writes the kept codes at their positions and
  * code 0 elsewhere (if i0 == i1 the second kept code wins). vals [N,K/4], meta [N,K/8] ->
  * codes [N,K/2]. Errors: NULL, SHAPE, ALIGN, HIP. */

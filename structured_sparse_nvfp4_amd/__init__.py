@@ -29,6 +29,7 @@ _SIGS = {
     "ssn_version": ([], _int),
     "nvfp4_quantize": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _vp, _int, _vp], _int),
+    "nvfp4_sp24_produce": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _int),
     "sp24_prune": ([_vp, _int, _i64, _i64, _vp, _vp], _int),
     "sp24_check": ([_vp, _i64, _i64, _vp, _vp, _vp], _int),
     "sp24_compress": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
@@ -161,6 +162,34 @@ def nvfp4_dequantize(codes, scales, tensor_scale, out_dtype=torch.float32, out=N
     _check(lib().nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(tensor_scale), N, K, _ptr(out), dt,
                                   _stream(codes.device)))
     return out
+
+
+def nvfp4_sp24_produce(W, tensor_scale_in=None, vals=None, meta=None, scales=None, tensor_scale_out=None,
+                       codes=None, want_codes=False, bad_groups=None, prepare=False):
+    """Prune -> quantise -> compress W [N, K] (f32 or bf16) in one pass, bit-identical to sp24_prune,
+    nvfp4_quantize and sp24_compress in turn. Returns (vals u8 [N,K/4], meta u8 [N,K/8], scales u8
+    [N,K/16], s_t f32 [1], bad_groups int64 [1] device, codes u8 [N,K/2] of the pruned tensor or None)."""
+    N, K = W.shape
+    _need(W, W.dtype, "W")
+    dev = W.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    vals = vals if vals is not None else torch.empty((N, K // 4), **u8)
+    meta = meta if meta is not None else torch.empty((N, K // 8), **u8)
+    scales = scales if scales is not None else torch.empty((N, K // 16), **u8)
+    ts = tensor_scale_out if tensor_scale_out is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    bad = bad_groups if bad_groups is not None else torch.empty(1, dtype=torch.int64, device=dev)
+    if codes is None and want_codes:
+        codes = torch.empty((N, K // 2), **u8)
+    _need(vals, torch.uint8, "vals", (N, K // 4)); _need(meta, torch.uint8, "meta", (N, K // 8))
+    _need(scales, torch.uint8, "scales", (N, K // 16)); _need(ts, torch.float32, "tensor_scale_out", (1,))
+    _need(bad, torch.int64, "bad_groups", (1,))
+    if codes is not None:
+        _need(codes, torch.uint8, "codes", (N, K // 2))
+    if tensor_scale_in is not None:
+        _need(tensor_scale_in, torch.float32, "tensor_scale_in", (1,))
+    cargs = (_ptr(W), _wdt(W), N, K, _ptr(tensor_scale_in), _ptr(vals), _ptr(meta), _ptr(scales), _ptr(ts),
+             _ptr(codes), _ptr(bad), _stream(dev))
+    return _run("nvfp4_sp24_produce", cargs, prepare, (W, tensor_scale_in), (vals, meta, scales, ts, bad, codes))
 
 
 def sp24_prune(W, out=None, prepare=False):

@@ -86,6 +86,25 @@ int nvfp4_quantize(const void* W, int w_dtype, int64_t N, int64_t K, const float
                                          tensor_scale_out, as_stream(stream)), fn);
 }
 
+int nvfp4_sp24_produce(const void* W, int w_dtype, int64_t N, int64_t K, const float* tensor_scale_in,
+                       uint8_t* vals, uint8_t* meta, uint8_t* scales, float* tensor_scale_out, uint8_t* codes,
+                       int64_t* bad_groups, void* stream) {
+  const char* fn = "nvfp4_sp24_produce";
+  int st;
+  if ((st = check_nk(fn, N, K))) return st;
+  if ((st = check_dtype(fn, w_dtype, "w_dtype"))) return st;
+  REQUIRE_ELEM_PTR(tensor_scale_out);
+  REQUIRE_OPT_ELEM_PTR(tensor_scale_in);
+  REQUIRE_ELEM_PTR(bad_groups);
+  REQUIRE_OPT_PTR(codes);
+  if (N == 0 || K == 0)
+    return hip_status(ssn::launch_produce24(nullptr, 0, 0, 0, tensor_scale_in, nullptr, nullptr, nullptr,
+                                            tensor_scale_out, nullptr, bad_groups, as_stream(stream)), fn);
+  REQUIRE_PTR(W); REQUIRE_PTR(vals); REQUIRE_PTR(meta); REQUIRE_PTR(scales);
+  return hip_status(ssn::launch_produce24(W, w_dtype == SSN_BF16, N, K, tensor_scale_in, vals, meta, scales,
+                                          tensor_scale_out, codes, bad_groups, as_stream(stream)), fn);
+}
+
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int64_t N,
                      int64_t K, void* out, int out_dtype, void* stream) {
   const char* fn = "nvfp4_dequantize";

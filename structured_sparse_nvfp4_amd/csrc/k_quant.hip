@@ -12,6 +12,7 @@
 
 #include "common.hpp"
 #include "launch.hpp"
+#include "sp24_rules.hpp"
 
 namespace ssn {
 namespace {
@@ -246,6 +247,100 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nbl
   }
 }
 
+// ---- fused 2:4 producer: prune -> quantise -> compress in one pass over W.
+// ("NVFP4 vs 2:4 sparse", robertz.co, section on what the ecosystem supports: the tool that
+// pruned and packed 2:4 checkpoints was withdrawn; "NVFP4 Without FP4 Hardware", ai-muninn.com,
+// section "Convert BF16 to NVFP4 yourself".) The result is bit-identical to sp24_prune, then
+// nvfp4_quantize, then sp24_compress:
+//  - pruning keeps the two largest |w| of every group of four, so the largest |w| of any block
+//    of 16 and of the whole tensor survives: the tensor scale and every block scale equal those
+//    of the unpruned tensor, and the amax pass runs on W itself;
+//  - the pruned entries become +0.0 (code 0x0) before the block is quantised exactly as in
+//    k_quantize, and each group's four codes are compressed by the shared 2:4 rule (which still
+//    decides, so a kept value that rounds to zero is handled as compress would).
+// Layout and traversal as k_quantize (wave chunks of 64 blocks, LDS transpose, lane = block).
+// Per block: vals 4 bytes, meta 2 bytes, scale 1 byte, and (optional) the 8 code bytes of the
+// pruned tensor. A group that still has fewer than two zero codes (impossible after pruning) is
+// counted in *bad like sp24_compress does.
+template <int BF16>
+__global__ __launch_bounds__(kThreads) void k_produce24(const void* W, size_t nblocks, const float* ts,
+                                                        uint8_t* vals, uint8_t* meta, uint8_t* scales,
+                                                        uint8_t* codes, int64_t* bad) {
+  constexpr int P = BF16 ? 2 : 4;              // 16-byte pieces per block
+  __shared__ u32x4 tr[kThreads / 64][kQBlocks * P];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4* t = tr[wave];
+  const size_t nchunks = (nblocks + kQBlocks - 1) / kQBlocks;
+  const size_t c0 = ((size_t)blockIdx.x * (kThreads / 64) + wave) * kQIter;
+  const double st = (double)*ts;
+  uint32_t nbad = 0;
+  for (int it = 0; it < kQIter; ++it) {
+    if (c0 + it >= nchunks) break;                               // uniform per wave
+    const size_t b0 = (nchunks - 1 - (c0 + it)) * kQBlocks;      // first block of the chunk
+    const u32x4* src = (const u32x4*)W + b0 * P;
+    u32x4 v[P];
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int p = 64 * u + lane;
+      v[u] = b0 + p / P < nblocks ? ld_nt(src + p) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int p = 64 * u + lane, b = p / P;
+      t[b * P + ((p % P) ^ q_swz<BF16>(b))] = v[u];
+    }
+    __asm__ volatile("" ::: "memory");
+    float w[16];
+#pragma unroll
+    for (int x = 0; x < P; ++x) {
+      const u32x4 r = t[lane * P + (x ^ q_swz<BF16>(lane))];
+      if (BF16) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { w[8 * x + 2 * e] = bf16_lo(r[e]); w[8 * x + 2 * e + 1] = bf16_hi(r[e]); }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[4 * x + e] = __uint_as_float(r[e]);
+      }
+    }
+    __asm__ volatile("" ::: "memory");
+    if (b0 + lane < nblocks) {
+      // prune: entry i of a group is dropped when two entries outrank it (|w_j| > |w_i|, or equal
+      // with j < i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = fabsf(w[4 * g + i]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          int outrank = 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) outrank += (a[j] > a[i]) || (a[j] == a[i] && j < i);
+          if (outrank >= 2) w[4 * g + i] = 0.0f;
+        }
+      }
+      u32x2 code;
+      uint32_t S;
+      quantize_block(w, st, code, S);
+      const size_t b = b0 + lane;
+      uint32_t vw = 0, mw = 0;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t r = compress_group((code[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
+        nbad += r >> 12;
+        vw |= (r & 0xFFu) << (8 * g);
+        mw |= ((r >> 8) & 0xFu) << (4 * g);
+      }
+      *(uint32_t*)(vals + b * 4) = vw;
+      *(uint16_t*)(meta + b * 2) = (uint16_t)mw;
+      scales[b] = (uint8_t)S;
+      if (codes) *(u32x2*)(codes + b * 8) = code;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) nbad += __shfl_xor(nbad, off, 64);
+  if (lane == 0 && nbad) atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
+}
+
 // double -> f32 rounded to odd: truncate, then set the last bit if anything was dropped. A
 // later rounding to bf16 (16 fewer bits) is then the correctly rounded bf16 of the double.
 __device__ __forceinline__ float to_f32_round_odd(double x) {
@@ -320,6 +415,8 @@ __global__ __launch_bounds__(kThreads) void k_prune(const void* W, int w_bf16, s
   }
 }
 
+__global__ void k_zero_i64(int64_t* p) { *p = 0; }
+
 inline unsigned grid_for(size_t n, int per_block) { return (unsigned)((n + per_block - 1) / per_block); }
 
 }  // namespace
@@ -331,7 +428,7 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
   // any K % 16 == 0 tensor); the quantisation kernel overwrites them afterwards.
   float* part = (float*)codes;
   unsigned nparts = 0;
-  if (!ts_in) {
+  if (!ts_in && n) {                               // an empty tensor has no maximum: s_t = 0
     const size_t n16 = n / (w_bf16 ? 8 : 4);
     nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece * kAmaxIters - 1) / (kAmaxPiece * kAmaxIters));
     hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
@@ -345,6 +442,34 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
       hipLaunchKernelGGL(k_quantize<1>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
     else
       hipLaunchKernelGGL(k_quantize<0>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_produce24(const void* W, int w_bf16, int64_t N, int64_t K, const float* ts_in, uint8_t* vals,
+                            uint8_t* meta, uint8_t* scales, float* ts_out, uint8_t* codes, int64_t* bad,
+                            hipStream_t s) {
+  const size_t n = (size_t)N * (size_t)K;
+  // block maxima parked in the vals output (N*K/4 bytes, >= 4 bytes per amax block)
+  float* part = (float*)vals;
+  unsigned nparts = 0;
+  if (!ts_in && n) {
+    const size_t n16 = n / (w_bf16 ? 8 : 4);
+    nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece * kAmaxIters - 1) / (kAmaxPiece * kAmaxIters));
+    hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
+  }
+  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
+  hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, s, bad);
+  const size_t nb = n / 16;
+  if (nb) {
+    const size_t waves = ((nb + kQBlocks - 1) / kQBlocks + kQIter - 1) / kQIter;
+    const dim3 grid(grid_for(waves, kThreads / 64));
+    if (w_bf16)
+      hipLaunchKernelGGL(k_produce24<1>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, vals, meta, scales,
+                         codes, bad);
+    else
+      hipLaunchKernelGGL(k_produce24<0>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, vals, meta, scales,
+                         codes, bad);
   }
   return hipGetLastError();
 }

@@ -1,27 +1,16 @@
 // 2:4 check, compress and decompress of NVFP4 codes on gfx950. HBM-bound streaming kernels:
 // each lane moves 16 B of codes (32 codes = 8 groups of four) per step with a 128-bit load.
-//
-// Rule ("Sparse GPU FLOPS Need the Right Zeros in the Right Places", leviathansystems.co,
-// section "The operation determines which four entries belong together"): a group of four
-// consecutive codes along K is eligible when at least two are zero; a code is zero when its
-// three magnitude bits are 0 (so 0x8, the FP4 negative zero, is zero). The check is per group
-// (same page, section "Two half-zero vectors produce different pattern answers").
-// Compressed form ("NVFP4 vs 2:4 sparse", robertz.co, section "What 2:4 actually is"): the two
-// kept codes plus a 2-bit position each. Kept positions are the nonzero codes first, then the
-// lowest-index zeros, in ascending order; a failing group is written as vals 0x00 with
-// positions (0, 1) and counted.
+// The eligibility and compression rules themselves are in sp24_rules.hpp; the check is per
+// group ("Sparse GPU FLOPS Need the Right Zeros in the Right Places", leviathansystems.co,
+// section "Two half-zero vectors produce different pattern answers").
 #include "common.hpp"
 #include "launch.hpp"
+#include "sp24_rules.hpp"
 
 namespace ssn {
 namespace {
 
 constexpr int kThreads = 256;
-
-// bit 4i of the result is set when nibble i of w has zero magnitude bits
-__device__ __forceinline__ uint32_t zero_nibbles(uint32_t w) {
-  return ~(w | (w >> 1) | (w >> 2)) & 0x11111111u;
-}
 
 __global__ void k_init_counters(int64_t* bad, int64_t* first) {
   *bad = 0;
@@ -76,22 +65,6 @@ __global__ __launch_bounds__(kThreads) void k_check(const u32x4* codes, size_t n
     atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
     if (first) atomicMin((unsigned long long*)first, (unsigned long long)fb);
   }
-}
-
-// Compress one group (16-bit word of four codes): returns vals byte | pos nibble << 8 | fail << 12
-__device__ __forceinline__ uint32_t compress_group(uint32_t g) {
-  const uint32_t z = zero_nibbles(g) & 0x1111u;
-  // nonzero mask over the 4 positions
-  const uint32_t nz = (~((z & 1u) | ((z >> 3) & 2u) | ((z >> 6) & 4u) | ((z >> 9) & 8u))) & 0xFu;
-  const uint32_t cnt = __builtin_popcount(nz);
-  if (cnt > 2) return 0x0u | (0x4u << 8) | (1u << 12);
-  uint32_t sel = nz;
-  if (cnt == 1) sel |= (~nz & 0xFu) & (0u - (~nz & 0xFu));   // add the lowest zero position
-  if (cnt == 0) sel = 0x3u;                                    // two lowest zero positions
-  const uint32_t i0 = __builtin_ctz(sel);
-  const uint32_t i1 = 31u - __builtin_clz(sel);
-  const uint32_t c0 = (g >> (4 * i0)) & 0xFu, c1 = (g >> (4 * i1)) & 0xFu;
-  return (c0 | (c1 << 4)) | ((i0 | (i1 << 2)) << 8);
 }
 
 __global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_t n16, u32x2* vals,
