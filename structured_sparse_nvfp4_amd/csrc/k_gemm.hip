@@ -45,7 +45,13 @@ constexpr int kGemmWGM = SSN_GEMM_WGM;   // waves along M in the dense tile (1 o
 #ifndef SSN_GEMM_TM
 #define SSN_GEMM_TM 256
 #endif
-constexpr int kGemmTM = SSN_GEMM_TM;     // activation rows of the dense tile (256: one block per CU, 128: two)
+constexpr int kGemmTM = SSN_GEMM_TM;
+// Issue each stage's direct loads in four parts over the MFMA steps of the previous stage
+// instead of one burst at the stage boundary.
+#ifndef SSN_GEMM_SPREAD
+#define SSN_GEMM_SPREAD 1
+#endif
+constexpr bool kSpreadLoads = SSN_GEMM_SPREAD != 0;     // activation rows of the dense tile (256: one block per CU, 128: two)
 
 // One LDS ring slot (bytes) of a tile with TM activation rows and 256 weight rows (tile-local).
 //   X      [TM][128 B]   activation k-chunk c of row r at physical chunk c ^ swz(r)
@@ -152,6 +158,41 @@ __device__ __forceinline__ void issue_stage(const StageSrc<WF, TM>& g, int st, c
   lds_dma4(sr, g.so, st * (kTK / 16), slot + L::kSc + wave * 256);
 }
 
+// Load `idx` of a stage (scales, then the weight loads, then the activation loads): the loads of
+// a stage can be issued in four parts spread over the MFMA steps instead of in one burst.
+template <int WF, int TM>
+__device__ __forceinline__ void issue_one(const StageSrc<WF, TM>& g, int st, char* slot, int wave, int idx) {
+  using L = Slot<WF, TM>;
+  constexpr int nW = WF == kDense ? 2 : 3;
+  if (idx == 0) {
+    lds_dma4(buf_rsrc(g.sb), g.so, st * (kTK / 16), slot + L::kSc + wave * 256);
+  } else if (idx <= nW) {
+    const int i = idx - 1;
+    if constexpr (WF == kDense) {
+      lds_dma16(buf_rsrc(g.wb), g.wo[i], st * (kTK / 2), slot + L::kW + (2 * wave + i) * 1024);
+    } else {
+      if (i == 0) lds_dma16(buf_rsrc(g.wb), g.wo[0], st * (kTK / 4), slot + L::kW + wave * 1024);
+      else lds_dma4(buf_rsrc(g.mb), g.mo[i - 1], st * (kTK / 8), slot + L::kMeta + (2 * wave + i - 1) * 256);
+    }
+  } else {
+    const int i = idx - 1 - nW;
+    lds_dma16(buf_rsrc(g.xb), g.xo[i], st * (kTK * 2), slot + L::kX + (TM / 32 * wave + i) * 1024);
+  }
+}
+
+template <int WF, int TM>
+constexpr int part_loads(int part) {
+  constexpr int n = Slot<WF, TM>::kLoads, per = (n + 3) / 4;
+  return part * per >= n ? 0 : ((part + 1) * per > n ? n - part * per : per);
+}
+
+template <int WF, int TM, int PART>
+__device__ __forceinline__ void issue_part(const StageSrc<WF, TM>& g, int st, char* slot, int wave) {
+  constexpr int per = (Slot<WF, TM>::kLoads + 3) / 4;
+#pragma unroll
+  for (int idx = PART * per; idx < (PART + 1) * per && idx < Slot<WF, TM>::kLoads; ++idx) issue_one<WF, TM>(g, st, slot, wave, idx);
+}
+
 // 16-byte activation chunk `c` of tile row r
 __device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c) {
   return *(const u32x4*)(slot + r * 128 + 16 * (c ^ swz(r)));
@@ -211,7 +252,8 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   const StageSrc<WF, TM> src = stage_src<WF, TM>(X, w0, w1, scales, M, N, K, m0, n0, wave, lane);
   issue_stage<WF, TM>(src, 0, lds, wave);
   issue_stage<WF, TM>(src, min(1, last), lds + L::kBytes, wave);
-  issue_stage<WF, TM>(src, min(2, last), lds + 2 * L::kBytes, wave);
+  if constexpr (kSpreadLoads) issue_part<WF, TM, 0>(src, min(2, last), lds + 2 * L::kBytes, wave);
+  else issue_stage<WF, TM>(src, min(2, last), lds + 2 * L::kBytes, wave);
 
   u32x4 wc[NB];         // this stage's weights (per column block) and their scale pair
   uint32_t wsc[NB];
@@ -247,7 +289,8 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     }
   };
 
-  wait_vmcnt<2 * L::kLoads>();
+  if constexpr (kSpreadLoads) wait_vmcnt<L::kLoads + part_loads<WF, TM>(0)>();
+  else wait_vmcnt<2 * L::kLoads>();
   stage_barrier();
   load_w_regs(lds, wc, wsc);
   read_a(lds, 0, abuf[0]);
@@ -257,8 +300,14 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     constexpr int S = decltype(slot_c)::value;
     const char* slot = lds + S * L::kBytes;
     const char* next = lds + ((S + 1) % kStages) * L::kBytes;
+    char* fill = lds + ((S + 2) % kStages) * L::kBytes;   // stage st + 2: its first part is in flight
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
+      if constexpr (kSpreadLoads) {
+        if (s == 0) issue_part<WF, TM, 1>(src, min(st + 2, last), fill, wave);
+        else if (s == 1) issue_part<WF, TM, 2>(src, min(st + 2, last), fill, wave);
+        else issue_part<WF, TM, 3>(src, min(st + 2, last), fill, wave);
+      }
       read_a(slot, s + 1, abuf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);         // operand reads go out first, a whole step ahead
       bf16x8 bn[NB];
@@ -273,7 +322,8 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
     wait_vmcnt<L::kLoads>();                     // ... and stage st + 1 has landed
     stage_barrier();
-    issue_stage<WF, TM>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    if constexpr (kSpreadLoads) issue_part<WF, TM, 0>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    else issue_stage<WF, TM>(src, min(st + 3, last), lds + S * L::kBytes, wave);
     u32x4 wn_[NB];
     uint32_t wsn[NB];
     bf16x8 bn[NB];
