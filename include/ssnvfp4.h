@@ -154,7 +154,7 @@ int sp24_compress(const uint8_t* codes, int64_t N, int64_t K, uint8_t* vals, uin
 /* ---------------------------------------------------------------------------------------------
  * nvfp4_sp24_produce — the 2:4 weight producer in one pass over W: the result of sp24_prune,
  * then nvfp4_quantize, then sp24_compress, bit for bit ("NVFP4 vs 2:4 sparse", robertz.co,
- * section on what the ecosystem supports: the tool that pruned and packed 2:4 checkpoints was
+ * section "Where it is supported in software": the tool that pruned and packed 2:4 checkpoints was
  * withdrawn; "NVFP4 Without FP4 Hardware", ai-muninn.com, sections "Convert BF16 to NVFP4
  * yourself" and "The shared global scale").
  * Pruning keeps the two largest |w| of each group of four along K (ties to the lower index) and

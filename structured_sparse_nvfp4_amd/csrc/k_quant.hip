@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nbl
 }
 
 // ---- fused 2:4 producer: prune -> quantise -> compress in one pass over W.
-// ("NVFP4 vs 2:4 sparse", robertz.co, section on what the ecosystem supports: the tool that
+// ("NVFP4 vs 2:4 sparse", robertz.co, section "Where it is supported in software": the tool that
 // pruned and packed 2:4 checkpoints was withdrawn; "NVFP4 Without FP4 Hardware", ai-muninn.com,
 // section "Convert BF16 to NVFP4 yourself".) The result is bit-identical to sp24_prune, then
 // nvfp4_quantize, then sp24_compress:
