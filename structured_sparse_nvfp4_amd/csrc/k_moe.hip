@@ -565,6 +565,9 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
 // next, routed-row chunk fastest, so workgroups that share weight rows run side by side.
 // For the SiLU-gate form the 32 rows of group g are gate rows 16g..16g+15 and up rows
 // I + 16g..I + 16g + 15; D row n of lane m holds gate row n and up row n + 16 at i and i + 8.
+#ifndef SSN_SW_WPE
+#define SSN_SW_WPE 2
+#endif
 constexpr int kSwRows = 32, kSwM = 32;
 #ifndef SSN_SW_RING
 #define SSN_SW_RING 4
@@ -579,8 +582,8 @@ struct SwChunk {
   u32x4 x[4];     // activation pieces (dense: k = 32h + 8s; 2:4: 16t + 8h and 32 + 16t + 8h)
 };
 
-template <int WF, int EPI, int KS>
-__global__ __launch_bounds__(KS * 64) void k_moe_stream(
+template <int WF, int EPI, int KS, int NCH>
+__global__ __launch_bounds__(KS * 64) __attribute__((amdgpu_waves_per_eu(SSN_SW_WPE))) void k_moe_stream(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -617,7 +620,9 @@ __global__ __launch_bounds__(KS * 64) void k_moe_stream(
   __syncthreads();
   const int total = pre[E];
   const int n = lane & 31, h = lane >> 5;
-  const int nch = K / 64;
+  // NCH > 0: K / 64 known at compile time, so the chunk loop unrolls completely (no ring
+  // registers carried around a loop back-edge, whose moves would wait for the loads in flight)
+  const int nch = NCH > 0 ? NCH : K / 64;
   const int c_lo = nch * wave / KS, c_hi = nch * (wave + 1) / KS;   // this wave's chunks
   const size_t rowA = WF == kDense ? K / 2 : K / 4;        // main bytes per weight row
   for (int it = blockIdx.x; it < total; it += gridDim.x) {
@@ -682,11 +687,15 @@ __global__ __launch_bounds__(KS * 64) void k_moe_stream(
       SwChunk<WF> ring[kSwRing];
 #pragma unroll
       for (int u = 0; u < kSwRing; ++u) ring[u] = load(c_lo + u);
+#pragma unroll
       for (int c = c_lo; c < c_hi; c += kSwRing) {
 #pragma unroll
         for (int u = 0; u < kSwRing; ++u) {
           const SwChunk<WF> cur = ring[u];
           ring[u] = load(c + u + kSwRing);
+          // the refill goes out here, a ring length ahead of its use: without this fence the
+          // scheduler sinks it next to the arithmetic and the wait for it drains the ring
+          __builtin_amdgcn_sched_barrier(0);
           const float f0 = e4m3_f32_sel<0>(cur.sc), f1 = e4m3_f32_sel<1>(cur.sc);
           if constexpr (WF == kDense) {
 #pragma unroll
@@ -829,8 +838,8 @@ hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
   return launch_moe_gemm_t<WF, EPI, 64>(a, s);
 }
 
-template <int WF, int EPI>
-hipError_t launch_moe_stream_t(const MoeGemmArgs& a, hipStream_t s) {
+template <int WF, int EPI, int NCH>
+hipError_t launch_moe_stream_n(const MoeGemmArgs& a, hipStream_t s) {
   const int G = (int)(a.N / kSwRows);
   // items <= G * (touched experts + R / 32) <= G * (min(E, R) + R / 32); extra workgroups exit
   // after the item scan, and a workgroup loops over items when the grid is capped
@@ -842,16 +851,25 @@ hipError_t launch_moe_stream_t(const MoeGemmArgs& a, hipStream_t s) {
   // Few items and a long K: split K over four waves per item so that enough loads are in flight
   if ((long)G * touched < 2048 && a.K / 64 >= 16) {
     const size_t lds = 2 * stride * sizeof(int) + 3 * 16 * 64 * sizeof(float);
-    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 4>), dim3(grid), dim3(4 * 64), lds, s, a.X, (int)a.x_rows, (int)a.K,
-                       a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16,
-                       a.ktiled);
+    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 4, NCH>), dim3(grid), dim3(4 * 64), lds, s, a.X, (int)a.x_rows,
+                       (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1, a.scales, a.ts, a.Y,
+                       a.y_bf16, a.ktiled);
   } else {
     const size_t lds = 2 * stride * sizeof(int);
-    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 1>), dim3(grid), dim3(64), lds, s, a.X, (int)a.x_rows, (int)a.K,
+    hipLaunchKernelGGL((k_moe_stream<WF, EPI, 1, NCH>), dim3(grid), dim3(64), lds, s, a.X, (int)a.x_rows, (int)a.K,
                        a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16,
                        a.ktiled);
   }
   return hipGetLastError();
+}
+
+// the expert shapes of the grouped FFN (D = 2048 and I = 512: 32 and 8 chunks) get a fully
+// unrolled chunk loop; other K run the generic loop
+template <int WF, int EPI>
+hipError_t launch_moe_stream_t(const MoeGemmArgs& a, hipStream_t s) {
+  if (a.K == 2048) return launch_moe_stream_n<WF, EPI, 32>(a, s);
+  if (a.K == 512) return launch_moe_stream_n<WF, EPI, 8>(a, s);
+  return launch_moe_stream_n<WF, EPI, 0>(a, s);
 }
 
 }  // namespace
