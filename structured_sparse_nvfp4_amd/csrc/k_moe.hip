@@ -111,8 +111,9 @@ __global__ __launch_bounds__(1024) void k_route_scan(const int32_t* __restrict__
 }
 
 // Stable placement of the 256 entries [f0, f0 + 256): inside a wave the rank among equal ids
-// comes from ballots, across the four waves from per-wave counts wc[4][E] (zero on entry and on
-// return); cur[e] (next output row of expert e) advances past the round's rows.
+// comes from ballots over the id bits, across the four waves from per-wave counts wc[4][E]
+// (zero on entry and on return); cur[e] (next output row of expert e) advances past the
+// round's rows.
 __device__ __forceinline__ void route_place_round(const int32_t* __restrict__ ids, int F, int k, int E, int f0,
                                                   int32_t* cur, int32_t* wc, int32_t* __restrict__ row_token,
                                                   int32_t* __restrict__ row_slot, int32_t* __restrict__ row_of) {
@@ -120,18 +121,17 @@ __device__ __forceinline__ void route_place_round(const int32_t* __restrict__ id
   const int f = f0 + threadIdx.x;
   const int e = f < F ? ids[f] : -1;
   const bool valid = f < F && e >= 0 && e < E;
-  unsigned long long active = __ballot(valid);
-  int rank = 0, cnt = 0;
-  while (active) {
-    const int leader = __ffsll((long long)active) - 1;
-    const int el = __shfl(e, leader, 64);
-    const unsigned long long m = __ballot(valid && e == el);
-    if (valid && e == el) {
-      rank = __popcll(m & ((1ull << lane) - 1ull));
-      cnt = __popcll(m);
-    }
-    active &= ~m;
+  // lanes of this wave holding the same expert id: one ballot per id bit, each lane keeping
+  // the lanes that agree with it on that bit (no exchange of values between lanes)
+  const int bits = E > 1 ? 32 - __clz(E - 1) : 0;
+  unsigned long long same = __ballot(valid);
+  for (int b = 0; b < bits; ++b) {
+    const bool on = (e >> b) & 1;
+    const unsigned long long s = __ballot(valid && on);
+    same &= on ? s : ~s;
   }
+  const int rank = __popcll(same & ((1ull << lane) - 1ull));
+  const int cnt = __popcll(same);
   if (valid && rank == 0) wc[wave * E + e] = cnt;
   __syncthreads();
   if (valid) {
@@ -774,39 +774,77 @@ __global__ __launch_bounds__(256) void k_pack_ktiles(const uint32_t* __restrict_
 }
 
 // ------------------------------------------------------------------------------ combine
-// out[t, :] = sum_j w[t, j] * Yd[row_of[t, j], :]; one block per token, j in slot order.
+// out[t, :] = sum_j w[t, j] * Yd[row_of[t, j], :], j in slot order. Work item (t, c) covers the
+// 1024 columns [1024 c, 1024 c + 1024) of token t, four per thread; blocks stride over the
+// T * ceil(D / 1024) items. The slots are taken eight at a time: their rows and weights first,
+// then the eight row loads together, then the adds in slot order, so a token's k rows are
+// fetched in k / 8 round trips rather than k.
+constexpr int kCombineCols = 1024, kCombineBatch = 8;
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 combine_load(const void* Yd, int r, int D, int d0, bool full) {
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  if (BF16) {
+    const uint16_t* y = (const uint16_t*)Yd + (size_t)r * D + d0;
+    if (full) {
+      const uint2 p = *(const uint2*)y;
+      v[0] = __uint_as_float(p.x << 16); v[1] = __uint_as_float(p.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(p.y << 16); v[3] = __uint_as_float(p.y & 0xFFFF0000u);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (d0 + i < D) v[i] = __uint_as_float((uint32_t)y[i] << 16);
+    }
+  } else {
+    const float* y = (const float*)Yd + (size_t)r * D + d0;
+    if (full) v = *(const f32x4*)y;
+    else
+      for (int i = 0; i < 4; ++i)
+        if (d0 + i < D) v[i] = y[i];
+  }
+  return v;
+}
+
+template <bool BF16>
+__device__ __forceinline__ void combine_cols(const void* __restrict__ Yd, int R, const int32_t* __restrict__ row_of,
+                                             const float* __restrict__ w, int k, int D, float* __restrict__ out,
+                                             int64_t t, int d0) {
+  const bool full = d0 + 3 < D && (D & 3) == 0;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+    int r[kCombineBatch];
+    float wt[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u) {
+      const int jj = j0 + u;
+      r[u] = jj < k ? row_of[(size_t)t * k + jj] : -1;
+      wt[u] = jj < k ? w[(size_t)t * k + jj] : 0.f;
+      if (r[u] >= R) r[u] = -1;
+    }
+    f32x4 v[kCombineBatch];
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      v[u] = r[u] >= 0 ? combine_load<BF16>(Yd, r[u], D, d0, full) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kCombineBatch; ++u)
+      if (r[u] >= 0)
+        for (int i = 0; i < 4; ++i) acc[i] += wt[u] * v[u][i];
+  }
+  if (full) *(f32x4*)(out + (size_t)t * D + d0) = acc;
+  else
+    for (int i = 0; i < 4; ++i)
+      if (d0 + i < D) out[(size_t)t * D + d0 + i] = acc[i];
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd, int R,
                                                      const int32_t* __restrict__ row_of,
                                                      const float* __restrict__ w, int k, int D,
-                                                     float* __restrict__ out) {
-  const int t = blockIdx.x;
-  for (int d0 = 4 * threadIdx.x; d0 < D; d0 += 4 * 256) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bool full = d0 + 3 < D && (D & 3) == 0;
-    for (int jj = 0; jj < k; ++jj) {
-      const int r = row_of[(size_t)t * k + jj];
-      if (r < 0 || r >= R) continue;
-      const float wt = w[(size_t)t * k + jj];
-      if (BF16) {
-        const uint16_t* y = (const uint16_t*)Yd + (size_t)r * D;
-        for (int i = 0; i < 4; ++i)
-          if (d0 + i < D) acc[i] += wt * __uint_as_float((uint32_t)y[d0 + i] << 16);
-      } else {
-        const float* y = (const float*)Yd + (size_t)r * D;
-        if (full) {
-          const f32x4 v = *(const f32x4*)(y + d0);
-          for (int i = 0; i < 4; ++i) acc[i] += wt * v[i];
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (d0 + i < D) acc[i] += wt * y[d0 + i];
-        }
-      }
-    }
-    if (full) *(f32x4*)(out + (size_t)t * D + d0) = acc;
-    else
-      for (int i = 0; i < 4; ++i)
-        if (d0 + i < D) out[(size_t)t * D + d0 + i] = acc[i];
+                                                     float* __restrict__ out, int64_t T) {
+  const int64_t chunks = (D + kCombineCols - 1) / kCombineCols;
+  for (int64_t item = blockIdx.x; item < T * chunks; item += gridDim.x) {
+    const int64_t t = item / chunks;
+    const int d0 = (int)(item - t * chunks) * kCombineCols + 4 * threadIdx.x;
+    if (d0 < D) combine_cols<BF16>(Yd, R, row_of, w, k, D, out, t, d0);
   }
 }
 
@@ -926,10 +964,12 @@ hipError_t launch_moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int6
 
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,
                               int64_t T, int k, int64_t D, float* out, hipStream_t s) {
+  const int64_t items = T * ((D + kCombineCols - 1) / kCombineCols);
+  const dim3 grid((unsigned)std::min<int64_t>(items, 1 << 20));
   if (yd_bf16)
-    hipLaunchKernelGGL(k_moe_combine<true>, dim3((unsigned)T), dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out);
+    hipLaunchKernelGGL(k_moe_combine<true>, grid, dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out, T);
   else
-    hipLaunchKernelGGL(k_moe_combine<false>, dim3((unsigned)T), dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out);
+    hipLaunchKernelGGL(k_moe_combine<false>, grid, dim3(256), 0, s, Yd, (int)R, row_of, w, k, (int)D, out, T);
   return hipGetLastError();
 }
 

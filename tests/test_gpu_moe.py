@@ -44,7 +44,8 @@ def _check_route(ids, E):
     assert F == ids.shape[0] * ids.shape[1]
 
 
-@pytest.mark.parametrize("T,E,k", [(50, 7, 3), (300, 64, 10), (1, 5, 2), (2000, 512, 10), (4096, 512, 10)])
+@pytest.mark.parametrize("T,E,k", [(50, 7, 3), (300, 64, 10), (1, 5, 2), (2000, 512, 10), (4096, 512, 10),
+                                   (256, 1, 4), (102, 2048, 10), (103, 2048, 10), (32, 512, 10)])
 def test_route_matches_oracle(T, E, k):
     if k <= E and T > 1:
         ids, _ = synth.routing(T, E, k, 1.1, seed=T + E)
@@ -53,9 +54,10 @@ def test_route_matches_oracle(T, E, k):
     _check_route(ids, E)
 
 
-def test_route_repeated_ids_and_invalid_ids():
+@pytest.mark.parametrize("T", [700, 60])   # the multi-kernel routing (F > 1024) and the one-block one
+def test_route_repeated_ids_and_invalid_ids(T):
     rng = np.random.default_rng(5)
-    ids = rng.integers(-2, 9, size=(700, 4)).astype(np.int32)   # repeats, and ids outside [0, 7)
+    ids = rng.integers(-2, 9, size=(T, 4)).astype(np.int32)   # repeats, and ids outside [0, 7)
     _check_route(ids, 7)
 
 
@@ -221,6 +223,35 @@ def test_combine_weighted_sum():
     want = np.einsum("tj,tjd->td", w.astype(np.float64), Yd.astype(np.float64)[rows])
     got = host(out).astype(np.float64)
     assert np.all(np.abs(got - want) <= 1e-6 * np.einsum("tj,tjd->td", np.abs(w), np.abs(Yd)[rows]) + 1e-30)
+
+
+@pytest.mark.parametrize("T,k,D,bf16", [(3, 10, 2500, False), (5, 17, 2049, False), (2, 10, 2050, True),
+                                        (1, 64, 1024, True), (70, 3, 6, False)])
+def test_combine_slots_columns_and_skipped_rows(T, k, D, bf16):
+    """Slot counts across the eight-slot batches, column counts across 1024-column items with
+    ragged and non-multiple-of-4 tails, bf16 rows, and rows outside [0, R) skipped. Against
+    the fp64 sum: an f32 sum of k products (fused or not) is within (k + 1) * 2^-24 of the sum
+    of their magnitudes."""
+    rng = np.random.default_rng(T * 1000 + k)
+    R = T * k
+    Yd = rng.standard_normal((R, D)).astype(np.float32)
+    if bf16:   # values exactly representable in bf16
+        Yd = (Yd.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    rows = rng.permutation(R).astype(np.int32)
+    rows[rng.random(R) < 0.2] = -1
+    rows[rng.random(R) < 0.05] = R + 3
+    yd = dev(Yd).to(torch.bfloat16) if bf16 else dev(Yd)
+    out = host(ssn.moe_combine(yd, dev(rows), dev(w)))
+    want = np.zeros((T, D))
+    mag = np.zeros((T, D))
+    r2 = rows.reshape(T, k)
+    for t in range(T):
+        for j in range(k):
+            if 0 <= r2[t, j] < R:
+                want[t] += float(w[t, j]) * Yd[r2[t, j]].astype(np.float64)
+                mag[t] += abs(float(w[t, j])) * np.abs(Yd[r2[t, j]]).astype(np.float64)
+    assert np.all(np.abs(out.astype(np.float64) - want) <= (k + 1) * 2.0 ** -24 * mag)
 
 
 # ------------------------------------------------------------------------------ whole FFN
