@@ -6,14 +6,16 @@ Prints ONE JSON line. ``value`` / ``ms_per_step`` / ``roofline`` / ``cpu_baselin
 decode workload, where a step is one pass of the whole hot path over one batch of synthetic
 input (X [M, 5120] bf16 for M in {1, 4, 8}; W [13824, 5120] float32 ~ N(0, 0.02)):
 
-    nvfp4_quantize(W)                        dense NVFP4 weights
-    sp24_prune(W) -> nvfp4_quantize          2:4-pruned NVFP4 weights
+    sp24_prune(W) -> W_pruned, s_t           2:4 prune; s_t = fl32(amax|W| / 2688) taken on the way
+    nvfp4_quantize(W, s_t)                   dense NVFP4 weights
+    nvfp4_quantize(W_pruned, s_t)            2:4-pruned NVFP4 weights (same s_t: pruning keeps
+                                             every group's largest |w|)
     sp24_check, sp24_compress                2:4 eligibility and compression
     gemm_nvfp4_dense  at M = 1, 4, 8         decode GEMVs on dense weights
     gemm_nvfp4_sp24   at M = 1, 4, 8         decode GEMVs on compressed weights
 
 Inputs are resident in HBM before timing starts. The K timed steps run call by call: all K
-quantisations, then all K prunes, and so on (every step has its own ring slot of outputs, so
+prunes, then all K quantisations, and so on (every step has its own ring slot of outputs, so
 the work is the same as K steps in order); HIP events on the launch stream bracket each batch,
 which gives every kernel's average duration over back-to-back launches. The GEMVs read weight
 copies written many calls earlier (a ring larger than the 256 MB Infinity Cache), so they read
@@ -66,7 +68,7 @@ def bytes_quantize(N, K, w_bytes=4):
 
 
 def bytes_prune(N, K, w_bytes=4):
-    return 2 * N * K * w_bytes
+    return 2 * N * K * w_bytes + 4          # W read, W_pruned written, s_t written
 
 
 def bytes_check(N, K):
@@ -170,10 +172,11 @@ def run_decode(args, torch, ssn, synth):
                    ts=torch.empty(1, dtype=torch.float32, device=dev), vals=torch.empty((N, K // 4), **u8),
                    meta=torch.empty((N, K // 8), **u8), bad=torch.empty(1, dtype=torch.int64, device=dev),
                    first=torch.empty(1, dtype=torch.int64, device=dev)) for _ in range(RING)]
+    ts_w = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(RING)]   # s_t from the prune
     Yd = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
     Ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
     Xm = {M: X[:M].contiguous() for M in Ms}
-    names = ["quantize", "prune", "quantize_pruned", "check", "compress"] + \
+    names = ["prune", "quantize", "quantize_pruned", "check", "compress"] + \
             [f"gemv_dense_M{M}" for M in Ms] + [f"gemv_sp24_M{M}" for M in Ms]
     extra = ["producer_fused"]           # timed beside the step, not part of it
     prod = [dict(vals=torch.empty((N, K // 4), **u8), meta=torch.empty((N, K // 8), **u8),
@@ -184,11 +187,12 @@ def run_decode(args, torch, ssn, synth):
     for j in range(RING):
         d, sp, wp = dense[j], sparse[j], wps[j % 2]
         rd, rs = dense[(j + RING // 2) % RING], sparse[(j + RING // 2) % RING]
-        calls["quantize"].append(ssn.nvfp4_quantize(W, codes=d["codes"], scales=d["scales"], tensor_scale_out=d["ts"],
-                                                    prepare=True)[0])
-        calls["prune"].append(ssn.sp24_prune(W, out=wp, prepare=True)[0])
-        calls["quantize_pruned"].append(ssn.nvfp4_quantize(wp, codes=sp["codes"], scales=sp["scales"],
-                                                           tensor_scale_out=sp["ts"], prepare=True)[0])
+        calls["prune"].append(ssn.sp24_prune(W, out=wp, tensor_scale_out=ts_w[j], prepare=True)[0])
+        calls["quantize"].append(ssn.nvfp4_quantize(W, tensor_scale_in=ts_w[j], codes=d["codes"], scales=d["scales"],
+                                                    tensor_scale_out=d["ts"], prepare=True)[0])
+        calls["quantize_pruned"].append(ssn.nvfp4_quantize(wp, tensor_scale_in=ts_w[j], codes=sp["codes"],
+                                                           scales=sp["scales"], tensor_scale_out=sp["ts"],
+                                                           prepare=True)[0])
         calls["check"].append(ssn.sp24_check(sp["codes"], bad_groups=sp["bad"], first_bad=sp["first"],
                                              prepare=True)[0])
         calls["compress"].append(ssn.sp24_compress(sp["codes"], vals=sp["vals"], meta=sp["meta"],

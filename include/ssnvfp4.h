@@ -121,9 +121,15 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
  * sp24_prune — magnitude pruning to 2:4 along K: in every group of four keep the two entries
  * of largest |w| (equal magnitudes: the lower index wins) and write +0.0 to the other two.
  * This produces weights that pass sp24_check after quantisation. W, W_out: f32 or bf16
- * [N, K] (same dtype; W_out may equal W for in place). Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
+ * [N, K] (same dtype; W_out may equal W for in place). tensor_scale_out: f32 [1] or NULL;
+ * when given it receives s_t = fl32(amax|W| / 2688), the NVFP4 tensor scale of nvfp4_quantize
+ * ("NVFP4 Without FP4 Hardware", ai-muninn.com, section "The shared global scale"), taken
+ * while W is read. The largest entry of every group is kept, so this is the tensor scale of
+ * W and of the pruned tensor alike, bit for bit: passed to nvfp4_quantize as tensor_scale_in
+ * it spares that call its own pass over the weights. Errors: NULL, SHAPE, ALIGN, DTYPE, HIP.
  * ------------------------------------------------------------------------------------------- */
-int sp24_prune(const void* W, int w_dtype, int64_t N, int64_t K, void* W_out, void* stream);
+int sp24_prune(const void* W, int w_dtype, int64_t N, int64_t K, void* W_out, float* tensor_scale_out,
+               void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * sp24_check — per-group 2:4 eligibility of NVFP4 codes ("Sparse GPU FLOPS Need the Right Zeros

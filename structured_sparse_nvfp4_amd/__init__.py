@@ -30,7 +30,7 @@ _SIGS = {
     "nvfp4_quantize": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp], _int),
     "nvfp4_dequantize": ([_vp, _vp, _vp, _i64, _i64, _vp, _int, _vp], _int),
     "nvfp4_sp24_produce": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _int),
-    "sp24_prune": ([_vp, _int, _i64, _i64, _vp, _vp], _int),
+    "sp24_prune": ([_vp, _int, _i64, _i64, _vp, _vp, _vp], _int),
     "sp24_check": ([_vp, _i64, _i64, _vp, _vp, _vp], _int),
     "sp24_compress": ([_vp, _i64, _i64, _vp, _vp, _vp, _vp], _int),
     "sp24_decompress": ([_vp, _vp, _i64, _i64, _vp, _vp], _int),
@@ -192,14 +192,17 @@ def nvfp4_sp24_produce(W, tensor_scale_in=None, vals=None, meta=None, scales=Non
     return _run("nvfp4_sp24_produce", cargs, prepare, (W, tensor_scale_in), (vals, meta, scales, ts, bad, codes))
 
 
-def sp24_prune(W, out=None, prepare=False):
-    """2:4 magnitude prune along K (keep the two largest |w| of every group of four)."""
+def sp24_prune(W, out=None, tensor_scale_out=None, prepare=False):
+    """2:4 magnitude prune along K (keep the two largest |w| of every group of four). With
+    tensor_scale_out (f32 [1]) it also receives s_t of W, which is s_t of the pruned tensor too."""
     N, K = W.shape
     _need(W, W.dtype, "W")
     out = out if out is not None else torch.empty_like(W)
     _need(out, W.dtype, "out", (N, K))
-    cargs = (_ptr(W), _wdt(W), N, K, _ptr(out), _stream(W.device))
-    return _run("sp24_prune", cargs, prepare, (W,), out)
+    if tensor_scale_out is not None:
+        _need(tensor_scale_out, torch.float32, "tensor_scale_out", (1,))
+    cargs = (_ptr(W), _wdt(W), N, K, _ptr(out), _ptr(tensor_scale_out), _stream(W.device))
+    return _run("sp24_prune", cargs, prepare, (W, tensor_scale_out), out)
 
 
 def sp24_check(codes, bad_groups=None, first_bad=None, prepare=False):

@@ -117,14 +117,20 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* t
                                            as_stream(stream)), fn);
 }
 
-int sp24_prune(const void* W, int w_dtype, int64_t N, int64_t K, void* W_out, void* stream) {
+int sp24_prune(const void* W, int w_dtype, int64_t N, int64_t K, void* W_out, float* tensor_scale_out,
+               void* stream) {
   const char* fn = "sp24_prune";
   int st;
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, w_dtype, "w_dtype"))) return st;
-  if (N == 0 || K == 0) return ok();
+  REQUIRE_OPT_ELEM_PTR(tensor_scale_out);
+  if (N == 0 || K == 0) {   // an empty tensor has no maximum: s_t = 0
+    if (tensor_scale_out) return hip_status(ssn::launch_prune(nullptr, 0, 0, 0, nullptr, tensor_scale_out,
+                                                              as_stream(stream)), fn);
+    return ok();
+  }
   REQUIRE_PTR(W); REQUIRE_PTR(W_out);
-  return hip_status(ssn::launch_prune(W, w_dtype == SSN_BF16, N, K, W_out, as_stream(stream)), fn);
+  return hip_status(ssn::launch_prune(W, w_dtype == SSN_BF16, N, K, W_out, tensor_scale_out, as_stream(stream)), fn);
 }
 
 int sp24_check(const uint8_t* codes, int64_t N, int64_t K, int64_t* bad_groups, int64_t* first_bad,

@@ -12,7 +12,8 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
                            uint8_t* codes, uint8_t* scales, float* ts_out, hipStream_t s);
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t N,
                              int64_t K, void* out, int out_bf16, hipStream_t s);
-hipError_t launch_prune(const void* W, int w_bf16, int64_t N, int64_t K, void* out, hipStream_t s);
+// ts_out nullable: when given, receives s_t = fl32(amax|W| / 2688) gathered during the prune
+hipError_t launch_prune(const void* W, int w_bf16, int64_t N, int64_t K, void* out, float* ts_out, hipStream_t s);
 // prune -> quantise -> compress in one pass; codes (the pruned tensor's codes) nullable; bad device
 hipError_t launch_produce24(const void* W, int w_bf16, int64_t N, int64_t K, const float* ts_in, uint8_t* vals,
                             uint8_t* meta, uint8_t* scales, float* ts_out, uint8_t* codes, int64_t* bad,

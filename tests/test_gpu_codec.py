@@ -93,6 +93,35 @@ def test_prune_bit_exact(N, K, dtype):
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("N,K", SHAPES + [(0, 64), (3000, 4096)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prune_tensor_scale(N, K, dtype):
+    """The tensor scale sp24_prune gathers while it reads W is the oracle's s_t of W and of the
+    pruned tensor alike, bit for bit (3000 x 4096 needs more groups than the prune's blocks
+    take in one stride; its largest entry sits in the last group). nvfp4_quantize given that
+    scale writes the oracle's codes."""
+    w = _w(N, K, seed=21)
+    if N * K:
+        w[-1, -1] = 7.5
+    if dtype == "bf16":
+        wb = synth.f32_to_bf16_bits(w)
+        w = synth.bf16_bits_to_f32(wb)
+        W = dev(wb.view(np.int16)).view(torch.bfloat16)
+    else:
+        W = dev(w)
+    ts = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    Wp = ssn.sp24_prune(W, tensor_scale_out=ts)
+    st = quant.tensor_scale(w)
+    assert host(ts).view(np.uint32)[0] == np.float32(st).view(np.uint32)
+    assert np.float32(quant.tensor_scale(sp24.prune24(w))).view(np.uint32) == np.float32(st).view(np.uint32)
+    if N * K and N * K <= 256 * 512:
+        for src, ref in ((W, w), (Wp, sp24.prune24(w))):
+            codes, scales, ts2 = ssn.nvfp4_quantize(src, tensor_scale_in=ts)
+            rc, rs, _ = quant.quantize(ref, tensor_scale_in=st)
+            assert np.array_equal(host(codes), rc) and np.array_equal(host(scales), rs)
+            assert host(ts2).view(np.uint32)[0] == np.float32(st).view(np.uint32)
+
+
 def _codes_with_failures(N, K, seed, p_fail=0.01):
     """Oracle codes of a pruned tensor with a few groups broken (extra nonzero codes)."""
     c, _, _ = quant.quantize(sp24.prune24(_w(N, K, seed)))
