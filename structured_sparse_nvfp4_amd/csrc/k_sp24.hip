@@ -69,6 +69,9 @@ __global__ __launch_bounds__(kThreads) void k_check(const u32x4* codes, size_t n
 
 __global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_t n16, u32x2* vals,
                                                        uint32_t* meta, int64_t* bad) {
+  static_assert(kUnroll * 8 <= 32, "the entry sum counts the failures of at most 32 groups");
+  __shared__ uint32_t lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = compress_entry(threadIdx.x);
   const size_t base = (size_t)blockIdx.x * kThreads * kUnroll + threadIdx.x;
   u32x4 w[kUnroll];
 #pragma unroll
@@ -76,23 +79,25 @@ __global__ __launch_bounds__(kThreads) void k_compress(const u32x4* codes, size_
     const size_t i = base + (size_t)u * kThreads;
     w[u] = ld_nt(codes + (i < n16 ? i : 0));
   }
-  uint32_t nbad = 0;
+  __syncthreads();
+  uint32_t acc = 0;
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const size_t i = base + (size_t)u * kThreads;
     if (i >= n16) continue;
     uint32_t v[2] = {0u, 0u}, m = 0u;
-    for (int d = 0; d < 4; ++d) {
-      const uint32_t r0 = compress_group(w[u][d] & 0xFFFFu), r1 = compress_group(w[u][d] >> 16);
-      nbad += (r0 >> 12) + (r1 >> 12);
-      const int g = 2 * d;                   // group index within the 8
-      v[g >> 2] |= ((r0 & 0xFFu) << (8 * (g & 3))) | ((r1 & 0xFFu) << (8 * ((g + 1) & 3)));
-      m |= (((r0 >> 8) & 0xFu) << (4 * g)) | (((r1 >> 8) & 0xFu) << (4 * (g + 1)));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {              // word d holds groups 2d and 2d + 1
+      uint32_t v16, m8;
+      compress_word(w[u][d], lut, v16, m8, acc);
+      v[d >> 1] |= v16 << (16 * (d & 1));
+      m |= m8 << (8 * d);
     }
     u32x2 vo; vo[0] = v[0]; vo[1] = v[1];
     vals[i] = vo;
     meta[i] = m;
   }
+  uint32_t nbad = acc >> kFailShift;
   uint64_t unused = 0;
   block_reduce(nbad, unused);
   if (threadIdx.x == 0 && nbad) atomicAdd((unsigned long long*)bad, (unsigned long long)nbad);
