@@ -201,7 +201,7 @@ __device__ __forceinline__ int q_swz(int b) {
 
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nblocks, const float* ts,
-                                                       uint8_t* codes, uint8_t* scales) {
+                                                       uint8_t* codes, uint8_t* scales, float* ts_copy) {
   constexpr int P = BF16 ? 2 : 4;              // 16-byte pieces per block
   __shared__ u32x4 tr[kThreads / 64][kQBlocks * P];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nbl
   const size_t nchunks = (nblocks + kQBlocks - 1) / kQBlocks;
   const size_t c0 = ((size_t)blockIdx.x * (kThreads / 64) + wave) * kQIter;
   const double st = (double)*ts;
+  if (ts_copy && blockIdx.x == 0 && threadIdx.x == 0) *ts_copy = (float)st;   // the caller's s_t, passed on
   for (int it = 0; it < kQIter; ++it) {
     if (c0 + it >= nchunks) break;                               // uniform per wave
     const size_t b0 = (nchunks - 1 - (c0 + it)) * kQBlocks;      // first block of the chunk
@@ -266,14 +267,18 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* W, size_t nbl
 template <int BF16>
 __global__ __launch_bounds__(kThreads) void k_produce24(const void* W, size_t nblocks, const float* ts,
                                                         uint8_t* vals, uint8_t* meta, uint8_t* scales,
-                                                        uint8_t* codes, int64_t* bad) {
+                                                        uint8_t* codes, int64_t* bad, float* ts_copy) {
   constexpr int P = BF16 ? 2 : 4;              // 16-byte pieces per block
   __shared__ u32x4 tr[kThreads / 64][kQBlocks * P];
+  __shared__ uint32_t lut[16];                 // the 2:4 compression table
+  if (threadIdx.x < 16) lut[threadIdx.x] = compress_entry(threadIdx.x);
+  __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   u32x4* t = tr[wave];
   const size_t nchunks = (nblocks + kQBlocks - 1) / kQBlocks;
   const size_t c0 = ((size_t)blockIdx.x * (kThreads / 64) + wave) * kQIter;
   const double st = (double)*ts;
+  if (ts_copy && blockIdx.x == 0 && threadIdx.x == 0) *ts_copy = (float)st;   // the caller's s_t, passed on
   uint32_t nbad = 0;
   for (int it = 0; it < kQIter; ++it) {
     if (c0 + it >= nchunks) break;                               // uniform per wave
@@ -324,14 +329,11 @@ __global__ __launch_bounds__(kThreads) void k_produce24(const void* W, size_t nb
       uint32_t S;
       quantize_block(w, st, code, S);
       const size_t b = b0 + lane;
-      uint32_t vw = 0, mw = 0;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint32_t r = compress_group((code[g >> 1] >> (16 * (g & 1))) & 0xFFFFu);
-        nbad += r >> 12;
-        vw |= (r & 0xFFu) << (8 * g);
-        mw |= ((r >> 8) & 0xFu) << (4 * g);
-      }
+      uint32_t v0, v1, m0, m1, acc = 0;
+      compress_word(code[0], lut, v0, m0, acc);
+      compress_word(code[1], lut, v1, m1, acc);
+      nbad += acc >> kFailShift;
+      const uint32_t vw = v0 | (v1 << 16), mw = m0 | (m1 << 8);
       *(uint32_t*)(vals + b * 4) = vw;
       *(uint16_t*)(meta + b * 2) = (uint16_t)mw;
       scales[b] = (uint8_t)S;
@@ -487,15 +489,20 @@ hipError_t launch_quantize(const void* W, int w_bf16, int64_t N, int64_t K, cons
     nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece * kAmaxIters - 1) / (kAmaxPiece * kAmaxIters));
     hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
   }
-  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
   const size_t nb = n / 16;
+  // with the caller's s_t and blocks to quantise, the quantisation kernel passes s_t on itself
+  const bool pass_on = ts_in && nb;
+  if (!pass_on)
+    hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
+  const float* st = pass_on ? ts_in : ts_out;
+  float* copy = pass_on ? ts_out : nullptr;
   if (nb) {
     const size_t waves = ((nb + kQBlocks - 1) / kQBlocks + kQIter - 1) / kQIter;
     const dim3 grid(grid_for(waves, kThreads / 64));
     if (w_bf16)
-      hipLaunchKernelGGL(k_quantize<1>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
+      hipLaunchKernelGGL(k_quantize<1>, grid, dim3(kThreads), 0, s, W, nb, st, codes, scales, copy);
     else
-      hipLaunchKernelGGL(k_quantize<0>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, codes, scales);
+      hipLaunchKernelGGL(k_quantize<0>, grid, dim3(kThreads), 0, s, W, nb, st, codes, scales, copy);
   }
   return hipGetLastError();
 }
@@ -512,18 +519,20 @@ hipError_t launch_produce24(const void* W, int w_bf16, int64_t N, int64_t K, con
     nparts = (unsigned)std::max<size_t>(1, (n16 + kAmaxPiece * kAmaxIters - 1) / (kAmaxPiece * kAmaxIters));
     hipLaunchKernelGGL(k_amax, dim3(nparts), dim3(kThreads), 0, s, W, w_bf16, n, part);
   }
-  hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
-  hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, s, bad);
   const size_t nb = n / 16;
+  const bool pass_on = ts_in && nb;              // as in launch_quantize
+  if (!pass_on)
+    hipLaunchKernelGGL(k_finalize_scale, dim3(1), dim3(kFinThreads), 0, s, (const float*)part, nparts, ts_in, ts_out);
+  hipLaunchKernelGGL(k_zero_i64, dim3(1), dim3(1), 0, s, bad);
+  const float* st = pass_on ? ts_in : ts_out;
+  float* copy = pass_on ? ts_out : nullptr;
   if (nb) {
     const size_t waves = ((nb + kQBlocks - 1) / kQBlocks + kQIter - 1) / kQIter;
     const dim3 grid(grid_for(waves, kThreads / 64));
     if (w_bf16)
-      hipLaunchKernelGGL(k_produce24<1>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, vals, meta, scales,
-                         codes, bad);
+      hipLaunchKernelGGL(k_produce24<1>, grid, dim3(kThreads), 0, s, W, nb, st, vals, meta, scales, codes, bad, copy);
     else
-      hipLaunchKernelGGL(k_produce24<0>, grid, dim3(kThreads), 0, s, W, nb, (const float*)ts_out, vals, meta, scales,
-                         codes, bad);
+      hipLaunchKernelGGL(k_produce24<0>, grid, dim3(kThreads), 0, s, W, nb, st, vals, meta, scales, codes, bad, copy);
   }
   return hipGetLastError();
 }

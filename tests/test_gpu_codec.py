@@ -47,6 +47,11 @@ def test_quantize_ties_and_shared_scale():
     gc, gs, gt = ssn.nvfp4_quantize(dev(w), tensor_scale_in=dev(np.array([st], np.float32)))
     assert host(gt)[0] == st
     assert np.array_equal(host(gs), s) and np.array_equal(host(gc), c)
+    # the output scale may be the input scale itself
+    t = dev(np.array([st], np.float32))
+    gc, gs, gt = ssn.nvfp4_quantize(dev(w), tensor_scale_in=t, tensor_scale_out=t)
+    assert host(t)[0] == st
+    assert np.array_equal(host(gs), s) and np.array_equal(host(gc), c)
 
 
 def test_quantize_zero_and_subnormal_scales():
