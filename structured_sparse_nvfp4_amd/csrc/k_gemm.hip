@@ -260,18 +260,22 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   u32x4 abuf[2][MB];    // activation operands, double-buffered across MFMA steps
   bf16x8 bcur[NB];      // decoded weight operands of the current step
 
+  // the scale word is kept as loaded (all four 16-blocks of the stage) and this lane's pair is
+  // picked in the decode: a shift here would make the wave wait for the LDS read before the
+  // MFMAs that follow a stage boundary
   auto load_w_regs = [&](const char* slot, u32x4 (&c)[NB], uint32_t (&sc)[NB]) {
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt) {
       const int r = bn0 + 32 * nt + r32;
       c[nt] = lds_w<WF, TM>(slot, r, h);
-      sc[nt] = *(const uint32_t*)(slot + L::kSc + r * 4) >> (16 * h);   // 16-blocks 2h, 2h + 1
+      sc[nt] = *(const uint32_t*)(slot + L::kSc + r * 4);
     }
   };
   auto decode = [&](const u32x4 (&c)[NB], const uint32_t (&sc)[NB], int s, bf16x8 (&b)[NB]) {
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt) {
-      const float f = s < 2 ? e4m3_f32_sel<0>(sc[nt]) : e4m3_f32_sel<1>(sc[nt]);
+      const uint32_t pair = sc[nt] >> (16 * h);   // 16-blocks 2h, 2h + 1
+      const float f = s < 2 ? e4m3_f32_sel<0>(pair) : e4m3_f32_sel<1>(pair);
       b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(c[nt], s), f));
     }
   };
