@@ -432,14 +432,27 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 #ifndef SSN_PS_STAGES
 #define SSN_PS_STAGES 3
 #endif
+// Three 8-wave workgroups fit a CU by LDS (3 x 52.6 KB dense, 3 x 46 KB 2:4) when a wave keeps
+// to 80 registers (six waves per SIMD); at 84 and more only two fit. The 2:4 slab needs 94
+// (forced to 80 it spills), so it runs two.
+#ifndef SSN_PS_WPE
+#define SSN_PS_WPE 6
+#endif
+#ifndef SSN_P4_WPE
+#define SSN_P4_WPE 5
+#endif
 constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = SSN_PS_STAGES, kPsMaxM = 8;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
 constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
 constexpr int kPsBytes = kPsXOff + kPsMaxM * kPsXRow;          // one ring slot
 
-template <int F>   // output rows per lane: M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4
-__global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
+// F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4). FOLD: each block's product is
+// folded into the sums before the next block's is formed, so one 16-register result is live
+// and a wave fits 80 registers (three workgroups per CU); without it the four products are
+// formed together, which hides their latency better when the grid gives a CU fewer workgroups.
+template <int F, bool FOLD>
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(FOLD ? SSN_PS_WPE : 1))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ ts, void* __restrict__ Y,
@@ -496,7 +509,9 @@ __global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __res
       }
       const uint32_t sw = *(const uint32_t*)(b + kPsScOff + nl * kSRow + 4 * wave);
       const uint8_t* xr = b + kPsXOff + xm * kPsXRow;
-      f32x16 d[4];
+      // the products of blocks 0..3 times their scales enter each sum in block order (one FMA
+      // per needed row: result row 4h + i, i < F, of the 32x32 tile, column nl)
+      f32x16 d[FOLD ? 1 : 4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const u32x4 xv = *(const u32x4*)(xr + 2 * (16 * (4 * wave + j) + 8 * h));
@@ -506,13 +521,21 @@ __global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps(const uint16_t* __res
         bw[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 2));
         bw[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[j], 1.0f, 3));
         f32x16 z = {};
-        d[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv), as_bf16x8(bw), z, 0, 0, 0);
-      }
-      const float s0 = e4m3_f32_sel<0>(sw), s1 = e4m3_f32_sel<1>(sw), s2 = e4m3_f32_sel<2>(sw),
-                  s3 = e4m3_f32_sel<3>(sw);
+        d[FOLD ? 0 : j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xv), as_bf16x8(bw), z, 0, 0, 0);
+        if (FOLD) {
+          const float sj = j == 0 ? e4m3_f32_sel<0>(sw) : j == 1 ? e4m3_f32_sel<1>(sw)
+                         : j == 2 ? e4m3_f32_sel<2>(sw) : e4m3_f32_sel<3>(sw);
 #pragma unroll
-      for (int i = 0; i < F; ++i)      // result row 4h + i (i < 4) of the 32x32 tile, column nl
-        acc[i] = fmaf(s3, d[3][i], fmaf(s2, d[2][i], fmaf(s1, d[1][i], fmaf(s0, d[0][i], acc[i]))));
+          for (int i = 0; i < F; ++i) acc[i] = fmaf(sj, d[0][i], acc[i]);
+        }
+      }
+      if (!FOLD) {
+        const float s0 = e4m3_f32_sel<0>(sw), s1 = e4m3_f32_sel<1>(sw), s2 = e4m3_f32_sel<2>(sw),
+                    s3 = e4m3_f32_sel<3>(sw);
+#pragma unroll
+        for (int i = 0; i < F; ++i)
+          acc[i] = fmaf(s3, d[FOLD ? 0 : 3][i], fmaf(s2, d[FOLD ? 0 : 2][i], fmaf(s1, d[FOLD ? 0 : 1][i], fmaf(s0, d[0][i], acc[i]))));
+      }
     }
     __syncthreads();                               // every stage consumed: LDS holds the partial sums
     float* red = (float*)smem;
@@ -558,7 +581,7 @@ constexpr int kP4VOff = 0, kP4MOff = kPsRows * (kSK / 4), kP4SOff = kP4MOff + kP
 constexpr int kP4XOff = kP4SOff + kPsRows * kSRow;
 constexpr int kP4Bytes = kP4XOff + kPsMaxM * kPsXRow;
 
-__global__ __launch_bounds__(kPsWaves * 64) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(SSN_P4_WPE))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
                                                              const uint8_t* __restrict__ vals,
                                                              const uint8_t* __restrict__ meta,
                                                              const uint8_t* __restrict__ scales,
@@ -773,7 +796,8 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab: two workgroups per CU
     static bool ps_set = false;
     if (!ps_set) {
-      for (const void* f : {(const void*)k_gemv_ps<1>, (const void*)k_gemv_ps<2>, (const void*)k_gemv_ps<4>}) {
+      for (const void* f : {(const void*)k_gemv_ps<1, false>, (const void*)k_gemv_ps<2, false>,
+                            (const void*)k_gemv_ps<4, false>, (const void*)k_gemv_ps<4, true>}) {
         hipError_t e2 = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kPsStages * kPsBytes);
         if (e2 != hipSuccess) return e2;
       }
@@ -781,7 +805,12 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
     }
     const int G = (int)std::min<int64_t>((int64_t)SSN_GV_GRIDMUL * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
-    auto k = a.M == 1 ? k_gemv_ps<1> : a.M == 2 ? k_gemv_ps<2> : k_gemv_ps<4>;
+    // M > 2 with at least three 32-row groups per CU: the 80-register form, three workgroups
+    // per CU (measured at N = 131072: M = 4 88 -> 81 us, M = 8 95 -> 88 us; at N = 13824 it is
+    // 5-7% slower, so smaller grids keep the four products in flight)
+    const bool fold = a.M > 2 && (a.N + kPsRows - 1) / kPsRows >= 3 * (int64_t)cu_count();
+    auto k = a.M == 1 ? k_gemv_ps<1, false> : a.M == 2 ? k_gemv_ps<2, false>
+           : fold ? k_gemv_ps<4, true> : k_gemv_ps<4, false>;
     hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), kPsStages * kPsBytes, s, a.X, (int)a.M, (int)a.N, (int)a.K,
                        a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();

@@ -29,7 +29,8 @@ def _problem(M, N, K, seed, prune):
 DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
                (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
-               (3, 17000, 512)]                   # several row groups per decode workgroup
+               (3, 17000, 512),                   # several row groups per decode workgroup
+               (3, 24608, 512), (8, 24608, 512)]  # >= 3 row groups per CU: the 80-register fold form
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
