@@ -236,10 +236,12 @@ constexpr int kBigRows = 256;
 constexpr bool kSplitBig = false;
 constexpr int kBN = 256, kBK = 64;
 #ifndef SSN_MOE_STAGES
-#define SSN_MOE_STAGES 3
+#define SSN_MOE_STAGES 2
 #endif
-// ring slots (kStages - 1 stages in flight): deeper for the 64-row form, which runs two
-// workgroups per CU; the 256-row form fits three slots
+// ring slots of the 64-row form (kStages - 1 stages in flight). Two slots (34 KB, the epilogue
+// staging 35 KB) let four workgroups share a CU, three (51 KB) three, four (68 KB) two; on the
+// 4096-token, 512-expert FFN two were the fastest (2:4 up 516 -> 484 us, down 278 -> 253 us;
+// dense 2-6%). The 256-row form uses three slots.
 template <int BM>
 constexpr int moe_stages() { return BM == 64 ? SSN_MOE_STAGES : 3; }
 constexpr int kThreads = 256;
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd
 template <int WF, int EPI, int BM>
 hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   constexpr int bytes = moe_lds_bytes<WF, BM>();
-  static_assert(bytes <= 160 * 1024 && (BM != 64 || 2 * bytes <= 160 * 1024), "LDS budget: 64-row tiles run two workgroups per CU");
+  static_assert(bytes <= 160 * 1024 && (BM != 64 || 2 * bytes <= 160 * 1024), "LDS budget: 64-row tiles run at least two workgroups per CU");
   hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
