@@ -45,6 +45,7 @@ METRIC = "NVFP4 GEMM TFLOP/s & HBM GB/s, 2:4 vs dense, % of MI355X roofline"
 HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 matrix peak
 SPARSE_BF16_PEAK_TFLOPS = 5000.0  # the same with 2:4 structured sparsity (dense-equivalent)
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
 RING = 16                       # weight copies rotated by the GEMVs (16 x 40 MB > 2 x 256 MB cache)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -178,7 +179,9 @@ def run_decode(args, torch, ssn, synth):
     Xm = {M: X[:M].contiguous() for M in Ms}
     names = ["prune", "quantize", "quantize_pruned", "check", "compress"] + \
             [f"gemv_dense_M{M}" for M in Ms] + [f"gemv_sp24_M{M}" for M in Ms]
-    extra = ["producer_fused"]           # timed beside the step, not part of it
+    # timed beside the step, not part of it: the fused producer, and the 2:4 GEMVs in the plain
+    # skip-and-gather form (vector ALU) for comparison with the SMFMAC ones
+    extra = ["producer_fused"] + [f"gemv_sp24_gather_M{M}" for M in Ms]
     prod = [dict(vals=torch.empty((N, K // 4), **u8), meta=torch.empty((N, K // 8), **u8),
                  scales=torch.empty((N, K // 16), **u8), ts=torch.empty(1, dtype=torch.float32, device=dev),
                  bad=torch.empty(1, dtype=torch.int64, device=dev)) for _ in range(2)]
@@ -209,6 +212,9 @@ def run_decode(args, torch, ssn, synth):
                                             prepare=True)
             calls[f"gemv_sp24_M{M}"].append(p)
             used[f"gemv_sp24_M{M}"] = u
+            p, _ = ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"], Y=Ys[M],
+                                       algo=ssn.ALGO_VALU, prepare=True)
+            calls[f"gemv_sp24_gather_M{M}"].append(p)
     B = Batches(torch)
 
     def steps(count):
@@ -261,6 +267,15 @@ def run_decode(args, torch, ssn, synth):
         "unfused_chain_us": round(chain, 2), "speedup_vs_unfused_chain": round(chain / pus, 3),
         "note": "nvfp4_sp24_produce: prune -> quantize -> check -> compress of W in one pass (bit-identical); "
                 "not part of the step"}}
+    for M in Ms:
+        n = f"gemv_sp24_gather_M{M}"
+        us = B.us(n)
+        b = bytes_gemm(M, N, K, True, 4)
+        extras[n] = {"us": round(us, 2), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
+                     "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "algo": "valu",
+                     "smfmac_speedup_vs_gather": round(us / kernels[f"gemv_sp24_M{M}"]["us"], 3),
+                     "note": "2:4 GEMV in the skip-and-gather form (x gathered at the stored positions, "
+                             "vector ALU); not part of the step"}
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dominant]
     roof = {"kernel": dominant, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -297,8 +312,12 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
     del W
     Y = torch.empty((M, N), dtype=y_dtype, device="cuda")
     yb = 2 if y_dtype == torch.bfloat16 else 4
+    # the skip-and-gather form (vector ALU, x gathered at the stored positions) is the plain
+    # comparison point; it is far slower (about a second per prefill call), so it runs one or
+    # two timed calls after as many warm-up calls
     variants = [("dense_mfma", False, ssn.ALGO_MFMA), ("sp24_smfmac", True, ssn.ALGO_SMFMAC),
-                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA)]
+                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA), ("sp24_gather_valu", True, ssn.ALGO_VALU)]
+    vreps = {"sp24_gather_valu": min(reps, 2 if 2.0 * M * N * K < 1e12 else 1)}
     B = Batches(torch)
     preps = {}
     for vname, sparse, algo in variants:
@@ -308,10 +327,10 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
             p, _ = ssn.gemm_nvfp4_dense(X, dn[0], dn[1], dn[2], y_dtype=y_dtype, algo=algo, Y=Y, prepare=True)
         preps[vname] = p
     for vname in preps:                      # warm-up
-        B.run(vname, [preps[vname]] * 2)
+        B.run(vname, [preps[vname]] * min(2, vreps.get(vname, 2)))
     torch.cuda.synchronize()
     for vname in preps:
-        B.run(vname, [preps[vname]] * reps)
+        B.run(vname, [preps[vname]] * vreps.get(vname, reps))
     torch.cuda.synchronize()
     flops = 2.0 * M * N * K
     out = {"shape": {"M": M, "N": N, "K": K, "y": "bf16" if yb == 2 else "f32", "outliers": outliers},
@@ -326,10 +345,13 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
             e["mfma_frac_actual_vs_bf16_peak"] = round(e["tflops_actual"] / BF16_PEAK_TFLOPS, 4)
             if algo == ssn.ALGO_SMFMAC:
                 e["mfma_frac_vs_sparse_peak"] = round(e["tflops_dense_equiv"] / SPARSE_BF16_PEAK_TFLOPS, 4)
+            if algo == ssn.ALGO_VALU:
+                e["valu_frac_actual_vs_fp32_peak"] = round(e["tflops_actual"] / FP32_VECTOR_PEAK_TFLOPS, 4)
+                e["timed_calls"] = vreps["sp24_gather_valu"]
         else:
             e["mfma_frac"] = round(e["tflops_dense_equiv"] / BF16_PEAK_TFLOPS, 4)
         out[vname] = e
-    for vname in ("sp24_smfmac", "sp24_decompress_mfma"):
+    for vname in ("sp24_smfmac", "sp24_decompress_mfma", "sp24_gather_valu"):
         out[vname]["speedup_vs_dense"] = round(out["dense_mfma"]["us"] / out[vname]["us"], 3)
     del X, Y, dn, sp, preps
     torch.cuda.empty_cache()
