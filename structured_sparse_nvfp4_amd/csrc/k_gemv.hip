@@ -418,8 +418,9 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. Two 8-wave workgroups per CU, each owning a
-// contiguous range of weight rows (32-row groups), stream the rows through a 3-deep LDS ring of
+// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. 8-wave workgroups (three per CU when a wave
+// keeps to 80 registers, two above), each owning a contiguous range of weight rows (32-row
+// groups), stream the rows through a 3-deep LDS ring of
 // 512-wide K stages with direct-to-LDS loads (as the slab kernel above). The E4M3 block scale is
 // applied after the matrix product instead of before it: one v_mfma_f32_32x32x16_bf16 per
 // 16-wide scale block takes the E2M1 codes converted to bf16 unscaled (one
@@ -559,7 +560,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (two 8-wave workgroups per
+// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, two per
 // CU, 32-row groups, 512-wide K stages in a ring of kP4Stages LDS slots), with every direct load
 // a full 1 KB instruction: waves 0-3 load the vals of rows 8w..8w+7 (128 B each), waves 4-5 the
 // meta of rows 16(w-4)..+15 (64 B each), wave 6 the scales of all 32 rows (32 B each), and wave
@@ -793,7 +794,7 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
-  if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab: two workgroups per CU
+  if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab
     static bool ps_set = false;
     if (!ps_set) {
       for (const void* f : {(const void*)k_gemv_ps<1, false>, (const void*)k_gemv_ps<2, false>,
@@ -859,7 +860,7 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
                        (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
-  if (a.M <= 8) {    // two 8-wave workgroups per CU, 32-row groups
+  if (a.M <= 8) {    // 8-wave workgroups (two per CU at 94 registers), 32-row groups
     const int G = (int)std::min<int64_t>(2 * (int64_t)cu_count(), (a.N + 31) / 32);
     const int R = (int)((a.N + G - 1) / G);
     constexpr int lds8 = kD * SlabLayout<true, 8>::kBytes;
