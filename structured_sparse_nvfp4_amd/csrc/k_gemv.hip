@@ -729,22 +729,32 @@ __global__ __launch_bounds__(256) void k_gemm_valu(const uint16_t* __restrict__ 
       const u32x2 v = *(const u32x2*)(w0 + (size_t)n * (K / 4) + k / 4);
       const uint32_t mt = *(const uint32_t*)(w1 + (size_t)n * (K / 8) + k / 8);
       float w[16];
-      int kk[16];
       for (int d = 0; d < 2; ++d) {
         f32x2 p0 = fp4x2_f32<0>(v[d]), p1 = fp4x2_f32<1>(v[d]), p2 = fp4x2_f32<2>(v[d]), p3 = fp4x2_f32<3>(v[d]);
         const float s = d == 0 ? s0 : s1;     // groups 0..3 -> k 0..15 (block 0), 4..7 -> block 1
         w[8 * d + 0] = p0[0] * s; w[8 * d + 1] = p0[1] * s; w[8 * d + 2] = p1[0] * s; w[8 * d + 3] = p1[1] * s;
         w[8 * d + 4] = p2[0] * s; w[8 * d + 5] = p2[1] * s; w[8 * d + 6] = p3[0] * s; w[8 * d + 7] = p3[1] * s;
       }
-      for (int g = 0; g < 8; ++g) {
-        const uint32_t pos = (mt >> (4 * g)) & 0xFu;
-        kk[2 * g] = k + 4 * g + (int)(pos & 3u);
-        kk[2 * g + 1] = k + 4 * g + (int)(pos >> 2);
-      }
+      // the chunk's 32 activations of a row arrive as four 16-byte loads; the kept value at
+      // position p of group g is half p & 1 of word 2g + (p >> 1)
       for (int i = 0; i < mcount; ++i) {
-        const uint16_t* xr = X + (size_t)(m0 + i) * K;
+        const u32x4* xp = (const u32x4*)(X + (size_t)(m0 + i) * K + k);
+        u32x4 xv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) xv[t] = xp[t];
         float a = acc[i];
-        for (int t = 0; t < 16; ++t) a = fmaf(__uint_as_float((uint32_t)xr[kk[t]] << 16), w[t], a);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const uint32_t d0 = xv[g >> 1][2 * (g & 1)], d1 = xv[g >> 1][2 * (g & 1) + 1];
+          const uint32_t pos = (mt >> (4 * g)) & 0xFu;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const uint32_t p = e == 0 ? (pos & 3u) : (pos >> 2);
+            const uint32_t d = (p & 2u) ? d1 : d0;
+            const uint32_t bits = (p & 1u) ? (d & 0xFFFF0000u) : (d << 16);
+            a = fmaf(__uint_as_float(bits), w[2 * g + e], a);
+          }
+        }
         acc[i] = a;
       }
     }
