@@ -57,6 +57,11 @@ def test_validation_paths_return_codes_without_launching():
     assert L.sp24_check(p, 4, 64, n, n, n) == ssn.SSN_E_NULL
     assert b"bad_groups" in L.ssn_last_error()
     assert L.sp24_compress(_bad(0x1008), 4, 64, p, p, p, n) == ssn.SSN_E_ALIGN
+    # sp24_prune: the tensor scale output is optional, but a given one must be f32-aligned
+    assert L.sp24_prune(p, 0, 4, 48, p, n, n) == ssn.SSN_E_SHAPE
+    assert L.sp24_prune(p, 0, 4, 64, p, _bad(0x1002), n) == ssn.SSN_E_ALIGN
+    assert b"tensor_scale_out" in L.ssn_last_error()
+    assert L.sp24_prune(n, 0, 4, 64, p, n, n) == ssn.SSN_E_NULL
     assert L.nvfp4_quantize(p, 0, 4, 64, n, p, p, n, n) == ssn.SSN_E_NULL
     assert L.gemm_nvfp4_dense(p, 2, 4, 64, n, p, p, p, 0, 0, n, n) == ssn.SSN_E_NULL
     # dtype and algorithm codes
