@@ -96,8 +96,3 @@ def dequantize(codes: np.ndarray, scales: np.ndarray, s_t) -> np.ndarray:
     sc = np.repeat(e4m3_decode(scales), BLOCK, axis=1)
     return e2m1_decode(nib) * sc * np.float64(np.float32(s_t))
 
-
-def decoded_unit(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """E2M1(code) * E4M3(S) without the tensor scale, float64 [N, K] (exact)."""
-    nib = unpack_nibbles(codes)
-    return e2m1_decode(nib) * np.repeat(e4m3_decode(scales), BLOCK, axis=1)
