@@ -213,7 +213,7 @@ def run_decode(args, torch, ssn, synth):
             calls[f"gemv_sp24_M{M}"].append(p)
             used[f"gemv_sp24_M{M}"] = u
             p, _ = ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"], Y=Ys[M],
-                                       algo=ssn.ALGO_VALU, prepare=True)
+                                       algo=ssn.ALGO_GATHER, prepare=True)
             calls[f"gemv_sp24_gather_M{M}"].append(p)
     B = Batches(torch)
 
@@ -316,7 +316,7 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
     # comparison point; it is far slower (about a second per prefill call), so it runs one or
     # two timed calls after as many warm-up calls
     variants = [("dense_mfma", False, ssn.ALGO_MFMA), ("sp24_smfmac", True, ssn.ALGO_SMFMAC),
-                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA), ("sp24_gather_valu", True, ssn.ALGO_VALU)]
+                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA), ("sp24_gather_valu", True, ssn.ALGO_GATHER)]
     vreps = {"sp24_gather_valu": min(reps, 2 if 2.0 * M * N * K < 1e12 else 1)}
     B = Batches(torch)
     preps = {}
@@ -345,7 +345,7 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
             e["mfma_frac_actual_vs_bf16_peak"] = round(e["tflops_actual"] / BF16_PEAK_TFLOPS, 4)
             if algo == ssn.ALGO_SMFMAC:
                 e["mfma_frac_vs_sparse_peak"] = round(e["tflops_dense_equiv"] / SPARSE_BF16_PEAK_TFLOPS, 4)
-            if algo == ssn.ALGO_VALU:
+            if algo == ssn.ALGO_GATHER:
                 e["valu_frac_actual_vs_fp32_peak"] = round(e["tflops_actual"] / FP32_VECTOR_PEAK_TFLOPS, 4)
                 e["timed_calls"] = vreps["sp24_gather_valu"]
         else:

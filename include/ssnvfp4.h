@@ -70,16 +70,22 @@ enum { SSN_F32 = 0, SSN_BF16 = 1 };
 
 /* GEMM algorithms. Each call writes the one it ran to *algo_used (host int, nullable).
  * The matrix-core algorithms run decode-shaped kernels for M <= 16 (weights streamed once
- * through LDS) and 256 x 256 output tiles for larger M; the tiles need K % 64 == 0. AUTO picks
+ * through LDS) and 256 x 256 output tiles for larger M; the tiles need K % 64 == 0 and
+ * K <= 2^21 (a tile addresses its 256-row activation panel with 32-bit byte offsets). AUTO picks
  * MFMA for dense weights and SMFMAC for 2:4 weights, DECOMPRESS_MFMA when M <= 16 and
- * K % 64 != 0, and VALU when M > 16 and K % 64 != 0. */
+ * K % 64 != 0, and the vector-ALU kernels (VALU dense, GATHER 2:4) when M > 16 and the tiles do
+ * not apply. */
 enum {
   SSN_ALGO_AUTO = 0,             /* let the library choose; the choice is reported */
-  SSN_ALGO_VALU = 1,             /* plain vector-ALU kernel, any K % 32 == 0 (dense: FMA per
-                                    weight; 2:4: skip-and-gather of x at the stored positions) */
+  SSN_ALGO_VALU = 1,             /* plain vector-ALU kernel, any K % 32 == 0: dense weights, one
+                                    FMA per weight; with 2:4 weights it runs the GATHER kernel
+                                    and reports GATHER */
   SSN_ALGO_MFMA = 2,             /* dense: bf16 MFMA on weights decoded in registers */
   SSN_ALGO_SMFMAC = 3,           /* 2:4 only: sparse MFMA (v_smfmac) with the compressed weights
                                     as the sparse operand; needs K % 64 == 0 */
+  SSN_ALGO_GATHER = 4,           /* 2:4 only: skip-and-gather on the vector ALU: each kept value is
+                                    decoded with its scale and multiplied by the activation picked
+                                    at its stored position; any K % 32 == 0 */
   SSN_ALGO_DECOMPRESS_MFMA = 5,  /* 2:4 only: expand vals+meta to a dense tile and run the
                                     dense bf16 MFMA (computes on the zeros) */
   SSN_ALGO_STREAM = 6            /* grouped-expert calls only: one wave streams 32 weight rows
@@ -200,8 +206,8 @@ int gemm_nvfp4_dense(const uint16_t* X, int64_t M, int64_t N, int64_t K, const u
  * values of each group of four contribute, at their stored positions ("NVFP4 vs 2:4 sparse",
  * robertz.co, section "What 2:4 actually is": the pruned lanes are skipped).
  * vals [N, K/4], meta [N, K/8] (positions must satisfy i0 < i1, as sp24_compress writes them),
- * scales [N, K/16] (original K). algo: AUTO, VALU (skip-and-gather), SMFMAC (K % 64 == 0),
- * DECOMPRESS_MFMA. Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, HIP.
+ * scales [N, K/16] (original K). algo: AUTO, GATHER (skip-and-gather; VALU is accepted for it),
+ * SMFMAC (K % 64 == 0), DECOMPRESS_MFMA. Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, HIP.
  * ------------------------------------------------------------------------------------------- */
 int gemm_nvfp4_sp24(const uint16_t* X, int64_t M, int64_t N, int64_t K, const uint8_t* vals,
                     const uint8_t* meta, const uint8_t* scales, const float* tensor_scale, void* Y,

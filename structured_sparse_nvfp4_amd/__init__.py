@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libssnvfp4.so")
 
 SSN_OK, SSN_E_NULL, SSN_E_SHAPE, SSN_E_ALIGN, SSN_E_DTYPE, SSN_E_ALGO, SSN_E_HIP, SSN_E_RANGE = range(8)
 SSN_F32, SSN_BF16 = 0, 1
-ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_DECOMPRESS_MFMA, ALGO_STREAM = 0, 1, 2, 3, 5, 6
-ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac",
+ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_GATHER, ALGO_DECOMPRESS_MFMA, ALGO_STREAM = 0, 1, 2, 3, 4, 5, 6
+ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac", ALGO_GATHER: "gather",
               ALGO_DECOMPRESS_MFMA: "decompress_mfma", ALGO_STREAM: "stream"}
 EPI_NONE, EPI_SILU_GATE = 0, 1
 WLAYOUT_ROWS, WLAYOUT_KTILE64 = 0, 1

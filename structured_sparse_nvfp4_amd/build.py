@@ -24,7 +24,7 @@ CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"),
-] + os.environ.get("SSN_EXTRA_CFLAGS", "").split()
+]
 
 # The tiled matrix-core kernels are scheduled for instruction-level parallelism (one wave per
 # SIMD: operand reads for the next MFMA step are issued while the current step runs).

@@ -45,6 +45,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // rows (N, M) are indexed with 32-bit ints inside the kernels, tile origins included
 constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1024;
+// the 256x256 tiles address their activation panel (256 rows of K bf16) with 32-bit byte offsets
+constexpr int64_t kMaxTileK = (int64_t)1 << 21;
 
 int check_nk(const char* fn, int64_t N, int64_t K) {
   if (N < 0 || K < 0) return fail(SSN_E_SHAPE, "%s: negative size (N=%lld, K=%lld)", fn, (long long)N, (long long)K);
@@ -176,38 +178,41 @@ int gemm_common(const char* fn, const uint16_t* X, int64_t M, int64_t N, int64_t
   if (M > kMaxRows) return fail(SSN_E_SHAPE, "%s: M=%lld too large", fn, (long long)M);
   if ((st = check_nk(fn, N, K))) return st;
   if ((st = check_dtype(fn, y_dtype, "y_dtype"))) return st;
-  if (algo < SSN_ALGO_AUTO || algo > SSN_ALGO_DECOMPRESS_MFMA || algo == 4)
+  if (algo < SSN_ALGO_AUTO || algo > SSN_ALGO_DECOMPRESS_MFMA)
     return fail(SSN_E_ALGO, "%s: unknown algorithm %d", fn, algo);
-  if (!sp24 && (algo == SSN_ALGO_SMFMAC || algo == SSN_ALGO_DECOMPRESS_MFMA))
+  if (!sp24 && (algo == SSN_ALGO_SMFMAC || algo == SSN_ALGO_DECOMPRESS_MFMA || algo == SSN_ALGO_GATHER))
     return fail(SSN_E_ALGO, "%s: algorithm %d applies to 2:4 weights only", fn, algo);
   if (sp24 && algo == SSN_ALGO_MFMA)
     return fail(SSN_E_ALGO, "%s: use SMFMAC or DECOMPRESS_MFMA for 2:4 weights", fn);
-  if (M == 0 || N == 0) { if (algo_used) *algo_used = algo; return ok(); }
+  if (M == 0 || N == 0) { if (algo_used) *algo_used = (sp24 && algo == SSN_ALGO_VALU) ? SSN_ALGO_GATHER : algo; return ok(); }
   if (K == 0) return fail(SSN_E_SHAPE, "%s: K must be positive when M, N > 0", fn);
   REQUIRE_PTR(X); REQUIRE_PTR(w0); REQUIRE_PTR(scales); REQUIRE_ELEM_PTR(ts); REQUIRE_PTR(Y);
   if (sp24) REQUIRE_PTR(w1);
 
   // M <= 16: decode-shaped kernels (weights streamed once); otherwise 256x256 tiles, which
-  // take whole 64-wide K stages
+  // take whole 64-wide K stages and address a 256-row activation panel with 32-bit offsets
   const bool skinny = M <= 16;
-  int chosen = algo;
+  const bool tiles_fit = K % 64 == 0 && K <= kMaxTileK;
+  const int valu = sp24 ? SSN_ALGO_GATHER : SSN_ALGO_VALU;
+  int chosen = algo == SSN_ALGO_VALU ? valu : algo;
   if (algo == SSN_ALGO_AUTO) {
-    if (!skinny && K % 64) chosen = SSN_ALGO_VALU;
+    if (!skinny && !tiles_fit) chosen = valu;
     else if (!sp24) chosen = SSN_ALGO_MFMA;
     else chosen = (skinny && K % 64) ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_SMFMAC;
   }
   // explicit choices that do not apply to this shape are refused, never replaced
   if (chosen == SSN_ALGO_SMFMAC && skinny && K % 64)
     return fail(SSN_E_ALGO, "%s: SMFMAC for M <= 16 needs K %% 64 == 0 (K=%lld)", fn, (long long)K);
-  if (chosen != SSN_ALGO_VALU && !skinny && K % 64)
-    return fail(SSN_E_ALGO, "%s: matrix-core algorithm %d for M > 16 needs K %% 64 == 0 (K=%lld)", fn, chosen,
-                (long long)K);
+  if (chosen != valu && !skinny && !tiles_fit)
+    return fail(SSN_E_ALGO, "%s: matrix-core algorithm %d for M > 16 needs K %% 64 == 0 and K <= %lld (K=%lld)", fn,
+                chosen, (long long)kMaxTileK, (long long)K);
 
   ssn::GemmArgs a{X, M, N, K, w0, w1, scales, ts, Y, y_dtype == SSN_BF16};
   hipStream_t s = as_stream(stream);
   hipError_t e = hipSuccess;
   switch (chosen) {
-    case SSN_ALGO_VALU: e = sp24 ? ssn::launch_gemm_sp24_valu(a, s) : ssn::launch_gemm_dense_valu(a, s); break;
+    case SSN_ALGO_VALU: e = ssn::launch_gemm_dense_valu(a, s); break;
+    case SSN_ALGO_GATHER: e = ssn::launch_gemm_sp24_valu(a, s); break;
     case SSN_ALGO_MFMA: e = skinny ? ssn::launch_gemv_dense_mfma(a, s) : ssn::launch_gemm_dense_mfma(a, s); break;
     case SSN_ALGO_SMFMAC: e = skinny ? ssn::launch_gemv_sp24_smfmac(a, s) : ssn::launch_gemm_sp24_smfmac(a, s); break;
     case SSN_ALGO_DECOMPRESS_MFMA:

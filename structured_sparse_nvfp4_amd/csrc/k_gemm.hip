@@ -38,21 +38,6 @@ namespace {
 constexpr int kTM = 256, kTN = 256, kTK = 64;   // output tile and K-stage
 constexpr int kStages = 3;                       // stages resident in LDS
 constexpr int kThreads = 256;
-#ifndef SSN_GEMM_WGM
-#define SSN_GEMM_WGM 1
-#endif
-constexpr int kGemmWGM = SSN_GEMM_WGM;   // waves along M in the dense tile (1 or 2)
-#ifndef SSN_GEMM_TM
-#define SSN_GEMM_TM 256
-#endif
-constexpr int kGemmTM = SSN_GEMM_TM;
-// Issue each stage's direct loads in four parts over the MFMA steps of the previous stage
-// instead of one burst at the stage boundary.
-#ifndef SSN_GEMM_SPREAD
-#define SSN_GEMM_SPREAD 1
-#endif
-constexpr bool kSpreadLoads = SSN_GEMM_SPREAD != 0;     // activation rows of the dense tile (256: one block per CU, 128: two)
-
 // One LDS ring slot (bytes) of a tile with TM activation rows and 256 weight rows (tile-local).
 //   X      [TM][128 B]   activation k-chunk c of row r at physical chunk c ^ swz(r)
 //   dense: codes [256][32 B]  half h of row r at physical half h ^ ((r >> 3) & 1)
@@ -252,8 +237,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   const StageSrc<WF, TM> src = stage_src<WF, TM>(X, w0, w1, scales, M, N, K, m0, n0, wave, lane);
   issue_stage<WF, TM>(src, 0, lds, wave);
   issue_stage<WF, TM>(src, min(1, last), lds + L::kBytes, wave);
-  if constexpr (kSpreadLoads) issue_part<WF, TM, 0>(src, min(2, last), lds + 2 * L::kBytes, wave);
-  else issue_stage<WF, TM>(src, min(2, last), lds + 2 * L::kBytes, wave);
+  issue_part<WF, TM, 0>(src, min(2, last), lds + 2 * L::kBytes, wave);
 
   u32x4 wc[NB];         // this stage's weights (per column block) and their scale pair
   uint32_t wsc[NB];
@@ -293,8 +277,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     }
   };
 
-  if constexpr (kSpreadLoads) wait_vmcnt<L::kLoads + part_loads<WF, TM>(0)>();
-  else wait_vmcnt<2 * L::kLoads>();
+  wait_vmcnt<L::kLoads + part_loads<WF, TM>(0)>();
   stage_barrier();
   load_w_regs(lds, wc, wsc);
   read_a(lds, 0, abuf[0]);
@@ -307,11 +290,11 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     char* fill = lds + ((S + 2) % kStages) * L::kBytes;   // stage st + 2: its first part is in flight
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
-      if constexpr (kSpreadLoads) {
-        if (s == 0) issue_part<WF, TM, 1>(src, min(st + 2, last), fill, wave);
-        else if (s == 1) issue_part<WF, TM, 2>(src, min(st + 2, last), fill, wave);
-        else issue_part<WF, TM, 3>(src, min(st + 2, last), fill, wave);
-      }
+      // stage st + 2's loads, issued in four parts over the MFMA steps instead of one burst at
+      // the boundary (the load address/command queues were filling)
+      if (s == 0) issue_part<WF, TM, 1>(src, min(st + 2, last), fill, wave);
+      else if (s == 1) issue_part<WF, TM, 2>(src, min(st + 2, last), fill, wave);
+      else issue_part<WF, TM, 3>(src, min(st + 2, last), fill, wave);
       read_a(slot, s + 1, abuf[(s + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);         // operand reads go out first, a whole step ahead
       bf16x8 bn[NB];
@@ -326,8 +309,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
     __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0)
     wait_vmcnt<L::kLoads>();                     // ... and stage st + 1 has landed
     stage_barrier();
-    if constexpr (kSpreadLoads) issue_part<WF, TM, 0>(src, min(st + 3, last), lds + S * L::kBytes, wave);
-    else issue_stage<WF, TM>(src, min(st + 3, last), lds + S * L::kBytes, wave);
+    issue_part<WF, TM, 0>(src, min(st + 3, last), lds + S * L::kBytes, wave);
     u32x4 wn_[NB];
     uint32_t wsn[NB];
     bf16x8 bn[NB];
@@ -525,13 +507,13 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
 
 template <int WF>
 hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
-  constexpr int TM = kGemmTM;
+  constexpr int TM = kTM, WGM = 1;
   const int bytes = kStages * Slot<WF, TM>::kBytes;
-  const void* fn = (const void*)k_gemm_mfma<WF, kGemmWGM, TM>;
+  const void* fn = (const void*)k_gemm_mfma<WF, WGM, TM>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((a.M + TM - 1) / TM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL((k_gemm_mfma<WF, kGemmWGM, TM>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
+  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
                      (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
 }

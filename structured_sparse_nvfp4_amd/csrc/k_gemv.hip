@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "common.hpp"
+#include "device_once.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
 
@@ -30,21 +31,12 @@ constexpr int kWaves = 4;
 // Post-scale decode slabs: up to this many workgroups per CU, one 32-row group each, so that the
 // hardware starts a new group's loads while other groups on the CU finish (vocabulary-sized N
 // measured 11% faster than two workgroups looping over their groups).
-#ifndef SSN_GV_GRIDMUL
-#define SSN_GV_GRIDMUL 16
-#endif
 // 32 zero bytes: activation loads of K-slices outside the problem read here, so that the weights
 // loaded (from a clamped, valid address) for those slices are multiplied by zero.
 __device__ __attribute__((aligned(16))) uint32_t g_zero32[8];
-// Slices in flight per wave (ring depth). Build-time tunables.
-#ifndef SSN_GEMV_DENSE_RING
-#define SSN_GEMV_DENSE_RING 2
-#endif
-#ifndef SSN_GEMV_SPARSE_RING
-#define SSN_GEMV_SPARSE_RING 1
-#endif
-constexpr int kDenseRing = SSN_GEMV_DENSE_RING;    // 128-wide slices (dense)
-constexpr int kSparseRing = SSN_GEMV_SPARSE_RING;  // 256-wide slices (2:4)
+// Slices in flight per wave (ring depth).
+constexpr int kDenseRing = 2;    // 128-wide slices (dense)
+constexpr int kSparseRing = 1;  // 256-wide slices (2:4)
 
 __device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
 
@@ -430,19 +422,10 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // rows >= M read row 0 and are never stored), B = weights (column = weight row lane % 32); lane
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
-#ifndef SSN_PS_STAGES
-#define SSN_PS_STAGES 3
-#endif
 // Three 8-wave workgroups fit a CU by LDS (3 x 52.6 KB dense, 3 x 46 KB 2:4) when a wave keeps
 // to 80 registers (six waves per SIMD); at 84 and more only two fit. The 2:4 slab needs 94
 // (forced to 80 it spills), so it runs two.
-#ifndef SSN_PS_WPE
-#define SSN_PS_WPE 6
-#endif
-#ifndef SSN_P4_WPE
-#define SSN_P4_WPE 5
-#endif
-constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = SSN_PS_STAGES, kPsMaxM = 8;
+constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
 constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
@@ -453,7 +436,7 @@ constexpr int kPsBytes = kPsXOff + kPsMaxM * kPsXRow;          // one ring slot
 // and a wave fits 80 registers (three workgroups per CU); without it the four products are
 // formed together, which hides their latency better when the grid gives a CU fewer workgroups.
 template <int F, bool FOLD>
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(FOLD ? SSN_PS_WPE : 1))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(FOLD ? 6 : 1))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ ts, void* __restrict__ Y,
@@ -573,16 +556,13 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 // LDS slot: vals [32][128 B] (16-byte piece p of row r holds global piece p ^ (r & 7)), meta
 // [32][64 B] (piece p holds global piece p ^ ((r >> 1) & 3)), scales [32][32 B], activations
 // [8][1 KB + 16 B].
-#ifndef SSN_P4_STAGES
-#define SSN_P4_STAGES 3
-#endif
-constexpr int kP4Stages = SSN_P4_STAGES;
+constexpr int kP4Stages = 3;
 static_assert(kP4Stages >= 2 && kP4Stages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kP4VOff = 0, kP4MOff = kPsRows * (kSK / 4), kP4SOff = kP4MOff + kPsRows * (kSK / 8);
 constexpr int kP4XOff = kP4SOff + kPsRows * kSRow;
 constexpr int kP4Bytes = kP4XOff + kPsMaxM * kPsXRow;
 
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(SSN_P4_WPE))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(5))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
                                                              const uint8_t* __restrict__ vals,
                                                              const uint8_t* __restrict__ meta,
                                                              const uint8_t* __restrict__ scales,
@@ -776,45 +756,35 @@ __global__ __launch_bounds__(256) void k_gemm_valu(const uint16_t* __restrict__ 
 
 }  // namespace
 
-static int cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  return cus;
-}
-
 int slab_blocks(int64_t N) {
   const int64_t tiles = (N + 15) / 16;
   return (int)std::min<int64_t>(cu_count(), tiles);
 }
 
 hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemv_slab<false, kSlabWaves>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, kD * SlabLayout<false, kSlabWaves>::kBytes);
-    if (e1 != hipSuccess) return e1;
-    attr_set = true;
-  }
+  static PerDeviceOnce attr_once;
+  hipError_t e1 = once_per_device(attr_once, [] {
+    return hipFuncSetAttribute((const void*)k_gemv_slab<false, kSlabWaves>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               kD * SlabLayout<false, kSlabWaves>::kBytes);
+  });
+  if (e1 != hipSuccess) return e1;
   if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
     hipLaunchKernelGGL((k_gemv_mfma<false, kDenseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
   if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab
-    static bool ps_set = false;
-    if (!ps_set) {
+    static PerDeviceOnce ps_once;
+    hipError_t e2 = once_per_device(ps_once, [] {
       for (const void* f : {(const void*)k_gemv_ps<1, false>, (const void*)k_gemv_ps<2, false>,
                             (const void*)k_gemv_ps<4, false>, (const void*)k_gemv_ps<4, true>}) {
-        hipError_t e2 = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kPsStages * kPsBytes);
-        if (e2 != hipSuccess) return e2;
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kPsStages * kPsBytes);
+        if (e != hipSuccess) return e;
       }
-      ps_set = true;
-    }
-    const int G = (int)std::min<int64_t>((int64_t)SSN_GV_GRIDMUL * cu_count(), (a.N + kPsRows - 1) / kPsRows);
+      return hipSuccess;
+    });
+    if (e2 != hipSuccess) return e2;
+    const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
     // M > 2 with at least three 32-row groups per CU: the 80-register form, three workgroups
     // per CU (measured at N = 131072: M = 4 88 -> 81 us, M = 8 95 -> 88 us; at N = 13824 it is
@@ -842,29 +812,29 @@ hipError_t launch_gemv_sp24_decomp(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  static PerDeviceOnce attr_once;
+  hipError_t e1 = once_per_device(attr_once, [] {
     for (const void* f : {(const void*)k_gemv_slab<true, 8>, (const void*)k_gemv_slab<true, kSlabWaves>}) {
-      hipError_t e1 = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          kD * SlabLayout<true, kSlabWaves>::kBytes);
-      if (e1 != hipSuccess) return e1;
+      hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         kD * SlabLayout<true, kSlabWaves>::kBytes);
+      if (e != hipSuccess) return e;
     }
-    attr_set = true;
-  }
+    return hipSuccess;
+  });
+  if (e1 != hipSuccess) return e1;
   if (a.K % 256) {   // the slab kernel stages scale rows in 16-byte pieces: K/16 must be a multiple of 16
     hipLaunchKernelGGL((k_gemv_smfmac<kSparseRing>), dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, a.X,
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
   if (a.M <= kPsMaxM && a.K % kSK == 0) {   // full-width loads, 32x32x32 sparse MFMA per 64-k chunk
-    static bool p4_set = false;
-    if (!p4_set) {
-      hipError_t e2 = hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          kP4Stages * kP4Bytes);
-      if (e2 != hipSuccess) return e2;
-      p4_set = true;
-    }
-    const int G = (int)std::min<int64_t>((int64_t)SSN_GV_GRIDMUL * cu_count(), (a.N + kPsRows - 1) / kPsRows);
+    static PerDeviceOnce p4_once;
+    hipError_t e2 = once_per_device(p4_once, [] {
+      return hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 kP4Stages * kP4Bytes);
+    });
+    if (e2 != hipSuccess) return e2;
+    const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
     hipLaunchKernelGGL(k_gemv_ps24, dim3(G), dim3(kPsWaves * 64), kP4Stages * kP4Bytes, s, a.X, (int)a.M, (int)a.N,
                        (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);

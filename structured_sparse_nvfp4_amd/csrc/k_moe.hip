@@ -227,23 +227,14 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_small(const int32_t* __
 }
 
 // ------------------------------------------------------------------------------ grouped product
-// With kSplitBig, rows of an expert are cut into full 256-row tiles (run by the BM = 256 form,
-// which decodes each weight once per 256 rows) and a remainder of at most 255 rows in 64-row
-// tiles (BM = 64 form). Measured on the 512-expert top-10 workload, the split was slower than
-// 64-row tiles throughout (the 256-row launch has too few tiles to fill the chip), so it is
-// off; the 256-row form stays available for routings with many rows per expert.
-constexpr int kBigRows = 256;
-constexpr bool kSplitBig = false;
 constexpr int kBN = 256, kBK = 64;
-#ifndef SSN_MOE_STAGES
-#define SSN_MOE_STAGES 2
-#endif
-// ring slots of the 64-row form (kStages - 1 stages in flight). Two slots (34 KB, the epilogue
+// Ring slots of the 64-row tiles (kStages - 1 stages in flight). Two slots (34 KB, the epilogue
 // staging 35 KB) let four workgroups share a CU, three (51 KB) three, four (68 KB) two; on the
 // 4096-token, 512-expert FFN two were the fastest (2:4 up 516 -> 484 us, down 278 -> 253 us;
-// dense 2-6%). The 256-row form uses three slots.
+// dense 2-6%). 256-row tiles for the experts with many rows, beside 64-row tiles for the rest,
+// were slower throughout (the second launch has too few tiles to fill the chip).
 template <int BM>
-constexpr int moe_stages() { return BM == 64 ? SSN_MOE_STAGES : 3; }
+constexpr int moe_stages() { return 2; }
 constexpr int kThreads = 256;
 constexpr int kEpiNone = 0, kEpiSilu = 1;
 
@@ -278,21 +269,17 @@ __device__ __forceinline__ int xcd_contiguous(int b, int total) {
   return x * per + min(x, extra) + idx;
 }
 
-// Rows [o0, o1) of expert e, clamped into [0, R] so that inconsistent offsets cannot address
-// rows outside Y; then the part a tile form covers: full 256-row tiles (BIG) or the rest.
-template <bool BIG>
+// Rows [a, b) of expert e, clamped into [0, R] so that inconsistent offsets cannot address
+// rows outside Y.
 __device__ __forceinline__ void expert_part(const int32_t* off, int e, int R, int& a, int& b) {
-  const int o0 = min(max(off[e], 0), R);
-  const int o1 = min(max(off[e + 1], o0), R);
-  const int full = kSplitBig ? o0 + (o1 - o0) / kBigRows * kBigRows : o0;
-  a = BIG ? o0 : full;
-  b = BIG ? full : o1;
+  a = min(max(off[e], 0), R);
+  b = min(max(off[e + 1], a), R);
 }
 
 // Expert, first row and row count of linear tile bx (all threads of the block take part:
 // every thread sums the tiles of E / 256 experts, a block scan finds the owner). False when
 // bx is past the last tile (uniformly for the block).
-template <int BM, bool BIG>
+template <int BM>
 __device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx, int& e_out, int& r0_out,
                           int& cnt_out) {
   __shared__ int sm[8];
@@ -302,7 +289,7 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx,
   int t = 0;
   for (int e = e0; e < e1; ++e) {
     int a, b;
-    expert_part<BIG>(off, e, R, a, b);
+    expert_part(off, e, R, a, b);
     t += (b - a + BM - 1) / BM;
   }
   int inc = t;
@@ -321,7 +308,7 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx,
     int acc = excl;
     for (int e = e0; e < e1; ++e) {
       int a, b;
-      expert_part<BIG>(off, e, R, a, b);
+      expert_part(off, e, R, a, b);
       const int nt = (b - a + BM - 1) / BM;
       if (bx < acc + nt) {
         const int r0 = a + BM * (bx - acc);
@@ -337,7 +324,7 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx,
 }
 
 template <int WF, int EPI, int BM>
-__global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
+__global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -354,7 +341,7 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
   int e, r0, cnt;
   const int t = xcd_contiguous(blockIdx.x, gridDim.x);
   const int tn = t % ncols;
-  if (!find_tile<BM, BM == kBigRows>(off, E, R, t / ncols, e, r0, cnt)) return;
+  if (!find_tile<BM>(off, E, R, t / ncols, e, r0, cnt)) return;
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);
   cnt = __builtin_amdgcn_readfirstlane(cnt);
@@ -567,14 +554,8 @@ __global__ __launch_bounds__(kThreads, BM == 64 ? 2 : 1) void k_moe_gemm(
 // next, routed-row chunk fastest, so workgroups that share weight rows run side by side.
 // For the SiLU-gate form the 32 rows of group g are gate rows 16g..16g+15 and up rows
 // I + 16g..I + 16g + 15; D row n of lane m holds gate row n and up row n + 16 at i and i + 8.
-#ifndef SSN_SW_WPE
-#define SSN_SW_WPE 2
-#endif
 constexpr int kSwRows = 32, kSwM = 32;
-#ifndef SSN_SW_RING
-#define SSN_SW_RING 4
-#endif
-constexpr int kSwRing = SSN_SW_RING;
+constexpr int kSwRing = 4;
 __device__ __attribute__((aligned(16))) uint32_t g_sw_zero[16];   // 64 zero bytes
 
 template <int WF>
@@ -585,7 +566,7 @@ struct SwChunk {
 };
 
 template <int WF, int EPI, int KS, int NCH>
-__global__ __launch_bounds__(KS * 64) __attribute__((amdgpu_waves_per_eu(SSN_SW_WPE))) void k_moe_stream(
+__global__ __launch_bounds__(KS * 64) __attribute__((amdgpu_waves_per_eu(2))) void k_moe_stream(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -853,13 +834,12 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd
 template <int WF, int EPI, int BM>
 hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   constexpr int bytes = moe_lds_bytes<WF, BM>();
-  static_assert(bytes <= 160 * 1024 && (BM != 64 || 2 * bytes <= 160 * 1024), "LDS budget: 64-row tiles run at least two workgroups per CU");
+  static_assert(2 * bytes <= 160 * 1024, "LDS budget: 64-row tiles run at least two workgroups per CU");
   hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  // upper bound of the tile count: full 256-row tiles <= R / 256; remainders (< 256 rows per
-  // expert) in 64-row tiles <= R / 64 + min(E, R)
-  const long tiles = BM == kBigRows ? a.R / kBigRows : (a.R + BM - 1) / BM + (a.E < a.R ? a.E : a.R);
+  // upper bound of the tile count: R / BM + min(E, R) (each expert's last tile may be partial)
+  const long tiles = (a.R + BM - 1) / BM + (a.E < a.R ? a.E : a.R);
   if (tiles == 0) return hipSuccess;
   const int ntiles = EPI == kEpiSilu ? (int)((a.N / 2 + 127) / 128) : (int)((a.N + kBN - 1) / kBN);
   if (tiles * ntiles > 0x7fffffffL) return hipErrorInvalidValue;
@@ -871,10 +851,6 @@ hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
 
 template <int WF, int EPI>
 hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
-  if (kSplitBig) {
-    hipError_t e = launch_moe_gemm_t<WF, EPI, kBigRows>(a, s);
-    if (e != hipSuccess) return e;
-  }
   return launch_moe_gemm_t<WF, EPI, 64>(a, s);
 }
 

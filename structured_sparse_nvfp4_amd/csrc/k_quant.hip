@@ -28,16 +28,7 @@ __device__ __forceinline__ float load_w(const void* W, int w_bf16, size_t i) {
 // ---- amax over the tensor: one pass of one-shot blocks, each reading a contiguous run of
 // kThreads * kAmaxUnroll 16-byte pieces and writing its block maximum to a partial slot; the
 // scale kernel reduces the partials. No accumulator has to be cleared first.
-#ifndef SSN_AMAX_UNROLL
-#define SSN_AMAX_UNROLL 8
-#endif
-#ifndef SSN_AMAX_NT
-#define SSN_AMAX_NT 0
-#endif
-#ifndef SSN_AMAX_ITERS
-#define SSN_AMAX_ITERS 1
-#endif
-constexpr int kAmaxUnroll = SSN_AMAX_UNROLL, kAmaxIters = SSN_AMAX_ITERS;
+constexpr int kAmaxUnroll = 8, kAmaxIters = 1;
 constexpr size_t kAmaxPiece = (size_t)kThreads * kAmaxUnroll;   // 16-byte pieces per span; a block reads kAmaxIters spans
 
 __device__ __forceinline__ float absmax4(f32x4 v) {
@@ -62,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* W, int w_bf16, si
     for (int u = 0; u < kAmaxUnroll; ++u) {
       const size_t i = base + (size_t)u * kThreads;
       const u32x4* q = p + (i < n16 ? i : 0);                // piece 0 again past the end: harmless for a max
-      v[u] = SSN_AMAX_NT ? ld_nt(q) : *q;
+      v[u] = *q;
     }
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u)
@@ -189,15 +180,9 @@ __device__ __forceinline__ void quantize_block(const float (&w)[16], double st, 
 // conflicts. Chunks are visited from the end of W backwards, so the tail that the amax pass left
 // in the Infinity Cache is read first.
 constexpr int kQBlocks = 64;     // blocks per wave-chunk
-#ifndef SSN_Q_ITER
-#define SSN_Q_ITER 2
-#endif
-#ifndef SSN_P_ITER
-#define SSN_P_ITER 4
-#endif
 // chunks per wave: quantise (2 measured faster than 4 on 13824 x 5120 f32: 59 vs 63 us) and
 // the fused producer (4, with more arithmetic per block)
-constexpr int kQIter = SSN_Q_ITER, kPIter = SSN_P_ITER;
+constexpr int kQIter = 2, kPIter = 4;
 
 template <int BF16>
 __device__ __forceinline__ int q_swz(int b) {
@@ -430,14 +415,8 @@ __device__ __forceinline__ float prune_group(typename std::conditional<BF16 != 0
 // form runs a capped grid (kPruneAmaxGrid blocks) that strides over the tiles. Measured on
 // 13824 x 5120 f32: one group per thread 94 us without the maximum; with it, 4 groups per
 // thread on 2048 blocks 105 us (one block per tile: 69120 atomics, 795 us).
-#ifndef SSN_PRUNE_AMAX_UNROLL
-#define SSN_PRUNE_AMAX_UNROLL 4
-#endif
-#ifndef SSN_PRUNE_AMAX_GRID
-#define SSN_PRUNE_AMAX_GRID 2048
-#endif
-constexpr int kPruneAmaxUnroll = SSN_PRUNE_AMAX_UNROLL;
-constexpr unsigned kPruneAmaxGrid = SSN_PRUNE_AMAX_GRID;
+constexpr int kPruneAmaxUnroll = 4;
+constexpr unsigned kPruneAmaxGrid = 2048;
 template <int BF16, bool AMAX, int U>
 __global__ __launch_bounds__(kThreads) void k_prune(const void* W, size_t ngroups, void* out, unsigned* amax_bits) {
   using V = typename std::conditional<BF16 != 0, u32x2, u32x4>::type;

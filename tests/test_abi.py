@@ -136,3 +136,52 @@ def test_moe_validation_without_launch():
     assert L.moe_combine(n, 0, 0, n, n, 0, 4, 16, n, n) == ssn.SSN_OK
     assert L.moe_combine(p, 7, 4, p, p, 2, 2, 16, p, n) == ssn.SSN_E_DTYPE
     assert L.moe_ffn_workspace_bytes(4096, 10, 512, 512, 2048) > 4096 * 10 * 2048 * 4
+
+
+def _declared_params():
+    """name -> list of parameter declarations, parsed from the header."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(([^)]*)\)\s*;", text, flags=re.M):
+        params = [p.strip() for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = params
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    # every call (including those whose arguments differ from the problem statement's sketch:
+    # moe_route's row_of / bad_ids / workspace, the grouped product's x_rows / R / w_layout /
+    # algo_used, moe_combine's row_of, the whole-FFN call) is bound with the header's argument count
+    decl = _declared_params()
+    assert decl, "no declarations parsed"
+    for name, params in decl.items():
+        assert len(ssn._SIGS[name][0]) == len(params), name
+
+
+def test_algorithm_codes_match_the_header():
+    text = open(HEADER).read()
+    codes = {k: int(v) for k, v in re.findall(r"SSN_ALGO_(\w+)\s*=\s*(\d+)", text)}
+    assert codes == {"AUTO": 0, "VALU": 1, "MFMA": 2, "SMFMAC": 3, "GATHER": 4, "DECOMPRESS_MFMA": 5, "STREAM": 6}
+    for name, v in codes.items():
+        assert getattr(ssn, f"ALGO_{name}") == v
+
+
+def test_gather_algorithm_and_tile_k_limit():
+    L = ssn.lib()
+    p, n = _bad(), None
+    used = ctypes.c_int(-1)
+    # skip-and-gather is a 2:4 algorithm; the vector-ALU request on 2:4 weights reports it
+    assert L.gemm_nvfp4_dense(p, 2, 4, 64, p, p, p, p, 0, ssn.ALGO_GATHER, n, n) == ssn.SSN_E_ALGO
+    assert b"2:4 weights only" in L.ssn_last_error()
+    assert L.gemm_nvfp4_sp24(n, 0, 4, 64, n, n, n, n, n, 0, ssn.ALGO_GATHER, ctypes.byref(used), n) == ssn.SSN_OK
+    assert used.value == ssn.ALGO_GATHER
+    assert L.gemm_nvfp4_sp24(n, 0, 4, 64, n, n, n, n, n, 0, ssn.ALGO_VALU, ctypes.byref(used), n) == ssn.SSN_OK
+    assert used.value == ssn.ALGO_GATHER
+    # the 256 x 256 tiles address their activation panel with 32-bit offsets: K beyond 2^21 is
+    # refused for an explicit matrix-core choice at M > 16 (AUTO takes the vector-ALU kernels)
+    big_k = (1 << 21) + 64
+    assert L.gemm_nvfp4_dense(p, 17, 4, big_k, p, p, p, p, 0, ssn.ALGO_MFMA, n, n) == ssn.SSN_E_ALGO
+    assert b"K <= 2097152" in L.ssn_last_error()
+    for algo in (ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA):
+        assert L.gemm_nvfp4_sp24(p, 17, 4, big_k, p, p, p, p, p, 0, algo, n, n) == ssn.SSN_E_ALGO
+    assert L.gemm_nvfp4_dense(n, 0, 4, big_k, n, n, n, n, 0, ssn.ALGO_MFMA, n, n) == ssn.SSN_OK

@@ -12,7 +12,7 @@ from tests.gpu_util import assert_within_bound, dev, x_dev, y_host
 pytestmark = pytest.mark.gpu
 
 DENSE_ALGOS = [ssn.ALGO_AUTO, ssn.ALGO_MFMA, ssn.ALGO_VALU]
-SP24_ALGOS = [ssn.ALGO_AUTO, ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_VALU]
+SP24_ALGOS = [ssn.ALGO_AUTO, ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_GATHER, ssn.ALGO_VALU]
 
 
 def _problem(M, N, K, seed, prune):
@@ -30,7 +30,9 @@ DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 6
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
                (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
                (3, 17000, 512),                   # several row groups per decode workgroup
-               (3, 24608, 512), (8, 24608, 512)]  # >= 3 row groups per CU: the 80-register fold form
+               (3, 24608, 512), (8, 24608, 512),  # >= 3 row groups per CU: the 80-register fold form
+               # K % 256 == 0 but K % 512 != 0 (the decode slabs' partial last stage), M <= 8 and 9..16
+               (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
@@ -51,7 +53,9 @@ SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64
               (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
               # M <= 8, K % 512 == 0 (full-width-load decode kernel): ragged row groups, several
               # row groups per workgroup (N > 512 x 32), every M
-              (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024)]
+              (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024),
+              # K % 256 == 0 but K % 512 != 0: the slab kernels' partial last stage (8- and 16-wave forms)
+              (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768)]
 
 
 @pytest.mark.parametrize("M,N,K", SP24_CASES)
@@ -65,7 +69,8 @@ def test_sp24(M, N, K, algo):
     Y, B = gemm.gemm_sp24(x, vals, meta, s, st)
     g, used = ssn.gemm_nvfp4_sp24(x_dev(x), dev(vals), dev(meta), dev(s), dev(np.array([st], np.float32)),
                                   algo=algo)
-    assert used != ssn.ALGO_AUTO and (algo == ssn.ALGO_AUTO or used == algo)
+    want = ssn.ALGO_GATHER if algo == ssn.ALGO_VALU else algo     # the vector-ALU 2:4 form is skip-and-gather
+    assert used != ssn.ALGO_AUTO and (algo == ssn.ALGO_AUTO or used == want)
     assert_within_bound(y_host(g), Y, B, what=f"sp24 algo={used}")
 
 
@@ -100,7 +105,7 @@ def test_one_hot_rows_extract_weights_dense(algo):
 
 
 @pytest.mark.parametrize("rows", [16, 8])
-@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_VALU])
+@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_GATHER])
 def test_one_hot_rows_extract_weights_sp24(algo, rows):
     N, K = 48, 512
     ks_all = np.array([0, 1, 2, 3, 17, 63, 64, 100, 127, 128, 200, 255, 256, 301, 383, 510])
