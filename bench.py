@@ -1,40 +1,46 @@
 """Benchmark of the NVFP4 / 2:4 weight-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,prefill,head,moe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,head,moe]
 
-Prints ONE JSON line. ``value`` / ``ms_per_step`` / ``roofline`` / ``cpu_baseline`` describe the
-decode workload, where a step is one pass of the whole hot path over one batch of synthetic
-input (X [M, 5120] bf16 for M in {1, 4, 8}; W [13824, 5120] float32 ~ N(0, 0.02)):
+Prints ONE JSON line. The headline (``value``, ``ms_per_step``, ``roofline``) is the prefill
+product, the largest of the workloads: X bf16 [8192, 5120] ~ N(0, 1) times dense NVFP4 weights
+W [27648, 5120] (~ N(0, 0.02) with 1% of the entries x20 before quantisation), f32 accumulation,
+bf16 output, on the matrix cores (gemm_nvfp4_dense, 256 x 256 tiles). One step is one such
+product; ``value`` is its dense TFLOP/s (2 M N K per step over the host-clocked step time, K
+steps back to back between two synchronisations, inputs resident in HBM). ``roofline`` is
+that kernel's TFLOP/s from HIP events on its launch stream (average launch duration over the
+timed steps) against the published 2.5 PFLOP/s bf16 matrix peak. The 2:4 forms of the same
+product (sparse matrix cores, expanded-to-dense, skip-and-gather) are timed beside it with
+their speedup over dense.
 
-    sp24_prune(W) -> W_pruned, s_t           2:4 prune; s_t = fl32(amax|W| / 2688) taken on the way
-    nvfp4_quantize(W, s_t)                   dense NVFP4 weights
-    nvfp4_quantize(W_pruned, s_t)            2:4-pruned NVFP4 weights (same s_t: pruning keeps
-                                             every group's largest |w|)
-    sp24_check, sp24_compress                2:4 eligibility and compression
-    gemm_nvfp4_dense  at M = 1, 4, 8         decode GEMVs on dense weights
-    gemm_nvfp4_sp24   at M = 1, 4, 8         decode GEMVs on compressed weights
+Before any timing, every workload checks sampled outputs against the CPU oracle and stops if
+one is outside its bound. Each compute-bound workload records the GPU clock, power and
+temperature while it runs. Per kernel the bench reports the average over back-to-back launches
+(HIP events around the batch) and the median and minimum of at least 20 individually timed
+launches.
 
-Inputs are resident in HBM before timing starts. The K timed steps run call by call: all K
-prunes, then all K quantisations, and so on (every step has its own ring slot of outputs, so
-the work is the same as K steps in order); HIP events on the launch stream bracket each batch,
-which gives every kernel's average duration over back-to-back launches. The GEMVs read weight
-copies written many calls earlier (a ring larger than the 256 MB Infinity Cache), so they read
-HBM. ``value`` is the algorithmic bytes of the whole step divided by the step time;
-``roofline`` describes the kernel with the largest share of the step.
+``workloads`` adds: ``decode`` (the GEMVs at N = 13824, K = 5120, M = 1, 4, 8 on a ring of 16
+weight copies, and the weight-preparation calls on three rotating copies of W, each against
+8 TB/s and the measured copy bandwidth), ``square`` (4096^3, f32 out), ``head`` (N = 131072,
+K = 5120, M = 1, 8, 9), ``moe`` (512 experts, top-10 of Zipf(1.1), D = 2048, I = 512: 4096
+tokens stage by stage, and 1-32 tokens on the weight-streaming kernels). ``cpu_baseline`` is
+the oracle's dense prefill product on a sample of output columns, on the host cores.
 
-``workloads`` adds the other shapes, each timed the same way: the square (4096^3, f32 out) and
-prefill (8192 x 27648 x 5120, 1% outliers x20, bf16 out) products for dense MFMA, 2:4 SMFMAC
-and 2:4 expanded-to-dense MFMA, an output-head-shaped GEMV (N = 131072, K = 5120, M = 1, 8, 9),
-and the grouped-expert FFN (4096 tokens, 512 experts, top-10
-Zipf(1.1), D = 2048, I = 512) stage by stage, dense and 2:4, plus the same FFN at decode sizes
-(1, 4, 16, 32 tokens) against the full expert set, on the weight-streaming grouped kernels.
+    python bench.py --summarize KIND OUT DIR...
+
+turns rocprofv3 output directories into the text summaries kept under profiles/ (KIND: trace
+for --kernel-trace --stats runs; pmc for --pmc runs).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -42,12 +48,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "NVFP4 GEMM TFLOP/s & HBM GB/s, 2:4 vs dense, % of MI355X roofline"
-HBM_PEAK_GBPS = 8000.0          # MI355X published HBM3E bandwidth
-BF16_PEAK_TFLOPS = 2500.0       # MI355X published dense bf16 matrix peak
+HBM_PEAK_GBPS = 8000.0            # MI355X published HBM3E bandwidth
+BF16_PEAK_TFLOPS = 2500.0         # MI355X published dense bf16 matrix peak
 SPARSE_BF16_PEAK_TFLOPS = 5000.0  # the same with 2:4 structured sparsity (dense-equivalent)
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X published fp32 vector peak
-RING = 16                       # weight copies rotated by the GEMVs (16 x 40 MB > 2 x 256 MB cache)
+FP4_PEAK_TFLOPS = 10100.0         # MI355X published dense fp4 matrix peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak
+RING = 16                         # weight copies rotated by the GEMVs (16 x 40 MB > 2 x 256 MB cache)
+W_COPIES = 3                      # copies of the 283 MB f32 W rotated by the weight-preparation calls
+TRIALS = 20                       # individually timed launches per kernel (median, min)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "structured_sparse_nvfp4_amd", "csrc")
+PREFILL = dict(M=8192, N=27648, K=5120)
+DENSE_TILE_KERNEL = "k_gemm_mfma<0, 1, 256>"
 
 
 def parse():
@@ -55,10 +67,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workloads", default="decode,square,prefill,head,moe",
-                   help="comma list; decode is always run (it defines the step)")
+    p.add_argument("--workloads", default="decode,square,head,moe",
+                   help="comma list of workloads beside the prefill headline (which always runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=13824, help="weight rows of the oracle sample")
+    p.add_argument("--summarize", nargs="+", metavar="ARG",
+                   help="KIND OUT DIR...: summarise rocprofv3 output (KIND trace or pmc) into OUT")
     return p.parse_args()
 
 
@@ -92,26 +105,101 @@ def bytes_gemm(M, N, K, sparse, y_bytes):
     return (bytes_w_sp24(N, K) if sparse else bytes_w_dense(N, K)) + M * K * 2 + M * N * y_bytes
 
 
-class Batches:
-    """Event pairs around batches of back-to-back launches on the current stream (the stream
-    the prepared calls launch on)."""
+# ------------------------------------------------------------------------------------------
+class Timer:
+    """HIP events on the current stream (the stream the library's calls launch on): the average
+    over a batch of back-to-back launches, and individually timed launches."""
 
     def __init__(self, torch):
         self.torch = torch
-        self.ev = {}
+        self.batches = {}
+        self.trials = {}
 
-    def run(self, name, fns):
-        a = self.torch.cuda.Event(enable_timing=True)
-        b = self.torch.cuda.Event(enable_timing=True)
+    def _ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+    def batch(self, name, fns):
+        a, b = self._ev(), self._ev()
         a.record()
         for f in fns:
             f()
         b.record()
-        self.ev[name] = (a, b, len(fns))
+        self.batches[name] = (a, b, len(fns))
+
+    def each(self, name, fns):
+        evs = []
+        for f in fns:
+            a, b = self._ev(), self._ev()
+            a.record()
+            f()
+            b.record()
+            evs.append((a, b))
+        self.trials[name] = evs
 
     def us(self, name):
-        a, b, n = self.ev[name]
+        a, b, n = self.batches[name]
         return a.elapsed_time(b) * 1e3 / n
+
+    def stats(self, name):
+        ts = sorted(a.elapsed_time(b) * 1e3 for a, b in self.trials[name])
+        return {"median_us": round(statistics.median(ts), 2), "min_us": round(ts[0], 2), "trials": len(ts)}
+
+
+def gpu_state():
+    """Current GPU clock (sysfs), power and temperatures (amd-smi), best effort."""
+    out = {}
+    try:
+        for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+            for line in open(f):
+                if line.startswith("S:") or line.rstrip().endswith("*"):
+                    out["sclk_MHz"] = int(line.split(":")[1].strip().split("M")[0])
+                    break
+            if "sclk_MHz" in out:
+                break
+    except (OSError, ValueError, IndexError):
+        pass
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-t", "-c", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout)
+        g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+
+        def val(x):
+            return x.get("value") if isinstance(x, dict) else x
+        pw = g.get("power", {})
+        for key in ("socket_power", "current_socket_power", "average_socket_power"):
+            if key in pw and val(pw[key]) not in (None, "N/A"):
+                out["power_W"] = val(pw[key])
+                break
+        tp = g.get("temperature", {})
+        for key in ("hotspot", "edge", "mem"):
+            if key in tp and val(tp[key]) not in (None, "N/A"):
+                out[f"temp_{key}_C"] = val(tp[key])
+        ck = g.get("clock", {})
+        gfx = ck.get("gfx_0") or ck.get("gfx") or {}
+        if isinstance(gfx, dict) and "clk" in gfx:
+            out["gfx_clk_MHz"] = val(gfx["clk"])
+        mem = ck.get("mem_0") or ck.get("mem") or {}
+        if isinstance(mem, dict) and "clk" in mem:
+            out["mem_clk_MHz"] = val(mem["clk"])
+    except Exception as e:  # the tool's output format is not under this program's control
+        out["amd_smi_error"] = str(e)[:200]
+    return out
+
+
+def state_under_load(torch, fn, seconds=1.5):
+    """GPU state read while `fn` launches keep the GPU busy for about `seconds`, plus idle
+    readings before and after."""
+    before = gpu_state()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(); fn(); b.record(); b.synchronize()
+    n = max(1, int(seconds / max(a.elapsed_time(b) * 1e-3, 1e-5)))
+    for _ in range(n):
+        fn()
+    time.sleep(min(0.4, seconds / 3))
+    during = gpu_state()
+    torch.cuda.synchronize()
+    return {"before": before, "during": during, "after": gpu_state()}
 
 
 def hbm_probe(torch, ssn):
@@ -126,169 +214,84 @@ def hbm_probe(torch, ssn):
         dst.copy_(src)
         ssn.sp24_check(codes)
     torch.cuda.synchronize()
+    T = Timer(torch)
     res = {}
     for name, fn, nbytes in (("copy", lambda: dst.copy_(src), 2 * n), ("read", lambda: ssn.sp24_check(codes), n)):
-        ts = []
-        for _ in range(10):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(); fn(); b.record()
-            b.synchronize()
-            ts.append(a.elapsed_time(b))
-        ts.sort()
-        res[f"{name}_GBps"] = round(nbytes / (ts[len(ts) // 2] * 1e-3) / 1e9, 1)
+        T.each(name, [fn] * TRIALS)
+        torch.cuda.synchronize()
+        res[f"{name}_GBps"] = round(nbytes / (T.stats(name)["median_us"] * 1e-6) / 1e9, 1)
     del src, dst, codes
     torch.cuda.empty_cache()
     return res
 
 
-def traffic_for(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary, only if the kernel's
-    source is unchanged since the counters were taken (else None)."""
+def _source_hash(kernel_file):
+    """SHA-256 of a kernel's source file and the headers of the kernel directory it includes."""
+    h = hashlib.sha256()
+    for f in [os.path.join(CSRC, kernel_file)] + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(key):
+    """HBM bytes per launch from the committed counter summary, only while the kernel's sources
+    are unchanged since the counters were taken (else None)."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f).get(kernel)
-        if not t:
+            t = json.load(f).get(key)
+        if not t or _source_hash(t["source"]) != t["source_sha256"]:
             return None
-        with open(os.path.join(ROOT, t["source"]), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() != t["source_sha256"]:
-                return None
         return int(t["fetch_bytes"] + t["write_bytes"])
     except (OSError, KeyError, ValueError):
         return None
 
 
+def _bw(b, us, copy_gbps):
+    gbps = b / (us * 1e-6) / 1e9
+    return {"alg_bytes": b, "GBps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "copy_frac": round(gbps / copy_gbps, 4) if copy_gbps else None}
+
+
 # ------------------------------------------------------------------------------------------
-def run_decode(args, torch, ssn, synth):
-    N, K, Ms = 13824, 5120, (1, 4, 8)
-    dev = "cuda"
-    x = synth.activations(max(Ms), K)
-    w = synth.weights(N, K)
-    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).to(dev)
-    W = torch.from_numpy(w).to(dev)
-    u8 = dict(dtype=torch.uint8, device=dev)
-    wps = [torch.empty_like(W) for _ in range(2)]   # pruned copies, alternating
-    dense = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8),
-                  ts=torch.empty(1, dtype=torch.float32, device=dev)) for _ in range(RING)]
-    sparse = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8),
-                   ts=torch.empty(1, dtype=torch.float32, device=dev), vals=torch.empty((N, K // 4), **u8),
-                   meta=torch.empty((N, K // 8), **u8), bad=torch.empty(1, dtype=torch.int64, device=dev),
-                   first=torch.empty(1, dtype=torch.int64, device=dev)) for _ in range(RING)]
-    ts_w = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(RING)]   # s_t from the prune
-    Yd = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
-    Ys = {M: torch.empty((M, N), dtype=torch.float32, device=dev) for M in Ms}
-    Xm = {M: X[:M].contiguous() for M in Ms}
-    names = ["prune", "quantize", "quantize_pruned", "check", "compress"] + \
-            [f"gemv_dense_M{M}" for M in Ms] + [f"gemv_sp24_M{M}" for M in Ms]
-    # timed beside the step, not part of it: the fused producer, and the 2:4 GEMVs in the plain
-    # skip-and-gather form (vector ALU) for comparison with the SMFMAC ones
-    extra = ["producer_fused"] + [f"gemv_sp24_gather_M{M}" for M in Ms]
-    prod = [dict(vals=torch.empty((N, K // 4), **u8), meta=torch.empty((N, K // 8), **u8),
-                 scales=torch.empty((N, K // 16), **u8), ts=torch.empty(1, dtype=torch.float32, device=dev),
-                 bad=torch.empty(1, dtype=torch.int64, device=dev)) for _ in range(2)]
-    calls = {n: [] for n in names + extra}
-    used = {}
-    for j in range(RING):
-        d, sp, wp = dense[j], sparse[j], wps[j % 2]
-        rd, rs = dense[(j + RING // 2) % RING], sparse[(j + RING // 2) % RING]
-        calls["prune"].append(ssn.sp24_prune(W, out=wp, tensor_scale_out=ts_w[j], prepare=True)[0])
-        calls["quantize"].append(ssn.nvfp4_quantize(W, tensor_scale_in=ts_w[j], codes=d["codes"], scales=d["scales"],
-                                                    tensor_scale_out=d["ts"], prepare=True)[0])
-        calls["quantize_pruned"].append(ssn.nvfp4_quantize(wp, tensor_scale_in=ts_w[j], codes=sp["codes"],
-                                                           scales=sp["scales"], tensor_scale_out=sp["ts"],
-                                                           prepare=True)[0])
-        calls["check"].append(ssn.sp24_check(sp["codes"], bad_groups=sp["bad"], first_bad=sp["first"],
-                                             prepare=True)[0])
-        calls["compress"].append(ssn.sp24_compress(sp["codes"], vals=sp["vals"], meta=sp["meta"],
-                                                   bad_groups=sp["bad"], prepare=True)[0])
-        pf = prod[j % 2]
-        calls["producer_fused"].append(ssn.nvfp4_sp24_produce(W, vals=pf["vals"], meta=pf["meta"], scales=pf["scales"],
-                                                              tensor_scale_out=pf["ts"], bad_groups=pf["bad"],
-                                                              prepare=True)[0])
-        for M in Ms:
-            p, (_, u) = ssn.gemm_nvfp4_dense(Xm[M], rd["codes"], rd["scales"], rd["ts"], Y=Yd[M], prepare=True)
-            calls[f"gemv_dense_M{M}"].append(p)
-            used[f"gemv_dense_M{M}"] = u
-            p, (_, u) = ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"], Y=Ys[M],
-                                            prepare=True)
-            calls[f"gemv_sp24_M{M}"].append(p)
-            used[f"gemv_sp24_M{M}"] = u
-            p, _ = ssn.gemm_nvfp4_sp24(Xm[M], rs["vals"], rs["meta"], rs["scales"], rs["ts"], Y=Ys[M],
-                                       algo=ssn.ALGO_GATHER, prepare=True)
-            calls[f"gemv_sp24_gather_M{M}"].append(p)
-    B = Batches(torch)
+# parity before timing
+class ParityError(AssertionError):
+    pass
 
-    def steps(count):
-        # `count` steps, call by call; step i uses ring slot i % RING
-        for n in names:
-            B.run(n, [calls[n][i % RING] for i in range(count)])
 
-    steps(RING)                        # every ring slot holds valid weights
-    torch.cuda.synchronize()
-    steps(args.warmup)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    steps(args.steps)
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    for n in extra:
-        B.run(n, [calls[n][i % RING] for i in range(2)])
-        torch.cuda.synchronize()
-        B.run(n, [calls[n][i % RING] for i in range(args.steps)])
-    torch.cuda.synchronize()
+def _assert_bound(got, ref, base, out, what):
+    from oracle import gemm
+    import numpy as np
+    tol = gemm.bound(base, ref, out)
+    err = np.abs(got - ref)
+    if not np.all(err <= tol):
+        i = tuple(np.argwhere(~(err <= tol))[0])
+        raise ParityError(f"{what}: outside the parity bound at {i}: gpu={got[i]!r} oracle={ref[i]!r} tol={tol[i]!r}")
 
-    kb = {"quantize": bytes_quantize(N, K), "prune": bytes_prune(N, K), "quantize_pruned": bytes_quantize(N, K),
-          "check": bytes_check(N, K), "compress": bytes_compress(N, K)}
-    for M in Ms:
-        kb[f"gemv_dense_M{M}"] = bytes_gemm(M, N, K, False, 4)
-        kb[f"gemv_sp24_M{M}"] = bytes_gemm(M, N, K, True, 4)
-    kernels = {}
-    for name, b in kb.items():
-        us = B.us(name)
-        e = {"us": round(us, 2), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
-             "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
-        if name.startswith("gemv"):
-            M = int(name.split("_M")[1])
-            flops = 2 * M * N * K
-            e["tflops_dense_equiv"] = round(flops / (us * 1e-6) / 1e12, 3)
-            if "sp24" in name:
-                e["tflops_actual"] = round(flops / 2 / (us * 1e-6) / 1e12, 3)
-            e["algo"] = ssn.ALGO_NAMES.get(used[name].value, "?")
-        kernels[name] = e
-    for M in Ms:
-        kernels[f"gemv_sp24_M{M}"]["speedup_vs_dense"] = round(
-            kernels[f"gemv_dense_M{M}"]["us"] / kernels[f"gemv_sp24_M{M}"]["us"], 3)
-    step_bytes = sum(kb.values())
-    pb = N * K * 4 + N * K // 4 + N * K // 8 + N * K // 16 + 4
-    pus = B.us("producer_fused")
-    chain = sum(kernels[n]["us"] for n in ("prune", "quantize_pruned", "check", "compress"))
-    extras = {"producer_fused": {
-        "us": round(pus, 2), "alg_bytes": pb, "GBps": round(pb / (pus * 1e-6) / 1e9, 1),
-        "hbm_frac": round(pb / (pus * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-        "unfused_chain_us": round(chain, 2), "speedup_vs_unfused_chain": round(chain / pus, 3),
-        "note": "nvfp4_sp24_produce: prune -> quantize -> check -> compress of W in one pass (bit-identical); "
-                "not part of the step"}}
-    for M in Ms:
-        n = f"gemv_sp24_gather_M{M}"
-        us = B.us(n)
-        b = bytes_gemm(M, N, K, True, 4)
-        extras[n] = {"us": round(us, 2), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                     "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4), "algo": "valu",
-                     "smfmac_speedup_vs_gather": round(us / kernels[f"gemv_sp24_M{M}"]["us"], 3),
-                     "note": "2:4 GEMV in the skip-and-gather form (x gathered at the stored positions, "
-                             "vector ALU); not part of the step"}
-    dominant = max(kernels, key=lambda k: kernels[k]["us"])
-    dk = kernels[dominant]
-    roof = {"kernel": dominant, "bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(dk["GBps"] / HBM_PEAK_GBPS, 4), "traffic": traffic_for(dominant)}
-    result = {
-        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1), "unit": "GB/s", "ms_per_step": round(ms_step, 4),
-        "dtype": "bf16",
-        "config": {"workload": "decode: X bf16 [M in {1,4,8}, 5120] ~N(0,1); W f32 [13824, 5120] ~N(0,0.02); "
-                               "NVFP4 dense and 2:4-pruned+compressed; quantize, prune, check, compress, 6 GEMVs",
-                   "M": list(Ms), "N": N, "K": K, "weight_ring": RING, "step_alg_bytes": step_bytes},
-        "roofline": roof, "kernels": kernels, "extra_kernels": extras,
-    }
-    return result, (w, x)
+
+def _rows_of(t, rows, cols=None):
+    import numpy as np
+    torch = sys.modules["torch"]
+    sel = t[torch.from_numpy(np.asarray(rows)).to(t.device)]
+    if cols is not None:
+        sel = sel[:, torch.from_numpy(np.asarray(cols)).to(t.device)]
+    return sel.float().cpu().numpy().astype(np.float64)
+
+
+def check_product(x, w, st, ms, ns, y_dense, y_sp24, out, what):
+    """Sampled outputs of the dense and 2:4 products against the oracle (weights of the sampled
+    columns quantised by the oracle with the tensor scale of the whole W). y_dense / y_sp24 hold
+    the full outputs (sampled here at ms x ns)."""
+    from oracle import gemm, quant, sp24
+    c, s, _ = quant.quantize(w[ns], tensor_scale_in=st)
+    Y, B = gemm.gemm_dense(x[ms], c, s, st)
+    _assert_bound(_rows_of(y_dense, ms, ns), Y, B, out, f"{what} dense")
+    if y_sp24:
+        pc, ps, _ = quant.quantize(sp24.prune24(w[ns]), tensor_scale_in=st)
+        v, m, nb = sp24.compress(pc)
+        Y, B = gemm.gemm_sp24(x[ms], v, m, ps, st)
+        for name, y in y_sp24.items():
+            _assert_bound(_rows_of(y, ms, ns), Y, B, out, f"{what} 2:4 {name}")
 
 
 # ------------------------------------------------------------------------------------------
@@ -302,44 +305,78 @@ def _gpu_weights(ssn, W):
     return (codes, scales, ts), (vals, meta, ps, pts)
 
 
-def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
+def _gemm_variants(ssn):
+    return [("dense_mfma", False, ssn.ALGO_MFMA), ("sp24_smfmac", True, ssn.ALGO_SMFMAC),
+            ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA), ("sp24_gather_valu", True, ssn.ALGO_GATHER)]
+
+
+def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, args, headline=False):
+    """Dense and 2:4 products of one shape. With ``headline`` the dense product is also timed as
+    the bench's steps (K steps after W warm-up steps, host clock and HIP events)."""
+    from oracle import quant
     x = synth.activations(M, K)
     w = synth.weight_rows_with_outliers(N, K, 0, N, 0.01, 20.0) if outliers else synth.weights(N, K)
+    st = quant.tensor_scale(w)
     X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
     W = torch.from_numpy(w).cuda()
-    del w, x
     dn, sp = _gpu_weights(ssn, W)
     del W
-    Y = torch.empty((M, N), dtype=y_dtype, device="cuda")
-    yb = 2 if y_dtype == torch.bfloat16 else 4
-    # the skip-and-gather form (vector ALU, x gathered at the stored positions) is the plain
-    # comparison point; it is far slower (about a second per prefill call), so it runs one or
-    # two timed calls after as many warm-up calls
-    variants = [("dense_mfma", False, ssn.ALGO_MFMA), ("sp24_smfmac", True, ssn.ALGO_SMFMAC),
-                ("sp24_decompress_mfma", True, ssn.ALGO_DECOMPRESS_MFMA), ("sp24_gather_valu", True, ssn.ALGO_GATHER)]
-    vreps = {"sp24_gather_valu": min(reps, 2 if 2.0 * M * N * K < 1e12 else 1)}
-    B = Batches(torch)
-    preps = {}
+    torch.cuda.synchronize()
+    if float(dn[2].item()) != float(st) or float(sp[3].item()) != float(st):
+        raise ParityError("tensor scale differs from the oracle's")
+    out = "bf16" if y_dtype == torch.bfloat16 else "f32"
+    yb = 2 if out == "bf16" else 4
+    variants = _gemm_variants(ssn)
+    Ys = {v: torch.empty((M, N), dtype=y_dtype, device="cuda") for v, _, _ in variants}
+    preps, used = {}, {}
     for vname, sparse, algo in variants:
         if sparse:
-            p, _ = ssn.gemm_nvfp4_sp24(X, sp[0], sp[1], sp[2], sp[3], y_dtype=y_dtype, algo=algo, Y=Y, prepare=True)
+            p, (_, u) = ssn.gemm_nvfp4_sp24(X, sp[0], sp[1], sp[2], sp[3], y_dtype=y_dtype, algo=algo, Y=Ys[vname],
+                                            prepare=True)
         else:
-            p, _ = ssn.gemm_nvfp4_dense(X, dn[0], dn[1], dn[2], y_dtype=y_dtype, algo=algo, Y=Y, prepare=True)
-        preps[vname] = p
-    for vname in preps:                      # warm-up
-        B.run(vname, [preps[vname]] * min(2, vreps.get(vname, 2)))
+            p, (_, u) = ssn.gemm_nvfp4_dense(X, dn[0], dn[1], dn[2], y_dtype=y_dtype, algo=algo, Y=Ys[vname],
+                                             prepare=True)
+        preps[vname], used[vname] = p, u
+    for vname in preps:                       # one call each, then the parity check on their outputs
+        preps[vname]()
     torch.cuda.synchronize()
-    for vname in preps:
-        B.run(vname, [preps[vname]] * vreps.get(vname, reps))
-    torch.cuda.synchronize()
+    ms = sorted({0, 1, 255, 256, M // 2 + 3, M - 1})
+    ns = sorted({0, 1, 255, 256, N // 2 + 5, N - 1})
+    check_product(x, w, st, ms, ns, Ys["dense_mfma"], {v: Ys[v] for v, s_, _ in variants if s_}, out,
+                  f"{M}x{N}x{K}")
+    del w
     flops = 2.0 * M * N * K
-    out = {"shape": {"M": M, "N": N, "K": K, "y": "bf16" if yb == 2 else "f32", "outliers": outliers},
-           "flops_dense_equiv": flops}
+    res = {"shape": {"M": M, "N": N, "K": K, "y": out, "outliers": outliers}, "flops_dense_equiv": flops,
+           "parity": "sampled outputs of every variant within the oracle's bound"}
+    T = Timer(torch)
+    step = None
+    if headline:
+        dense = preps["dense_mfma"]
+        for _ in range(args.warmup):
+            dense()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        T.batch("steps", [dense] * args.steps)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        step = {"ms_per_step": ms_step, "event_us": T.us("steps")}
+    # one timed batch and TRIALS individually timed calls per variant; the skip-and-gather form
+    # takes about a second per prefill call, so it gets fewer
+    slow = {"sp24_gather_valu": 3 if flops > 1e12 else 5}
+    for vname in preps:
+        reps = slow.get(vname, TRIALS)
+        T.batch(vname + "_warm", [preps[vname]] * min(2, reps))
+        torch.cuda.synchronize()
+        T.batch(vname, [preps[vname]] * reps)
+        T.each(vname, [preps[vname]] * reps)
+        torch.cuda.synchronize()
+    res["gpu_state"] = state_under_load(torch, preps["dense_mfma"])
     for vname, sparse, algo in variants:
-        us = B.us(vname)
-        b = bytes_gemm(M, N, K, sparse, yb)
-        e = {"us": round(us, 1), "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
-             "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1)}
+        us = T.us(vname)
+        e = {"us": round(us, 1), **T.stats(vname), "algo": ssn.ALGO_NAMES.get(used[vname].value, "?"),
+             "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
+             "alg_bytes": bytes_gemm(M, N, K, sparse, yb),
+             "GBps": round(bytes_gemm(M, N, K, sparse, yb) / (us * 1e-6) / 1e9, 1)}
         if sparse:
             e["tflops_actual"] = round(flops / 2 / (us * 1e-6) / 1e12, 1)
             e["mfma_frac_actual_vs_bf16_peak"] = round(e["tflops_actual"] / BF16_PEAK_TFLOPS, 4)
@@ -347,57 +384,200 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, reps):
                 e["mfma_frac_vs_sparse_peak"] = round(e["tflops_dense_equiv"] / SPARSE_BF16_PEAK_TFLOPS, 4)
             if algo == ssn.ALGO_GATHER:
                 e["valu_frac_actual_vs_fp32_peak"] = round(e["tflops_actual"] / FP32_VECTOR_PEAK_TFLOPS, 4)
-                e["timed_calls"] = vreps["sp24_gather_valu"]
         else:
             e["mfma_frac"] = round(e["tflops_dense_equiv"] / BF16_PEAK_TFLOPS, 4)
-        out[vname] = e
+        res[vname] = e
     for vname in ("sp24_smfmac", "sp24_decompress_mfma", "sp24_gather_valu"):
-        out[vname]["speedup_vs_dense"] = round(out["dense_mfma"]["us"] / out[vname]["us"], 3)
-    del X, Y, dn, sp, preps
+        res[vname]["speedup_vs_dense"] = round(res["dense_mfma"]["us"] / res[vname]["us"], 3)
+    del X, Ys, dn, sp, preps
     torch.cuda.empty_cache()
-    return out
+    return res, step, x
 
 
+# ------------------------------------------------------------------------------------------
+def run_decode(torch, ssn, synth, copy_gbps):
+    """Decode GEMVs (N = 13824, K = 5120, M = 1, 4, 8) on a ring of weight copies, and the weight
+    preparation calls on rotating copies of W (each call reads a W last read two calls before,
+    with 566 MB read in between, more than the 256 MB Infinity Cache)."""
+    import numpy as np
+    from oracle import gemm, quant, sp24
+    N, K, Ms = 13824, 5120, (1, 4, 8)
+    x = synth.activations(max(Ms), K)
+    w = synth.weights(N, K)
+    st = quant.tensor_scale(w)
+    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    Ws = [torch.from_numpy(w).cuda()]
+    for _ in range(W_COPIES - 1):
+        Ws.append(Ws[0].clone())
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    i64 = dict(dtype=torch.int64, device="cuda")
+    dense = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8), ts=torch.empty(1, **f32))
+             for _ in range(RING)]
+    sparse = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8),
+                   ts=torch.empty(1, **f32), vals=torch.empty((N, K // 4), **u8), meta=torch.empty((N, K // 8), **u8),
+                   bad=torch.empty(1, **i64), first=torch.empty(1, **i64)) for _ in range(RING)]
+    wps = [torch.empty_like(Ws[0]) for _ in range(W_COPIES)]
+    ts_w = [torch.empty(1, **f32) for _ in range(W_COPIES)]
+    # weights of every ring slot: dense from W, 2:4 from the pruned W (GPU calls, checked below)
+    for j in range(RING):
+        ssn.sp24_prune(Ws[0], out=wps[0], tensor_scale_out=ts_w[0])
+        ssn.nvfp4_quantize(Ws[0], codes=dense[j]["codes"], scales=dense[j]["scales"], tensor_scale_out=dense[j]["ts"])
+        ssn.nvfp4_quantize(wps[0], tensor_scale_in=ts_w[0], codes=sparse[j]["codes"], scales=sparse[j]["scales"],
+                           tensor_scale_out=sparse[j]["ts"])
+        ssn.sp24_compress(sparse[j]["codes"], vals=sparse[j]["vals"], meta=sparse[j]["meta"], bad_groups=sparse[j]["bad"])
+    Y = {(M, f): torch.empty((M, N), **f32) for M in Ms for f in ("dense", "sp24", "gather")}
+    Xm = {M: X[:M].contiguous() for M in Ms}
+    calls, used = {}, {}
+    for j in range(RING):
+        d, s_ = dense[j], sparse[j]
+        for M in Ms:
+            p, (_, u) = ssn.gemm_nvfp4_dense(Xm[M], d["codes"], d["scales"], d["ts"], Y=Y[(M, "dense")], prepare=True)
+            calls.setdefault(f"gemv_dense_M{M}", []).append(p)
+            used[f"gemv_dense_M{M}"] = u
+            p, (_, u) = ssn.gemm_nvfp4_sp24(Xm[M], s_["vals"], s_["meta"], s_["scales"], s_["ts"], Y=Y[(M, "sp24")],
+                                            prepare=True)
+            calls.setdefault(f"gemv_sp24_M{M}", []).append(p)
+            used[f"gemv_sp24_M{M}"] = u
+            p, (_, u) = ssn.gemm_nvfp4_sp24(Xm[M], s_["vals"], s_["meta"], s_["scales"], s_["ts"], Y=Y[(M, "gather")],
+                                            algo=ssn.ALGO_GATHER, prepare=True)
+            calls.setdefault(f"gemv_sp24_gather_M{M}", []).append(p)
+            used[f"gemv_sp24_gather_M{M}"] = u
+        calls.setdefault("check", []).append(ssn.sp24_check(s_["codes"], bad_groups=s_["bad"], first_bad=s_["first"],
+                                                            prepare=True)[0])
+        calls.setdefault("compress", []).append(ssn.sp24_compress(s_["codes"], vals=s_["vals"], meta=s_["meta"],
+                                                                  bad_groups=s_["bad"], prepare=True)[0])
+    prod = [dict(vals=torch.empty((N, K // 4), **u8), meta=torch.empty((N, K // 8), **u8),
+                 scales=torch.empty((N, K // 16), **u8), ts=torch.empty(1, **f32), bad=torch.empty(1, **i64))
+            for _ in range(2)]
+    qd = [dict(codes=torch.empty((N, K // 2), **u8), scales=torch.empty((N, K // 16), **u8), ts=torch.empty(1, **f32))
+          for _ in range(2)]
+    for j in range(W_COPIES):
+        Wj, wp, q, pf = Ws[j], wps[j], qd[j % 2], prod[j % 2]
+        calls.setdefault("prune", []).append(ssn.sp24_prune(Wj, out=wp, tensor_scale_out=ts_w[j], prepare=True)[0])
+        calls.setdefault("quantize", []).append(ssn.nvfp4_quantize(Wj, codes=q["codes"], scales=q["scales"],
+                                                                   tensor_scale_out=q["ts"], prepare=True)[0])
+        calls.setdefault("quantize_given_scale", []).append(ssn.nvfp4_quantize(
+            Wj, tensor_scale_in=ts_w[j], codes=q["codes"], scales=q["scales"], tensor_scale_out=q["ts"], prepare=True)[0])
+        calls.setdefault("producer_fused", []).append(ssn.nvfp4_sp24_produce(
+            Wj, vals=pf["vals"], meta=pf["meta"], scales=pf["scales"], tensor_scale_out=pf["ts"], bad_groups=pf["bad"],
+            prepare=True)[0])
+    for n in calls:                          # every call once, then parity on what they wrote
+        for c in calls[n]:
+            c()
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 255, 6911, 13823])
+    ri = torch.from_numpy(rows).cuda()
+    c, s, _ = quant.quantize(w[rows], tensor_scale_in=st)
+    for q in (dense[0], qd[0]):
+        if not (np.array_equal(q["codes"][ri].cpu().numpy(), c) and np.array_equal(q["scales"][ri].cpu().numpy(), s)):
+            raise ParityError("decode: quantised weights differ from the oracle's")
+    pc, ps, _ = quant.quantize(sp24.prune24(w[rows]), tensor_scale_in=st)
+    v, m, _ = sp24.compress(pc)
+    for q in (sparse[0], prod[0]):
+        if not (np.array_equal(q["vals"][ri].cpu().numpy(), v) and np.array_equal(q["meta"][ri].cpu().numpy(), m)
+                and np.array_equal(q["scales"][ri].cpu().numpy(), ps)):
+            raise ParityError("decode: 2:4 compressed weights differ from the oracle's")
+    if int(sparse[0]["bad"].item()) != 0 or int(prod[0]["bad"].item()) != 0:
+        raise ParityError("decode: pruned weights fail the 2:4 check")
+    for M in Ms:
+        Yr, Br = gemm.gemm_dense(x[:M], c, s, st)
+        _assert_bound(_rows_of(Y[(M, "dense")].t(), rows).T, Yr, Br, "f32", f"decode dense M={M}")
+        Yr, Br = gemm.gemm_sp24(x[:M], v, m, ps, st)
+        for f in ("sp24", "gather"):
+            _assert_bound(_rows_of(Y[(M, f)].t(), rows).T, Yr, Br, "f32", f"decode {f} M={M}")
+    T = Timer(torch)
+    for n, cs in calls.items():
+        reps = max(TRIALS, 2 * len(cs))
+        seq = [cs[i % len(cs)] for i in range(reps)]
+        T.batch(n, seq)
+        T.each(n, seq)
+        torch.cuda.synchronize()
+    kb = {"prune": bytes_prune(N, K), "quantize": bytes_quantize(N, K), "quantize_given_scale": bytes_quantize(N, K),
+          "check": bytes_check(N, K), "compress": bytes_compress(N, K),
+          "producer_fused": N * K * 4 + N * K // 4 + N * K // 8 + N * K // 16 + 4}
+    for M in Ms:
+        kb[f"gemv_dense_M{M}"] = bytes_gemm(M, N, K, False, 4)
+        kb[f"gemv_sp24_M{M}"] = bytes_gemm(M, N, K, True, 4)
+        kb[f"gemv_sp24_gather_M{M}"] = bytes_gemm(M, N, K, True, 4)
+    kernels = {}
+    for name, b in kb.items():
+        us = T.us(name)
+        e = {"us": round(us, 2), **T.stats(name), **_bw(b, us, copy_gbps)}
+        if name.startswith("gemv"):
+            M = int(name.split("_M")[1])
+            e["tflops_dense_equiv"] = round(2 * M * N * K / (us * 1e-6) / 1e12, 3)
+            e["algo"] = ssn.ALGO_NAMES.get(used[name].value, "?")
+        kernels[name] = e
+    for M in Ms:
+        for f in ("sp24", "sp24_gather"):
+            kernels[f"gemv_{f}_M{M}"]["speedup_vs_dense"] = round(
+                kernels[f"gemv_dense_M{M}"]["us"] / kernels[f"gemv_{f}_M{M}"]["us"], 3)
+    kernels["producer_fused"]["unfused_chain_us"] = round(
+        sum(kernels[n]["us"] for n in ("prune", "quantize_given_scale", "check", "compress")), 2)
+    res = {"shape": {"N": N, "K": K, "M": list(Ms)}, "weight_ring": RING, "w_copies": W_COPIES,
+           "parity": "quantised and compressed weights bit-exact and GEMV outputs within bound on sampled rows",
+           "kernels": kernels,
+           "note": "prune, quantize (own amax pass), quantize_given_scale (the prune's s_t), check, compress and the "
+                   "fused producer are weight preparation; the GEMVs are the decode hot path"}
+    del Ws, wps, dense, sparse, prod, qd, calls, Y
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------------
 HEAD_N, HEAD_K, HEAD_MS = 131072, 5120, (1, 8, 9)
 
 
-def run_head(torch, ssn, synth, reps):
+def run_head(torch, ssn, synth, copy_gbps):
     """Output-head-shaped GEMV (vocabulary-sized N = 131072, K = 5120; M = 1, and 8 and 9 rows as
     in speculative verification): weights of 377 MB (dense) / 294 MB (2:4), larger than the
     Infinity Cache; two weight copies alternate so every call reads HBM."""
+    import numpy as np
+    from oracle import quant
     N, K = HEAD_N, HEAD_K
     x = synth.activations(max(HEAD_MS), K)
     X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
-    W = torch.from_numpy(synth.weights(N, K)).cuda()
+    w = synth.weights(N, K)
+    st = quant.tensor_scale(w)
+    cols = np.array([0, 65537, N - 1])
+    ws = w[cols].copy()
+    W = torch.from_numpy(w).cuda()
+    del w
     dn, sp = _gpu_weights(ssn, W)
     del W
     torch.cuda.empty_cache()
     dns = [dn, tuple(t.clone() for t in dn)]
     sps = [sp, tuple(t.clone() for t in sp)]
-    out = {"shape": {"N": N, "K": K, "M": list(HEAD_MS), "y": "f32"}, "weight_copies": 2}
+    out = {"shape": {"N": N, "K": K, "M": list(HEAD_MS), "y": "f32"}, "weight_copies": 2,
+           "parity": "outputs of three weight rows (columns 0, 65537, 131071) within the oracle's bound"}
+    dc = torch.from_numpy(cols).cuda()
     for M in HEAD_MS:
         Xm = X[:M].contiguous()
-        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        Yd = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        Ys = torch.empty((M, N), dtype=torch.float32, device="cuda")
         pd, ps, used = [], [], {}
         for d, s_ in zip(dns, sps):
-            p, (_, ud) = ssn.gemm_nvfp4_dense(Xm, d[0], d[1], d[2], Y=Y, prepare=True)
+            p, (_, ud) = ssn.gemm_nvfp4_dense(Xm, d[0], d[1], d[2], Y=Yd, prepare=True)
             pd.append(p)
-            p, (_, us_) = ssn.gemm_nvfp4_sp24(Xm, s_[0], s_[1], s_[2], s_[3], Y=Y, prepare=True)
+            p, (_, us_) = ssn.gemm_nvfp4_sp24(Xm, s_[0], s_[1], s_[2], s_[3], Y=Ys, prepare=True)
             ps.append(p)
             used = {"dense": ud, "sp24": us_}
-        B = Batches(torch)
-        for n, calls in (("dense", pd), ("sp24", ps)):
-            B.run(n, calls)
+        pd[0](); ps[0]()
         torch.cuda.synchronize()
-        for n, calls in (("dense", pd), ("sp24", ps)):
-            B.run(n, calls * reps)
-        torch.cuda.synchronize()
+        check_product(x[:M], ws, st, np.arange(M), np.arange(3), Yd[:, dc].contiguous(),
+                      {"smfmac": Ys[:, dc].contiguous()}, "f32", f"head M={M}")
+        T = Timer(torch)
+        for n, cs in (("dense", pd), ("sp24", ps)):
+            T.batch(n + "_warm", cs)
+            torch.cuda.synchronize()
+            T.batch(n, cs * (TRIALS // 2))
+            T.each(n, cs * (TRIALS // 2))
+            torch.cuda.synchronize()
         e = {}
         for n in ("dense", "sp24"):
-            us = B.us(n)
-            b = bytes_gemm(M, N, K, n == "sp24", 4)
-            e[n] = {"us": round(us, 1), "alg_bytes": b, "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                    "hbm_frac": round(b / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            us = T.us(n)
+            e[n] = {"us": round(us, 1), **T.stats(n), **_bw(bytes_gemm(M, N, K, n == "sp24", 4), us, copy_gbps),
                     "tflops_dense_equiv": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 2),
                     "algo": ssn.ALGO_NAMES.get(used[n].value, "?")}
         e["sp24"]["speedup_vs_dense"] = round(e["dense"]["us"] / e["sp24"]["us"], 3)
@@ -407,23 +587,38 @@ def run_head(torch, ssn, synth, reps):
     return out
 
 
-def run_moe(torch, ssn, synth, reps):
+# ------------------------------------------------------------------------------------------
+def _synth_experts(gen, E, rows, cols):
+    """All experts' float32 weights from the seeded generators, drawn on host threads."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    out = np.empty((E, rows, cols), np.float32)
+
+    def one(e):
+        out[e] = gen(e)
+    with ThreadPoolExecutor(max_workers=min(16, len(os.sched_getaffinity(0)))) as ex:
+        list(ex.map(one, range(E)))
+    return out
+
+
+def run_moe(torch, ssn, synth, copy_gbps):
+    import numpy as np
+    from oracle import moe, quant, sp24
     T, E, k, D, I = 4096, 512, 10, 2048, 512
     ids, wts = synth.routing(T, E, k, 1.1)
     x = synth.activations(T, D)
     X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
     dids, dw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
-    g = torch.Generator(device="cuda")
-    g.manual_seed(0)
+    up_f = _synth_experts(lambda e: synth.expert_up(e, I, D), E, 2 * I, D)
+    down_f = _synth_experts(lambda e: synth.expert_down(e, I, D), E, D, I)
 
-    def build(rows, cols, sparse):
+    def build(wf, rows, cols, sparse):
         c = torch.empty((E, rows, cols // (4 if sparse else 2)), dtype=torch.uint8, device="cuda")
         m = torch.empty((E, rows, cols // 8), dtype=torch.uint8, device="cuda") if sparse else None
         s = torch.empty((E, rows, cols // 16), dtype=torch.uint8, device="cuda")
         ts = torch.empty(E, dtype=torch.float32, device="cuda")
         for e in range(E):
-            Wf = torch.randn(rows, cols, device="cuda", generator=g) * 0.02
+            Wf = torch.from_numpy(wf[e]).cuda()
             if sparse:
                 Wf = ssn.sp24_prune(Wf)
                 codes, _, _ = ssn.nvfp4_quantize(Wf, scales=s[e], tensor_scale_out=ts[e:e + 1])
@@ -432,6 +627,14 @@ def run_moe(torch, ssn, synth, reps):
                 ssn.nvfp4_quantize(Wf, codes=c[e], scales=s[e], tensor_scale_out=ts[e:e + 1])
         return c, m, s, ts
 
+    def oracle_q(wf, e, sparse):
+        wt = sp24.prune24(wf[e]) if sparse else wf[e]
+        c, s, st = quant.quantize(wt)
+        if sparse:
+            v, m, _ = sp24.compress(c)
+            return ("sp24", v, m, s, st)
+        return ("dense", c, s, st)
+
     R = T * k
     flops = 2.0 * R * D * 2 * I + 2.0 * R * I * D
     counts = np.bincount(ids.ravel(), minlength=E)
@@ -439,11 +642,11 @@ def run_moe(torch, ssn, synth, reps):
                      "experts_touched": int((counts > 0).sum()), "max_rows": int(counts.max()),
                      "median_rows": float(np.median(counts))},
            "flops_dense_equiv": flops,
-           "note": "expert weights ~N(0, 0.02) drawn on the GPU (torch generator, seed 0); routing and X from the "
-                   "seeded synthetic generators"}
+           "note": "expert weights, routing and X from the seeded synthetic generators",
+           "parity": "routing offsets exact; token 2047 of the whole FFN within the oracle's bound"}
+    check_tokens = np.array([2047])
     for sparse in (False, True):
-        up_rows, down_rows = build(2 * I, D, sparse), build(D, I, sparse)
-        # weight preparation, once: the 64-k tiled layout of the grouped products
+        up_rows, down_rows = build(up_f, 2 * I, D, sparse), build(down_f, D, I, sparse)
         up, down = ssn.moe_pack_weights(up_rows), ssn.moe_pack_weights(down_rows)
         kt = ssn.WLAYOUT_KTILE64
         H = torch.empty((R, I), dtype=torch.bfloat16, device="cuda")
@@ -456,26 +659,48 @@ def run_moe(torch, ssn, synth, reps):
         p_down, _ = ssn.moe_grouped_gemm_nvfp4(H, None, off, R, down[0], down[2], down[3], w_meta=down[1], Y=Yd,
                                                prepare=True, w_layout=kt)
         p_comb, _ = ssn.moe_combine(Yd, ro, dw, prepare=True)
-        p_ffn, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up, down, prepare=True, w_layout=kt)
+        p_ffn, (ffn_out, ffn_bad) = ssn.moe_nvfp4_ffn(X, dids, dw, E, up, down, prepare=True, w_layout=kt)
         p_ffn_rows, _ = ssn.moe_nvfp4_ffn(X, dids, dw, E, up_rows, down_rows, prepare=True)
-        B = Batches(torch)
+        p_ffn()
+        torch.cuda.synchronize()
+        # parity before timing: routing offsets exact, two tokens' outputs within the FFN bound
+        _, eoff, _, _ = moe.route(ids, E)
+        if not np.array_equal(off.cpu().numpy().astype(np.int64), eoff) or int(ffn_bad.item()) != 0:
+            raise ParityError("moe: routing differs from the oracle's")
+        cache = {}
+
+        def qu(e):
+            if ("u", e) not in cache:
+                cache[("u", e)] = oracle_q(up_f, e, sparse)
+            return cache[("u", e)]
+
+        def qd(e):
+            if ("d", e) not in cache:
+                cache[("d", e)] = oracle_q(down_f, e, sparse)
+            return cache[("d", e)]
+        ref, tol, _ = moe.moe_ffn(x, ids, wts, qu, qd, E, I, tokens=check_tokens)
+        got = ffn_out[torch.from_numpy(check_tokens).cuda()].cpu().numpy().astype(np.float64)
+        if not np.all(np.abs(got - ref) <= tol):
+            raise ParityError(f"moe {'2:4' if sparse else 'dense'}: FFN output outside the bound")
+        Tm = Timer(torch)
         stages = [("route", p_route), ("up_silu_gate", p_up), ("down", p_down), ("combine", p_comb), ("ffn", p_ffn),
                   ("ffn_row_layout", p_ffn_rows)]
         for n, p in stages:
-            B.run(n, [p] * 2)
-        torch.cuda.synchronize()
-        for n, p in stages:
-            B.run(n, [p] * reps)
-        torch.cuda.synchronize()
+            Tm.batch(n + "_warm", [p] * 2)
+            torch.cuda.synchronize()
+            Tm.batch(n, [p] * 5)
+            Tm.each(n, [p] * TRIALS)
+            torch.cuda.synchronize()
         wbytes = sum(t.numel() for t in (up[0], up[1], up[2], down[0], down[1], down[2]) if t is not None)
         ffn_bytes = wbytes + T * D * 2 + 2 * R * I * 2 + T * D * 4
-        res = {n: {"us": round(B.us(n), 1)} for n, _ in stages}
+        res = {n: {"us": round(Tm.us(n), 1), **Tm.stats(n)} for n, _ in stages}
         us = res["ffn"]["us"]
         t_roof = max(flops / (2 if sparse else 1) / (BF16_PEAK_TFLOPS * 1e12), ffn_bytes / (HBM_PEAK_GBPS * 1e9))
         res["ffn"].update({"weight_layout": "ktile64", "weight_bytes": wbytes, "alg_bytes": ffn_bytes,
                            "tflops_dense_equiv": round(flops / (us * 1e-6) / 1e12, 1),
                            "GBps_alg": round(ffn_bytes / (us * 1e-6) / 1e9, 1),
                            "t_roof_us": round(t_roof * 1e6, 1), "frac_of_t_roof": round(t_roof / (us * 1e-6), 4)})
+        res["gpu_state"] = state_under_load(torch, p_ffn, seconds=1.0)
         out["sp24" if sparse else "dense"] = res
         del H, Yd, up_rows, down_rows
         torch.cuda.empty_cache()
@@ -484,8 +709,8 @@ def run_moe(torch, ssn, synth, reps):
         del up, down
         torch.cuda.empty_cache()
     out["sp24"]["ffn"]["speedup_vs_dense"] = round(out["dense"]["ffn"]["us"] / out["sp24"]["ffn"]["us"], 3)
-    for T in MOE_DECODE_TOKENS:
-        d, s_ = out["decode_dense"][f"T{T}"], out["decode_sp24"][f"T{T}"]
+    for T_ in MOE_DECODE_TOKENS:
+        d, s_ = out["decode_dense"][f"T{T_}"], out["decode_sp24"][f"T{T_}"]
         s_["ffn_speedup_vs_dense"] = round(d["ffn_us"] / s_["ffn_us"], 3)
     return out
 
@@ -539,14 +764,13 @@ def run_moe_decode(torch, ssn, synth, x, up, down, sparse, E, k, D, I):
             stages["down_tiles"].append(ssn.moe_grouped_gemm_nvfp4(
                 H, None, off, R, d[0], d[2], d[3], w_meta=d[1], Y=torch.empty_like(Yd), prepare=True, w_layout=kt,
                 algo=tiles)[0])
-        B = Batches(torch)
+        Tm = Timer(torch)
         for n, ps in stages.items():
-            B.run(n, ps)
-        torch.cuda.synchronize()
-        for n, ps in stages.items():
-            B.run(n, ps + ps)
-        torch.cuda.synchronize()
-        t = {n: B.us(n) for n in stages}
+            Tm.batch(n + "_warm", ps)
+            torch.cuda.synchronize()
+            Tm.batch(n, ps + ps)
+            torch.cuda.synchronize()
+        t = {n: Tm.us(n) for n in stages}
         wb = float(np.mean(touched)) * per_expert
         e = {"tokens": T, "rows": R, "experts_touched_mean": round(float(np.mean(touched)), 1),
              "weight_bytes_touched": int(wb), "algo": "+".join(sorted({ssn.ALGO_NAMES.get(a.value, "?") for a in used})),
@@ -563,40 +787,107 @@ def run_moe_decode(torch, ssn, synth, x, up, down, sparse, E, k, D, I):
 
 
 # ------------------------------------------------------------------------------------------
-def cpu_baseline_decode(w, x, rows):
-    """The oracle (unchanged) on the host: the decode step's calls over a sample of weight rows."""
-    from oracle import gemm, quant, sp24
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_prefill(x, cols=4096):
+    """The oracle (unchanged) on the host: the dense prefill product for all 8192 activation
+    rows and a sample of weight rows (output columns), including the oracle's quantisation of
+    those rows; reported as dense TFLOP/s of the sampled product."""
+    import numpy as np
+    import synth
+    from oracle import gemm, quant
     try:
         from threadpoolctl import threadpool_info
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         blas_threads = 1
-    N, K = w.shape
-    rows = min(rows, N)
-    ws = w[:rows]
+    M, N, K = PREFILL["M"], PREFILL["N"], PREFILL["K"]
     t0 = time.perf_counter()
-    st = quant.tensor_scale(w)
-    c, s, _ = quant.quantize(ws, tensor_scale_in=st)
-    wp = sp24.prune24(ws)
-    stp = quant.tensor_scale(wp)
-    pc, ps, _ = quant.quantize(wp, tensor_scale_in=stp)
-    sp24.check(pc)
-    v, m, _ = sp24.compress(pc)
-    for M in (1, 4, 8):
-        gemm.gemm_dense(x[:M], c, s, st)
-    for M in (1, 4, 8):
-        gemm.gemm_sp24(x[:M], v, m, ps, stp)
-    sec = time.perf_counter() - t0
-    b = (2 * bytes_quantize(rows, K) + bytes_prune(rows, K) + bytes_check(rows, K) + bytes_compress(rows, K)
-         + sum(bytes_gemm(M, rows, K, False, 4) + bytes_gemm(M, rows, K, True, 4) for M in (1, 4, 8)))
-    return {"value": round(b / sec / 1e9, 3), "unit": "GB/s", "cores": int(blas_threads), "kind": "oracle",
-            "sample": f"the decode step's calls on weight rows [0, {rows}) of {N} (K={K}), M in {{1,4,8}}; "
+    amax = 0.0
+    for r0 in range(0, N, 4096):   # the tensor scale needs the whole W's maximum
+        blk = synth.weight_rows_with_outliers(N, K, r0, min(N, r0 + 4096), 0.01, 20.0)
+        amax = max(amax, float(np.abs(blk).max()))
+    t_scale = time.perf_counter() - t0
+    st = quant.tensor_scale(np.full((1, 16), amax, np.float32))
+    w = synth.weight_rows_with_outliers(N, K, 0, cols, 0.01, 20.0)
+    t1 = time.perf_counter()
+    c, s, _ = quant.quantize(w, tensor_scale_in=st)
+    gemm.gemm_dense(x, c, s, st)
+    sec = time.perf_counter() - t1
+    flops = 2.0 * M * cols * K
+    return {"value": round(flops / sec / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"dense prefill product X [{M}, {K}] x weight rows [0, {cols}) of {N} (the oracle's quantisation "
+                      f"of those rows with the whole tensor's scale, then its float64 product and bound base); "
                       f"{sec:.1f} s on host cores; NumPy float64 oracle",
-            "seconds": round(sec, 2), "host_cores_available": len(os.sched_getaffinity(0))}
+            "seconds": round(sec, 2), "tensor_scale_pass_s": round(t_scale, 2), "cpu_model": cpu_model(),
+            "host_cores_available": len(os.sched_getaffinity(0))}
 
 
+# ------------------------------------------------------------------------------------------
+# rocprofv3 output -> profiles/ summaries
+def _read_csvs(d, pattern):
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", pattern), recursive=True):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize(kind, out, dirs, cmd_note):
+    """KIND trace: kernel_stats.csv of --kernel-trace --stats runs -> markdown table.
+    KIND pmc: counter_collection.csv of --pmc runs -> per-kernel, per-grid averages."""
+    lines = [f"# {os.path.splitext(os.path.basename(out))[0]}", "", "Command(s):", "", "```", cmd_note.strip(), "```", ""]
+    if kind == "trace":
+        for d in dirs:
+            rows = _read_csvs(d, "*kernel_stats.csv")
+            lines += [f"From `{os.path.basename(os.path.normpath(d))}`:", "",
+                      "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+            for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+                lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                             f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                             f"{float(r['Percentage']):.2f} |")
+            lines.append("")
+    else:
+        agg = {}
+        for d in dirs:
+            for r in _read_csvs(d, "*counter_collection.csv"):
+                key = (r["Kernel_Name"][:90], int(r.get("Grid_Size", 0) or 0), r["Counter_Name"])
+                a = agg.setdefault(key, [0.0, 0])
+                a[0] += float(r["Counter_Value"])
+                a[1] += 1
+        counters = sorted({k[2] for k in agg})
+        kern = sorted({(k[0], k[1]) for k in agg})
+        lines += ["Averages per dispatch (grid = work-items).", "",
+                  "| kernel | grid | dispatches | " + " | ".join(counters) + " |",
+                  "|---|---|---|" + "---|" * len(counters)]
+        for kname, grid in kern:
+            vals, nd = [], 0
+            for c in counters:
+                a = agg.get((kname, grid, c))
+                vals.append(f"{a[0] / a[1]:.1f}" if a else "")
+                nd = max(nd, a[1] if a else 0)
+            lines.append(f"| `{kname}` | {grid} | {nd} | " + " | ".join(vals) + " |")
+        lines.append("")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {out}")
+
+
+# ------------------------------------------------------------------------------------------
 def main():
     args = parse()
+    if args.summarize:
+        kind, out, *dirs = args.summarize
+        summarize(kind, out, dirs, os.environ.get("SSN_PROFILE_CMD", ""))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on one "
               f"GPU and has no collectives).", file=sys.stderr)
@@ -608,32 +899,46 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     ssn.lib()
-    wl = set(args.workloads.split(","))
+    wl = set(w for w in args.workloads.split(",") if w)
     hbm = hbm_probe(torch, ssn)
     print(f"[bench] hbm probe {hbm}", file=sys.stderr, flush=True)
-    res, (w, x) = run_decode(args, torch, ssn, synth)
-    print(f"[bench] decode done: {res['ms_per_step']} ms/step", file=sys.stderr, flush=True)
-    out = {"metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": res["config"],
-           "roofline": res["roofline"], "hbm_measured": hbm, "mfma_peak_bf16_TFLOPs": BF16_PEAK_TFLOPS,
-           "kernels": res["kernels"], "extra_kernels": res["extra_kernels"]}
-    work = {}
+    M, N, K = PREFILL["M"], PREFILL["N"], PREFILL["K"]
+    pre, step, x_pre = run_gemm_shape(torch, ssn, synth, M, N, K, torch.bfloat16, True, args, headline=True)
+    flops = 2.0 * M * N * K
+    ms_step = step["ms_per_step"]
+    kus = step["event_us"]
+    achieved = flops / (kus * 1e-6) / 1e12
+    print(f"[bench] prefill done: {ms_step:.4f} ms/step", file=sys.stderr, flush=True)
+    out = {"metric": METRIC, "value": round(flops / (ms_step * 1e-3) / 1e12, 1), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "prefill: X bf16 [8192, 5120] ~N(0,1) . W^T, W [27648, 5120] ~N(0,0.02) with 1% "
+                                  "outliers x20, dense NVFP4 weights decoded in registers, bf16 matrix cores, f32 "
+                                  "accumulate, bf16 out; one step = one product",
+                      "M": M, "N": N, "K": K, "weights": "nvfp4 dense", "step_flops": flops},
+           "roofline": {"kernel": DENSE_TILE_KERNEL, "bound": "mfma", "achieved": round(achieved, 1),
+                        "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                        "traffic": traffic_for("prefill_dense"), "avg_launch_us": round(kus, 2),
+                        "flops_per_launch": flops},
+           "sp24_vs_dense": {v: pre[v]["speedup_vs_dense"] for v in ("sp24_smfmac", "sp24_decompress_mfma",
+                                                                      "sp24_gather_valu")},
+           "hbm_measured": hbm}
+    work = {"prefill": pre}
+    if "decode" in wl:
+        work["decode"] = run_decode(torch, ssn, synth, hbm["copy_GBps"])
+        print("[bench] decode done", file=sys.stderr, flush=True)
     if "square" in wl:
-        work["square"] = run_gemm_shape(torch, ssn, synth, 4096, 4096, 4096, torch.float32, False, 10)
+        work["square"], _, _ = run_gemm_shape(torch, ssn, synth, 4096, 4096, 4096, torch.float32, False, args)
         print("[bench] square done", file=sys.stderr, flush=True)
-    if "prefill" in wl:
-        work["prefill"] = run_gemm_shape(torch, ssn, synth, 8192, 27648, 5120, torch.bfloat16, True, 5)
-        print("[bench] prefill done", file=sys.stderr, flush=True)
     if "head" in wl:
-        work["head"] = run_head(torch, ssn, synth, 10)
+        work["head"] = run_head(torch, ssn, synth, hbm["copy_GBps"])
         print("[bench] head done", file=sys.stderr, flush=True)
     if "moe" in wl:
-        work["moe"] = run_moe(torch, ssn, synth, 5)
+        work["moe"] = run_moe(torch, ssn, synth, hbm["copy_GBps"])
         print("[bench] moe done", file=sys.stderr, flush=True)
     out["workloads"] = work
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_decode(w, x, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline_prefill(x_pre)
         print("[bench] cpu baseline done", file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 

@@ -1,7 +1,7 @@
 """The decode workload at full size (X [8, 5120] bf16, W [13824, 5120]), run as the benchmark
 runs it (GPU prune -> quantise -> check -> compress -> GEMV at M = 1, 4, 8), checked against the
-oracle on a sample of weight rows (outputs the oracle computes one by one) and by properties
-that hold at any size."""
+oracle: quantised and compressed weights on a sample of rows, every output of the GEMVs (the
+oracle quantises all weight rows itself), and properties that hold at any size."""
 import numpy as np
 import pytest
 import torch
@@ -65,21 +65,35 @@ def test_check_and_compress_properties(full):
     assert torch.equal(back.cpu() & 0x77, full["pc"].cpu() & 0x77)   # magnitudes survive the round trip
 
 
+@pytest.fixture(scope="module")
+def oracle_all(full):
+    """The oracle's products of all 8 activation rows with every weight row (dense and 2:4),
+    quantised by the oracle in chunks with the tensor scale of the whole W."""
+    w, x = full["w"], full["x"]
+    Yd, Bd, Ys, Bs = [], [], [], []
+    for r0 in range(0, N, 2048):
+        c, s, _ = quant.quantize(w[r0:r0 + 2048], tensor_scale_in=full["st"])
+        Y, B = gemm.gemm_dense(x, c, s, full["st"])
+        Yd.append(Y); Bd.append(B)
+        pc, ps, _ = quant.quantize(sp24.prune24(w[r0:r0 + 2048]), tensor_scale_in=full["stp"])
+        v, m, nb = sp24.compress(pc)
+        assert nb == 0
+        Y, B = gemm.gemm_sp24(x, v, m, ps, full["stp"])
+        Ys.append(Y); Bs.append(B)
+    return dict(Yd=np.concatenate(Yd, 1), Bd=np.concatenate(Bd, 1), Ys=np.concatenate(Ys, 1), Bs=np.concatenate(Bs, 1))
+
+
 @pytest.mark.parametrize("M", [1, 4, 8])
-def test_gemv_dense_sampled(full, M):
+def test_gemv_dense_all_outputs(full, oracle_all, M):
     x = full["x"][:M]
     y, used = ssn.gemm_nvfp4_dense(x_dev(x), full["codes"], full["scales"], full["ts"])
-    c, s, _ = quant.quantize(full["w"][SAMPLE], tensor_scale_in=full["st"])
-    Y, B = gemm.gemm_dense(x, c, s, full["st"])
-    assert_within_bound(y_host(y)[:, SAMPLE], Y, B, what=f"dense M={M} algo={used}")
+    assert_within_bound(y_host(y), oracle_all["Yd"][:M], oracle_all["Bd"][:M], what=f"dense M={M} algo={used}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 8])
-@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA])
-def test_gemv_sp24_sampled(full, M, algo):
+@pytest.mark.parametrize("algo", [ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_GATHER])
+def test_gemv_sp24_all_outputs(full, oracle_all, M, algo):
     x = full["x"][:M]
     y, used = ssn.gemm_nvfp4_sp24(x_dev(x), full["vals"], full["meta"], full["ps"], full["pts"], algo=algo)
-    c, s, _ = quant.quantize(full["wp"], tensor_scale_in=full["stp"])
-    v, m, _ = sp24.compress(c)
-    Y, B = gemm.gemm_sp24(x, v, m, s, full["stp"])
-    assert_within_bound(y_host(y)[:, SAMPLE], Y, B, what=f"sp24 M={M} algo={used}")
+    assert used == algo
+    assert_within_bound(y_host(y), oracle_all["Ys"][:M], oracle_all["Bs"][:M], what=f"sp24 M={M} algo={used}")

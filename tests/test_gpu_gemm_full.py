@@ -1,7 +1,9 @@
 """The square (4096 x 4096 x 4096, f32 out) and prefill (X [8192, 5120], W [27648, 5120] with 1%
 of entries x20 before pruning, bf16 out) products at full size, launched as the benchmark
 launches them, checked against the oracle on sampled outputs (rows and columns that straddle
-tile edges) and by properties that hold at any size."""
+tile edges), on one whole output row, one whole output column and one whole interior 256 x 256
+tile (the oracle quantises every weight row itself, in chunks), and by properties that hold at
+any size."""
 import numpy as np
 import pytest
 import torch
@@ -36,7 +38,8 @@ def _setup(M, N, K, w):
 def square():
     M = N = K = 4096
     d = _setup(M, N, K, synth.weights(N, K))
-    d.update(M=M, N=N, K=K, ms=_sample(M, [1000, 3001]), ns=_sample(N, [777, 2222]), out="f32")
+    d.update(M=M, N=N, K=K, ms=_sample(M, [1000, 3001]), ns=_sample(N, [777, 2222]), out="f32",
+             whole_row=2345, whole_col=1234, tile=(7, 9))
     yield d
     d.clear()
     torch.cuda.empty_cache()
@@ -47,7 +50,8 @@ def prefill():
     M, N, K = 8192, 27648, 5120
     w = synth.weight_rows_with_outliers(N, K, 0, N, p=0.01, mult=20.0)
     d = _setup(M, N, K, w)
-    d.update(M=M, N=N, K=K, ms=_sample(M, [5000]), ns=_sample(N, [13824, 20000]), out="bf16")
+    d.update(M=M, N=N, K=K, ms=_sample(M, [5000]), ns=_sample(N, [13824, 20000]), out="bf16",
+             whole_row=5001, whole_col=20001, tile=(17, 61))
     yield d
     d.clear()
     torch.cuda.empty_cache()
@@ -82,6 +86,70 @@ def _check(d, sparse, algo):
                                          (True, ssn.ALGO_DECOMPRESS_MFMA)])
 def test_square(square, sparse, algo):
     _check(square, sparse, algo)
+
+
+CHUNK = 2048
+
+
+def _oracle_weights(d):
+    """The oracle's dense and 2:4 weights for every row of W (chunked), with the tensor scale of
+    the whole W."""
+    if "oq" not in d:
+        w, st, N = d["w"], d["st"], d["N"]
+        cs, ss, vs, ms_, ps_ = [], [], [], [], []
+        for r0 in range(0, N, CHUNK):
+            c, s, _ = quant.quantize(w[r0:r0 + CHUNK], tensor_scale_in=st)
+            pc, ps, _ = quant.quantize(sp24.prune24(w[r0:r0 + CHUNK]), tensor_scale_in=st)
+            v, m, nb = sp24.compress(pc)
+            assert nb == 0
+            cs.append(c); ss.append(s); vs.append(v); ms_.append(m); ps_.append(ps)
+        d["oq"] = dict(c=np.concatenate(cs), s=np.concatenate(ss), v=np.concatenate(vs), m=np.concatenate(ms_),
+                       ps=np.concatenate(ps_))
+    return d["oq"]
+
+
+def _oracle_block(d, rows, cols, sparse):
+    """Oracle product and bound base for activation rows `rows` x weight rows `cols` (chunked)."""
+    oq = _oracle_weights(d)
+    Ys, Bs = [], []
+    for c0 in range(0, len(cols), CHUNK):
+        cc = cols[c0:c0 + CHUNK]
+        if sparse:
+            Y, B = gemm.gemm_sp24(d["x"][rows], oq["v"][cc], oq["m"][cc], oq["ps"][cc], d["st"])
+        else:
+            Y, B = gemm.gemm_dense(d["x"][rows], oq["c"][cc], oq["s"][cc], d["st"])
+        Ys.append(Y); Bs.append(B)
+    return np.concatenate(Ys, axis=1), np.concatenate(Bs, axis=1)
+
+
+def _whole(d, sparse, algo):
+    """A whole output row, a whole output column and a whole interior 256 x 256 tile."""
+    ydt = torch.bfloat16 if d["out"] == "bf16" else torch.float32
+    if sparse:
+        y, used = ssn.gemm_nvfp4_sp24(d["X"], d["vals"], d["meta"], d["ps"], d["pts"], y_dtype=ydt, algo=algo)
+    else:
+        y, used = ssn.gemm_nvfp4_dense(d["X"], d["codes"], d["scales"], d["ts"], y_dtype=ydt, algo=algo)
+    assert used == algo
+    M, N = d["M"], d["N"]
+    m_row, n_col = d["whole_row"], d["whole_col"]
+    tm, tn = d["tile"]
+    blocks = [("row", np.array([m_row]), np.arange(N)), ("column", np.arange(M), np.array([n_col])),
+              ("tile", np.arange(256 * tm, 256 * tm + 256), np.arange(256 * tn, 256 * tn + 256))]
+    for what, rows, cols in blocks:
+        Y, B = _oracle_block(d, rows, cols, sparse)
+        got = y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
+        assert_within_bound(got, Y, B, out=d["out"], what=f"{'sp24' if sparse else 'dense'} algo={used} whole {what}")
+
+
+@pytest.mark.parametrize("sparse,algo", [(False, ssn.ALGO_MFMA), (True, ssn.ALGO_SMFMAC),
+                                         (True, ssn.ALGO_DECOMPRESS_MFMA)])
+def test_square_whole_row_column_tile(square, sparse, algo):
+    _whole(square, sparse, algo)
+
+
+@pytest.mark.parametrize("sparse,algo", [(False, ssn.ALGO_MFMA), (True, ssn.ALGO_SMFMAC)])
+def test_prefill_whole_row_column_tile(prefill, sparse, algo):
+    _whole(prefill, sparse, algo)
 
 
 @pytest.mark.parametrize("sparse,algo", [(False, ssn.ALGO_MFMA), (True, ssn.ALGO_SMFMAC),
