@@ -24,10 +24,11 @@ the pages that define the method:
 
 Modules: ``formats`` (E2M1 / E4M3 / bf16 codecs), ``quant`` (NVFP4 quantise/decode),
 ``sp24`` (2:4 prune, check, compress, decompress), ``gemm`` (fp64 products and the error
-bound), ``moe`` (routing, SiLU-gated expert FFN, combine), ``accounting`` (bytes, bits
-per weight, roofline and Amdahl arithmetic).
+bound), ``moe`` (routing, SiLU-gated expert FFN, combine), ``mx`` (MXFP4 quantisation of
+activations and weights and the W4A4 product), ``accounting`` (bytes, bits per weight,
+roofline and Amdahl arithmetic).
 
 Parity status of each function is stated in its docstring; none is "parity unpinned"
 except where said.
 """
-from . import formats, quant, sp24, gemm, moe, accounting  # noqa: F401
+from . import formats, quant, sp24, gemm, moe, mx, accounting  # noqa: F401
