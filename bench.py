@@ -797,10 +797,10 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline_prefill(x, cols=4096):
+def cpu_baseline_prefill(x, cols=PREFILL["N"], chunk=4096):
     """The oracle (unchanged) on the host: the dense prefill product for all 8192 activation
-    rows and a sample of weight rows (output columns), including the oracle's quantisation of
-    those rows; reported as dense TFLOP/s of the sampled product."""
+    rows and weight rows [0, cols) (output columns), including the oracle's quantisation of
+    those rows, in chunks of weight rows; reported as dense TFLOP/s of that product."""
     import numpy as np
     import synth
     from oracle import gemm, quant
@@ -817,16 +817,18 @@ def cpu_baseline_prefill(x, cols=4096):
         amax = max(amax, float(np.abs(blk).max()))
     t_scale = time.perf_counter() - t0
     st = quant.tensor_scale(np.full((1, 16), amax, np.float32))
-    w = synth.weight_rows_with_outliers(N, K, 0, cols, 0.01, 20.0)
-    t1 = time.perf_counter()
-    c, s, _ = quant.quantize(w, tensor_scale_in=st)
-    gemm.gemm_dense(x, c, s, st)
-    sec = time.perf_counter() - t1
+    sec = 0.0
+    for r0 in range(0, cols, chunk):
+        w = synth.weight_rows_with_outliers(N, K, r0, min(cols, r0 + chunk), 0.01, 20.0)
+        t1 = time.perf_counter()
+        c, s, _ = quant.quantize(w, tensor_scale_in=st)
+        gemm.gemm_dense(x, c, s, st)
+        sec += time.perf_counter() - t1
     flops = 2.0 * M * cols * K
     return {"value": round(flops / sec / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
             "sample": f"dense prefill product X [{M}, {K}] x weight rows [0, {cols}) of {N} (the oracle's quantisation "
-                      f"of those rows with the whole tensor's scale, then its float64 product and bound base); "
-                      f"{sec:.1f} s on host cores; NumPy float64 oracle",
+                      f"of those rows with the whole tensor's scale, then its float64 product and bound base, in "
+                      f"chunks of {chunk} rows); {sec:.1f} s on host cores; NumPy float64 oracle",
             "seconds": round(sec, 2), "tensor_scale_pass_s": round(t_scale, 2), "cpu_model": cpu_model(),
             "host_cores_available": len(os.sched_getaffinity(0))}
 
@@ -841,9 +843,61 @@ def _read_csvs(d, pattern):
     return rows
 
 
+def _pmc_avg(d, counter):
+    """{(kernel, grid): (average value per dispatch, dispatches)} of one counter."""
+    agg = {}
+    for r in _read_csvs(d, "*counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        key = (r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0))
+        a = agg.setdefault(key, [0.0, 0])
+        a[0] += float(r["Counter_Value"])
+        a[1] += 1
+    return {k: (v[0] / v[1], v[1]) for k, v in agg.items()}
+
+
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 1 << 31          # the bandwidth probe's device copy: 2 GiB read and 2 GiB written
+
+
+def traffic_entry(fetch_dir, write_dir, kernel, grid, source, summary):
+    """HBM bytes per launch of `kernel` at `grid` from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for the 2 GiB probe copy."""
+    fe, wr = _pmc_avg(fetch_dir, "FETCH_SIZE"), _pmc_avg(write_dir, "WRITE_SIZE")
+
+    def copy_cal(tab):
+        c = [v for (k, g), v in tab.items() if k.startswith(COPY_KERNEL)]
+        big = max(c, key=lambda v: v[0])[0]
+        return COPY_BYTES / (big * 1024.0)
+
+    def pick(tab):
+        m = [v for (k, g), v in tab.items() if k.startswith(kernel) and g == grid]
+        if not m:
+            raise SystemExit(f"no dispatch of {kernel} with grid {grid}")
+        return m[0][0]
+    cf, cw = copy_cal(fe), copy_cal(wr)
+    return {"kernels": [kernel], "grid": grid, "source": source, "source_sha256": _source_hash(source),
+            "fetch_bytes": int(pick(fe) * 1024 * cf), "write_bytes": int(pick(wr) * 1024 * cw),
+            "fetch_calibration": round(cf, 4), "write_calibration": round(cw, 4), "summary": summary}
+
+
 def summarize(kind, out, dirs, cmd_note):
     """KIND trace: kernel_stats.csv of --kernel-trace --stats runs -> markdown table.
-    KIND pmc: counter_collection.csv of --pmc runs -> per-kernel, per-grid averages."""
+    KIND pmc: counter_collection.csv of --pmc runs -> per-kernel, per-grid averages.
+    KIND traffic: OUT is profiles/traffic.json; DIRS = KEY KERNEL GRID SOURCE SUMMARY FETCH_DIR
+    WRITE_DIR: adds or replaces that entry."""
+    if kind == "traffic":
+        key, kernel, grid, source, summary, fdir, wdir = dirs
+        try:
+            with open(out) as f:
+                t = json.load(f)
+        except OSError:
+            t = {}
+        t[key] = traffic_entry(fdir, wdir, kernel, int(grid), source, summary)
+        with open(out, "w") as f:
+            json.dump(t, f, indent=1)
+        print(f"{key}: {t[key]}")
+        return
     lines = [f"# {os.path.splitext(os.path.basename(out))[0]}", "", "Command(s):", "", "```", cmd_note.strip(), "```", ""]
     if kind == "trace":
         for d in dirs:
