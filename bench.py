@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 / 2:4 weight-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,head,moe]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,head,moe,w4a4]
 
 Prints ONE JSON line. The headline (``value``, ``ms_per_step``, ``roofline``) is the prefill
 product, the largest of the workloads: X bf16 [8192, 5120] ~ N(0, 1) times dense NVFP4 weights
@@ -23,8 +23,10 @@ launches.
 weight copies, and the weight-preparation calls on three rotating copies of W, each against
 8 TB/s and the measured copy bandwidth), ``square`` (4096^3, f32 out), ``head`` (N = 131072,
 K = 5120, M = 1, 8, 9), ``moe`` (512 experts, top-10 of Zipf(1.1), D = 2048, I = 512: 4096
-tokens stage by stage, and 1-32 tokens on the weight-streaming kernels). ``cpu_baseline`` is
-the oracle's dense prefill product on a sample of output columns, on the host cores.
+tokens stage by stage, and 1-32 tokens on the weight-streaming kernels), ``w4a4`` (the W4A4
+variant at the prefill and square shapes: activations quantised to MXFP4 in every step, the FP4 x
+FP4 product on the block-scaled matrix cores, against the 10.1 PFLOP/s FP4 peak).
+``cpu_baseline`` is the oracle's dense prefill product on the host cores.
 
     python bench.py --summarize KIND OUT DIR...
 
@@ -67,7 +69,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workloads", default="decode,square,head,moe",
+    p.add_argument("--workloads", default="decode,square,head,moe,w4a4",
                    help="comma list of workloads beside the prefill headline (which always runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -787,6 +789,63 @@ def run_moe_decode(torch, ssn, synth, x, up, down, sparse, E, k, D, I):
 
 
 # ------------------------------------------------------------------------------------------
+def run_w4a4(torch, ssn, synth, M, N, K, outliers, dense_us):
+    """The W4A4 variant at one shape: bf16 activations quantised to MXFP4 on the fly
+    (mxfp4_quantize, part of every step), weights quantised once (timed too, as preparation),
+    and the FP4 x FP4 product on the block-scaled matrix cores, bf16 out."""
+    import numpy as np
+    from oracle import mx
+    x = synth.activations(M, K)
+    w = synth.weight_rows_with_outliers(N, K, 0, N, 0.01, 20.0) if outliers else synth.weights(N, K)
+    X = torch.from_numpy(x.view("int16")).view(torch.bfloat16).cuda()
+    W = torch.from_numpy(w).cuda()
+    xc, xs = ssn.mxfp4_quantize(X)
+    wc, ws = ssn.mxfp4_quantize(W)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    p_q, _ = ssn.mxfp4_quantize(X, codes=xc, scales=xs, prepare=True)
+    p_w, _ = ssn.mxfp4_quantize(W, codes=wc, scales=ws, prepare=True)
+    p_g, (_, used) = ssn.gemm_mxfp4(xc, xs, M, wc, ws, N, K, y_dtype=torch.bfloat16, Y=Y, prepare=True)
+    p_g()
+    torch.cuda.synchronize()
+    ms = np.array(sorted({0, 1, 255, 256, M // 2 + 3, M - 1}))
+    ns = np.array(sorted({0, 1, 255, 256, N // 2 + 5, N - 1}))
+    qxc, qxs = mx.quantize_bf16(x[ms])
+    qwc, qws = mx.quantize(w[ns])
+    Yr, Br = mx.gemm_w4a4(qxc, qxs, qwc, qws)
+    _assert_bound(_rows_of(Y, ms, ns), Yr, Br, "bf16", f"w4a4 {M}x{N}x{K}")
+    del w, W
+    T = Timer(torch)
+    for n, p in (("quantize_x", p_q), ("quantize_w", p_w), ("gemm", p_g)):
+        T.batch(n + "_warm", [p] * 2)
+        torch.cuda.synchronize()
+        T.batch(n, [p] * TRIALS)
+        T.each(n, [p] * TRIALS)
+        torch.cuda.synchronize()
+    flops = 2.0 * M * N * K
+    g_us, q_us = T.us("gemm"), T.us("quantize_x")
+    qx_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
+    res = {"shape": {"M": M, "N": N, "K": K, "y": "bf16", "outliers": outliers},
+           "format": "MXFP4 activations and weights (E2M1, E8M0 scale per 32 along K), tiled for the matrix cores",
+           "parity": "sampled outputs within the oracle's bound",
+           "gemm": {"us": round(g_us, 1), **T.stats("gemm"), "algo": ssn.ALGO_NAMES.get(used.value, "?"),
+                    "tflops": round(flops / (g_us * 1e-6) / 1e12, 1),
+                    "frac_of_fp4_peak": round(flops / (g_us * 1e-6) / 1e12 / FP4_PEAK_TFLOPS, 4)},
+           "quantize_x": {"us": round(q_us, 1), **T.stats("quantize_x"), "alg_bytes": qx_bytes,
+                          "GBps": round(qx_bytes / (q_us * 1e-6) / 1e9, 1)},
+           "quantize_w": {"us": round(T.us("quantize_w"), 1), **T.stats("quantize_w"), "alg_bytes": qw_bytes,
+                          "GBps": round(qw_bytes / (T.us("quantize_w") * 1e-6) / 1e9, 1)},
+           "step_us": round(g_us + q_us, 1),
+           "step_tflops": round(flops / ((g_us + q_us) * 1e-6) / 1e12, 1)}
+    if dense_us:
+        res["speedup_vs_w4a16_dense"] = round(dense_us / (g_us + q_us), 3)
+    res["gpu_state"] = state_under_load(torch, p_g)
+    del X, Y, xc, xs, wc, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------------------------------
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -990,6 +1049,12 @@ def main():
     if "moe" in wl:
         work["moe"] = run_moe(torch, ssn, synth, hbm["copy_GBps"])
         print("[bench] moe done", file=sys.stderr, flush=True)
+    if "w4a4" in wl:
+        work["w4a4"] = {"prefill": run_w4a4(torch, ssn, synth, M, N, K, True, pre["dense_mfma"]["us"])}
+        if "square" in work:
+            work["w4a4"]["square"] = run_w4a4(torch, ssn, synth, 4096, 4096, 4096, False,
+                                              work["square"]["dense_mfma"]["us"])
+        print("[bench] w4a4 done", file=sys.stderr, flush=True)
     out["workloads"] = work
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_prefill(x_pre)

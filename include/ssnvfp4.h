@@ -311,6 +311,51 @@ int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_i
                   const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids,
                   void* workspace, int64_t workspace_bytes, void* stream);
 
+/* =============================================================================================
+ * W4A4 variant: activations quantised as well ("Trying to beat the bandwidth", NVIDIA developer
+ * forum: block-scaled FP4 x FP4 is the FP4 tensor cores' performance unlock, W4A16 has to
+ * dequantise first; "NVFP4 Without FP4 Hardware", ai-muninn.com, section "Convert BF16 to NVFP4
+ * yourself": W4A4 checkpoints carry activation scales). gfx950's block-scaled matrix cores take
+ * E2M1 operands with one E8M0 (power-of-two) scale per 32 values along K, the OCP MX format, so
+ * both operands of this variant are MXFP4:
+ *   codes: E2M1 nibbles as for NVFP4 (element k = 2j in the low nibble of byte j);
+ *   scales: one E8M0 byte per 32 consecutive values along K, value 2^(b - 127);
+ *   quantisation of a block: e = floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for an
+ *   all-zero block); code = sign | E2M1 nearest-even of |v| / 2^e, saturating at 6.
+ * Layouts (SSN_MX_ROWS: codes [R, K/2], scales [R, K/32] row-major; SSN_MX_TILED: the order the
+ * matrix cores read, rows padded to a multiple of 32 and K to a multiple of 256 with zero codes
+ * and scale byte 0):
+ *   codes  [R32/32][K256/64][64][16 B]: entry l of piece (rb, ks) holds row 32 rb + l % 32,
+ *          k = 64 ks + 32 (l / 32) .. + 31;
+ *   scales [R32/32][K256/256][64][4 B]: byte s of entry l of piece (rb, kg) is the scale of row
+ *          32 rb + l % 32 for k = 256 kg + 64 s + 32 (l / 32) .. + 31.
+ * ============================================================================================= */
+enum { SSN_MX_ROWS = 0, SSN_MX_TILED = 1 };
+
+/* mxfp4_tiled_bytes — bytes of the SSN_MX_TILED codes array for [R, K] (return value) and of its
+ * scales array (*scale_bytes, host, nullable); -1 for invalid sizes (K % 32 != 0, negative). */
+int64_t mxfp4_tiled_bytes(int64_t R, int64_t K, int64_t* scale_bytes);
+
+/* ---------------------------------------------------------------------------------------------
+ * mxfp4_quantize — MXFP4 quantisation of V [R, K] (f32 or bf16, v_dtype; finite) into codes and
+ * scales of the given layout (SSN_MX_ROWS: [R, K/2] and [R, K/32]; SSN_MX_TILED: the sizes
+ * mxfp4_tiled_bytes gives, padding written as zeros). Rounding decisions are exact.
+ * Errors: NULL, SHAPE (K % 32), ALIGN, DTYPE, RANGE (layout), HIP.
+ * ------------------------------------------------------------------------------------------- */
+int mxfp4_quantize(const void* V, int v_dtype, int64_t R, int64_t K, int layout, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * gemm_mxfp4 — the W4A4 product Y = X_hat . W_hat^T on the block-scaled FP4 matrix cores
+ * (v_mfma_scale_f32_32x32x64_f8f6f4), f32 accumulation: X_hat from x_codes / x_scales (M rows),
+ * W_hat from w_codes / w_scales (N rows), both in the SSN_MX_TILED layout of [M, K] and [N, K];
+ * Y [M, N] of y_dtype (SSN_F32 or SSN_BF16, nearest-even). algo: AUTO or MFMA (reported in
+ * *algo_used, host, nullable). Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, HIP.
+ * ------------------------------------------------------------------------------------------- */
+int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const uint8_t* w_codes,
+               const uint8_t* w_scales, int64_t N, int64_t K, void* Y, int y_dtype, int algo, int* algo_used,
+               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,7 @@ ALGO_AUTO, ALGO_VALU, ALGO_MFMA, ALGO_SMFMAC, ALGO_GATHER, ALGO_DECOMPRESS_MFMA,
 ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFMAC: "smfmac", ALGO_GATHER: "gather",
               ALGO_DECOMPRESS_MFMA: "decompress_mfma", ALGO_STREAM: "stream"}
 EPI_NONE, EPI_SILU_GATE = 0, 1
+MX_ROWS, MX_TILED = 0, 1
 WLAYOUT_ROWS, WLAYOUT_KTILE64 = 0, 1
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -45,6 +46,9 @@ _SIGS = {
     "moe_ffn_workspace_bytes": ([_i64, _int, _int, _i64, _i64], _i64),
     "moe_nvfp4_ffn": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp,
                        _vp, _vp, _vp, _vp, _vp, _i64, _vp], _int),
+    "mxfp4_tiled_bytes": ([_i64, _i64, _vp], _i64),
+    "mxfp4_quantize": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp], _int),
+    "gemm_mxfp4": ([_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _vp], _int),
 }
 
 _lib = None
@@ -410,3 +414,57 @@ def moe_nvfp4_ffn(X, topk_ids, topk_weights, E, up, down, out=None, prepare=Fals
              _ptr(up[2]), _ptr(up[3]), _ptr(down[0]), _ptr(down[1]), _ptr(down[2]), _ptr(down[3]), _ptr(out),
              _ptr(bad), _ptr(ws), nws, _stream(dev))
     return _run("moe_nvfp4_ffn", cargs, prepare, (X, topk_ids, topk_weights, up, down, ws), (out, bad))
+
+
+
+# ------------------------------------------------------------------------------------------------
+# W4A4 variant (MXFP4 activations and weights)
+
+
+def mxfp4_tiled_bytes(R, K):
+    """(code bytes, scale bytes) of the MX_TILED layout of [R, K]."""
+    sb = ctypes.c_int64(0)
+    cb = lib().mxfp4_tiled_bytes(R, K, ctypes.byref(sb))
+    if cb < 0:
+        raise ValueError(f"invalid MXFP4 sizes R={R}, K={K}")
+    return cb, sb.value
+
+
+def mxfp4_quantize(V, layout=MX_TILED, codes=None, scales=None, prepare=False):
+    """MXFP4 quantisation of V [R, K] (f32 or bf16). Returns (codes, scales) as uint8 tensors:
+    [R, K/2] and [R, K/32] for MX_ROWS, flat arrays of mxfp4_tiled_bytes for MX_TILED."""
+    R, K = V.shape
+    _need(V, V.dtype, "V")
+    dev = V.device
+    if layout == MX_ROWS:
+        cshape, sshape = (R, K // 2), (R, K // 32)
+    else:
+        cb, sb = mxfp4_tiled_bytes(R, K)
+        cshape, sshape = (cb,), (sb,)
+    codes = codes if codes is not None else torch.empty(cshape, dtype=torch.uint8, device=dev)
+    scales = scales if scales is not None else torch.empty(sshape, dtype=torch.uint8, device=dev)
+    _need(codes, torch.uint8, "codes", cshape); _need(scales, torch.uint8, "scales", sshape)
+    cargs = (_ptr(V), _wdt(V), R, K, int(layout), _ptr(codes), _ptr(scales), _stream(dev))
+    return _run("mxfp4_quantize", cargs, prepare, (V,), (codes, scales))
+
+
+def gemm_mxfp4(x_codes, x_scales, M, w_codes, w_scales, N, K, y_dtype=torch.float32, algo=ALGO_AUTO, Y=None,
+               prepare=False):
+    """W4A4 product Y [M, N] = X_hat . W_hat^T from MX_TILED operands. Returns (Y, algorithm)."""
+    for t, n, (R, ) in ((x_codes, "x_codes", (M,)), (w_codes, "w_codes", (N,))):
+        _need(t, torch.uint8, n, (mxfp4_tiled_bytes(R, K)[0],))
+    _need(x_scales, torch.uint8, "x_scales", (mxfp4_tiled_bytes(M, K)[1],))
+    _need(w_scales, torch.uint8, "w_scales", (mxfp4_tiled_bytes(N, K)[1],))
+    dev = x_codes.device
+    Y = Y if Y is not None else torch.empty((M, N), dtype=y_dtype, device=dev)
+    dt = SSN_F32 if Y.dtype == torch.float32 else SSN_BF16 if Y.dtype == torch.bfloat16 else None
+    if dt is None:
+        raise TypeError("Y must be float32 or bfloat16")
+    _need(Y, Y.dtype, "Y", (M, N))
+    used = ctypes.c_int(-1)
+    cargs = (_ptr(x_codes), _ptr(x_scales), M, _ptr(w_codes), _ptr(w_scales), N, K, _ptr(Y), dt, algo,
+             ctypes.byref(used), _stream(dev))
+    if prepare:
+        return Prepared("gemm_mxfp4", cargs, (x_codes, x_scales, w_codes, w_scales, used, Y)), (Y, used)
+    _check(lib().gemm_mxfp4(*cargs))
+    return Y, used.value

@@ -4,6 +4,7 @@
 #include <stdio.h>
 
 #include "../../include/ssnvfp4.h"
+#include "device_once.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -409,6 +410,49 @@ int moe_nvfp4_ffn(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_i
                                    down_ts, SSN_EPI_NONE, Yd, SSN_F32, SSN_ALGO_AUTO, nullptr, stream)))
     return st;
   return moe_combine(Yd, SSN_F32, F, row_of, topk_weights, T, k, D, out, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// W4A4 variant: MXFP4 activations and weights
+extern "C" {
+
+int64_t mxfp4_tiled_bytes(int64_t R, int64_t K, int64_t* scale_bytes) {
+  if (R < 0 || K < 0 || K % 32 || R > kMaxRows || K > ((int64_t)1 << 30)) return -1;
+  if (scale_bytes) *scale_bytes = ssn::mx_tiled_scale_bytes(R, K);
+  return ssn::mx_tiled_code_bytes(R, K);
+}
+
+int mxfp4_quantize(const void* V, int v_dtype, int64_t R, int64_t K, int layout, uint8_t* codes, uint8_t* scales,
+                   void* stream) {
+  const char* fn = "mxfp4_quantize";
+  int st;
+  if ((st = check_nk(fn, R, K))) return st;
+  if ((st = check_dtype(fn, v_dtype, "v_dtype"))) return st;
+  if (layout != SSN_MX_ROWS && layout != SSN_MX_TILED) return fail(SSN_E_RANGE, "%s: unknown layout %d", fn, layout);
+  if (R == 0 || K == 0) return ok();
+  REQUIRE_PTR(V); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
+  return hip_status(ssn::launch_mx_quantize(V, v_dtype == SSN_BF16, R, K, layout == SSN_MX_TILED, codes, scales,
+                                            as_stream(stream)), fn);
+}
+
+int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const uint8_t* w_codes,
+               const uint8_t* w_scales, int64_t N, int64_t K, void* Y, int y_dtype, int algo, int* algo_used,
+               void* stream) {
+  const char* fn = "gemm_mxfp4";
+  int st;
+  if (M < 0 || M > kMaxRows) return fail(SSN_E_SHAPE, "%s: bad M=%lld", fn, (long long)M);
+  if ((st = check_nk(fn, N, K))) return st;
+  if ((st = check_dtype(fn, y_dtype, "y_dtype"))) return st;
+  if (algo != SSN_ALGO_AUTO && algo != SSN_ALGO_MFMA)
+    return fail(SSN_E_ALGO, "%s: algorithm %d is not available (the block-scaled matrix cores only)", fn, algo);
+  if (algo_used) *algo_used = SSN_ALGO_MFMA;
+  if (M == 0 || N == 0) return ok();
+  if (K == 0) return fail(SSN_E_SHAPE, "%s: K must be positive when M, N > 0", fn);
+  REQUIRE_PTR(x_codes); REQUIRE_PTR(x_scales); REQUIRE_PTR(w_codes); REQUIRE_PTR(w_scales); REQUIRE_PTR(Y);
+  return hip_status(ssn::launch_gemm_mx(x_codes, x_scales, M, w_codes, w_scales, N, K, Y, y_dtype == SSN_BF16,
+                                        as_stream(stream)), fn);
 }
 
 }  // extern "C"

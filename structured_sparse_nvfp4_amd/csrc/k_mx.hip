@@ -1,0 +1,313 @@
+// W4A4 variant: MXFP4 quantisation (activations and weights) and the FP4 x FP4 product on the
+// block-scaled matrix cores of gfx950.
+//
+// Block-scaled FP4 x FP4 is what the pages call the FP4 tensor cores' performance unlock
+// ("Trying to beat the bandwidth", NVIDIA developer forum: W4A16 has to dequantise to BF16
+// first). gfx950's v_mfma_scale_f32_32x32x64_f8f6f4 multiplies E2M1 operands and applies one
+// E8M0 (power-of-two) scale per 32 values along K to each operand, the OCP MX format, so both
+// operands of this variant are MXFP4: E2M1 codes plus an E8M0 scale per 32 along K, the scale
+// exponent floor(log2(amax)) - 2 (the OCP reference rule).
+//
+// MFMA tile layout (SSN_MX_TILED): the quantiser can write codes and scales in the order the
+// matrix-core operands are read, so the product streams 1 KB pieces straight into LDS and every
+// lane reads its operand with one 16-byte LDS read:
+//   codes  [R/32][K/64][64 lanes][16 B]: lane l holds row 32 rb + l % 32, codes of
+//          k = 64 ks + 32 (l / 32) .. + 31 (two per byte, even k in the low nibble);
+//   scales [R/32][K/256][64 lanes][4 B]: byte s of lane l is the scale of row 32 rb + l % 32 for
+//          k = 256 kg + 64 s + 32 (l / 32) .. + 31 (the byte the MFMA selects for step s).
+// R is padded to a multiple of 32 and K to a multiple of 256 with zero codes and scale byte 0
+// (value 0 x 2^-127 = 0), so padding adds nothing to a product.
+#include <algorithm>
+
+#include "common.hpp"
+#include "device_once.hpp"
+#include "launch.hpp"
+#include "pipeline.hpp"
+#include "tile.hpp"
+
+namespace ssn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------------------------
+// quantisation: four lanes per 32-value block, eight values per lane (one or two 16-byte loads),
+// the block maximum by two lane exchanges.
+
+// E2M1 magnitude code of r >= 0 (exact), nearest with ties to the even code, saturating at 6:
+// the boundaries are the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5, ties going down at 0.25, 1.25,
+// 2.5, 5 (to codes 0, 2, 4, 6) and up at 0.75, 1.75, 3.5 (to codes 2, 4, 6)
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+  return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) + (uint32_t)(r >= 1.75f) +
+         (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) + (uint32_t)(r > 5.0f);
+}
+
+// floor(log2(a)) - 2 clamped to [-127, 127] for a > 0 finite; -127 for a == 0
+__device__ __forceinline__ int mx_exponent(float a) {
+  if (!(a > 0.f)) return -127;
+  const uint32_t u = __float_as_uint(a);
+  int e = (int)((u >> 23) & 0xFF) - 127;
+  if ((u >> 23) == 0) e = -127 - (__clz(u) - 9);   // subnormal: 2^-149 * m, m < 2^23
+  return max(-127, min(127, e - 2));
+}
+
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* V, int64_t g, float (&v)[8]) {
+  if constexpr (BF16) {
+    const u32x4 w = *((const u32x4*)V + g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(w[i]); v[2 * i + 1] = bf16_hi(w[i]); }
+  } else {
+    const f32x4 a = *((const f32x4*)V + 2 * g), b = *((const f32x4*)V + 2 * g + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+}
+
+// byte offsets of the tiled layout
+__device__ __forceinline__ size_t tiled_code_offset(int64_t r, int64_t k, int64_t k64) {
+  // piece of 16 bytes holding k .. k + 31 (k % 32 == 0) of row r
+  const int64_t rb = r >> 5, ks = k >> 6, lane = (r & 31) + 32 * ((k >> 5) & 1);
+  return (size_t)(((rb * k64 + ks) << 6) + lane) << 4;
+}
+__device__ __forceinline__ size_t tiled_scale_offset(int64_t r, int64_t k, int64_t k256) {
+  const int64_t rb = r >> 5, kg = k >> 8, lane = (r & 31) + 32 * ((k >> 5) & 1), s = (k >> 6) & 3;
+  return ((size_t)(((rb * k256 + kg) << 6) + lane) << 2) + (size_t)s;
+}
+
+// groups g of eight values over [R, K] in row-major order; thread t of the grid takes
+// g = t, t + stride, ...; the four lanes of a block share it (block = g / 4, lanes aligned to 4)
+template <bool BF16, bool TILED>
+__global__ __launch_bounds__(256) void k_mx_quantize(const void* __restrict__ V, int64_t R, int64_t K,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t groups = R * (K / 8);
+  const int64_t k64 = (K + 255) / 256 * 4, k256 = (K + 255) / 256;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
+    float v[8];
+    load8<BF16>(V, g, v);
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    const int e = mx_exponent(a);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float r = __builtin_amdgcn_ldexpf(fabsf(v[i]), -e);     // exact: a power-of-two scale
+      const uint32_t c = e2m1_code(r) | ((__float_as_uint(v[i]) >> 28) & 8u);
+      word |= c << (4 * i);
+    }
+    const int64_t row = g / (K / 8), k = (g - row * (K / 8)) * 8;
+    if constexpr (TILED) {
+      *(uint32_t*)(codes + tiled_code_offset(row, k & ~(int64_t)31, k64) + ((k & 31) >> 1)) = word;
+      if ((g & 3) == 0) scales[tiled_scale_offset(row, k, k256)] = (uint8_t)(e + 127);
+    } else {
+      ((uint32_t*)codes)[g] = word;
+      if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(e + 127);
+    }
+  }
+}
+
+// zero fill of the tiled layout's padding (rows R .. R32 and k from K to K256): every byte of
+// the layout is written once by exactly one of the two kernels
+__global__ __launch_bounds__(256) void k_mx_pad(int64_t R, int64_t K, uint8_t* __restrict__ codes,
+                                                uint8_t* __restrict__ scales) {
+  const int64_t R32 = (R + 31) / 32 * 32, K256 = (K + 255) / 256 * 256;
+  const int64_t k64 = K256 / 64, k256 = K256 / 256;
+  const int64_t pieces = R32 * (K256 / 32);               // 16-byte code pieces (32 values)
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces; p += stride) {
+    const int64_t row = p / (K256 / 32), k = (p - row * (K256 / 32)) * 32;
+    if (row < R && k < K) continue;
+    *(u32x4*)(codes + tiled_code_offset(row, k, k64)) = u32x4{0u, 0u, 0u, 0u};
+    scales[tiled_scale_offset(row, k, k256)] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// product: Y = X_hat . W_hat^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1).
+// 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns 128 x 128 (4 x 4 blocks
+// of 32 x 32). A K stage is 256 wide (four MFMA steps): X and W pieces of the tile's eight row
+// blocks each (8 x 4 KB), their scales (8 x 256 B each); two stages resident, loaded by the
+// direct-to-LDS copies one stage ahead.
+constexpr int kMT = 256, kMN = 256;
+constexpr int kMxThreads = 256;
+constexpr int kMxBlocks = 8;                          // 32-row blocks per tile side
+constexpr int kMxStageX = kMxBlocks * 4096;           // codes of the tile's rows for one stage
+constexpr int kMxStageS = kMxBlocks * 256;            // their scales
+constexpr int kMxSlot = 2 * kMxStageX + 2 * kMxStageS;   // X codes, W codes, X scales, W scales
+constexpr int kMxLds = 2 * kMxSlot;
+constexpr int kMxLoads = 2 * 2 * 4 + 2 * 2;           // per wave per stage: 16 one-KB code copies, 4 scale copies
+
+constexpr int kXcds = 8, kGroupM = 4;
+__device__ __forceinline__ void mx_tile_of(int b, int total, int tiles_m, int tiles_n, int& tm, int& tn) {
+  // consecutive logical tiles share an XCD (workgroups are dealt to the eight XCDs round-robin)
+  // and walk down GROUP tile rows before moving right
+  const int per = total / kXcds, extra = total % kXcds;
+  const int x = b % kXcds, idx = b / kXcds;
+  const int t = x * per + min(x, extra) + idx;
+  const int span = kGroupM * tiles_n;
+  const int first = (t / span) * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - first);
+  const int tin = t % span;
+  tm = first + tin % gsize;
+  tn = tin / gsize;
+}
+
+__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb, int step) {
+  const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  // format 4 = E2M1 for both operands; the scale byte of step s is byte s of the scale word
+  switch (step) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 3, (int)sa, 3, (int)sb);
+  }
+}
+
+__global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int M, const uint8_t* __restrict__ wc,
+               const uint8_t* __restrict__ ws, int N, int K, void* __restrict__ Y, int y_bf16) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (M + kMT - 1) / kMT, tiles_n = (N + kMN - 1) / kMN;
+  int tm, tn;
+  mx_tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  const int k64 = (K + 255) / 256 * 4, k256 = k64 / 4, nst = k256;
+  const int mb_last = (M + 31) / 32 - 1, nb_last = (N + 31) / 32 - 1;
+  // this wave copies row blocks 2 wave, 2 wave + 1 of X and of W (clamped to the last block of
+  // the padded layout; their results are not stored) and their scale pieces
+  const int xb0 = min(8 * tm + 2 * wave, mb_last), xb1 = min(8 * tm + 2 * wave + 1, mb_last);
+  const int wb0 = min(8 * tn + 2 * wave, nb_last), wb1 = min(8 * tn + 2 * wave + 1, nb_last);
+  auto issue = [&](int st, char* slot) {
+    const int xbs[2] = {xb0, xb1}, wbs[2] = {wb0, wb1};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const size_t xo = ((size_t)xbs[i] * k64 + 4 * st + s) * 1024 + 16 * lane;
+        const size_t wo = ((size_t)wbs[i] * k64 + 4 * st + s) * 1024 + 16 * lane;
+        lds_dma16(xc + xo, slot + (2 * wave + i) * 4096 + s * 1024);
+        lds_dma16(wc + wo, slot + kMxStageX + (2 * wave + i) * 4096 + s * 1024);
+      }
+    }
+    // scale pieces: 256 bytes per block and stage; lane l copies 4 bytes of block 2 wave + l / 64
+    // ... as two 4-byte copies of 64 lanes (one per block) for X and for W
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const size_t so_x = ((size_t)xbs[i] * k256 + st) * 256 + 4 * lane;
+      const size_t so_w = ((size_t)wbs[i] * k256 + st) * 256 + 4 * lane;
+      lds_dma4(xs + so_x, slot + 2 * kMxStageX + (2 * wave + i) * 256);
+      lds_dma4(ws + so_w, slot + 2 * kMxStageX + kMxStageS + (2 * wave + i) * 256);
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc[i][j][t] = 0.f;
+
+  issue(0, lds);
+  issue(min(1, nst - 1), lds + kMxSlot);
+  for (int st = 0; st < nst; ++st) {
+    char* slot = lds + (st & 1) * kMxSlot;
+    wait_vmcnt<kMxLoads>();               // stage st has landed (stage st + 1 may be in flight)
+    stage_barrier();
+    uint32_t sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = *(const uint32_t*)(slot + 2 * kMxStageX + (4 * wm + i) * 256 + 4 * lane);
+      sb[i] = *(const uint32_t*)(slot + 2 * kMxStageX + kMxStageS + (4 * wn + i) * 256 + 4 * lane);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = *(const u32x4*)(slot + (4 * wm + i) * 4096 + s * 1024 + 16 * lane);
+        b[i] = *(const u32x4*)(slot + kMxStageX + (4 * wn + i) * 4096 + s * 1024 + 16 * lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(a[i], b[j], acc[i][j], sa[i], sb[j], s);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the slot are done
+    stage_barrier();                      // ... and every wave's: the slot can be refilled
+    issue(min(st + 2, nst - 1), slot);    // past the end the last stage is copied again (not used)
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // epilogue: lane holds rows 8 (t / 4) + 4 (l / 32) + t % 4 of each 32 x 32 block, column
+  // l % 32; each 32-row block of the wave (32 x 128) is staged in LDS and leaves as 16-byte
+  // pieces of a row
+  const bool vec = (N & 3) == 0;
+  constexpr int kTS = 132;
+  float* T = (float*)(lds + wave * (32 * kTS * 4));
+  const int r32 = lane & 31, h = lane >> 5;
+  const int m0 = kMT * tm + 128 * wm, n0 = kMN * tn + 128 * wn;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) T[(8 * (t >> 2) + 4 * h + (t & 3)) * kTS + 32 * j + r32] = acc[i][j][t];
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    const int c4 = lane & 31;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r = (lane >> 5) + 2 * q;
+      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
+      const int m = m0 + 32 * i + r, n = n0 + 4 * c4;
+      if (m < M && n < N) store4(Y, y_bf16, N, m, n, v, vec);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+  }
+}
+
+}  // namespace
+
+int64_t mx_tiled_code_bytes(int64_t R, int64_t K) { return (R + 31) / 32 * 32 * ((K + 255) / 256 * 128); }
+int64_t mx_tiled_scale_bytes(int64_t R, int64_t K) { return (R + 31) / 32 * 32 * ((K + 255) / 256 * 8); }
+
+hipError_t launch_mx_quantize(const void* V, int v_bf16, int64_t R, int64_t K, int tiled, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s) {
+  const int64_t groups = R * (K / 8);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((groups + 255) / 256, 64 * (int64_t)cu_count()));
+  if (tiled) {
+    const int64_t pieces = (R + 31) / 32 * 32 * ((K + 255) / 256 * 8);
+    const unsigned pg = (unsigned)std::max<int64_t>(1, std::min<int64_t>((pieces + 255) / 256, 16 * (int64_t)cu_count()));
+    hipLaunchKernelGGL(k_mx_pad, dim3(pg), dim3(256), 0, s, R, K, codes, scales);
+    if (groups > 0) {
+      if (v_bf16) hipLaunchKernelGGL((k_mx_quantize<true, true>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+      else hipLaunchKernelGGL((k_mx_quantize<false, true>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+    }
+  } else if (groups > 0) {
+    if (v_bf16) hipLaunchKernelGGL((k_mx_quantize<true, false>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+    else hipLaunchKernelGGL((k_mx_quantize<false, false>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const uint8_t* xc, const uint8_t* xs, int64_t M, const uint8_t* wc, const uint8_t* ws,
+                          int64_t N, int64_t K, void* Y, int y_bf16, hipStream_t s) {
+  static PerDeviceOnce attr_once;
+  hipError_t e = once_per_device(attr_once, [] {
+    return hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+  });
+  if (e != hipSuccess) return e;
+  const unsigned tiles = (unsigned)(((M + kMT - 1) / kMT) * ((N + kMN - 1) / kMN));
+  hipLaunchKernelGGL(k_gemm_mx, dim3(tiles), dim3(kMxThreads), kMxLds, s, xc, xs, (int)M, wc, ws, (int)N, (int)K, Y,
+                     y_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace ssn

@@ -76,4 +76,12 @@ hipError_t launch_moe_pack_ktiles(const uint8_t* src, int64_t E, int64_t N, int6
 hipError_t launch_moe_combine(const void* Yd, int yd_bf16, int64_t R, const int32_t* row_of, const float* w,
                               int64_t T, int k, int64_t D, float* out, hipStream_t s);
 
+// W4A4 variant (MXFP4 operands on the block-scaled matrix cores)
+int64_t mx_tiled_code_bytes(int64_t R, int64_t K);
+int64_t mx_tiled_scale_bytes(int64_t R, int64_t K);
+hipError_t launch_mx_quantize(const void* V, int v_bf16, int64_t R, int64_t K, int tiled, uint8_t* codes,
+                              uint8_t* scales, hipStream_t s);
+hipError_t launch_gemm_mx(const uint8_t* xc, const uint8_t* xs, int64_t M, const uint8_t* wc, const uint8_t* ws,
+                          int64_t N, int64_t K, void* Y, int y_bf16, hipStream_t s);
+
 }  // namespace ssn
