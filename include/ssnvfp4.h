@@ -356,6 +356,24 @@ int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const
                const uint8_t* w_scales, int64_t N, int64_t K, void* Y, int y_dtype, int algo, int* algo_used,
                void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * moe_nvfp4_ffn_noalloc — moe_nvfp4_ffn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments and results are those of moe_nvfp4_ffn. The workspace is a
+ * static device array of the library, one copy per GPU, 32 MiB, held until the process ends;
+ * a routing whose moe_ffn_workspace_bytes(T, k, E, I, D) exceeds it is refused with
+ * SSN_E_RANGE before anything is launched (decode-sized routings need a few MiB: 32 tokens x
+ * top-10 at D = 2048, I = 512 need 3 MiB). The call allocates nothing. Every call on a GPU
+ * uses that GPU's one array: calls that overlap on one GPU (two streams, or two host threads)
+ * race and must be ordered by the caller. Errors: those of moe_nvfp4_ffn, and RANGE.
+ * ------------------------------------------------------------------------------------------- */
+int moe_nvfp4_ffn_noalloc(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids,
+                          const float* topk_weights, int k, int E, int64_t I, int sparse, int w_layout,
+                          const uint8_t* up_main, const uint8_t* up_meta, const uint8_t* up_scales,
+                          const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
+                          const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

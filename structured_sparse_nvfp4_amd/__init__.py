@@ -49,6 +49,8 @@ _SIGS = {
     "mxfp4_tiled_bytes": ([_i64, _i64, _vp], _i64),
     "mxfp4_quantize": ([_vp, _int, _i64, _i64, _int, _vp, _vp, _vp], _int),
     "gemm_mxfp4": ([_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _vp], _int),
+    "moe_nvfp4_ffn_noalloc": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _vp], _int),
 }
 
 _lib = None
@@ -468,3 +470,20 @@ def gemm_mxfp4(x_codes, x_scales, M, w_codes, w_scales, N, K, y_dtype=torch.floa
         return Prepared("gemm_mxfp4", cargs, (x_codes, x_scales, w_codes, w_scales, used, Y)), (Y, used)
     _check(lib().gemm_mxfp4(*cargs))
     return Y, used.value
+
+def moe_nvfp4_ffn_noalloc(X, topk_ids, topk_weights, E, up, down, out, bad_ids, w_layout=WLAYOUT_ROWS):
+    """moe_nvfp4_ffn with the library's static per-GPU workspace instead of a caller-provided
+    one: the call itself allocates nothing (out f32 [T, D] and bad_ids int64 [1] are the
+    caller's). Routings needing more than the static workspace are refused."""
+    T, D = X.shape
+    _, k = topk_ids.shape
+    I = up[2].shape[1] // 2
+    sparse = up[1] is not None
+    _need(X, torch.bfloat16, "X"); _need(topk_ids, torch.int32, "topk_ids", (T, k))
+    _need(topk_weights, torch.float32, "topk_weights", (T, k))
+    _need(out, torch.float32, "out", (T, D)); _need(bad_ids, torch.int64, "bad_ids", (1,))
+    _check(lib().moe_nvfp4_ffn_noalloc(_ptr(X), T, D, _ptr(topk_ids), _ptr(topk_weights), k, E, I, int(sparse),
+                                       int(w_layout), _ptr(up[0]), _ptr(up[1]), _ptr(up[2]), _ptr(up[3]),
+                                       _ptr(down[0]), _ptr(down[1]), _ptr(down[2]), _ptr(down[3]), _ptr(out),
+                                       _ptr(bad_ids), _stream(X.device)))
+    return out, bad_ids

@@ -456,3 +456,50 @@ int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
+// Allocation-free whole FFN: its workspace is a static device array, one copy per GPU, held
+// until the process ends. Every kernel writes the workspace bytes it later reads (routing
+// arrays, H, Yd), so nothing needs clearing between calls; calls that overlap on one GPU share
+// the array and race.
+namespace {
+
+constexpr int64_t kNoAllocScratchBytes = (int64_t)32 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kNoAllocScratchBytes];
+
+ssn::PerDeviceOnce g_scratch_once;
+void* g_scratch_ptr[ssn::kMaxDevices];
+
+// The device address of this GPU's copy of `scratch` (the host-side name is only a stand-in).
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= ssn::kMaxDevices) return hipGetSymbolAddress(out, HIP_SYMBOL(scratch));
+  e = ssn::once_per_device(g_scratch_once, [&] { return hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch)); });
+  *out = g_scratch_ptr[dev];
+  return e;
+}
+
+}  // namespace
+
+extern "C" int moe_nvfp4_ffn_noalloc(const uint16_t* X, int64_t T, int64_t D, const int32_t* topk_ids,
+                                     const float* topk_weights, int k, int E, int64_t I, int sparse, int w_layout,
+                                     const uint8_t* up_main, const uint8_t* up_meta, const uint8_t* up_scales,
+                                     const float* up_ts, const uint8_t* down_main, const uint8_t* down_meta,
+                                     const uint8_t* down_scales, const float* down_ts, float* out, int64_t* bad_ids,
+                                     void* stream) {
+  const char* fn = "moe_nvfp4_ffn_noalloc";
+  int st;
+  if ((st = check_route_shape(fn, T, k, E))) return st;
+  if (I <= 0 || D <= 0 || I % 64 || D % 64)
+    return fail(SSN_E_SHAPE, "%s: I=%lld and D=%lld must be positive multiples of 64", fn, (long long)I, (long long)D);
+  const int64_t need = moe_ffn_workspace_bytes(T, k, E, I, D);
+  if (need > kNoAllocScratchBytes)
+    return fail(SSN_E_RANGE, "%s: this FFN needs %lld bytes of workspace; the static scratch holds %lld", fn,
+                (long long)need, (long long)kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = hip_status(scratch_address(&ws), fn))) return st;
+  return moe_nvfp4_ffn(X, T, D, topk_ids, topk_weights, k, E, I, sparse, w_layout, up_main, up_meta, up_scales, up_ts,
+                       down_main, down_meta, down_scales, down_ts, out, bad_ids, ws, kNoAllocScratchBytes, stream);
+}
