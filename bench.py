@@ -227,11 +227,22 @@ def hbm_probe(torch, ssn):
     return res
 
 
+HOST_ONLY_HEADERS = {"launch.hpp", "device_once.hpp"}   # launcher declarations and host set-up
+
+
 def _source_hash(kernel_file):
-    """SHA-256 of a kernel's source file and the headers of the kernel directory it includes."""
+    """SHA-256 of a kernel's source file and of the device headers it includes (headers that
+    hold only host-side declarations are left out)."""
+    import re
     h = hashlib.sha256()
-    for f in [os.path.join(CSRC, kernel_file)] + sorted(glob.glob(os.path.join(CSRC, "*.hpp"))):
-        with open(f, "rb") as fh:
+    path = os.path.join(CSRC, kernel_file)
+    with open(path, "rb") as fh:
+        text = fh.read()
+    h.update(text)
+    for inc in sorted(set(re.findall(rb'#include "([\w.]+\.hpp)"', text))):
+        if inc.decode() in HOST_ONLY_HEADERS:
+            continue
+        with open(os.path.join(CSRC, inc.decode()), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -354,6 +365,10 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, args, headline
     step = None
     if headline:
         dense = preps["dense_mfma"]
+        t_w = time.perf_counter()            # the clock ramps up from idle: warm up for at least 0.5 s
+        while time.perf_counter() - t_w < 0.5:
+            dense()
+            torch.cuda.synchronize()
         for _ in range(args.warmup):
             dense()
         torch.cuda.synchronize()
@@ -961,12 +976,24 @@ def summarize(kind, out, dirs, cmd_note):
     if kind == "trace":
         for d in dirs:
             rows = _read_csvs(d, "*kernel_stats.csv")
-            lines += [f"From `{os.path.basename(os.path.normpath(d))}`:", "",
+            lines += [f"From `{os.path.basename(os.path.normpath(d))}` (--stats, per kernel name):", "",
                       "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
             for r in sorted(rows, key=lambda r: -float(r.get("TotalDurationNs", 0))):
                 lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                              f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                              f"{float(r['Percentage']):.2f} |")
+            lines.append("")
+            per = {}
+            for r in _read_csvs(d, "*kernel_trace.csv"):
+                g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+                us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+                per.setdefault((name[:90], g), []).append(us)
+            lines += ["The same dispatches by kernel and grid (work-items); median and mean in us:", "",
+                      "| kernel | grid | calls | median us | mean us | min us |", "|---|---|---|---|---|---|"]
+            for (k, g), v in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+                v = sorted(v)
+                lines.append(f"| `{k}` | {g} | {len(v)} | {v[len(v) // 2]:.2f} | {sum(v) / len(v):.2f} | {v[0]:.2f} |")
             lines.append("")
     else:
         agg = {}
