@@ -1,6 +1,6 @@
 """Benchmark of the NVFP4 / 2:4 weight-GEMM hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,head,moe,w4a4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads decode,square,head,moe,w4a4,refs]
 
 Prints ONE JSON line. The headline (``value``, ``ms_per_step``, ``roofline``) is the prefill
 product, the largest of the workloads: X bf16 [8192, 5120] ~ N(0, 1) times dense NVFP4 weights
@@ -25,7 +25,9 @@ weight copies, and the weight-preparation calls on three rotating copies of W, e
 K = 5120, M = 1, 8, 9), ``moe`` (512 experts, top-10 of Zipf(1.1), D = 2048, I = 512: 4096
 tokens stage by stage, and 1-32 tokens on the weight-streaming kernels), ``w4a4`` (the W4A4
 variant at the prefill and square shapes: activations quantised to MXFP4 in every step, the FP4 x
-FP4 product on the block-scaled matrix cores, against the 10.1 PFLOP/s FP4 peak).
+FP4 product on the block-scaled matrix cores, against the 10.1 PFLOP/s FP4 peak), ``refs``
+(comparison points: the vendor bf16 GEMM at the prefill and square shapes, and a plain streaming
+read at the decode GEMV's size).
 ``cpu_baseline`` is the oracle's dense prefill product on the host cores.
 
     python bench.py --summarize KIND OUT DIR...
@@ -69,7 +71,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=30)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workloads", default="decode,square,head,moe,w4a4",
+    p.add_argument("--workloads", default="decode,square,head,moe,w4a4,refs",
                    help="comma list of workloads beside the prefill headline (which always runs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--summarize", nargs="+", metavar="ARG",
@@ -749,7 +751,7 @@ def run_moe_decode(torch, ssn, synth, x, up, down, sparse, E, k, D, I):
     res = {"weight_copies": MOE_RING, "weight_layout": "ktile64",
            "note": "stages timed over back-to-back calls, each on its own weight copy and routing draw (seeds "
                    "100..119)"}
-    tiles = ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
+    tiles = ssn.ALGO_SMFMAC if sparse else ssn.ALGO_MFMA
     for T in MOE_DECODE_TOKENS:
         R = T * k
         X = torch.from_numpy(x[:T].view("int16")).view(torch.bfloat16).cuda()
@@ -858,6 +860,47 @@ def run_w4a4(torch, ssn, synth, M, N, K, outliers, dense_us):
     del X, Y, xc, xs, wc, ws
     torch.cuda.empty_cache()
     return res
+
+
+# ------------------------------------------------------------------------------------------
+def run_references(torch, ssn, copy_gbps):
+    """Comparison points measured in the same run: the vendor bf16 GEMM (hipBLASLt through
+    torch.matmul, bf16 in and out, operands contiguous) at the prefill and square shapes, and
+    the plainest streaming read at the decode GEMV's size (sp24_check over 40 MB of zero codes,
+    on a ring of copies larger than the Infinity Cache)."""
+    out = {}
+    for name, (M, N, K) in (("prefill", (8192, 27648, 5120)), ("square", (4096, 4096, 4096))):
+        A = torch.randn(M, K, device="cuda").to(torch.bfloat16)
+        B = (torch.randn(K, N, device="cuda") * 0.02).to(torch.bfloat16).contiguous()
+        C = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        fn = lambda: torch.matmul(A, B, out=C)
+        T = Timer(torch)
+        T.batch("warm", [fn] * 3)
+        torch.cuda.synchronize()
+        T.batch("mm", [fn] * TRIALS)
+        T.each("mm", [fn] * TRIALS)
+        torch.cuda.synchronize()
+        us = T.us("mm")
+        out[f"bf16_gemm_vendor_{name}"] = {"us": round(us, 1), **T.stats("mm"), "shape": [M, N, K],
+                                           "tflops": round(2.0 * M * N * K / (us * 1e-6) / 1e12, 1),
+                                           "note": "torch.matmul bf16 x bf16 -> bf16 (hipBLASLt)"}
+        del A, B, C
+    torch.cuda.empty_cache()
+    n_bytes = 13824 * 2560                                  # the decode weights' codes (35.4 MB)
+    ring = [torch.zeros((13824, 2560), dtype=torch.uint8, device="cuda") for _ in range(24)]
+    calls = [ssn.sp24_check(r, prepare=True)[0] for r in ring]
+    T = Timer(torch)
+    T.batch("warm", calls)
+    torch.cuda.synchronize()
+    T.batch("read", calls * 2)
+    T.each("read", calls)
+    torch.cuda.synchronize()
+    us = T.us("read")
+    out["streaming_read_decode_size"] = {"us": round(us, 2), **T.stats("read"), **_bw(n_bytes, us, copy_gbps),
+                                         "note": "sp24_check over 35.4 MB of zero codes, 24 rotating copies"}
+    del ring, calls
+    torch.cuda.empty_cache()
+    return out
 
 
 # ------------------------------------------------------------------------------------------
@@ -1076,6 +1119,9 @@ def main():
     if "moe" in wl:
         work["moe"] = run_moe(torch, ssn, synth, hbm["copy_GBps"])
         print("[bench] moe done", file=sys.stderr, flush=True)
+    if "refs" in wl:
+        work["references"] = run_references(torch, ssn, hbm["copy_GBps"])
+        print("[bench] references done", file=sys.stderr, flush=True)
     if "w4a4" in wl:
         work["w4a4"] = {"prefill": run_w4a4(torch, ssn, synth, M, N, K, True, pre["dense_mfma"]["us"])}
         if "square" in work:

@@ -253,13 +253,14 @@ int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_
  * y_dtype. R: rows of Y (offsets are clamped into [0, R]); source rows are clamped into
  * [0, x_rows). Needs K % 64 == 0 and, for SILU_GATE, N even. w_layout: SSN_WLAYOUT_ROWS (the
  * arrays as above, as nvfp4_quantize / sp24_compress write them) or SSN_WLAYOUT_KTILE64 (all
- * three arrays as moe_pack_ktiles writes them). algo: MFMA (dense) or DECOMPRESS_MFMA (2:4,
+ * three arrays as moe_pack_ktiles writes them). algo: MFMA (dense), SMFMAC (2:4, the sparse
+ * matrix cores with the stored vals/meta as the compressed operand) or DECOMPRESS_MFMA (2:4,
  * expanded to a dense operand in registers) run 64-row x 256-column output tiles; STREAM (dense
  * or 2:4, N % 32 == 0) cuts the work along the weight rows instead, one wave per (expert, 32
  * weight rows, up to 32 routed rows), for routings with few rows per expert ("NVFP4 vs 2:4
  * sparse", robertz.co, section "Where a decode step actually spends itself": the expert weight
  * read is the cost). AUTO picks STREAM when N % 32 == 0 and R <= 4 E (dense) or R <= 10 E (2:4),
- * else the tiles.
+ * else the tiles (MFMA dense, SMFMAC 2:4).
  * algo_used: host, nullable.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, RANGE, HIP.
  * ------------------------------------------------------------------------------------------- */

@@ -308,13 +308,14 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   if (epilogue != SSN_EPI_NONE && epilogue != SSN_EPI_SILU_GATE)
     return fail(SSN_E_RANGE, "%s: unknown epilogue %d", fn, epilogue);
   if (epilogue == SSN_EPI_SILU_GATE && N % 2) return fail(SSN_E_SHAPE, "%s: SILU_GATE needs N even (N=%lld)", fn, (long long)N);
-  const int tiles = sparse ? SSN_ALGO_DECOMPRESS_MFMA : SSN_ALGO_MFMA;
+  const int tiles = sparse ? SSN_ALGO_SMFMAC : SSN_ALGO_MFMA;
   const bool can_stream = N % 32 == 0;
   // measured crossover (512 experts, D = 2048, I = 512): streaming wins up to ~4 rows per expert
   // for dense weights and ~10 for 2:4 weights
   const int64_t stream_max = (sparse ? 10 : 4) * (int64_t)E;
   const int chosen = algo == SSN_ALGO_AUTO ? (can_stream && R <= stream_max ? SSN_ALGO_STREAM : tiles) : algo;
-  if (chosen != tiles && chosen != SSN_ALGO_STREAM)
+  const bool tile_algo = chosen == tiles || (sparse && chosen == SSN_ALGO_DECOMPRESS_MFMA);
+  if (!tile_algo && chosen != SSN_ALGO_STREAM)
     return fail(SSN_E_ALGO, "%s: algorithm %d is not available for %s expert weights", fn, algo,
                 sparse ? "2:4" : "dense");
   if (chosen == SSN_ALGO_STREAM && !can_stream)
@@ -329,7 +330,7 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   if (sparse) REQUIRE_PTR(w_meta);
   ssn::MoeGemmArgs a{X, x_rows, K, row_token, expert_offsets, E, R, N, w_main, sparse ? w_meta : nullptr, w_scales,
                      tensor_scales, Y, y_dtype == SSN_BF16, sparse, epilogue == SSN_EPI_SILU_GATE,
-                     w_layout == SSN_WLAYOUT_KTILE64};
+                     w_layout == SSN_WLAYOUT_KTILE64, chosen == SSN_ALGO_SMFMAC};
   return hip_status(chosen == SSN_ALGO_STREAM ? ssn::launch_moe_stream(a, as_stream(stream))
                                               : ssn::launch_moe_gemm(a, as_stream(stream)), fn);
 }

@@ -323,7 +323,12 @@ __device__ bool find_tile(const int32_t* __restrict__ off, int E, int R, int bx,
   return true;
 }
 
-template <int WF, int EPI, int BM>
+// SMF (2:4 weights only): the products run on the sparse matrix cores, v_smfmac_f32_32x32x32_bf16
+// with the stored vals/meta as the compressed A operand (weights) and the activations as B, as in
+// the square/prefill tiles; the accumulators then hold the transposed tile, which the epilogue
+// undoes while staging. Otherwise the weights are expanded to dense codes and multiplied on
+// v_mfma_f32_32x32x16_bf16 (activations = A).
+template <int WF, int EPI, int BM, bool SMF = false>
 __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
     const uint16_t* __restrict__ X, int x_rows, int K, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ off, int E, int R, int N, const uint8_t* __restrict__ w0,
@@ -425,6 +430,43 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
     stage_barrier();            // ... for every wave; slot (st - 1) % kStages is no longer read
     issue(min(st + kStages - 1, last), lds + ((st + kStages - 1) % kStages) * L::kBytes);
     const char* slot = lds + (st % kStages) * L::kBytes;
+    if constexpr (SMF) {
+      static_assert(WF == kSp24, "the sparse matrix cores take 2:4 weights");
+      // A: weight rows (tile columns) 64 wave + 32 at + r32; lane half h holds the kept values of
+      // 16-blocks 2h and 2h + 1 of the stage (word t: block 2h + t), their positions and scales
+      u32x2 v[2];
+      uint32_t mw[2], sc[2];
+#pragma unroll
+      for (int at = 0; at < 2; ++at) {
+        const int tc = 64 * wave + 32 * at + r32;
+        v[at] = *(const u32x2*)(slot + L::kW + tc * 16 + 8 * h);
+        mw[at] = *(const uint32_t*)(slot + L::kMeta + tc * 8 + 4 * h);
+        sc[at] = *(const uint32_t*)(slot + L::kSc + tc * 4) >> (16 * h);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        // B: activation row 32 bt + r32, k chunks 2t + h and 4 + 2t + h of the stage
+        u32x8 bx[MT];
+#pragma unroll
+        for (int bt = 0; bt < MT; ++bt) {
+          const int r = 32 * bt + r32;
+          const u32x4 lo = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((2 * t + h) ^ swz(r)));
+          const u32x4 hi = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 + 2 * t + h) ^ swz(r)));
+          bx[bt][0] = lo[0]; bx[bt][1] = lo[1]; bx[bt][2] = lo[2]; bx[bt][3] = lo[3];
+          bx[bt][4] = hi[0]; bx[bt][5] = hi[1]; bx[bt][6] = hi[2]; bx[bt][7] = hi[3];
+        }
+#pragma unroll
+        for (int at = 0; at < 2; ++at) {
+          const float f = t == 0 ? e4m3_f32_sel<0>(sc[at]) : e4m3_f32_sel<1>(sc[at]);
+          const bf16x8 a = as_bf16x8(fp4x8_bf16(v[at][t], f));
+          const int idx = (int)((mw[at] >> (16 * t)) & 0xFFFFu);
+#pragma unroll
+          for (int bt = 0; bt < MT; ++bt)
+            acc[bt][at] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, as_bf16x16(bx[bt]), acc[bt][at], idx, 0, 0);
+        }
+      }
+      continue;
+    }
     u32x4 wc[2];
     uint32_t wsc[2];
 #pragma unroll
@@ -473,7 +515,10 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
   wait_vmcnt<0>();
   __syncthreads();   // ring slots are free for the epilogue staging
 
-  // lane holds rows 8(i/4) + 4h + i%4 of each 32-row block mt, tile column 64 wave + 32 nt + r32
+  // dense: lane holds rows 8(i/4) + 4h + i%4 of each 32-row block mt, tile column 64 wave + 32 nt
+  // + r32; SMF: the transpose, row r32 of block mt and tile column 64 wave + 32 nt + 8(i/4) + 4h + i%4
+  auto erow = [&](int i) { return SMF ? r32 : 8 * (i >> 2) + 4 * h + (i & 3); };
+  auto ecol = [&](int nt, int i) { return SMF ? 32 * nt + 8 * (i >> 2) + 4 * h + (i & 3) : 32 * nt + r32; };
   const float sc = ts[e];
   if constexpr (EPI == kEpiNone) {
     const bool vec = (N & 3) == 0;
@@ -484,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          T[(8 * (i >> 2) + 4 * h + (i & 3)) * kStageStrideNone + 32 * nt + r32] = acc[mt][nt][i] * sc;
+          T[erow(i) * kStageStrideNone + ecol(nt, i)] = acc[mt][nt][i] * sc;
       __builtin_amdgcn_s_waitcnt(0xC07F);
       const int c4 = lane & 15;
 #pragma unroll
@@ -508,7 +553,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            U[(32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * S + 64 * (wave - 2) + 32 * nt + r32] = acc[mt][nt][i] * sc;
+            U[(32 * mt + erow(i)) * S + 64 * (wave - 2) + ecol(nt, i)] = acc[mt][nt][i] * sc;
     }
     __syncthreads();
     if (wave < 2) {
@@ -518,7 +563,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float* p = U + (32 * mt + 8 * (i >> 2) + 4 * h + (i & 3)) * S + 64 * wave + 32 * nt + r32;
+            float* p = U + (32 * mt + erow(i)) * S + 64 * wave + ecol(nt, i);
             const float g = acc[mt][nt][i] * sc;
             *p = g / (1.0f + expf(-g)) * *p;      // silu(g) * u
           }
@@ -831,11 +876,11 @@ __global__ __launch_bounds__(256) void k_moe_combine(const void* __restrict__ Yd
   }
 }
 
-template <int WF, int EPI, int BM>
+template <int WF, int EPI, int BM, bool SMF = false>
 hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   constexpr int bytes = moe_lds_bytes<WF, BM>();
   static_assert(2 * bytes <= 160 * 1024, "LDS budget: 64-row tiles run at least two workgroups per CU");
-  hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM>,
+  hipError_t e = hipFuncSetAttribute((const void*)k_moe_gemm<WF, EPI, BM, SMF>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   // upper bound of the tile count: R / BM + min(E, R) (each expert's last tile may be partial)
@@ -843,7 +888,7 @@ hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   const int ntiles = EPI == kEpiSilu ? (int)((a.N / 2 + 127) / 128) : (int)((a.N + kBN - 1) / kBN);
   if (tiles * ntiles > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM>), dim3((unsigned)(tiles * ntiles)), dim3(kThreads), bytes, s,
+  hipLaunchKernelGGL((k_moe_gemm<WF, EPI, BM, SMF>), dim3((unsigned)(tiles * ntiles)), dim3(kThreads), bytes, s,
                      a.X, (int)a.x_rows, (int)a.K, a.row_token, a.offsets, a.E, (int)a.R, (int)a.N, a.w0, a.w1,
                      a.scales, a.ts, a.Y, a.y_bf16, ntiles, a.ktiled);
   return hipGetLastError();
@@ -851,6 +896,8 @@ hipError_t launch_moe_gemm_t(const MoeGemmArgs& a, hipStream_t s) {
 
 template <int WF, int EPI>
 hipError_t launch_moe_gemm_both(const MoeGemmArgs& a, hipStream_t s) {
+  if constexpr (WF == kSp24)
+    if (a.smfmac) return launch_moe_gemm_t<WF, EPI, 64, true>(a, s);
   return launch_moe_gemm_t<WF, EPI, 64>(a, s);
 }
 

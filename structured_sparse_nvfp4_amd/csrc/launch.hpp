@@ -63,6 +63,7 @@ struct MoeGemmArgs {
   void* Y;                  // [R, N] (or [R, N/2] for the SiLU-gate form)
   int y_bf16, sparse, silu;
   int ktiled;               // weights (all three arrays) in the 64-k tiled layout [E][K/64][N][piece]
+  int smfmac = 0;           // 2:4 tiles on the sparse matrix cores (else expanded to dense)
 };
 
 size_t moe_route_workspace(int64_t F, int E);

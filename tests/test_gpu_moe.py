@@ -107,11 +107,22 @@ def test_pack_ktiles_matches_definition(piece):
         assert np.array_equal(got, _ktiles(a, piece))
 
 
-@pytest.mark.parametrize("algo", ["tiles", "stream"])
+def _tile_algo(algo, sparse):
+    """The algorithm a parametrised grouped-product test asks for (AUTO for the default tiles)."""
+    if algo == "stream":
+        return ssn.ALGO_STREAM, ssn.ALGO_STREAM
+    if algo == "tiles_expand":
+        return ssn.ALGO_DECOMPRESS_MFMA, ssn.ALGO_DECOMPRESS_MFMA
+    return ssn.ALGO_AUTO, (ssn.ALGO_SMFMAC if sparse else ssn.ALGO_MFMA)
+
+
+@pytest.mark.parametrize("algo", ["tiles", "tiles_expand", "stream"])
 @pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
 @pytest.mark.parametrize("gather", [True, False])
 def test_grouped_product_rows(sparse, gather, layout, algo):
+    if algo == "tiles_expand" and not sparse:
+        pytest.skip("the expanded-dense tiles are a 2:4 algorithm")
     T, E, k, N, K = 90, 6, 3, 320, 192
     x = synth.activations(T, K, seed=11)
     ids = np.random.default_rng(3).integers(0, E, size=(T, k)).astype(np.int32)
@@ -129,9 +140,8 @@ def test_grouped_product_rows(sparse, gather, layout, algo):
         x = x[rts]
     if layout == ssn.WLAYOUT_KTILE64:
         dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
-    want = ssn.ALGO_STREAM if algo == "stream" else ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
-    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta, w_layout=layout,
-                                         algo=ssn.ALGO_STREAM if algo == "stream" else ssn.ALGO_AUTO)
+    ask, want = _tile_algo(algo, sparse)
+    y, used = ssn.moe_grouped_gemm_nvfp4(X, rtok, off, R, dm, dsc, dts, w_meta=dmeta, w_layout=layout, algo=ask)
     assert used == want
     yh = y_host(y)
     for e in range(E):
@@ -142,10 +152,12 @@ def test_grouped_product_rows(sparse, gather, layout, algo):
         assert_within_bound(yh[r0:r1], Y, B, what=f"expert {e}")
 
 
-@pytest.mark.parametrize("algo", ["tiles", "stream"])
+@pytest.mark.parametrize("algo", ["tiles", "tiles_expand", "stream"])
 @pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
 @pytest.mark.parametrize("sparse", [False, True])
 def test_grouped_silu_gate(sparse, layout, algo):
+    if algo == "tiles_expand" and not sparse:
+        pytest.skip("the expanded-dense tiles are a 2:4 algorithm")
     T, E, k, D, I = 70, 5, 2, 128, 160
     x = synth.activations(T, D, seed=12)
     ids = np.random.default_rng(4).integers(0, E, size=(T, k)).astype(np.int32)
@@ -155,11 +167,10 @@ def test_grouped_silu_gate(sparse, layout, algo):
     R = T * k
     if layout == ssn.WLAYOUT_KTILE64:
         dm, dmeta, dsc, dts = ssn.moe_pack_weights((dm, dmeta, dsc, dts))
-    tiles = ssn.ALGO_DECOMPRESS_MFMA if sparse else ssn.ALGO_MFMA
-    al = ssn.ALGO_STREAM if algo == "stream" else tiles
+    ask, want = _tile_algo(algo, sparse)
     H, used = ssn.moe_grouped_gemm_nvfp4(x_dev(x), rt, off, R, dm, dsc, dts, w_meta=dmeta,
-                                         epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, w_layout=layout, algo=al)
-    assert used == al
+                                         epilogue=ssn.EPI_SILU_GATE, y_dtype=torch.bfloat16, w_layout=layout, algo=ask)
+    assert used == want
     Hh = y_host(H)
     offs, rts = host(off).astype(np.int64), host(rt).astype(np.int64)
     for e in range(E):
