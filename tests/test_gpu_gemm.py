@@ -33,7 +33,7 @@ DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 6
                (3, 24608, 512), (8, 24608, 512),  # >= 3 row groups per CU: the 80-register fold form
                # K % 256 == 0 but K % 512 != 0 (the decode slabs' partial last stage), M <= 8 and 9..16
                (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
-               # few row groups (all resident): the deep-ring post-scale slab for every activation-row count
+               # few row groups per CU, every activation-row count of the post-scale slab
                (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536), (7, 333, 3072)]
 
 
@@ -58,7 +58,7 @@ SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64
               (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024),
               # K % 256 == 0 but K % 512 != 0: the slab kernels' partial last stage (8- and 16-wave forms)
               (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
-              # few row groups (all resident): the deep-ring 2:4 slab for every activation-row count
+              # few row groups per CU, every activation-row count of the 2:4 slab
               (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536)]
 
 
