@@ -191,17 +191,39 @@ def gpu_state():
     return out
 
 
-def state_under_load(torch, fn, seconds=1.5):
-    """GPU state read while `fn` launches keep the GPU busy for about `seconds`, plus idle
-    readings before and after."""
+def _sclk_now():
+    try:
+        for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+            for line in open(f):
+                if line.startswith("S:") or line.rstrip().endswith("*"):
+                    return int(line.split(":")[1].strip().split("M")[0])
+    except (OSError, ValueError, IndexError):
+        pass
+    return None
+
+
+def state_under_load(torch, fn, seconds=3.0):
+    """GPU state while `fn` launches keep the GPU busy for about `seconds`: the clock (sysfs)
+    sampled five times, then one amd-smi reading (power, temperatures, clocks), all taken while
+    the queued launches still run; plus idle readings before and after."""
     before = gpu_state()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(); fn(); b.record(); b.synchronize()
     n = max(1, int(seconds / max(a.elapsed_time(b) * 1e-3, 1e-5)))
+    done = torch.cuda.Event()
     for _ in range(n):
         fn()
-    time.sleep(min(0.4, seconds / 3))
+    done.record()
+    time.sleep(0.3)
+    sclk = []
+    for _ in range(5):
+        v = _sclk_now()
+        if v is not None:
+            sclk.append(v)
+        time.sleep(0.1)
     during = gpu_state()
+    during["sclk_samples_MHz"] = sclk
+    during["still_running"] = not done.query()
     torch.cuda.synchronize()
     return {"before": before, "during": during, "after": gpu_state()}
 
@@ -899,6 +921,20 @@ def run_references(torch, ssn, copy_gbps):
     out["streaming_read_decode_size"] = {"us": round(us, 2), **T.stats("read"), **_bw(n_bytes, us, copy_gbps),
                                          "note": "sp24_check over 35.4 MB of zero codes, 24 rotating copies"}
     del ring, calls
+    src = [torch.zeros(n_bytes, dtype=torch.uint8, device="cuda") for _ in range(12)]
+    dst = [torch.empty_like(t) for t in src]
+    calls = [(lambda a=a, b=b: b.copy_(a)) for a, b in zip(src, dst)]
+    T = Timer(torch)
+    T.batch("warm", calls)
+    torch.cuda.synchronize()
+    T.batch("copy", calls * 2)
+    T.each("copy", calls * 2)
+    torch.cuda.synchronize()
+    us = T.us("copy")
+    out["device_copy_decode_size"] = {"us": round(us, 2), **T.stats("copy"),
+                                      "GBps_read_plus_write": round(2 * n_bytes / (us * 1e-6) / 1e9, 1),
+                                      "note": "torch copy_ of 35.4 MB (read and written), 12 rotating pairs"}
+    del src, dst, calls
     torch.cuda.empty_cache()
     return out
 
