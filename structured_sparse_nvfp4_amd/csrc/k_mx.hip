@@ -18,6 +18,7 @@
 // R is padded to a multiple of 32 and K to a multiple of 256 with zero codes and scale byte 0
 // (value 0 x 2^-127 = 0), so padding adds nothing to a product.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 #include "device_once.hpp"
@@ -129,17 +130,22 @@ __global__ __launch_bounds__(256) void k_mx_pad(int64_t R, int64_t K, uint8_t* _
 // ---------------------------------------------------------------------------------------------
 // product: Y = X_hat . W_hat^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1).
 // 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns 128 x 128 (4 x 4 blocks
-// of 32 x 32). A K stage is 256 wide (four MFMA steps): X and W pieces of the tile's eight row
-// blocks each (8 x 4 KB), their scales (8 x 256 B each); two stages resident, loaded by the
-// direct-to-LDS copies one stage ahead.
+// of 32 x 32). A K stage is 128 wide (two MFMA steps): X and W pieces of the tile's eight row
+// blocks each (8 x 2 KB), and the scale pieces of the 256-wide group the stage belongs to (8 x
+// 256 B each; the two stages of a group load the same piece). Four ring slots, so three stages
+// are in flight while one is multiplied; a slot is refilled right after the barrier that shows
+// every wave is done with it. Each step's operands are read from LDS while the previous step's
+// MFMAs run.
 constexpr int kMT = 256, kMN = 256;
 constexpr int kMxThreads = 256;
 constexpr int kMxBlocks = 8;                          // 32-row blocks per tile side
-constexpr int kMxStageX = kMxBlocks * 4096;           // codes of the tile's rows for one stage
-constexpr int kMxStageS = kMxBlocks * 256;            // their scales
+constexpr int kMxSlots = 4;                           // ring slots (stages of 128 K)
+constexpr int kMxStageX = kMxBlocks * 2048;           // codes of the tile's rows for one stage
+constexpr int kMxStageS = kMxBlocks * 256;            // the scale pieces of their 256-wide group
 constexpr int kMxSlot = 2 * kMxStageX + 2 * kMxStageS;   // X codes, W codes, X scales, W scales
-constexpr int kMxLds = 2 * kMxSlot;
-constexpr int kMxLoads = 2 * 2 * 4 + 2 * 2;           // per wave per stage: 16 one-KB code copies, 4 scale copies
+constexpr int kMxLds = kMxSlots * kMxSlot;
+constexpr int kMxLoads = 2 * 2 * 2 + 2 * 2;           // per wave per stage: 8 one-KB code copies, 4 scale copies
+static_assert(kMxLds <= 160 * 1024, "LDS budget");
 
 constexpr int kXcds = 8, kGroupM = 4;
 __device__ __forceinline__ void mx_tile_of(int b, int total, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -156,16 +162,13 @@ __device__ __forceinline__ void mx_tile_of(int b, int total, int tiles_m, int ti
   tn = tin / gsize;
 }
 
-__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb, int step) {
+// format 4 = E2M1 for both operands; the scale byte of step S of a 256-wide group is byte S of
+// the lane's scale word (op_sel)
+template <int S>
+__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t sa, uint32_t sb) {
   const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
   const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-  // format 4 = E2M1 for both operands; the scale byte of step s is byte s of the scale word
-  switch (step) {
-    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
-    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 1, (int)sa, 1, (int)sb);
-    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 2, (int)sa, 2, (int)sb);
-    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 3, (int)sa, 3, (int)sb);
-  }
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, S, (int)sa, S, (int)sb);
 }
 
 __global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -177,7 +180,7 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
   const int tiles_m = (M + kMT - 1) / kMT, tiles_n = (N + kMN - 1) / kMN;
   int tm, tn;
   mx_tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
-  const int k64 = (K + 255) / 256 * 4, k256 = k64 / 4, nst = k256;
+  const int k64 = (K + 255) / 256 * 4, k256 = k64 / 4, nst = 2 * k256;   // nst is even
   const int mb_last = (M + 31) / 32 - 1, nb_last = (N + 31) / 32 - 1;
   // this wave copies row blocks 2 wave, 2 wave + 1 of X and of W (clamped to the last block of
   // the padded layout; their results are not stored) and their scale pieces
@@ -188,19 +191,18 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const size_t xo = ((size_t)xbs[i] * k64 + 4 * st + s) * 1024 + 16 * lane;
-        const size_t wo = ((size_t)wbs[i] * k64 + 4 * st + s) * 1024 + 16 * lane;
-        lds_dma16(xc + xo, slot + (2 * wave + i) * 4096 + s * 1024);
-        lds_dma16(wc + wo, slot + kMxStageX + (2 * wave + i) * 4096 + s * 1024);
+      for (int s = 0; s < 2; ++s) {
+        const size_t xo = ((size_t)xbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
+        const size_t wo = ((size_t)wbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
+        lds_dma16(xc + xo, slot + (2 * wave + i) * 2048 + s * 1024);
+        lds_dma16(wc + wo, slot + kMxStageX + (2 * wave + i) * 2048 + s * 1024);
       }
     }
-    // scale pieces: 256 bytes per block and stage; lane l copies 4 bytes of block 2 wave + l / 64
-    // ... as two 4-byte copies of 64 lanes (one per block) for X and for W
+    // scale pieces of the stage's 256-wide group: 256 bytes per block, 4 bytes per lane
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const size_t so_x = ((size_t)xbs[i] * k256 + st) * 256 + 4 * lane;
-      const size_t so_w = ((size_t)wbs[i] * k256 + st) * 256 + 4 * lane;
+      const size_t so_x = ((size_t)xbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
+      const size_t so_w = ((size_t)wbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
       lds_dma4(xs + so_x, slot + 2 * kMxStageX + (2 * wave + i) * 256);
       lds_dma4(ws + so_w, slot + 2 * kMxStageX + kMxStageS + (2 * wave + i) * 256);
     }
@@ -214,34 +216,45 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
 #pragma unroll
       for (int t = 0; t < 16; ++t) acc[i][j][t] = 0.f;
 
-  issue(0, lds);
-  issue(min(1, nst - 1), lds + kMxSlot);
-  for (int st = 0; st < nst; ++st) {
-    char* slot = lds + (st & 1) * kMxSlot;
-    wait_vmcnt<kMxLoads>();               // stage st has landed (stage st + 1 may be in flight)
-    stage_barrier();
+  auto read_ops = [&](const char* slot, int s, u32x4 (&a)[4], u32x4 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[i] = *(const u32x4*)(slot + (4 * wm + i) * 2048 + s * 1024 + 16 * lane);
+      b[i] = *(const u32x4*)(slot + kMxStageX + (4 * wn + i) * 2048 + s * 1024 + 16 * lane);
+    }
+  };
+  // stage st (parity P: steps 2P, 2P + 1 of its 256-wide group) from slot st % kMxSlots
+  auto stage = [&](auto parity, int st) {
+    constexpr int P = decltype(parity)::value;
+    const char* slot = lds + (st % kMxSlots) * kMxSlot;
+    wait_vmcnt<2 * kMxLoads>();           // stage st has landed (st + 1, st + 2 may be in flight)
+    stage_barrier();                      // ... for every wave; slot (st - 1) % kMxSlots is free
+    issue(min(st + 3, nst - 1), lds + ((st + 3) % kMxSlots) * kMxSlot);   // past the end: a repeat, unused
     uint32_t sa[4], sb[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       sa[i] = *(const uint32_t*)(slot + 2 * kMxStageX + (4 * wm + i) * 256 + 4 * lane);
       sb[i] = *(const uint32_t*)(slot + 2 * kMxStageX + kMxStageS + (4 * wn + i) * 256 + 4 * lane);
     }
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+    read_ops(slot, 0, a0, b0);
+    read_ops(slot, 1, a1, b1);            // step 1's operands are read while step 0 multiplies
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 a[4], b[4];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = *(const u32x4*)(slot + (4 * wm + i) * 4096 + s * 1024 + 16 * lane);
-        b[i] = *(const u32x4*)(slot + kMxStageX + (4 * wn + i) * 4096 + s * 1024 + 16 * lane);
-      }
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4<2 * P>(a0[i], b0[j], acc[i][j], sa[i], sb[j]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4(a[i], b[j], acc[i][j], sa[i], sb[j], s);
-    }
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's reads of the slot are done
-    stage_barrier();                      // ... and every wave's: the slot can be refilled
-    issue(min(st + 2, nst - 1), slot);    // past the end the last stage is copied again (not used)
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4<2 * P + 1>(a1[i], b1[j], acc[i][j], sa[i], sb[j]);
+  };
+
+  issue(0, lds);
+  issue(1, lds + kMxSlot);
+  issue(min(2, nst - 1), lds + 2 * kMxSlot);
+  for (int st = 0; st < nst; st += 2) {
+    stage(std::integral_constant<int, 0>{}, st);
+    stage(std::integral_constant<int, 1>{}, st + 1);
   }
   wait_vmcnt<0>();
   __syncthreads();
