@@ -423,8 +423,9 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
 // Three 8-wave workgroups fit a CU by LDS (3 x 52.6 KB dense, 3 x 46 KB 2:4) when a wave keeps
-// to 80 registers (six waves per SIMD); at 84 and more only two fit. The 2:4 slab needs 94
-// (forced to 80 it spills), so it runs two.
+// to 80 registers (six waves per SIMD); at 84 and more only two fit. The 2:4 slab below keeps to
+// 80 as well (measured at N = 131072, M = 1..8: 82-88 us with two workgroups per CU, 72-80 us
+// with three).
 constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
@@ -543,9 +544,10 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, two per
-// CU, 32-row groups, 512-wide K stages in a ring of kP4Stages LDS slots), with every direct load
-// a full 1 KB instruction: waves 0-3 load the vals of rows 8w..8w+7 (128 B each), waves 4-5 the
+// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, three
+// per CU, 32-row groups, 512-wide K stages in a ring of kP4Stages LDS slots), with every direct
+// load a full 1 KB buffer load (one wave-uniform resource per group, one 32-bit offset per lane,
+// so a wave keeps to 80 registers): waves 0-3 load the vals of rows 8w..8w+7 (128 B each), waves 4-5 the
 // meta of rows 16(w-4)..+15 (64 B each), wave 6 the scales of all 32 rows (32 B each), and wave
 // m < M activation row m. Wave w then multiplies the 64-wide K chunk w of the stage for all 32
 // rows: two v_smfmac_f32_32x32x32_bf16 with the stored vals/meta as the compressed A operand and
@@ -558,44 +560,66 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 // [8][1 KB + 16 B].
 constexpr int kP4Stages = 3;
 static_assert(kP4Stages >= 2 && kP4Stages <= 5, "wait_stages covers up to three stages in flight");
-constexpr int kP4VOff = 0, kP4MOff = kPsRows * (kSK / 4), kP4SOff = kP4MOff + kPsRows * (kSK / 8);
-constexpr int kP4XOff = kP4SOff + kPsRows * kSRow;
-constexpr int kP4Bytes = kP4XOff + kPsMaxM * kPsXRow;
 
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(5))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
+// One ring slot of the 2:4 slab (512-wide stage, 32 rows, up to kPsMaxM activation rows).
+struct P4Slot {
+  static constexpr int kV = kSK / 4, kMt = kSK / 8, kSc = kSK / 16;   // bytes per row per stage
+  static constexpr int kVP = kV / 16, kMP = kMt / 16, kSP = kSc / 16;   // 16-byte pieces per row
+  static constexpr int kVOff = 0, kMOff = kPsRows * kV, kSOff = kMOff + kPsRows * kMt;
+  static constexpr int kXOff = kSOff + kPsRows * kSc;
+  static constexpr int kBytes = kXOff + kPsMaxM * kPsXRow;
+  static constexpr int kVLoads = kPsRows * kV / 1024, kMLoads = kPsRows * kMt / 1024, kSLoads = kPsRows * kSc / 1024;
+  static constexpr int kLoads = kVLoads + kMLoads + kSLoads;           // 1 KB weight loads per stage (7)
+  static_assert(kLoads <= kPsWaves, "one weight load per wave");
+};
+
+// 16-byte piece swizzles of a vals row (8 pieces) and a meta row (4 pieces)
+__device__ __forceinline__ int p4_vswz(int r) { return r & 7; }
+__device__ __forceinline__ int p4_mswz(int r) { return (r >> 1) & 3; }
+
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
                                                              const uint8_t* __restrict__ vals,
                                                              const uint8_t* __restrict__ meta,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ ts, void* __restrict__ Y,
                                                              int y_bf16, int R) {
+  using L = P4Slot;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
   const int nst = K / kSK;
   const int h = lane >> 5, nl = lane & 31;
   const int xm = nl < M ? nl : 0;
-  // direct loads of this wave per stage
-  const int nload = (wave < 7 ? 1 : 0) + (wave < M ? 1 : 0);
+  // direct loads of this wave per stage: weight load `wave` (waves < 7), activation row `wave`
+  const int nload = (wave < L::kLoads ? 1 : 0) + (wave < M ? 1 : 0);
+  const auto xr = buf_rsrc(X + (size_t)min(wave, M - 1) * K);
+  // this wave's weight load: row r of the group (rows past the block repeat its last row) and
+  // byte offset poff in it, from a buffer resource at the group's first row; a stage adds its
+  // wave-uniform K offset
+  const uint8_t* wbase;
+  int r;
+  uint32_t poff, rowb, kstep, wdst;   // rowb: bytes of a row; kstep: bytes of a row per stage
+  if (wave < L::kVLoads) {
+    r = wave * (1024 / L::kV) + lane / L::kVP;
+    poff = 16u * ((lane % L::kVP) ^ p4_vswz(r));
+    wbase = vals; rowb = K / 4; kstep = L::kV; wdst = L::kVOff + wave * 1024;
+  } else if (wave < L::kVLoads + L::kMLoads) {
+    const int i = wave - L::kVLoads;
+    r = i * (1024 / L::kMt) + lane / L::kMP;
+    poff = 16u * ((lane % L::kMP) ^ p4_mswz(r));
+    wbase = meta; rowb = K / 8; kstep = L::kMt; wdst = L::kMOff + i * 1024;
+  } else {
+    r = lane / L::kSP;
+    poff = 16u * (lane % L::kSP);
+    wbase = scales; rowb = K / 16; kstep = L::kSc; wdst = L::kSOff;
+  }
   for (int g0 = row_lo; g0 < row_hi; g0 += kPsRows) {
+    const auto wr = buf_rsrc(wbase + (size_t)g0 * rowb);
+    const uint32_t voff = (uint32_t)min(r, row_hi - 1 - g0) * rowb + poff;
     auto issue = [&](int st) {
-      uint8_t* b = smem + (st % kP4Stages) * kP4Bytes;
-      const int k0 = st * kSK;
-      if (wave < 4) {                              // vals: rows 8w + l/8, piece l % 8
-        const int r = 8 * wave + (lane >> 3);
-        const int n = min(g0 + r, row_hi - 1);
-        const int q = (lane & 7) ^ (r & 7);
-        lds_dma16(vals + (size_t)n * (K / 4) + k0 / 4 + 16 * q, b + kP4VOff + wave * 1024);
-      } else if (wave < 6) {                       // meta: rows 16(w - 4) + l/4, piece l % 4
-        const int r = 16 * (wave - 4) + (lane >> 2);
-        const int n = min(g0 + r, row_hi - 1);
-        const int q = (lane & 3) ^ ((r >> 1) & 3);
-        lds_dma16(meta + (size_t)n * (K / 8) + k0 / 8 + 16 * q, b + kP4MOff + (wave - 4) * 1024);
-      } else if (wave == 6) {                      // scales: rows l/2, piece l % 2
-        const int r = lane >> 1;
-        const int n = min(g0 + r, row_hi - 1);
-        lds_dma16(scales + (size_t)n * (K / 16) + k0 / 16 + 16 * (lane & 1), b + kP4SOff);
-      }
-      if (wave < M) lds_dma16(X + (size_t)wave * K + k0 + 8 * lane, b + kP4XOff + wave * kPsXRow);
+      uint8_t* b = smem + (st % kP4Stages) * L::kBytes;
+      if (wave < L::kLoads) lds_dma16(wr, voff, (uint32_t)st * kstep, b + wdst);
+      if (wave < M) lds_dma16(xr, 16u * lane, (uint32_t)st * (2 * kSK), b + L::kXOff + wave * kPsXRow);
     };
     f32x16 acc;
 #pragma unroll
@@ -611,16 +635,16 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(5
       else wait_vmcnt<0>();
       stage_barrier();
       if (st + kP4Stages - 1 < nst) issue(st + kP4Stages - 1);
-      const uint8_t* b = smem + (st % kP4Stages) * kP4Bytes;
-      const u32x2 v = *(const u32x2*)(b + kP4VOff + nl * (kSK / 4) + 16 * (wave ^ (nl & 7)) + 8 * h);
-      const uint32_t mw = *(const uint32_t*)(b + kP4MOff + nl * (kSK / 8) + 16 * ((wave >> 1) ^ ((nl >> 1) & 3)) +
+      const uint8_t* b = smem + (st % kP4Stages) * L::kBytes;
+      const u32x2 v = *(const u32x2*)(b + L::kVOff + nl * L::kV + 16 * (wave ^ p4_vswz(nl)) + 8 * h);
+      const uint32_t mw = *(const uint32_t*)(b + L::kMOff + nl * L::kMt + 16 * ((wave >> 1) ^ p4_mswz(nl)) +
                                              8 * (wave & 1) + 4 * h);
-      const uint32_t sw = *(const uint16_t*)(b + kP4SOff + nl * kSRow + 4 * wave + 2 * h);
-      const uint8_t* xr = b + kP4XOff + xm * kPsXRow + 2 * (64 * wave + 8 * h);
+      const uint32_t sw = *(const uint16_t*)(b + L::kSOff + nl * L::kSc + 4 * wave + 2 * h);
+      const uint8_t* xrow = b + L::kXOff + xm * kPsXRow + 2 * (64 * wave + 8 * h);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const u32x4 lo = *(const u32x4*)(xr + 2 * (16 * t));
-        const u32x4 hi = *(const u32x4*)(xr + 2 * (32 + 16 * t));
+        const u32x4 lo = *(const u32x4*)(xrow + 2 * (16 * t));
+        const u32x4 hi = *(const u32x4*)(xrow + 2 * (32 + 16 * t));
         u32x8 bx;
         bx[0] = lo[0]; bx[1] = lo[1]; bx[2] = lo[2]; bx[3] = lo[3];
         bx[4] = hi[0]; bx[5] = hi[1]; bx[6] = hi[2]; bx[7] = hi[3];
@@ -830,13 +854,12 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   if (a.M <= kPsMaxM && a.K % kSK == 0) {   // full-width loads, 32x32x32 sparse MFMA per 64-k chunk
     static PerDeviceOnce p4_once;
     hipError_t e2 = once_per_device(p4_once, [] {
-      return hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 kP4Stages * kP4Bytes);
+      return hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Stages * P4Slot::kBytes);
     });
     if (e2 != hipSuccess) return e2;
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
-    hipLaunchKernelGGL(k_gemv_ps24, dim3(G), dim3(kPsWaves * 64), kP4Stages * kP4Bytes, s, a.X, (int)a.M, (int)a.N,
+    hipLaunchKernelGGL(k_gemv_ps24, dim3(G), dim3(kPsWaves * 64), kP4Stages * P4Slot::kBytes, s, a.X, (int)a.M, (int)a.N,
                        (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }

@@ -56,6 +56,8 @@ SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64
               # M <= 8, K % 512 == 0 (full-width-load decode kernel): ragged row groups, several
               # row groups per workgroup (N > 512 x 32), every M
               (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024),
+              # M = 1, K % 1024 == 0: the 1024-wide stage form
+              (1, 1000, 1024), (1, 17000, 2048), (1, 33, 3072),
               # K % 256 == 0 but K % 512 != 0: the slab kernels' partial last stage (8- and 16-wave forms)
               (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
               # few row groups per CU, every activation-row count of the 2:4 slab
