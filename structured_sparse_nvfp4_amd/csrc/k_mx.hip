@@ -129,28 +129,30 @@ __global__ __launch_bounds__(256) void k_mx_pad(int64_t R, int64_t K, uint8_t* _
 
 // ---------------------------------------------------------------------------------------------
 // product: Y = X_hat . W_hat^T on v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1 x E2M1).
-// 256 x 256 output tile per workgroup of four waves; wave (wm, wn) owns 128 x 128 (4 x 4 blocks
-// of 32 x 32). A K stage is 128 wide (two MFMA steps): X and W pieces of the tile's eight row
-// blocks each (8 x 2 KB), and the scale pieces of the 256-wide group the stage belongs to (8 x
-// 256 B each; the two stages of a group load the same piece). Four ring slots, so three stages
-// are in flight while one is multiplied; a slot is refilled right after the barrier that shows
-// every wave is done with it. Each step's operands are read from LDS while the previous step's
-// MFMAs run.
+// 256 x 256 output tile per workgroup of NWV waves: wave (wm, wn) owns 128 rows x 256 / (NWV / 2)
+// columns (4 x NBK blocks of 32 x 32). A K stage is 128 wide (two MFMA steps): X and W pieces of
+// the tile's eight row blocks each (8 x 2 KB), and the scale pieces of the 256-wide group the
+// stage belongs to (8 x 256 B each; the two stages of a group load the same piece). Four ring
+// slots, so three stages are in flight while one is multiplied; a slot is refilled right after
+// the barrier that shows every wave is done with it. Each step's operands are read from LDS while
+// the previous step's MFMAs run. Eight waves (two per SIMD, 128 x 64 each) measured 7% faster
+// than four (128 x 128 each) at 8192 x 27648 x 5120 and 10% at 4096^3: while one wave waits on
+// LDS or the barrier the other's matrix ops run, and the operands need no decode, so the second
+// wave adds no vector-ALU work.
 constexpr int kMT = 256, kMN = 256;
-constexpr int kMxThreads = 256;
 constexpr int kMxBlocks = 8;                          // 32-row blocks per tile side
 constexpr int kMxSlots = 4;                           // ring slots (stages of 128 K)
 constexpr int kMxStageX = kMxBlocks * 2048;           // codes of the tile's rows for one stage
 constexpr int kMxStageS = kMxBlocks * 256;            // the scale pieces of their 256-wide group
 constexpr int kMxSlot = 2 * kMxStageX + 2 * kMxStageS;   // X codes, W codes, X scales, W scales
 constexpr int kMxLds = kMxSlots * kMxSlot;
-constexpr int kMxLoads = 2 * 2 * 2 + 2 * 2;           // per wave per stage: 8 one-KB code copies, 4 scale copies
+constexpr int kMxWaves = 8;
 static_assert(kMxLds <= 160 * 1024, "LDS budget");
 
 constexpr int kXcds = 8, kGroupM = 4;
 __device__ __forceinline__ void mx_tile_of(int b, int total, int tiles_m, int tiles_n, int& tm, int& tn) {
   // consecutive logical tiles share an XCD (workgroups are dealt to the eight XCDs round-robin)
-  // and walk down GROUP tile rows before moving right
+  // and walk down kGroupM tile rows before moving right (4, 8 and 16 measured alike)
   const int per = total / kXcds, extra = total % kXcds;
   const int x = b % kXcds, idx = b / kXcds;
   const int t = x * per + min(x, extra) + idx;
@@ -171,82 +173,88 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, S, (int)sa, S, (int)sb);
 }
 
-__global__ __launch_bounds__(kMxThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int M, const uint8_t* __restrict__ wc,
                const uint8_t* __restrict__ ws, int N, int K, void* __restrict__ Y, int y_bf16) {
+  constexpr int BPW = kMxBlocks / NWV;                // row blocks of X and of W each wave copies
+  constexpr int WN = NWV / 2, NBK = kMxBlocks / WN;   // waves along N, W blocks per wave
+  constexpr int kLoads = BPW * 2 * 2 + BPW * 2;       // per wave per stage: code copies, scale copies
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int tiles_m = (M + kMT - 1) / kMT, tiles_n = (N + kMN - 1) / kMN;
   int tm, tn;
   mx_tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
   const int k64 = (K + 255) / 256 * 4, k256 = k64 / 4, nst = 2 * k256;   // nst is even
   const int mb_last = (M + 31) / 32 - 1, nb_last = (N + 31) / 32 - 1;
-  // this wave copies row blocks 2 wave, 2 wave + 1 of X and of W (clamped to the last block of
-  // the padded layout; their results are not stored) and their scale pieces
-  const int xb0 = min(8 * tm + 2 * wave, mb_last), xb1 = min(8 * tm + 2 * wave + 1, mb_last);
-  const int wb0 = min(8 * tn + 2 * wave, nb_last), wb1 = min(8 * tn + 2 * wave + 1, nb_last);
-  auto issue = [&](int st, char* slot) {
-    const int xbs[2] = {xb0, xb1}, wbs[2] = {wb0, wb1};
+  // this wave copies row blocks BPW wave + i of X and of W (clamped to the last block of the
+  // padded layout; their results are not stored) and their scale pieces
+  int xbs[BPW], wbs[BPW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < BPW; ++i) {
+    xbs[i] = min(8 * tm + BPW * wave + i, mb_last);
+    wbs[i] = min(8 * tn + BPW * wave + i, nb_last);
+  }
+  auto issue = [&](int st, char* slot) {
+#pragma unroll
+    for (int i = 0; i < BPW; ++i) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const size_t xo = ((size_t)xbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
         const size_t wo = ((size_t)wbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
-        lds_dma16(xc + xo, slot + (2 * wave + i) * 2048 + s * 1024);
-        lds_dma16(wc + wo, slot + kMxStageX + (2 * wave + i) * 2048 + s * 1024);
+        lds_dma16(xc + xo, slot + (BPW * wave + i) * 2048 + s * 1024);
+        lds_dma16(wc + wo, slot + kMxStageX + (BPW * wave + i) * 2048 + s * 1024);
       }
     }
     // scale pieces of the stage's 256-wide group: 256 bytes per block, 4 bytes per lane
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < BPW; ++i) {
       const size_t so_x = ((size_t)xbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
       const size_t so_w = ((size_t)wbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
-      lds_dma4(xs + so_x, slot + 2 * kMxStageX + (2 * wave + i) * 256);
-      lds_dma4(ws + so_w, slot + 2 * kMxStageX + kMxStageS + (2 * wave + i) * 256);
+      lds_dma4(xs + so_x, slot + 2 * kMxStageX + (BPW * wave + i) * 256);
+      lds_dma4(ws + so_w, slot + 2 * kMxStageX + kMxStageS + (BPW * wave + i) * 256);
     }
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][NBK];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NBK; ++j)
 #pragma unroll
       for (int t = 0; t < 16; ++t) acc[i][j][t] = 0.f;
 
-  auto read_ops = [&](const char* slot, int s, u32x4 (&a)[4], u32x4 (&b)[4]) {
+  auto read_ops = [&](const char* slot, int s, u32x4 (&a)[4], u32x4 (&b)[NBK]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[i] = *(const u32x4*)(slot + (4 * wm + i) * 2048 + s * 1024 + 16 * lane);
-      b[i] = *(const u32x4*)(slot + kMxStageX + (4 * wn + i) * 2048 + s * 1024 + 16 * lane);
-    }
+    for (int i = 0; i < 4; ++i) a[i] = *(const u32x4*)(slot + (4 * wm + i) * 2048 + s * 1024 + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) b[j] = *(const u32x4*)(slot + kMxStageX + (NBK * wn + j) * 2048 + s * 1024 + 16 * lane);
   };
   // stage st (parity P: steps 2P, 2P + 1 of its 256-wide group) from slot st % kMxSlots
   auto stage = [&](auto parity, int st) {
     constexpr int P = decltype(parity)::value;
     const char* slot = lds + (st % kMxSlots) * kMxSlot;
-    wait_vmcnt<2 * kMxLoads>();           // stage st has landed (st + 1, st + 2 may be in flight)
+    wait_vmcnt<2 * kLoads>();             // stage st has landed (st + 1, st + 2 may be in flight)
     stage_barrier();                      // ... for every wave; slot (st - 1) % kMxSlots is free
     issue(min(st + 3, nst - 1), lds + ((st + 3) % kMxSlots) * kMxSlot);   // past the end: a repeat, unused
-    uint32_t sa[4], sb[4];
+    uint32_t sa[4], sb[NBK];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa[i] = *(const uint32_t*)(slot + 2 * kMxStageX + (4 * wm + i) * 256 + 4 * lane);
-      sb[i] = *(const uint32_t*)(slot + 2 * kMxStageX + kMxStageS + (4 * wn + i) * 256 + 4 * lane);
-    }
-    u32x4 a0[4], b0[4], a1[4], b1[4];
+    for (int i = 0; i < 4; ++i) sa[i] = *(const uint32_t*)(slot + 2 * kMxStageX + (4 * wm + i) * 256 + 4 * lane);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j)
+      sb[j] = *(const uint32_t*)(slot + 2 * kMxStageX + kMxStageS + (NBK * wn + j) * 256 + 4 * lane);
+    u32x4 a0[4], b0[NBK], a1[4], b1[NBK];
     read_ops(slot, 0, a0, b0);
     read_ops(slot, 1, a1, b1);            // step 1's operands are read while step 0 multiplies
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4<2 * P>(a0[i], b0[j], acc[i][j], sa[i], sb[j]);
+      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P>(a0[i], b0[j], acc[i][j], sa[i], sb[j]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_fp4<2 * P + 1>(a1[i], b1[j], acc[i][j], sa[i], sb[j]);
+      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P + 1>(a1[i], b1[j], acc[i][j], sa[i], sb[j]);
   };
 
   issue(0, lds);
@@ -260,24 +268,24 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
   __syncthreads();
 
   // epilogue: lane holds rows 8 (t / 4) + 4 (l / 32) + t % 4 of each 32 x 32 block, column
-  // l % 32; each 32-row block of the wave (32 x 128) is staged in LDS and leaves as 16-byte
+  // l % 32; each 32-row block of the wave (32 x 32 NBK) is staged in LDS and leaves as 16-byte
   // pieces of a row
   const bool vec = (N & 3) == 0;
-  constexpr int kTS = 132;
+  constexpr int kTS = 32 * NBK + 4, kPR = 8 * NBK;
   float* T = (float*)(lds + wave * (32 * kTS * 4));
   const int r32 = lane & 31, h = lane >> 5;
-  const int m0 = kMT * tm + 128 * wm, n0 = kMN * tn + 128 * wn;
+  const int m0 = kMT * tm + 128 * wm, n0 = kMN * tn + 32 * NBK * wn;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NBK; ++j)
 #pragma unroll
       for (int t = 0; t < 16; ++t) T[(8 * (t >> 2) + 4 * h + (t & 3)) * kTS + 32 * j + r32] = acc[i][j][t];
     __builtin_amdgcn_s_waitcnt(0xC07F);
-    const int c4 = lane & 31;
+    const int c4 = lane % kPR;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r = (lane >> 5) + 2 * q;
+    for (int q = 0; q < 32 * kPR / 64; ++q) {
+      const int r = lane / kPR + (64 / kPR) * q;
       const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
       const int m = m0 + 32 * i + r, n = n0 + 4 * c4;
       if (m < M && n < N) store4(Y, y_bf16, N, m, n, v, vec);
@@ -314,12 +322,12 @@ hipError_t launch_gemm_mx(const uint8_t* xc, const uint8_t* xs, int64_t M, const
                           int64_t N, int64_t K, void* Y, int y_bf16, hipStream_t s) {
   static PerDeviceOnce attr_once;
   hipError_t e = once_per_device(attr_once, [] {
-    return hipFuncSetAttribute((const void*)k_gemm_mx, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    return hipFuncSetAttribute((const void*)k_gemm_mx<kMxWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
   });
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((M + kMT - 1) / kMT) * ((N + kMN - 1) / kMN));
-  hipLaunchKernelGGL(k_gemm_mx, dim3(tiles), dim3(kMxThreads), kMxLds, s, xc, xs, (int)M, wc, ws, (int)N, (int)K, Y,
-                     y_bf16);
+  hipLaunchKernelGGL(k_gemm_mx<kMxWaves>, dim3(tiles), dim3(64 * kMxWaves), kMxLds, s, xc, xs, (int)M, wc, ws, (int)N,
+                     (int)K, Y, y_bf16);
   return hipGetLastError();
 }
 
