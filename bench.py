@@ -936,6 +936,32 @@ def run_references(torch, ssn, copy_gbps):
                                       "note": "torch copy_ of 35.4 MB (read and written), 12 rotating pairs"}
     del src, dst, calls
     torch.cuda.empty_cache()
+    out.update(run_mfma_ceiling(torch, ssn))
+    return out
+
+
+def run_mfma_ceiling(torch, ssn):
+    """The matrix-core rate this GPU sustains on register-resident random operands (the
+    library's calibration launch): the power limit's ceiling for the bf16 products (W4A16 tiles)
+    and the FP4 products (W4A4), beside the published peaks the roofline is priced against."""
+    out = {}
+    sink = torch.empty(ssn.mfma_probe_sink_floats(), dtype=torch.float32, device="cuda")
+    for kind, name, peak in ((ssn.PROBE_BF16, "bf16_32x32x16", BF16_PEAK_TFLOPS),
+                             (ssn.PROBE_FP4, "fp4_32x32x64", FP4_PEAK_TFLOPS)):
+        for wps in (1, 2):
+            flops = ssn.mfma_probe(kind, wps, 4096, sink)
+            calls = [(lambda s=seed: ssn.mfma_probe(kind, wps, 4096, sink, seed=s)) for seed in range(10)]
+            T = Timer(torch)
+            T.batch("warm", calls[:3])
+            torch.cuda.synchronize()
+            T.batch("probe", calls)
+            torch.cuda.synchronize()
+            us = T.us("probe")
+            tf = flops / (us * 1e-6) / 1e12
+            out[f"mfma_ceiling_{name}_{wps}wave_per_simd"] = {
+                "us_per_launch": round(us, 1), "tflops": round(tf, 1), "frac_of_published_peak": round(tf / peak, 4),
+                "note": "register-resident operands with random bits, back-to-back matrix ops, 10 launches"}
+    del sink
     return out
 
 

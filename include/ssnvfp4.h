@@ -358,6 +358,31 @@ int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const
                void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Calibration (measurement only; no product path calls it). The roofline of the compute-bound
+ * products is priced against the published matrix-core peaks, which assume the full clock.
+ * mfma_probe measures what the GPU sustains instead: every wave issues back-to-back matrix ops
+ * on register-resident operands whose bits are random (drawn once per lane from a hash of the
+ * lane, the workgroup and `seed`), so the rate is set by the power limit that real data meets,
+ * not by memory: the ceiling a product kernel of the same instruction can approach at best.
+ * ------------------------------------------------------------------------------------------- */
+enum { SSN_PROBE_BF16 = 0, SSN_PROBE_FP4 = 1 };
+
+/* Floats the sink of mfma_probe needs (device memory, 4-byte aligned): one per launched thread
+ * of the largest launch. */
+int64_t mfma_probe_sink_floats(void);
+
+/*
+ * mfma_probe — launch cu_count * waves_per_simd workgroups of 256 threads (waves_per_simd waves on
+ * each SIMD), each wave issuing `iters` rounds of 16 (one wave per SIMD) or 8 (two) independent
+ * v_mfma_f32_32x32x16_bf16 (kind SSN_PROBE_BF16) or v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1
+ * codes with unit scales (SSN_PROBE_FP4). `sink` (mfma_probe_sink_floats() floats) receives one
+ * value per thread so the work is kept; `*flops` (optional, host) receives the launch's
+ * floating-point operations. The caller times the launch on `stream`. Errors: kind,
+ * waves_per_simd (1 or 2) or iters outside [1, 2^24]: SSN_E_RANGE; sink NULL: SSN_E_NULL.
+ */
+int mfma_probe(int kind, int waves_per_simd, int iters, uint32_t seed, float* sink, double* flops, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * moe_nvfp4_ffn_noalloc — moe_nvfp4_ffn without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation). Arguments and results are those of moe_nvfp4_ffn. The workspace is a

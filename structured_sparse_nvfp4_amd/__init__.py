@@ -23,6 +23,7 @@ ALGO_NAMES = {ALGO_AUTO: "auto", ALGO_VALU: "valu", ALGO_MFMA: "mfma", ALGO_SMFM
 EPI_NONE, EPI_SILU_GATE = 0, 1
 MX_ROWS, MX_TILED = 0, 1
 WLAYOUT_ROWS, WLAYOUT_KTILE64 = 0, 1
+PROBE_BF16, PROBE_FP4 = 0, 1
 
 _vp, _i64, _int = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 _SIGS = {
@@ -51,6 +52,8 @@ _SIGS = {
     "gemm_mxfp4": ([_vp, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _int, _int, _vp, _vp], _int),
     "moe_nvfp4_ffn_noalloc": ([_vp, _i64, _i64, _vp, _vp, _int, _int, _i64, _int, _int, _vp, _vp, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _vp], _int),
+    "mfma_probe_sink_floats": ([], _i64),
+    "mfma_probe": ([_int, _int, _int, ctypes.c_uint32, _vp, _vp, _vp], _int),
 }
 
 _lib = None
@@ -487,3 +490,19 @@ def moe_nvfp4_ffn_noalloc(X, topk_ids, topk_weights, E, up, down, out, bad_ids, 
                                        _ptr(down[0]), _ptr(down[1]), _ptr(down[2]), _ptr(down[3]), _ptr(out),
                                        _ptr(bad_ids), _stream(X.device)))
     return out, bad_ids
+
+
+def mfma_probe_sink_floats():
+    return int(lib().mfma_probe_sink_floats())
+
+
+def mfma_probe(kind, waves_per_simd, iters, sink, seed=0, stream_device=None):
+    """Calibration launch (see include/ssnvfp4.h): register-resident matrix ops on random
+    operands. Returns the launch's floating-point operations; the caller times it."""
+    fl = ctypes.c_double(0.0)
+    _need(sink, torch.float32, "sink")
+    if sink.numel() < mfma_probe_sink_floats():
+        raise ValueError(f"sink needs {mfma_probe_sink_floats()} floats")
+    _check(lib().mfma_probe(kind, waves_per_simd, iters, seed & 0xFFFFFFFF, _ptr(sink), ctypes.byref(fl),
+                            _stream(sink.device)))
+    return fl.value

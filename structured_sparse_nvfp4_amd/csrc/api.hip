@@ -459,6 +459,26 @@ int gemm_mxfp4(const uint8_t* x_codes, const uint8_t* x_scales, int64_t M, const
 }  // extern "C"
 
 // ---------------------------------------------------------------------------------------------
+// Calibration
+extern "C" {
+
+int64_t mfma_probe_sink_floats(void) { return (int64_t)ssn::cu_count() * 2 * 256; }
+
+int mfma_probe(int kind, int waves_per_simd, int iters, uint32_t seed, float* sink, double* flops, void* stream) {
+  const char* fn = "mfma_probe";
+  if (kind != SSN_PROBE_BF16 && kind != SSN_PROBE_FP4) return fail(SSN_E_RANGE, "%s: unknown kind %d", fn, kind);
+  if (waves_per_simd != 1 && waves_per_simd != 2)
+    return fail(SSN_E_RANGE, "%s: waves_per_simd must be 1 or 2 (got %d)", fn, waves_per_simd);
+  if (iters <= 0 || iters > (1 << 24)) return fail(SSN_E_RANGE, "%s: iters=%d outside [1, 2^24]", fn, iters);
+  REQUIRE_ELEM_PTR(sink);
+  const double per_op = kind == SSN_PROBE_BF16 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
+  if (flops) *flops = per_op * (waves_per_simd == 1 ? 16 : 8) * (double)iters * ssn::cu_count() * waves_per_simd * 4;
+  return hip_status(ssn::launch_mfma_probe(kind, waves_per_simd, iters, seed, sink, as_stream(stream)), fn);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------------
 // Allocation-free whole FFN: its workspace is a static device array, one copy per GPU, held
 // until the process ends. Every kernel writes the workspace bytes it later reads (routing
 // arrays, H, Yd), so nothing needs clearing between calls; calls that overlap on one GPU share

@@ -85,4 +85,8 @@ hipError_t launch_mx_quantize(const void* V, int v_bf16, int64_t R, int64_t K, i
 hipError_t launch_gemm_mx(const uint8_t* xc, const uint8_t* xs, int64_t M, const uint8_t* wc, const uint8_t* ws,
                           int64_t N, int64_t K, void* Y, int y_bf16, hipStream_t s);
 
+// calibration: register-resident matrix ops on random operands (cu_count() * waves_per_simd
+// workgroups of 256 threads; sink holds one float per thread)
+hipError_t launch_mfma_probe(int kind, int waves_per_simd, int iters, uint32_t seed, float* sink, hipStream_t s);
+
 }  // namespace ssn

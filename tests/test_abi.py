@@ -185,3 +185,15 @@ def test_gather_algorithm_and_tile_k_limit():
     for algo in (ssn.ALGO_SMFMAC, ssn.ALGO_DECOMPRESS_MFMA):
         assert L.gemm_nvfp4_sp24(p, 17, 4, big_k, p, p, p, p, p, 0, algo, n, n) == ssn.SSN_E_ALGO
     assert L.gemm_nvfp4_dense(n, 0, 4, big_k, n, n, n, n, 0, ssn.ALGO_MFMA, n, n) == ssn.SSN_OK
+
+
+def test_mfma_probe_validation_without_launch():
+    # the calibration call rejects its ranges before anything is launched
+    L = ssn.lib()
+    p, n = ctypes.c_void_p(4096), None
+    assert L.mfma_probe(2, 1, 16, 0, p, n, n) == ssn.SSN_E_RANGE
+    assert L.mfma_probe(ssn.PROBE_BF16, 3, 16, 0, p, n, n) == ssn.SSN_E_RANGE
+    assert L.mfma_probe(ssn.PROBE_FP4, 1, 0, 0, p, n, n) == ssn.SSN_E_RANGE
+    assert L.mfma_probe(ssn.PROBE_FP4, 2, (1 << 24) + 1, 0, p, n, n) == ssn.SSN_E_RANGE
+    assert L.mfma_probe(ssn.PROBE_BF16, 1, 16, 0, None, n, n) == ssn.SSN_E_NULL
+    assert L.mfma_probe(ssn.PROBE_BF16, 1, 16, 0, ctypes.c_void_p(4098), n, n) == ssn.SSN_E_ALIGN
