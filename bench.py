@@ -44,7 +44,6 @@ import hashlib
 import json
 import os
 import statistics
-import subprocess
 import sys
 import time
 
@@ -149,45 +148,39 @@ class Timer:
         return {"median_us": round(statistics.median(ts), 2), "min_us": round(ts[0], 2), "trials": len(ts)}
 
 
-def gpu_state():
-    """Current GPU clock (sysfs), power and temperatures (amd-smi), best effort."""
-    out = {}
+def _hwmon_read(path, scale):
     try:
-        for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
-            for line in open(f):
-                if line.startswith("S:") or line.rstrip().endswith("*"):
-                    out["sclk_MHz"] = int(line.split(":")[1].strip().split("M")[0])
-                    break
-            if "sclk_MHz" in out:
-                break
-    except (OSError, ValueError, IndexError):
-        pass
-    try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-t", "-c", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        d = json.loads(r.stdout)
-        g = d["gpu_data"][0] if isinstance(d, dict) and "gpu_data" in d else (d[0] if isinstance(d, list) else d)
+        with open(path) as f:
+            return round(int(f.read().strip()) / scale, 1)
+    except (OSError, ValueError):
+        return None
 
-        def val(x):
-            return x.get("value") if isinstance(x, dict) else x
-        pw = g.get("power", {})
-        for key in ("socket_power", "current_socket_power", "average_socket_power"):
-            if key in pw and val(pw[key]) not in (None, "N/A"):
-                out["power_W"] = val(pw[key])
-                break
-        tp = g.get("temperature", {})
-        for key in ("hotspot", "edge", "mem"):
-            if key in tp and val(tp[key]) not in (None, "N/A"):
-                out[f"temp_{key}_C"] = val(tp[key])
-        ck = g.get("clock", {})
-        gfx = ck.get("gfx_0") or ck.get("gfx") or {}
-        if isinstance(gfx, dict) and "clk" in gfx:
-            out["gfx_clk_MHz"] = val(gfx["clk"])
-        mem = ck.get("mem_0") or ck.get("mem") or {}
-        if isinstance(mem, dict) and "clk" in mem:
-            out["mem_clk_MHz"] = val(mem["clk"])
-    except Exception as e:  # the tool's output format is not under this program's control
-        out["amd_smi_error"] = str(e)[:200]
+
+def gpu_state():
+    """Current GPU clock, power and temperatures from sysfs (pp_dpm_sclk and the amdgpu hwmon
+    files), best effort. No tool is started: a child process of a program that has initialised
+    the GPU must not exec another program."""
+    out = {}
+    v = _sclk_now()
+    if v is not None:
+        out["sclk_MHz"] = v
+    for hw in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+        for name, key in (("power1_average", "power_W"), ("power1_input", "power_W")):
+            if key not in out:
+                w = _hwmon_read(os.path.join(hw, name), 1e6)
+                if w is not None:
+                    out[key] = w
+        for t in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
+            try:
+                with open(t.replace("_input", "_label")) as f:
+                    label = f.read().strip().lower()
+            except OSError:
+                label = os.path.basename(t).split("_")[0]
+            c = _hwmon_read(t, 1e3)
+            if c is not None:
+                out[f"temp_{label}_C"] = c
+        if out.get("power_W") is not None:
+            break
     return out
 
 
@@ -1023,16 +1016,18 @@ def _read_csvs(d, pattern):
 
 
 def _pmc_avg(d, counter):
-    """{(kernel, grid): (average value per dispatch, dispatches)} of one counter."""
+    """{(kernel, grid): (average value per dispatch, dispatches, largest value)} of one counter."""
     agg = {}
     for r in _read_csvs(d, "*counter_collection.csv"):
         if r["Counter_Name"] != counter:
             continue
         key = (r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0))
-        a = agg.setdefault(key, [0.0, 0])
-        a[0] += float(r["Counter_Value"])
+        a = agg.setdefault(key, [0.0, 0, 0.0])
+        v = float(r["Counter_Value"])
+        a[0] += v
         a[1] += 1
-    return {k: (v[0] / v[1], v[1]) for k, v in agg.items()}
+        a[2] = max(a[2], v)
+    return {k: (v[0] / v[1], v[1], v[2]) for k, v in agg.items()}
 
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
@@ -1045,8 +1040,9 @@ def traffic_entry(fetch_dir, write_dir, kernel, grid, source, summary):
     fe, wr = _pmc_avg(fetch_dir, "FETCH_SIZE"), _pmc_avg(write_dir, "WRITE_SIZE")
 
     def copy_cal(tab):
-        c = [v for (k, g), v in tab.items() if k.startswith(COPY_KERNEL)]
-        big = max(c, key=lambda v: v[0])[0]
+        # the largest single copy dispatch is the 2 GiB probe (the runtime's copy kernel has one
+        # grid for every size, so averages per grid mix the probe with smaller copies)
+        big = max(v[2] for (k, g), v in tab.items() if k.startswith(COPY_KERNEL))
         return COPY_BYTES / (big * 1024.0)
 
     def pick(tab):
