@@ -339,17 +339,21 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   constexpr int kTS = 32 * NB + 4;                  // staging row stride (floats): 16-byte aligned, banks shifted
   constexpr int kPR = 8 * NB;                       // 16-byte pieces per staged row
   float* T = (float*)(lds + wave * (32 * kTS * 4));
+  // the lane index again, from the lane mask count: a value the compiler cannot take from the
+  // prologue, so it is not kept in a register (or spilled) across the K loop
+  const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int er32 = el & 31, eh = el >> 5;
 #pragma unroll
   for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) T[(8 * (i >> 2) + 4 * h + (i & 3)) * kTS + 32 * nt + r32] = acc[mt][nt][i] * st_scale;
+      for (int i = 0; i < 16; ++i) T[(8 * (i >> 2) + 4 * eh + (i & 3)) * kTS + 32 * nt + er32] = acc[mt][nt][i] * st_scale;
     __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's stores to T are done
-    const int c4 = lane % kPR;
+    const int c4 = el % kPR;
 #pragma unroll
     for (int j = 0; j < 32 * kPR / 64; ++j) {
-      const int r = lane / kPR + (64 / kPR) * j;
+      const int r = el / kPR + (64 / kPR) * j;
       const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
       const int m = m0 + am + 32 * mt + r, n = n0 + bn0 + 4 * c4;
       if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
