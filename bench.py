@@ -197,23 +197,26 @@ def _sclk_now():
 
 def state_under_load(torch, fn, seconds=3.0):
     """GPU state while `fn` launches keep the GPU busy for about `seconds`: the clock (sysfs)
-    sampled five times, then one amd-smi reading (power, temperatures, clocks), all taken while
-    the queued launches still run; plus idle readings before and after."""
+    sampled five times, then one reading of power and temperatures (sysfs), all taken while the
+    queued launches still run (`still_running` says whether they did); plus idle readings
+    before and after."""
     before = gpu_state()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(); fn(); b.record(); b.synchronize()
-    n = max(1, int(seconds / max(a.elapsed_time(b) * 1e-3, 1e-5)))
+    # at most 5000 launches (under a profiler every launch is slow), so short kernels queue less
+    # than `seconds` of work: the clock is sampled early and over a short window
+    n = min(5000, max(1, int(seconds / max(a.elapsed_time(b) * 1e-3, 1e-5))))
     done = torch.cuda.Event()
     for _ in range(n):
         fn()
     done.record()
-    time.sleep(0.3)
+    time.sleep(0.2)
     sclk = []
     for _ in range(5):
         v = _sclk_now()
         if v is not None:
             sclk.append(v)
-        time.sleep(0.1)
+        time.sleep(0.05)
     during = gpu_state()
     during["sclk_samples_MHz"] = sclk
     during["still_running"] = not done.query()
