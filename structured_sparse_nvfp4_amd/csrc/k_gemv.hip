@@ -851,7 +851,9 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
-  if (a.M <= kPsMaxM && a.K % kSK == 0) {   // full-width loads, 32x32x32 sparse MFMA per 64-k chunk
+  // full-width loads, 32x32x32 sparse MFMA per 64-k chunk; its buffer offsets (32 rows of a row
+  // group, an activation row) are 32-bit, so K stays below 2^27
+  if (a.M <= kPsMaxM && a.K % kSK == 0 && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce p4_once;
     hipError_t e2 = once_per_device(p4_once, [] {
       return hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Stages * P4Slot::kBytes);
