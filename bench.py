@@ -164,6 +164,9 @@ def gpu_state():
     v = _sclk_now()
     if v is not None:
         out["sclk_MHz"] = v
+    v = _dpm_now("mclk")
+    if v is not None:
+        out["mclk_MHz"] = v
     for hw in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
         for name, key in (("power1_average", "power_W"), ("power1_input", "power_W")):
             if key not in out:
@@ -184,15 +187,20 @@ def gpu_state():
     return out
 
 
-def _sclk_now():
+def _dpm_now(kind="sclk"):
+    """Current level (MHz) of a pp_dpm_* clock table in sysfs (the line marked '*')."""
     try:
-        for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+        for f in glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}"):
             for line in open(f):
                 if line.startswith("S:") or line.rstrip().endswith("*"):
                     return int(line.split(":")[1].strip().split("M")[0])
     except (OSError, ValueError, IndexError):
         pass
     return None
+
+
+def _sclk_now():
+    return _dpm_now("sclk")
 
 
 def state_under_load(torch, fn, seconds=3.0):
@@ -408,6 +416,10 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, args, headline
         T.each(vname, [preps[vname]] * reps)
         torch.cuda.synchronize()
     res["gpu_state"] = state_under_load(torch, preps["dense_mfma"])
+    sc = res["gpu_state"]["during"].get("sclk_samples_MHz") or []
+    if sc:   # the published peak is at 2.4 GHz; the same matrix rate at the clock measured under load
+        mhz = sorted(sc)[len(sc) // 2]
+        res["bf16_peak_at_measured_sclk_tflops"] = round(BF16_PEAK_TFLOPS * mhz / 2400.0, 1)
     for vname, sparse, algo in variants:
         us = T.us(vname)
         e = {"us": round(us, 1), **T.stats(vname), "algo": ssn.ALGO_NAMES.get(used[vname].value, "?"),
@@ -1000,12 +1012,37 @@ def cpu_baseline_prefill(x, cols=PREFILL["N"], chunk=4096):
         gemm.gemm_dense(x, c, s, st)
         sec += time.perf_counter() - t1
     flops = 2.0 * M * cols * K
+    stages = oracle_stage_rates()
     return {"value": round(flops / sec / 1e12, 5), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "stages": stages,
             "sample": f"dense prefill product X [{M}, {K}] x weight rows [0, {cols}) of {N} (the oracle's quantisation "
                       f"of those rows with the whole tensor's scale, then its float64 product and bound base, in "
                       f"chunks of {chunk} rows); {sec:.1f} s on host cores; NumPy float64 oracle",
             "seconds": round(sec, 2), "tensor_scale_pass_s": round(t_scale, 2), "cpu_model": cpu_model(),
             "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+def oracle_stage_rates(rows=2048):
+    """The oracle's weight-side stages on rows [0, rows) of the decode weight W [13824, 5120]:
+    prune, quantise (given the tensor scale), check and compress, each timed once, as the GB/s
+    of the bytes the GPU calls move for the same rows."""
+    import numpy as np
+    import synth
+    from oracle import quant, sp24
+    N, K = 13824, 5120
+    w = synth.weight_rows(N, K, 0, rows)
+    st = quant.tensor_scale(w)
+    out = {}
+    t = time.perf_counter(); wp = sp24.prune24(w); dt = time.perf_counter() - t
+    out["prune"] = {"s": round(dt, 3), "GBps": round(2 * rows * K * 4 / dt / 1e9, 3)}
+    t = time.perf_counter(); c, _, _ = quant.quantize(wp, tensor_scale_in=st); dt = time.perf_counter() - t
+    out["quantize"] = {"s": round(dt, 3), "GBps": round((rows * K * 4 + rows * K // 2 + rows * K // 16) / dt / 1e9, 3)}
+    t = time.perf_counter(); sp24.check(c); dt = time.perf_counter() - t
+    out["check"] = {"s": round(dt, 3), "GBps": round(rows * K / 2 / dt / 1e9, 3)}
+    t = time.perf_counter(); sp24.compress(c); dt = time.perf_counter() - t
+    out["compress"] = {"s": round(dt, 3), "GBps": round((rows * K / 2 + rows * K / 4 + rows * K / 8) / dt / 1e9, 3)}
+    out["sample"] = f"weight rows [0, {rows}) of the decode W [{N}, {K}] (no outliers), NumPy oracle, one call each"
+    return out
 
 
 # ------------------------------------------------------------------------------------------
