@@ -438,9 +438,44 @@ def run_gemm_shape(torch, ssn, synth, M, N, K, y_dtype, outliers, args, headline
         res[vname] = e
     for vname in ("sp24_smfmac", "sp24_decompress_mfma", "sp24_gather_valu"):
         res[vname]["speedup_vs_dense"] = round(res["dense_mfma"]["us"] / res[vname]["us"], 3)
-    del X, Ys, dn, sp, preps
+    if headline:
+        del Ys, sp, preps
+        res["k_sweep"] = k_sweep(torch, ssn, X, dn, y_dtype)
     torch.cuda.empty_cache()
     return res, step, x
+
+
+def k_sweep(torch, ssn, X, dn, y_dtype, ks=(1024, 2048, 3072, 5120)):
+    """The dense tile on the first k columns of the same activations and weights, for several k:
+    a least-squares line through the launch times splits each launch into a part proportional
+    to K (the tile's main loop) and a fixed part (tile start, output write). Timing only: the
+    products are sub-products of the one checked above."""
+    M, K = X.shape
+    N = dn[0].shape[0]
+    pts = []
+    for k in ks:
+        if k > K or k % 64:
+            continue
+        Xk = X[:, :k].contiguous()
+        ck, sk = dn[0][:, :k // 2].contiguous(), dn[1][:, :k // 16].contiguous()
+        Y = torch.empty((M, N), dtype=y_dtype, device="cuda")
+        p, _ = ssn.gemm_nvfp4_dense(Xk, ck, sk, dn[2], y_dtype=y_dtype, algo=ssn.ALGO_MFMA, Y=Y, prepare=True)
+        T = Timer(torch)
+        T.batch("warm", [p] * 2)
+        torch.cuda.synchronize()
+        T.batch("k", [p] * TRIALS)
+        torch.cuda.synchronize()
+        pts.append((k, T.us("k")))
+        del Xk, ck, sk, Y, p
+    n = len(pts)
+    mk = sum(k for k, _ in pts) / n
+    mt = sum(t for _, t in pts) / n
+    slope = sum((k - mk) * (t - mt) for k, t in pts) / sum((k - mk) ** 2 for k, _ in pts)
+    fixed = mt - slope * mk
+    torch.cuda.empty_cache()
+    return {"points_us": {str(k): round(t, 1) for k, t in pts}, "us_per_k": round(slope, 4),
+            "fixed_us": round(fixed, 1), "k_part_tflops": round(2.0 * M * N / (slope * 1e-6) / 1e12, 1),
+            "note": f"dense tile at M = {M}, N = {N} on the first k columns; launch time = fixed + us_per_k * K"}
 
 
 # ------------------------------------------------------------------------------------------
