@@ -14,6 +14,7 @@
 
 namespace ssn {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -64,10 +65,16 @@ __device__ __forceinline__ bf16x16 as_bf16x16(u32x8 v) { return __builtin_bit_ca
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// f32 -> bf16 bits, round to nearest even (inputs are finite)
+// f32 -> bf16 bits, round to nearest even (inputs are finite), on the conversion instruction
+// (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// two f32 -> a packed bf16 pair (lo in the low half), round to nearest even, one instruction
+__device__ __forceinline__ uint32_t pk_bf16_rne(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 template <typename T>

@@ -11,7 +11,8 @@
 //  - every wave decodes its own weights from LDS into matrix operands in registers: a weight is
 //    decoded once per output tile and never written back.
 //
-// Dense and 2:4-expanded products (v_mfma_f32_32x32x16_bf16, activations = A, weights = B):
+// Dense and 2:4-expanded products (v_mfma_f32_32x32x16_bf16, weights = A, activations = B, so
+//   each 32 x 32 block is a block of Y^T and a lane ends with four consecutive outputs of a row):
 //   wave w owns all 256 rows x columns [64w, 64w + 64) of the tile: 8 x 2 blocks of 32 x 32.
 //   Lane l (r = l % 32, h = l / 32) feeds k = 8h..8h+7 of each 16-wide MFMA step. The kernel
 //   maps MFMA step s of a 64-wide stage to k = 32h + 8s + j, so one lane's weights for a whole
@@ -25,6 +26,7 @@
 //   robertz.co, section "What 2:4 actually is": two kept values plus a 2-bit index each).
 //
 // K must be a multiple of 64 (whole stages; every per-row weight piece is then aligned).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -203,7 +205,7 @@ __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
 // weight rows [64 WGM * wn, +64 WGM) of the tile, MB x NB blocks of 32 x 32. With WGM = 2 each
 // activation operand read from LDS feeds four MFMAs instead of two (half the LDS read traffic
 // of WGM = 1), and each weight is decoded by two waves instead of one.
-template <int WF, int WGM, int TM>
+template <int WF, int WGM, int TM, bool YB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(256 / TM, 256 / TM)))
 void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
                  const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
@@ -221,6 +223,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   const int r32 = lane & 31, h = lane >> 5;
   const int nst = K / kTK, last = nst - 1;
   const int am = 32 * MB * wm, bn0 = 32 * NB * wn;  // first activation / weight row of the wave
+  const float st_scale = *ts;   // loaded here: its latency is hidden by the K loop, not the epilogue
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -273,7 +276,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
       const bf16x8 av = as_bf16x8(a[mt]);
 #pragma unroll
       for (int nt = 0; nt < NB; ++nt)
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[nt], acc[mt][nt], 0, 0, 0);
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nt], av, acc[mt][nt], 0, 0, 0);
     }
   };
 
@@ -330,40 +333,79 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   }
   wait_vmcnt<0>();   // the duplicate stages past the end have landed before the wave exits
 
-  // epilogue: lane holds rows 8(i/4) + 4h + i%4 of each 32x32 block, column r32. Each row
-  // block of the wave (32 rows x 32 NB columns) is staged in LDS and leaves as 16-byte pieces
-  // of a row.
-  const float st_scale = *ts;
-  const bool vec = (N & 3) == 0;
+  // epilogue: the blocks are Y^T (weights = A, activations = B), so lane (r32, h) holds
+  // Y[m][n .. n + 3] for m = 32 mt + r32 and n = 32 nt + 8 g + 4 h (plus the wave's offsets) in
+  // acc[mt][nt][4g .. 4g + 3]. Each 32-row block of the wave (32 rows x 32 NB columns) is staged
+  // in LDS and leaves as row-contiguous pieces: bf16 output is rounded first and staged as
+  // 16-byte pieces of 8 values (piece c of row r at position c ^ (r & 7)), so a read of eight
+  // lanes covers one 128-byte row and every lane stores 16 bytes; f32 output is staged as
+  // 16-byte pieces of 4 values (piece q at q ^ (r & 7)).
   __syncthreads();                                  // every wave is done with the ring slots
-  constexpr int kTS = 32 * NB + 4;                  // staging row stride (floats): 16-byte aligned, banks shifted
-  constexpr int kPR = 8 * NB;                       // 16-byte pieces per staged row
-  float* T = (float*)(lds + wave * (32 * kTS * 4));
   // the lane index again, from the lane mask count: a value the compiler cannot take from the
   // prologue, so it is not kept in a register (or spilled) across the K loop
   const int el = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int er32 = el & 31, eh = el >> 5;
+  if constexpr (YB) {                               // bf16 output (y_bf16 != 0)
+    constexpr int kPR = 4 * NB;                     // 16-byte pieces (8 bf16) per staged row
+    char* T = lds + wave * (32 * kPR * 16);
+    const bool vec = (N & 7) == 0;
 #pragma unroll
-  for (int mt = 0; mt < MB; ++mt) {
+    for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < NB; ++nt)
+      for (int nt = 0; nt < NB; ++nt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) T[(8 * (i >> 2) + 4 * eh + (i & 3)) * kTS + 32 * nt + er32] = acc[mt][nt][i] * st_scale;
-    __builtin_amdgcn_s_waitcnt(0xC07F);             // lgkmcnt(0): this wave's stores to T are done
-    const int c4 = el % kPR;
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[mt][nt];
+          u32x2 w;
+          w[0] = pk_bf16_rne(a[4 * g] * st_scale, a[4 * g + 1] * st_scale);
+          w[1] = pk_bf16_rne(a[4 * g + 2] * st_scale, a[4 * g + 3] * st_scale);
+          const int c = 4 * nt + g;
+          *(u32x2*)(T + er32 * (16 * kPR) + 16 * (c ^ (er32 & 7)) + 8 * eh) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);           // lgkmcnt(0): this wave's stores to T are done
+      const int c = el % kPR;
 #pragma unroll
-    for (int j = 0; j < 32 * kPR / 64; ++j) {
-      const int r = el / kPR + (64 / kPR) * j;
-      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
-      const int m = m0 + am + 32 * mt + r, n = n0 + bn0 + 4 * c4;
-      if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
+      for (int j = 0; j < 32 * kPR / 64; ++j) {
+        const int r = el / kPR + (64 / kPR) * j;
+        const u32x4 v = *(const u32x4*)(T + r * (16 * kPR) + 16 * (c ^ (r & 7)));
+        const int m = m0 + am + 32 * mt + r;
+        if (m < M) store8_bf16(Y, N, m, n0 + bn0 + 8 * c, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);           // reads of T done before the next block overwrites it
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);             // reads of T done before the next block overwrites it
+  } else {
+    constexpr int kPR = 8 * NB;                     // 16-byte pieces (4 f32) per staged row
+    float* T = (float*)(lds + wave * (32 * kPR * 16));
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < NB; ++nt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[mt][nt][4 * g + i];
+          const int q = 8 * nt + 2 * g + eh;
+          *(f32x4*)(T + er32 * (4 * kPR) + 4 * (q ^ (er32 & 7))) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int p = el % kPR;
+#pragma unroll
+      for (int j = 0; j < 32 * kPR / 64; ++j) {
+        const int r = el / kPR + (64 / kPR) * j;
+        const f32x4 v = *(const f32x4*)(T + r * (4 * kPR) + 4 * (p ^ (r & 7))) * st_scale;
+        const int m = m0 + am + 32 * mt + r;
+        if (m < M) store4(Y, 0, N, m, n0 + bn0 + 4 * p, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------------------------
 // 2:4 weights on the sparse matrix cores: Y^T tile = W (compressed A) x X^T (B).
+template <bool YB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ vals,
                    const uint8_t* __restrict__ meta, const uint8_t* __restrict__ scales,
@@ -378,6 +420,7 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
   const int m0 = tm * kTM, n0 = tn * kTN;
   const int r32 = lane & 31, q = lane >> 5;
   const int nst = K / kTK, last = nst - 1;
+  const float st_scale = *ts;   // loaded here: its latency is hidden by the K loop, not the epilogue
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -477,65 +520,104 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
 
   // epilogue: lane holds weight rows 8(i/4) + 4q + i%4 of each block, activation row r32, i.e.
   // Y[m][n .. n + 3] for n = 32 at + 8 g + 4 q. Each activation row block of the wave (32 rows x
-  // 128 columns) is staged in LDS and leaves as 16-byte pieces of a row.
-  const float st_scale = *ts;
-  const bool vec = (N & 3) == 0;
+  // 128 columns) is staged in LDS and leaves as row-contiguous pieces: bf16 output is rounded
+  // first and staged as 16-byte pieces of 8 values (piece c of row r at position c ^ (r & 7)),
+  // f32 output as pieces of 4 values in padded rows.
   __syncthreads();
-  constexpr int kTS = 132;
-  float* T = (float*)(lds + wave * (32 * kTS * 4));
+  if constexpr (YB) {
+    char* T = lds + wave * (32 * 256);
+    const bool vec = (N & 7) == 0;
 #pragma unroll
-  for (int bt = 0; bt < 4; ++bt) {
+    for (int bt = 0; bt < 4; ++bt) {
 #pragma unroll
-    for (int at = 0; at < 4; ++at)
+      for (int at = 0; at < 4; ++at)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v;
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[at][bt];
+          u32x2 w;
+          w[0] = pk_bf16_rne(a[4 * g] * st_scale, a[4 * g + 1] * st_scale);
+          w[1] = pk_bf16_rne(a[4 * g + 2] * st_scale, a[4 * g + 3] * st_scale);
+          const int c = 4 * at + g;
+          *(u32x2*)(T + r32 * 256 + 16 * (c ^ (r32 & 7)) + 8 * q) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int c = lane & 15;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = acc[at][bt][4 * g + i] * st_scale;
-        *(f32x4*)(T + r32 * kTS + 32 * at + 8 * g + 4 * q) = v;
+      for (int j = 0; j < 8; ++j) {
+        const int r = (lane >> 4) + 4 * j;
+        const u32x4 v = *(const u32x4*)(T + r * 256 + 16 * (c ^ (r & 7)));
+        const int m = m0 + 128 * wm + 32 * bt + r;
+        if (m < M) store8_bf16(Y, N, m, n0 + 128 * wn + 8 * c, v, vec);
       }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    const int c4 = lane & 31;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int r = (lane >> 5) + 2 * j;
-      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
-      const int m = m0 + 128 * wm + 32 * bt + r, n = n0 + 128 * wn + 4 * c4;
-      if (m < M) store4(Y, y_bf16, N, m, n, v, vec);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+  } else {
+    const bool vec = (N & 3) == 0;
+    constexpr int kTS = 132;
+    float* T = (float*)(lds + wave * (32 * kTS * 4));
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+#pragma unroll
+      for (int at = 0; at < 4; ++at)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[at][bt][4 * g + i] * st_scale;
+          *(f32x4*)(T + r32 * kTS + 32 * at + 8 * g + 4 * q) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int c4 = lane & 31;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = (lane >> 5) + 2 * j;
+        const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
+        const int m = m0 + 128 * wm + 32 * bt + r, n = n0 + 128 * wn + 4 * c4;
+        if (m < M) store4(Y, 0, N, m, n, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
   }
 }
 
 
 
-template <int WF>
+template <int WF, bool YB>
 hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
   constexpr int TM = kTM, WGM = 1;
   const int bytes = kStages * Slot<WF, TM>::kBytes;
-  const void* fn = (const void*)k_gemm_mfma<WF, WGM, TM>;
+  const void* fn = (const void*)k_gemm_mfma<WF, WGM, TM, YB>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((a.M + TM - 1) / TM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
-                     (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM, YB>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M,
+                     (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  return hipGetLastError();
+}
+
+template <bool YB>
+hipError_t launch_smfmac_tiles(const GemmArgs& a, hipStream_t s) {
+  const int bytes = kStages * Slot<kSp24>::kBytes;
+  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_smfmac<YB>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
+  const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
+  hipLaunchKernelGGL(k_gemm_smfmac<YB>, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N, (int)a.K,
+                     a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) { return launch_mfma_tiles<kDense>(a, s); }
+hipError_t launch_gemm_dense_mfma(const GemmArgs& a, hipStream_t s) {
+  return a.y_bf16 ? launch_mfma_tiles<kDense, true>(a, s) : launch_mfma_tiles<kDense, false>(a, s);
+}
 
-hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s) { return launch_mfma_tiles<kSp24>(a, s); }
+hipError_t launch_gemm_sp24_decomp(const GemmArgs& a, hipStream_t s) {
+  return a.y_bf16 ? launch_mfma_tiles<kSp24, true>(a, s) : launch_mfma_tiles<kSp24, false>(a, s);
+}
 
 hipError_t launch_gemm_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
-  const int bytes = kStages * Slot<kSp24>::kBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gemm_smfmac, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)(((a.M + kTM - 1) / kTM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL(k_gemm_smfmac, dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N, (int)a.K,
-                     a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
-  return hipGetLastError();
+  return a.y_bf16 ? launch_smfmac_tiles<true>(a, s) : launch_smfmac_tiles<false>(a, s);
 }
 
 }  // namespace ssn

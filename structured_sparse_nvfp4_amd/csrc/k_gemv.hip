@@ -66,8 +66,8 @@ __device__ __forceinline__ void store_tile16(f32x4 acc, float* red, int M, int N
   } else {
     uint16_t* y = (uint16_t*)Y + (size_t)m * N + n;
     if (n + 3 < N && ((N & 3) == 0)) {
-      u32x2 o; o[0] = f32_to_bf16_rne(s[0]) | (f32_to_bf16_rne(s[1]) << 16);
-      o[1] = f32_to_bf16_rne(s[2]) | (f32_to_bf16_rne(s[3]) << 16);
+      u32x2 o; o[0] = pk_bf16_rne(s[0], s[1]);
+      o[1] = pk_bf16_rne(s[2], s[3]);
       *(u32x2*)y = o;
     } else {
       for (int i = 0; i < 4; ++i) if (n + i < N) y[i] = (uint16_t)f32_to_bf16_rne(s[i]);

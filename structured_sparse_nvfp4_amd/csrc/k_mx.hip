@@ -173,7 +173,7 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, u32x4 b, f32x16 c, uint32_t 
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, S, (int)sa, S, (int)sb);
 }
 
-template <int NWV>
+template <int NWV, bool YB>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(NWV / 4, NWV / 4)))
 void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, int M, const uint8_t* __restrict__ wc,
                const uint8_t* __restrict__ ws, int N, int K, void* __restrict__ Y, int y_bf16) {
@@ -250,11 +250,11 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P>(a0[i], b0[j], acc[i][j], sa[i], sb[j]);
+      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P>(b0[j], a0[i], acc[i][j], sb[j], sa[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P + 1>(a1[i], b1[j], acc[i][j], sa[i], sb[j]);
+      for (int j = 0; j < NBK; ++j) acc[i][j] = mfma_fp4<2 * P + 1>(b1[j], a1[i], acc[i][j], sb[j], sa[i]);
   };
 
   issue(0, lds);
@@ -267,30 +267,69 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
   wait_vmcnt<0>();
   __syncthreads();
 
-  // epilogue: lane holds rows 8 (t / 4) + 4 (l / 32) + t % 4 of each 32 x 32 block, column
-  // l % 32; each 32-row block of the wave (32 x 32 NBK) is staged in LDS and leaves as 16-byte
-  // pieces of a row
-  const bool vec = (N & 3) == 0;
-  constexpr int kTS = 32 * NBK + 4, kPR = 8 * NBK;
-  float* T = (float*)(lds + wave * (32 * kTS * 4));
+  // epilogue: the blocks are Y^T (weights = A, activations = B), so lane l holds
+  // Y[m][n .. n + 3] for m = 32 i + l % 32 and n = 32 j + 8 g + 4 (l / 32) (plus the wave's
+  // offsets) in acc[i][j][4g .. 4g + 3]. Each 32-row block of the wave (32 x 32 NBK) is staged in
+  // LDS and leaves as row-contiguous pieces: bf16 output rounded first, 16-byte pieces of 8 values
+  // (piece c of row r at position c ^ (r & 7)); f32 output as 16-byte pieces of 4 values (piece
+  // q at q ^ (r & 7)).
   const int r32 = lane & 31, h = lane >> 5;
   const int m0 = kMT * tm + 128 * wm, n0 = kMN * tn + 32 * NBK * wn;
+  if constexpr (YB) {
+    constexpr int kPR = 4 * NBK;                      // 16-byte pieces (8 bf16) per staged row
+    static_assert(kPR >= 8, "swizzle spans eight pieces");
+    char* T = lds + wave * (32 * kPR * 16);
+    const bool vec = (N & 7) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < NBK; ++j)
+      for (int j = 0; j < NBK; ++j)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) T[(8 * (t >> 2) + 4 * h + (t & 3)) * kTS + 32 * j + r32] = acc[i][j][t];
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    const int c4 = lane % kPR;
+        for (int g = 0; g < 4; ++g) {
+          u32x2 w;
+          w[0] = pk_bf16_rne(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          w[1] = pk_bf16_rne(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          const int c = 4 * j + g;
+          *(u32x2*)(T + r32 * (16 * kPR) + 16 * (c ^ (r32 & 7)) + 8 * h) = w;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int c = lane % kPR;
 #pragma unroll
-    for (int q = 0; q < 32 * kPR / 64; ++q) {
-      const int r = lane / kPR + (64 / kPR) * q;
-      const f32x4 v = *(const f32x4*)(T + r * kTS + 4 * c4);
-      const int m = m0 + 32 * i + r, n = n0 + 4 * c4;
-      if (m < M && n < N) store4(Y, y_bf16, N, m, n, v, vec);
+      for (int q = 0; q < 32 * kPR / 64; ++q) {
+        const int r = lane / kPR + (64 / kPR) * q;
+        const u32x4 v = *(const u32x4*)(T + r * (16 * kPR) + 16 * (c ^ (r & 7)));
+        const int m = m0 + 32 * i + r, n = n0 + 8 * c;
+        if (m < M && n < N) store8_bf16(Y, N, m, n, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+  } else {
+    constexpr int kPR = 8 * NBK;                      // 16-byte pieces (4 f32) per staged row
+    float* T = (float*)(lds + wave * (32 * kPR * 16));
+    const bool vec = (N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < NBK; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = acc[i][j][4 * g + t];
+          const int q = 8 * j + 2 * g + h;
+          *(f32x4*)(T + r32 * (4 * kPR) + 4 * (q ^ (r32 & 7))) = v;
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      const int p = lane % kPR;
+#pragma unroll
+      for (int q = 0; q < 32 * kPR / 64; ++q) {
+        const int r = lane / kPR + (64 / kPR) * q;
+        const f32x4 v = *(const f32x4*)(T + r * (4 * kPR) + 4 * (p ^ (r & 7)));
+        const int m = m0 + 32 * i + r, n = n0 + 4 * p;
+        if (m < M && n < N) store4(Y, 0, N, m, n, v, vec);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+    }
   }
 }
 
@@ -322,12 +361,18 @@ hipError_t launch_gemm_mx(const uint8_t* xc, const uint8_t* xs, int64_t M, const
                           int64_t N, int64_t K, void* Y, int y_bf16, hipStream_t s) {
   static PerDeviceOnce attr_once;
   hipError_t e = once_per_device(attr_once, [] {
-    return hipFuncSetAttribute((const void*)k_gemm_mx<kMxWaves>, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    hipError_t e1 = hipFuncSetAttribute((const void*)k_gemm_mx<kMxWaves, true>, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
+    if (e1 != hipSuccess) return e1;
+    return hipFuncSetAttribute((const void*)k_gemm_mx<kMxWaves, false>, hipFuncAttributeMaxDynamicSharedMemorySize, kMxLds);
   });
   if (e != hipSuccess) return e;
   const unsigned tiles = (unsigned)(((M + kMT - 1) / kMT) * ((N + kMN - 1) / kMN));
-  hipLaunchKernelGGL(k_gemm_mx<kMxWaves>, dim3(tiles), dim3(64 * kMxWaves), kMxLds, s, xc, xs, (int)M, wc, ws, (int)N,
-                     (int)K, Y, y_bf16);
+  if (y_bf16)
+    hipLaunchKernelGGL((k_gemm_mx<kMxWaves, true>), dim3(tiles), dim3(64 * kMxWaves), kMxLds, s, xc, xs, (int)M, wc, ws,
+                       (int)N, (int)K, Y, y_bf16);
+  else
+    hipLaunchKernelGGL((k_gemm_mx<kMxWaves, false>), dim3(tiles), dim3(64 * kMxWaves), kMxLds, s, xc, xs, (int)M, wc, ws,
+                       (int)N, (int)K, Y, y_bf16);
   return hipGetLastError();
 }
 

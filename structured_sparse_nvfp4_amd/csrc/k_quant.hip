@@ -372,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void k_dequantize(const uint8_t* codes, c
       for (int u = 0; u < 4; ++u) {
         float a = to_f32_round_odd((double)(v[8 * t + 2 * u] * s) * (double)st);
         float c2 = to_f32_round_odd((double)(v[8 * t + 2 * u + 1] * s) * (double)st);
-        r[u] = f32_to_bf16_rne(a) | (f32_to_bf16_rne(c2) << 16);
+        r[u] = pk_bf16_rne(a, c2);
       }
       o[t] = r;
     }

@@ -58,8 +58,8 @@ __device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n,
   if (vec && n + 3 < N) {
     if (y_bf16) {
       u32x2 o;
-      o[0] = f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16);
-      o[1] = f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16);
+      o[0] = pk_bf16_rne(v[0], v[1]);
+      o[1] = pk_bf16_rne(v[2], v[3]);
       *(u32x2*)((uint16_t*)Y + idx) = o;
     } else {
       *(f32x4*)((float*)Y + idx) = v;
@@ -68,6 +68,20 @@ __device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n,
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (n + i < N) store_val(Y, y_bf16, idx + i, v[i]);
+  }
+}
+
+// Eight consecutive bf16 outputs Y[m][n..n+7], packed in pairs (element 2i in the low half of
+// v[i]). `vec`: N % 8 == 0, so the piece is 16-byte aligned; otherwise, and at the right edge,
+// element by element.
+__device__ __forceinline__ void store8_bf16(void* Y, int N, int m, int n, u32x4 v, bool vec) {
+  uint16_t* y = (uint16_t*)Y + (size_t)m * N + n;
+  if (vec && n + 7 < N) {
+    *(u32x4*)y = v;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (n + i < N) y[i] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
   }
 }
 
