@@ -180,11 +180,6 @@ __device__ __forceinline__ void issue_part(const StageSrc<WF, TM>& g, int st, ch
   for (int idx = PART * per; idx < (PART + 1) * per && idx < Slot<WF, TM>::kLoads; ++idx) issue_one<WF, TM>(g, st, slot, wave, idx);
 }
 
-// 16-byte activation chunk `c` of tile row r
-__device__ __forceinline__ u32x4 lds_x(const char* slot, int r, int c) {
-  return *(const u32x4*)(slot + r * 128 + 16 * (c ^ swz(r)));
-}
-
 // One lane's weights for one stage: dense 32 codes, or 2:4 (vals word 0, vals word 1, meta)
 template <int WF, int TM = kTM>
 __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
@@ -266,9 +261,19 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
       b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(c[nt], s), f));
     }
   };
+  // Byte offset in a slot of the activation piece of MFMA step s for row block mt: row
+  // am + 32 mt + r32, chunk (4h + s) ^ swz(row). With am a multiple of 64 the swizzle depends on
+  // mt only through mt & 1, so eight per-lane offsets (s, mt & 1) plus the constant 4096 mt
+  // address every read (the constant folds into the instruction's offset field).
+  static_assert(WGM == 1 || WGM == 2, "am = 32 MB wm must be a multiple of 64");
+  uint32_t xoff[4][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) xoff[s][p] = (uint32_t)((am + r32) * 128 + 16 * ((4 * h + s) ^ swz(r32 + 32 * p)));
   auto read_a = [&](const char* slot, int s, u32x4 (&a)[MB]) {
 #pragma unroll
-    for (int mt = 0; mt < MB; ++mt) a[mt] = lds_x(slot, am + 32 * mt + r32, 4 * h + s);
+    for (int mt = 0; mt < MB; ++mt) a[mt] = *(const u32x4*)(slot + 4096 * mt + xoff[s][mt & 1]);
   };
   auto mfmas = [&](const u32x4 (&a)[MB], const bf16x8 (&b)[NB]) {
 #pragma unroll
@@ -450,11 +455,22 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
   };
   // B (activations) of MFMA step t: col r32 of block bt; k = 16t + 8q + j (j < 8) and
   // 32 + 16t + 8q + j - 8 (j >= 8)
+  // per-lane byte offsets of those pieces: row 128 wm + 32 bt + r32, chunk c ^ swz(row), where
+  // the swizzle depends on bt only through bt & 1 (the constant 4096 bt folds into the
+  // instruction's offset field)
+  uint32_t xoff[2][2][2];   // [t][lo / hi][bt & 1]
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+        xoff[t][u][p] = (uint32_t)((128 * wm + r32) * 128 + 16 * ((4 * u + 2 * t + q) ^ swz(r32 + 32 * p)));
   auto read_b = [&](const char* slot, int t, u32x8 (&b)[4]) {
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
-      const int r = 128 * wm + 32 * bt + r32;
-      const u32x4 lo = lds_x(slot, r, 2 * t + q), hi = lds_x(slot, r, 4 + 2 * t + q);
+      const u32x4 lo = *(const u32x4*)(slot + 4096 * bt + xoff[t][0][bt & 1]);
+      const u32x4 hi = *(const u32x4*)(slot + 4096 * bt + xoff[t][1][bt & 1]);
       b[bt][0] = lo[0]; b[bt][1] = lo[1]; b[bt][2] = lo[2]; b[bt][3] = lo[3];
       b[bt][4] = hi[0]; b[bt][5] = hi[1]; b[bt][6] = hi[2]; b[bt][7] = hi[3];
     }
