@@ -30,6 +30,7 @@
 #include <type_traits>
 
 #include "common.hpp"
+#include "device_once.hpp"
 #include "launch.hpp"
 #include "pipeline.hpp"
 #include "tile.hpp"
@@ -204,16 +205,17 @@ template <int WF, int WGM, int TM, bool YB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(256 / TM, 256 / TM)))
 void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
                  const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
-                 void* __restrict__ Y, int y_bf16) {
+                 void* __restrict__ Y, int y_bf16, int ldy) {
   using L = Slot<WF, TM>;
   constexpr int MB = TM / 32 / WGM, NB = 2 * WGM;       // 32 x 32 blocks per wave along M and N
   constexpr int VS = NB == 2 ? 3 : 5, VB = NB == 2 ? 3 : 6;   // decode instructions per MFMA slot
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % (4 / WGM), wm = wave / (4 / WGM);
+  // the launch covers the first gridDim.x tiles of the tile order of an M x N product
   const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + kTN - 1) / kTN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m * tiles_n, tiles_m, tiles_n, tm, tn);
+  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * TM, n0 = tn * kTN;
   const int r32 = lane & 31, h = lane >> 5;
   const int nst = K / kTK, last = nst - 1;
@@ -353,7 +355,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   if constexpr (YB) {                               // bf16 output (y_bf16 != 0)
     constexpr int kPR = 4 * NB;                     // 16-byte pieces (8 bf16) per staged row
     char* T = lds + wave * (32 * kPR * 16);
-    const bool vec = (N & 7) == 0;
+    const bool vec = (ldy & 7) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
     for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
@@ -374,14 +376,14 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
         const int r = el / kPR + (64 / kPR) * j;
         const u32x4 v = *(const u32x4*)(T + r * (16 * kPR) + 16 * (c ^ (r & 7)));
         const int m = m0 + am + 32 * mt + r;
-        if (m < M) store8_bf16(Y, N, m, n0 + bn0 + 8 * c, v, vec);
+        if (m < M) store8_bf16_ld(Y, ldy, N, m, n0 + bn0 + 8 * c, v, vec);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);           // reads of T done before the next block overwrites it
     }
   } else {
     constexpr int kPR = 8 * NB;                     // 16-byte pieces (4 f32) per staged row
     float* T = (float*)(lds + wave * (32 * kPR * 16));
-    const bool vec = (N & 3) == 0;
+    const bool vec = (ldy & 3) == 0 && ((uintptr_t)Y & 15) == 0;
 #pragma unroll
     for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
@@ -401,7 +403,7 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
         const int r = el / kPR + (64 / kPR) * j;
         const f32x4 v = *(const f32x4*)(T + r * (4 * kPR) + 4 * (p ^ (r & 7))) * st_scale;
         const int m = m0 + am + 32 * mt + r;
-        if (m < M) store4(Y, 0, N, m, n0 + bn0 + 4 * p, v, vec);
+        if (m < M) store4_ld(Y, 0, ldy, N, m, n0 + bn0 + 4 * p, v, vec);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);
     }
@@ -598,17 +600,44 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
 
 
 
-template <int WF, bool YB>
-hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
-  constexpr int TM = kTM, WGM = 1;
+// Tiles of TM rows over activation rows [row0, row0 + M) and weight rows [col0, col0 + N) of
+// the product: the first `grid` tiles of that sub-product's tile order.
+template <int WF, int TM, bool YB>
+hipError_t launch_tiles_region(const GemmArgs& a, int64_t row0, int64_t col0, int64_t M, int64_t N, unsigned grid,
+                               hipStream_t s) {
+  constexpr int WGM = 1;
   const int bytes = kStages * Slot<WF, TM>::kBytes;
   const void* fn = (const void*)k_gemm_mfma<WF, WGM, TM, YB>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
   if (e != hipSuccess) return e;
-  const unsigned tiles = (unsigned)(((a.M + TM - 1) / TM) * ((a.N + kTN - 1) / kTN));
-  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM, YB>), dim3(tiles), dim3(kThreads), bytes, s, a.X, (int)a.M,
-                     (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
+  const uint16_t* X = a.X + row0 * a.K;
+  const uint8_t* w0 = a.w0 + col0 * (WF == kDense ? a.K / 2 : a.K / 4);
+  const uint8_t* w1 = WF == kDense ? a.w1 : a.w1 + col0 * (a.K / 8);
+  const uint8_t* sc = a.scales + col0 * (a.K / 16);
+  void* Y = (char*)a.Y + (row0 * a.N + col0) * (a.y_bf16 ? 2 : 4);
+  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM, YB>), dim3(grid), dim3(kThreads), bytes, s, X, (int)M, (int)N, (int)a.K,
+                     w0, w1, sc, a.ts, Y, a.y_bf16, (int)a.N);
   return hipGetLastError();
+}
+
+// 256 x 256 tiles, one workgroup per CU. When the last round of tiles would leave more than half
+// of the CUs idle, those last `rem` tiles of the order (with whole kGroupM-row groups they form a
+// rectangle: the last kGroupM tile rows x the last rem / kGroupM tile columns) run as a second
+// launch of 128 x 256 tiles, twice as many, which two workgroups per CU can hold.
+template <int WF, bool YB>
+hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
+  const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + kTN - 1) / kTN, tiles = tiles_m * tiles_n;
+  const int64_t cu = cu_count(), rem = tiles % cu;
+  if (tiles > cu && rem > 0 && 2 * rem <= cu && tiles_m % kGroupM == 0 && rem % kGroupM == 0 &&
+      rem <= kGroupM * tiles_n) {
+    hipError_t e = launch_tiles_region<WF, kTM, YB>(a, 0, 0, a.M, a.N, (unsigned)(tiles - rem), s);
+    if (e != hipSuccess) return e;
+    const int64_t row0 = (tiles_m - kGroupM) * kTM, col0 = (tiles_n - rem / kGroupM) * kTN;
+    const int64_t M2 = a.M - row0, N2 = a.N - col0;
+    constexpr int TM2 = kTM / 2;
+    return launch_tiles_region<WF, TM2, YB>(a, row0, col0, M2, N2, (unsigned)(((M2 + TM2 - 1) / TM2) * (rem / kGroupM)), s);
+  }
+  return launch_tiles_region<WF, kTM, YB>(a, 0, 0, a.M, a.N, (unsigned)tiles, s);
 }
 
 template <bool YB>

@@ -51,10 +51,11 @@ __device__ __forceinline__ void store_val(void* Y, int y_bf16, size_t idx, float
   else ((float*)Y)[idx] = v;
 }
 
-// Four consecutive outputs Y[m][n..n+3] (already scaled). `vec`: N % 4 == 0, so the piece is
-// 16-byte (f32) or 8-byte (bf16) aligned; otherwise, and at the right edge, element by element.
-__device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n, f32x4 v, bool vec) {
-  const size_t idx = (size_t)m * N + n;
+// Four consecutive outputs Y[m][n..n+3] (already scaled) of a row-major Y with row stride ld
+// and N columns. `vec`: the piece is 16-byte (f32) or 8-byte (bf16) aligned (ld % 4 == 0 and an
+// aligned Y); otherwise, and at the right edge, element by element.
+__device__ __forceinline__ void store4_ld(void* Y, int y_bf16, int ld, int N, int m, int n, f32x4 v, bool vec) {
+  const size_t idx = (size_t)m * ld + n;
   if (vec && n + 3 < N) {
     if (y_bf16) {
       u32x2 o;
@@ -71,11 +72,16 @@ __device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n,
   }
 }
 
-// Eight consecutive bf16 outputs Y[m][n..n+7], packed in pairs (element 2i in the low half of
-// v[i]). `vec`: N % 8 == 0, so the piece is 16-byte aligned; otherwise, and at the right edge,
-// element by element.
-__device__ __forceinline__ void store8_bf16(void* Y, int N, int m, int n, u32x4 v, bool vec) {
-  uint16_t* y = (uint16_t*)Y + (size_t)m * N + n;
+// the same for a dense row-major Y (row stride N)
+__device__ __forceinline__ void store4(void* Y, int y_bf16, int N, int m, int n, f32x4 v, bool vec) {
+  store4_ld(Y, y_bf16, N, N, m, n, v, vec);
+}
+
+// Eight consecutive bf16 outputs Y[m][n..n+7] of a row-major Y with row stride ld and N
+// columns, packed in pairs (element 2i in the low half of v[i]). `vec`: the piece is 16-byte
+// aligned (ld % 8 == 0 and an aligned Y); otherwise, and at the right edge, element by element.
+__device__ __forceinline__ void store8_bf16_ld(void* Y, int ld, int N, int m, int n, u32x4 v, bool vec) {
+  uint16_t* y = (uint16_t*)Y + (size_t)m * ld + n;
   if (vec && n + 7 < N) {
     *(u32x4*)y = v;
   } else {
@@ -83,6 +89,11 @@ __device__ __forceinline__ void store8_bf16(void* Y, int N, int m, int n, u32x4 
     for (int i = 0; i < 8; ++i)
       if (n + i < N) y[i] = (uint16_t)(v[i >> 1] >> (16 * (i & 1)));
   }
+}
+
+// the same for a dense row-major Y (row stride N)
+__device__ __forceinline__ void store8_bf16(void* Y, int N, int m, int n, u32x4 v, bool vec) {
+  store8_bf16_ld(Y, N, N, m, n, v, vec);
 }
 
 }  // namespace ssn

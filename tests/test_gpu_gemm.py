@@ -170,3 +170,27 @@ def test_empty_and_degenerate():
     x1 = torch.ones((2, 32), dtype=torch.bfloat16, device="cuda")
     y, _ = ssn.gemm_nvfp4_dense(x1, c, s, ts)
     assert torch.count_nonzero(y).item() == 0
+
+
+# 16 x 17 tiles of 256 x 256 = one round of 256 plus 16: the last 16 tiles of the order (the last
+# four tile rows x the last four tile columns) run as a second launch of 128 x 256 tiles, whose
+# output rows are strided by the full N; ragged M and N put partial tiles in that second launch
+@pytest.mark.parametrize("M,N", [(4096, 4352), (4000, 4300)])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_tiles_with_split_tail(M, N, out, sparse):
+    K = 192
+    x, c, s, st = _problem(M, N, K, seed=M + N + (1 if sparse else 0), prune=sparse)
+    ts = dev(np.array([st], np.float32))
+    ydt = torch.bfloat16 if out == "bf16" else torch.float32
+    if sparse:
+        vals, meta, _ = sp24.compress(c)
+        Y, B = gemm.gemm_sp24(x, vals, meta, s, st)
+        g, used = ssn.gemm_nvfp4_sp24(x_dev(x), dev(vals), dev(meta), dev(s), ts, y_dtype=ydt,
+                                      algo=ssn.ALGO_DECOMPRESS_MFMA)
+        assert used == ssn.ALGO_DECOMPRESS_MFMA
+    else:
+        Y, B = gemm.gemm_dense(x, c, s, st)
+        g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), ts, y_dtype=ydt, algo=ssn.ALGO_MFMA)
+        assert used == ssn.ALGO_MFMA
+    assert_within_bound(y_host(g), Y, B, out=out, what=f"split tail {M}x{N} {out}")
