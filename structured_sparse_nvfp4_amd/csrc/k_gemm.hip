@@ -201,21 +201,20 @@ __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
 // weight rows [64 WGM * wn, +64 WGM) of the tile, MB x NB blocks of 32 x 32. With WGM = 2 each
 // activation operand read from LDS feeds four MFMAs instead of two (half the LDS read traffic
 // of WGM = 1), and each weight is decoded by two waves instead of one.
+// Tile `tile` of the first `total` tiles in the tile order of an M x N product (Y row stride ldy).
 template <int WF, int WGM, int TM, bool YB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(256 / TM, 256 / TM)))
-void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
-                 const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
-                 void* __restrict__ Y, int y_bf16, int ldy) {
+__device__ __forceinline__ void mfma_tile(const uint16_t* __restrict__ X, int M, int N, int K,
+                                          const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
+                                          const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+                                          void* __restrict__ Y, int ldy, int tile, int total, char* lds) {
   using L = Slot<WF, TM>;
   constexpr int MB = TM / 32 / WGM, NB = 2 * WGM;       // 32 x 32 blocks per wave along M and N
   constexpr int VS = NB == 2 ? 3 : 5, VB = NB == 2 ? 3 : 6;   // decode instructions per MFMA slot
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wave % (4 / WGM), wm = wave / (4 / WGM);
-  // the launch covers the first gridDim.x tiles of the tile order of an M x N product
   const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + kTN - 1) / kTN;
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_of(tile, total, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * TM, n0 = tn * kTN;
   const int r32 = lane & 31, h = lane >> 5;
   const int nst = K / kTK, last = nst - 1;
@@ -410,6 +409,28 @@ void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint
   }
 }
 
+// The first `nbig` workgroups take the 256 x 256 tiles of the product in tile order. When the
+// last round of those would leave more than half of the CUs idle, the tiles of that round (the
+// bottom-right rectangle from activation row row0 and weight row col0) are taken instead by the
+// workgroups after them as twice as many 128 x 256 tiles: dispatched last, they go to the CUs
+// that finish first.
+template <int WF, bool YB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm_mfma(const uint16_t* __restrict__ X, int M, int N, int K, const uint8_t* __restrict__ w0,
+                 const uint8_t* __restrict__ w1, const uint8_t* __restrict__ scales, const float* __restrict__ ts,
+                 void* __restrict__ Y, int nbig, int row0, int col0) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  if ((int)blockIdx.x < nbig) {
+    mfma_tile<WF, 1, kTM, YB>(X, M, N, K, w0, w1, scales, ts, Y, N, blockIdx.x, nbig, lds);
+  } else {
+    const size_t wrow = WF == kDense ? K / 2 : K / 4;
+    mfma_tile<WF, 1, kTM / 2, YB>(X + (size_t)row0 * K, M - row0, N - col0, K, w0 + (size_t)col0 * wrow,
+                                  WF == kDense ? w1 : w1 + (size_t)col0 * (K / 8), scales + (size_t)col0 * (K / 16),
+                                  ts, (char*)Y + ((size_t)row0 * N + col0) * (YB ? 2 : 4), N, blockIdx.x - nbig,
+                                  gridDim.x - nbig, lds);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // 2:4 weights on the sparse matrix cores: Y^T tile = W (compressed A) x X^T (B).
 template <bool YB>
@@ -600,44 +621,27 @@ void k_gemm_smfmac(const uint16_t* __restrict__ X, int M, int N, int K, const ui
 
 
 
-// Tiles of TM rows over activation rows [row0, row0 + M) and weight rows [col0, col0 + N) of
-// the product: the first `grid` tiles of that sub-product's tile order.
-template <int WF, int TM, bool YB>
-hipError_t launch_tiles_region(const GemmArgs& a, int64_t row0, int64_t col0, int64_t M, int64_t N, unsigned grid,
-                               hipStream_t s) {
-  constexpr int WGM = 1;
-  const int bytes = kStages * Slot<WF, TM>::kBytes;
-  const void* fn = (const void*)k_gemm_mfma<WF, WGM, TM, YB>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  const uint16_t* X = a.X + row0 * a.K;
-  const uint8_t* w0 = a.w0 + col0 * (WF == kDense ? a.K / 2 : a.K / 4);
-  const uint8_t* w1 = WF == kDense ? a.w1 : a.w1 + col0 * (a.K / 8);
-  const uint8_t* sc = a.scales + col0 * (a.K / 16);
-  void* Y = (char*)a.Y + (row0 * a.N + col0) * (a.y_bf16 ? 2 : 4);
-  hipLaunchKernelGGL((k_gemm_mfma<WF, WGM, TM, YB>), dim3(grid), dim3(kThreads), bytes, s, X, (int)M, (int)N, (int)a.K,
-                     w0, w1, sc, a.ts, Y, a.y_bf16, (int)a.N);
-  return hipGetLastError();
-}
-
-// 256 x 256 tiles, one workgroup per CU. When the last round of tiles would leave more than half
-// of the CUs idle, those last `rem` tiles of the order (with whole kGroupM-row groups they form a
-// rectangle: the last kGroupM tile rows x the last rem / kGroupM tile columns) run as a second
-// launch of 128 x 256 tiles, twice as many, which two workgroups per CU can hold.
 template <int WF, bool YB>
 hipError_t launch_mfma_tiles(const GemmArgs& a, hipStream_t s) {
+  const int bytes = kStages * Slot<WF, kTM>::kBytes;   // the 128-row tiles need less
+  const void* fn = (const void*)k_gemm_mfma<WF, YB>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
   const int64_t tiles_m = (a.M + kTM - 1) / kTM, tiles_n = (a.N + kTN - 1) / kTN, tiles = tiles_m * tiles_n;
   const int64_t cu = cu_count(), rem = tiles % cu;
+  int64_t nbig = tiles, row0 = 0, col0 = 0, grid = tiles;
+  // with whole kGroupM-row groups, the last rem tiles of the order are the last kGroupM tile
+  // rows x the last rem / kGroupM tile columns
   if (tiles > cu && rem > 0 && 2 * rem <= cu && tiles_m % kGroupM == 0 && rem % kGroupM == 0 &&
       rem <= kGroupM * tiles_n) {
-    hipError_t e = launch_tiles_region<WF, kTM, YB>(a, 0, 0, a.M, a.N, (unsigned)(tiles - rem), s);
-    if (e != hipSuccess) return e;
-    const int64_t row0 = (tiles_m - kGroupM) * kTM, col0 = (tiles_n - rem / kGroupM) * kTN;
-    const int64_t M2 = a.M - row0, N2 = a.N - col0;
-    constexpr int TM2 = kTM / 2;
-    return launch_tiles_region<WF, TM2, YB>(a, row0, col0, M2, N2, (unsigned)(((M2 + TM2 - 1) / TM2) * (rem / kGroupM)), s);
+    nbig = tiles - rem;
+    row0 = (tiles_m - kGroupM) * kTM;
+    col0 = (tiles_n - rem / kGroupM) * kTN;
+    grid = nbig + ((a.M - row0 + kTM / 2 - 1) / (kTM / 2)) * (rem / kGroupM);
   }
-  return launch_tiles_region<WF, kTM, YB>(a, 0, 0, a.M, a.N, (unsigned)tiles, s);
+  hipLaunchKernelGGL((k_gemm_mfma<WF, YB>), dim3((unsigned)grid), dim3(kThreads), bytes, s, a.X, (int)a.M, (int)a.N,
+                     (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, (int)nbig, (int)row0, (int)col0);
+  return hipGetLastError();
 }
 
 template <bool YB>
