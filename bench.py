@@ -62,7 +62,7 @@ TRIALS = 20                       # individually timed launches per kernel (medi
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "structured_sparse_nvfp4_amd", "csrc")
 PREFILL = dict(M=8192, N=27648, K=5120)
-DENSE_TILE_KERNEL = "k_gemm_mfma<0, 1, 256>"
+DENSE_TILE_KERNEL = "k_gemm_mfma<0, true>"
 
 
 def parse():
