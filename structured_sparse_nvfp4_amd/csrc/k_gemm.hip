@@ -1,4 +1,5 @@
-// Prefill-shaped and square products (M > 16): 256x256 output tiles on the matrix cores.
+// Prefill-shaped and square products (M > 16): 256x256 output tiles on the matrix cores (and
+// 128x256 tiles for a half-empty last round of them).
 //
 // The square and prefill shapes are compute-bound ("NVFP4 Without FP4 Hardware", ai-muninn.com,
 // section on prefill: unpacking is extra work on top of the dense product), so the design keeps
@@ -13,13 +14,13 @@
 //
 // Dense and 2:4-expanded products (v_mfma_f32_32x32x16_bf16, weights = A, activations = B, so
 //   each 32 x 32 block is a block of Y^T and a lane ends with four consecutive outputs of a row):
-//   wave w owns all 256 rows x columns [64w, 64w + 64) of the tile: 8 x 2 blocks of 32 x 32.
+//   wave w owns all TM rows x columns [64w, 64w + 64) of the tile: TM / 32 x 2 blocks of 32 x 32.
 //   Lane l (r = l % 32, h = l / 32) feeds k = 8h..8h+7 of each 16-wide MFMA step. The kernel
 //   maps MFMA step s of a 64-wide stage to k = 32h + 8s + j, so one lane's weights for a whole
 //   stage are 16 contiguous code bytes (32 codes, two E4M3 scale blocks).
 // 2:4 products on the sparse matrix cores (v_smfmac_f32_32x32x32_bf16, weights = compressed A,
-//   activations = B): the roles swap, the tile computes Y^T, and wave (wn, wm) owns 128 weight
-//   rows x 128 activation rows (4 x 4 blocks). The two 16-wide halves of MFMA step t take the
+//   activations = B, blocks of Y^T as above): wave (wn, wm) owns 128 weight rows x 128
+//   activation rows (4 x 4 blocks). The two 16-wide halves of MFMA step t take the
 //   16-blocks 2H + t of the stage (H = 0, 1), so each lane's compressed weights for a stage are
 //   8 contiguous vals bytes, 4 meta bytes and 2 scale bytes. The compressed layout of this
 //   library is the SMFMAC A operand and index operand as stored ("NVFP4 vs 2:4 sparse",
@@ -197,7 +198,7 @@ __device__ __forceinline__ u32x4 lds_w(const char* slot, int r, int h) {
 
 // ---------------------------------------------------------------------------------------------
 // Dense (or 2:4 expanded to dense) x activations on v_mfma_f32_32x32x16_bf16.
-// WGM x (4 / WGM) waves: wave (wm, wn) owns activation rows [256/WGM * wm, +256/WGM) and
+// WGM x (4 / WGM) waves: wave (wm, wn) owns activation rows [TM/WGM * wm, +TM/WGM) and
 // weight rows [64 WGM * wn, +64 WGM) of the tile, MB x NB blocks of 32 x 32. With WGM = 2 each
 // activation operand read from LDS feeds four MFMAs instead of two (half the LDS read traffic
 // of WGM = 1), and each weight is decoded by two waves instead of one.
