@@ -32,8 +32,9 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------------------------
-// quantisation: four lanes per 32-value block, eight values per lane (one or two 16-byte loads),
-// the block maximum by two lane exchanges.
+// quantisation. Row-major layout: four lanes per 32-value block, eight values per lane (one or
+// two 16-byte loads), the block maximum by two lane exchanges. Tiled layout: one lane per block
+// (see k_mx_quantize_tiled).
 
 // E2M1 magnitude code of r >= 0 (exact), nearest with ties to the even code, saturating at 6:
 // the boundaries are the midpoints 0.25 0.75 1.25 1.75 2.5 3.5 5, ties going down at 0.25, 1.25,
@@ -65,24 +66,12 @@ __device__ __forceinline__ void load8(const void* V, int64_t g, float (&v)[8]) {
   }
 }
 
-// byte offsets of the tiled layout
-__device__ __forceinline__ size_t tiled_code_offset(int64_t r, int64_t k, int64_t k64) {
-  // piece of 16 bytes holding k .. k + 31 (k % 32 == 0) of row r
-  const int64_t rb = r >> 5, ks = k >> 6, lane = (r & 31) + 32 * ((k >> 5) & 1);
-  return (size_t)(((rb * k64 + ks) << 6) + lane) << 4;
-}
-__device__ __forceinline__ size_t tiled_scale_offset(int64_t r, int64_t k, int64_t k256) {
-  const int64_t rb = r >> 5, kg = k >> 8, lane = (r & 31) + 32 * ((k >> 5) & 1), s = (k >> 6) & 3;
-  return ((size_t)(((rb * k256 + kg) << 6) + lane) << 2) + (size_t)s;
-}
-
 // groups g of eight values over [R, K] in row-major order; thread t of the grid takes
 // g = t, t + stride, ...; the four lanes of a block share it (block = g / 4, lanes aligned to 4)
-template <bool BF16, bool TILED>
+template <bool BF16>
 __global__ __launch_bounds__(256) void k_mx_quantize(const void* __restrict__ V, int64_t R, int64_t K,
                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   const int64_t groups = R * (K / 8);
-  const int64_t k64 = (K + 255) / 256 * 4, k256 = (K + 255) / 256;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups; g += stride) {
     float v[8];
@@ -100,30 +89,54 @@ __global__ __launch_bounds__(256) void k_mx_quantize(const void* __restrict__ V,
       const uint32_t c = e2m1_code(r) | ((__float_as_uint(v[i]) >> 28) & 8u);
       word |= c << (4 * i);
     }
-    const int64_t row = g / (K / 8), k = (g - row * (K / 8)) * 8;
-    if constexpr (TILED) {
-      *(uint32_t*)(codes + tiled_code_offset(row, k & ~(int64_t)31, k64) + ((k & 31) >> 1)) = word;
-      if ((g & 3) == 0) scales[tiled_scale_offset(row, k, k256)] = (uint8_t)(e + 127);
-    } else {
-      ((uint32_t*)codes)[g] = word;
-      if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(e + 127);
-    }
+    ((uint32_t*)codes)[g] = word;
+    if ((g & 3) == 0) scales[g >> 2] = (uint8_t)(e + 127);
   }
 }
 
-// zero fill of the tiled layout's padding (rows R .. R32 and k from K to K256): every byte of
-// the layout is written once by exactly one of the two kernels
-__global__ __launch_bounds__(256) void k_mx_pad(int64_t R, int64_t K, uint8_t* __restrict__ codes,
-                                                uint8_t* __restrict__ scales) {
-  const int64_t R32 = (R + 31) / 32 * 32, K256 = (K + 255) / 256 * 256;
-  const int64_t k64 = K256 / 64, k256 = K256 / 256;
-  const int64_t pieces = R32 * (K256 / 32);               // 16-byte code pieces (32 values)
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces; p += stride) {
-    const int64_t row = p / (K256 / 32), k = (p - row * (K256 / 32)) * 32;
-    if (row < R && k < K) continue;
-    *(u32x4*)(codes + tiled_code_offset(row, k, k64)) = u32x4{0u, 0u, 0u, 0u};
-    scales[tiled_scale_offset(row, k, k256)] = 0;
+// Matrix-core tiled layout: one wave per 32 rows x 256 k (four 64-k pieces). Lane l takes row
+// 32 rb + l % 32 and the k half l / 32 of every piece, i.e. one whole 32-value block per piece,
+// so its 16 code bytes are its slice of the piece (a piece leaves as one 1 KB store of the wave)
+// and its four scale bytes, one per piece, are one word. Rows past R and k past K are written as
+// zeros, so every byte of the layout is written once, by this kernel alone.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_mx_quantize_tiled(const void* __restrict__ V, int64_t R, int64_t K,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t k256 = (K + 255) / 256, k64 = 4 * k256;
+  const int64_t items = (R + 31) / 32 * k256;
+  const int lane = threadIdx.x & 63;
+  const int64_t wstride = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t it = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); it < items; it += wstride) {
+    const int64_t rb = it / k256, kg = it - rb * k256;
+    const int64_t r = 32 * rb + (lane & 31);
+    uint32_t sword = 0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t k0 = 256 * kg + 64 * s + 32 * (lane >> 5);
+      u32x4 cw = {0u, 0u, 0u, 0u};
+      if (r < R && k0 < K) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float w8[8];
+          load8<BF16>(V, (r * K + k0) / 8 + j, w8);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[8 * j + i] = w8[i];
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(v[i]));
+        const int e = mx_exponent(a);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const float q = __builtin_amdgcn_ldexpf(fabsf(v[i]), -e);   // exact: a power-of-two scale
+          cw[i >> 3] |= (e2m1_code(q) | ((__float_as_uint(v[i]) >> 28) & 8u)) << (4 * (i & 7));
+        }
+        sword |= (uint32_t)(e + 127) << (8 * s);
+      }
+      *(u32x4*)(codes + ((size_t)((rb * k64 + 4 * kg + s) * 64 + lane) << 4)) = cw;
+    }
+    *(uint32_t*)(scales + ((size_t)((rb * k256 + kg) * 64 + lane) << 2)) = sword;
   }
 }
 
@@ -343,16 +356,15 @@ hipError_t launch_mx_quantize(const void* V, int v_bf16, int64_t R, int64_t K, i
   const int64_t groups = R * (K / 8);
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((groups + 255) / 256, 64 * (int64_t)cu_count()));
   if (tiled) {
-    const int64_t pieces = (R + 31) / 32 * 32 * ((K + 255) / 256 * 8);
-    const unsigned pg = (unsigned)std::max<int64_t>(1, std::min<int64_t>((pieces + 255) / 256, 16 * (int64_t)cu_count()));
-    hipLaunchKernelGGL(k_mx_pad, dim3(pg), dim3(256), 0, s, R, K, codes, scales);
-    if (groups > 0) {
-      if (v_bf16) hipLaunchKernelGGL((k_mx_quantize<true, true>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
-      else hipLaunchKernelGGL((k_mx_quantize<false, true>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+    const int64_t items = (R + 31) / 32 * ((K + 255) / 256);   // one wave each, four per workgroup
+    const unsigned tg = (unsigned)std::min<int64_t>((items + 3) / 4, 64 * (int64_t)cu_count());
+    if (items > 0) {
+      if (v_bf16) hipLaunchKernelGGL((k_mx_quantize_tiled<true>), dim3(tg), dim3(256), 0, s, V, R, K, codes, scales);
+      else hipLaunchKernelGGL((k_mx_quantize_tiled<false>), dim3(tg), dim3(256), 0, s, V, R, K, codes, scales);
     }
   } else if (groups > 0) {
-    if (v_bf16) hipLaunchKernelGGL((k_mx_quantize<true, false>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
-    else hipLaunchKernelGGL((k_mx_quantize<false, false>), dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+    if (v_bf16) hipLaunchKernelGGL(k_mx_quantize<true>, dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
+    else hipLaunchKernelGGL(k_mx_quantize<false>, dim3(grid), dim3(256), 0, s, V, R, K, codes, scales);
   }
   return hipGetLastError();
 }
