@@ -238,6 +238,15 @@ constexpr int moe_stages() { return 2; }
 constexpr int kThreads = 256;
 constexpr int kEpiNone = 0, kEpiSilu = 1;
 
+// silu(g) = g / (1 + exp(-g)) on the hardware's base-2 exponential and reciprocal
+// (exp(-g) = 2^(-g log2 e)); relative error a few 1e-7 for |g| of a few units, ~1e-6 at |g| = 20,
+// far inside half a bf16 ulp of H (2^-9). Large -g: 2^(..) overflows to inf and the reciprocal
+// gives 0, so silu -> -0; large g: 2^(..) underflows to 0 and silu -> g.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // One LDS ring slot (bytes): activations [BM][128 B] (chunk swizzle), weights of the 256 tile
 // columns (dense codes [256][32 B] with half swizzle, or 2:4 vals [256][16 B] + meta
 // [256][8 B]), scales [256][4 B].
@@ -565,7 +574,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
           for (int i = 0; i < 16; ++i) {
             float* p = U + (32 * mt + erow(i)) * S + 64 * wave + ecol(nt, i);
             const float g = acc[mt][nt][i] * sc;
-            *p = g / (1.0f + expf(-g)) * *p;      // silu(g) * u
+            *p = silu_f32(g) * *p;                 // silu(g) * u
           }
     }
     __syncthreads();
@@ -767,7 +776,7 @@ __global__ __launch_bounds__(KS * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const float gt = acc[4 * b + i] * sc, up = acc[8 + 4 * b + i] * sc;
-              v[i] = gt / (1.0f + expf(-gt)) * up;     // silu(g) * u
+              v[i] = silu_f32(gt) * up;                // silu(g) * u
             }
             store4(Y, y_bf16, I, r0 + n, 16 * g + 8 * b + 4 * h, v, (I & 3) == 0);
           }
