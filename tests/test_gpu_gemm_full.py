@@ -2,7 +2,8 @@
 of entries x20 before pruning, bf16 out) products at full size, launched as the benchmark
 launches them, checked against the oracle on sampled outputs (rows and columns that straddle
 tile edges), on one whole output row, one whole output column and one whole interior 256 x 256
-tile (the oracle quantises every weight row itself, in chunks), and by properties that hold at
+tile (at the prefill shape also a whole tile of the last half-round, which runs as 128-row
+tiles; the oracle quantises every weight row itself, in chunks), and by properties that hold at
 any size."""
 import numpy as np
 import pytest
@@ -50,8 +51,10 @@ def prefill():
     M, N, K = 8192, 27648, 5120
     w = synth.weight_rows_with_outliers(N, K, 0, N, p=0.01, mult=20.0)
     d = _setup(M, N, K, w)
+    # 3456 tiles on 256 CUs: the last half-round (tile rows 28..31 x tile columns 76..107) runs as
+    # 128 x 256 tiles in the dense and expanded forms; tile (31, 100) is checked whole as well
     d.update(M=M, N=N, K=K, ms=_sample(M, [5000]), ns=_sample(N, [13824, 20000]), out="bf16",
-             whole_row=5001, whole_col=20001, tile=(17, 61))
+             whole_row=5001, whole_col=20001, tile=(17, 61), tail_tile=(31, 100))
     yield d
     d.clear()
     torch.cuda.empty_cache()
@@ -135,6 +138,9 @@ def _whole(d, sparse, algo):
     tm, tn = d["tile"]
     blocks = [("row", np.array([m_row]), np.arange(N)), ("column", np.arange(M), np.array([n_col])),
               ("tile", np.arange(256 * tm, 256 * tm + 256), np.arange(256 * tn, 256 * tn + 256))]
+    if "tail_tile" in d:
+        um, un = d["tail_tile"]
+        blocks.append(("tail tile", np.arange(256 * um, 256 * um + 256), np.arange(256 * un, 256 * un + 256)))
     for what, rows, cols in blocks:
         Y, B = _oracle_block(d, rows, cols, sparse)
         got = y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].float().cpu().numpy().astype(np.float64)
