@@ -7,7 +7,7 @@ import torch
 import structured_sparse_nvfp4_amd as ssn
 import synth
 from oracle import gemm, quant, sp24
-from tests.gpu_util import assert_within_bound, dev, x_dev, y_host
+from tests.gpu_util import assert_within_bound, dev, host, x_dev, y_host
 
 pytestmark = pytest.mark.gpu
 
@@ -194,3 +194,39 @@ def test_tiles_with_split_tail(M, N, out, sparse):
         g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(c), dev(s), ts, y_dtype=ydt, algo=ssn.ALGO_MFMA)
         assert used == ssn.ALGO_MFMA
     assert_within_bound(y_host(g), Y, B, out=out, what=f"split tail {M}x{N} {out}")
+
+
+# A one-hot row of X picks one decoded weight, so every bf16 output is the exact product
+# E2M1 * E4M3 * s_t (at most 15 significant bits, exact in f32) rounded once. With s_t = 1 + 2^-8
+# the products of power-of-two weights sit exactly halfway between two bf16 values with an even
+# lower neighbour and the rest above halfway; with 1 + 2^-7 there are ties whose lower neighbour is
+# odd, exact values and values below halfway. Comparing bit for bit pins round-to-nearest-even in
+# the bf16 epilogue of every product form.
+ROUND_CASES = [("dense", ssn.ALGO_MFMA, 300), ("dense", ssn.ALGO_MFMA, 16), ("dense", ssn.ALGO_MFMA, 4),
+               ("dense", ssn.ALGO_MFMA, 1), ("sp24", ssn.ALGO_SMFMAC, 300), ("sp24", ssn.ALGO_DECOMPRESS_MFMA, 300),
+               ("sp24", ssn.ALGO_SMFMAC, 8), ("sp24", ssn.ALGO_SMFMAC, 1)]
+
+
+@pytest.mark.parametrize("form,algo,M", ROUND_CASES)
+@pytest.mark.parametrize("ts_val", [1.0 + 2.0 ** -8, 1.0 + 2.0 ** -7])
+def test_bf16_output_rounds_to_nearest_even(form, algo, M, ts_val):
+    N, K = 290, 512
+    xb, ks = _one_hot_tiled(M, K, 3)
+    _, c, s, _ = _problem(1, N, K, seed=8, prune=form == "sp24")
+    ts = dev(np.array([ts_val], np.float32))
+    if form == "sp24":
+        vals, meta, _ = sp24.compress(c)
+        g, used = ssn.gemm_nvfp4_sp24(x_dev(xb), dev(vals), dev(meta), dev(s), ts, y_dtype=torch.bfloat16, algo=algo)
+        w = quant.dequantize(sp24.decompress(vals, meta), s, ts_val)
+    else:
+        g, used = ssn.gemm_nvfp4_dense(x_dev(xb), dev(c), dev(s), ts, y_dtype=torch.bfloat16, algo=algo)
+        w = quant.dequantize(c, s, ts_val)
+    assert used == algo
+    exact = w[:, ks].T
+    f = exact.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), exact)
+    assert ((f.view(np.uint32) & 0xFFFF) == 0x8000).any()          # the case holds exact ties
+    # a weight coded -0 gives a sum of signed zeros, which is +0; compare zeros by value
+    got, want = host(g), synth.f32_to_bf16_bits(f)
+    got, want = np.where(got == 0x8000, 0, got), np.where(want == 0x8000, 0, want)
+    assert np.array_equal(got, want)
