@@ -290,6 +290,29 @@ def test_ffn_reduced_config(sparse, layout):
     assert np.all(err <= tol), f"max excess {float((err - tol).max())}"
 
 
+# every token routed to the same k experts: those experts hold all T rows (ragged last tiles),
+# every other expert is empty (the first and last expert among them); T = 300 takes the tiled
+# products, T = 8 the streaming kernel
+@pytest.mark.parametrize("T", [300, 8])
+@pytest.mark.parametrize("layout", [ssn.WLAYOUT_ROWS, ssn.WLAYOUT_KTILE64])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_ffn_all_tokens_on_the_same_experts(sparse, layout, T):
+    E, k, D, I = 64, 4, 256, 128
+    x = synth.activations(T, D, seed=15)
+    chosen = np.array([3, 7, 8, 62], np.int32)
+    ids = np.tile(chosen, (T, 1))
+    w = synth.rng(16).random((T, k)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    qu, qd, up, down = _ffn_weights(E, I, D, sparse)
+    if layout == ssn.WLAYOUT_KTILE64:
+        up, down = ssn.moe_pack_weights(up), ssn.moe_pack_weights(down)
+    out, bad = ssn.moe_nvfp4_ffn(x_dev(x), dev(ids), dev(w), E, up, down, w_layout=layout)
+    ref, tol, _ = moe.moe_ffn(x, ids, w, lambda e: qu[e], lambda e: qd[e], E, I)
+    assert int(host(bad)[0]) == 0
+    err = np.abs(y_host(out) - ref)
+    assert np.all(err <= tol), f"max excess {float((err - tol).max())}"
+
+
 def _full_gpu_weights(E, I, D, sparse):
     """All experts quantised (and pruned/compressed) on the GPU from the synthetic weights."""
     def build(gen, rows, cols):
