@@ -29,7 +29,7 @@ def _problem(M, N, K, seed, prune):
 DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 64, 1024), (5, 48, 4096),
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
                (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
-               (3, 17000, 512),                   # several row groups per decode workgroup
+               (3, 17000, 512),                   # ragged last row group of the decode slabs
                (3, 24608, 512), (8, 24608, 512),  # >= 3 row groups per CU: the 80-register fold form
                # K % 256 == 0 but K % 512 != 0 (the decode slabs' partial last stage), M <= 8 and 9..16
                (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
@@ -53,10 +53,9 @@ def test_dense(M, N, K, algo, prune):
 SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64, 1024), (4, 48, 4096),
               (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
               (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
-              # M <= 8, K % 512 == 0 (full-width-load decode kernel): ragged row groups, several
-              # row groups per workgroup (N > 512 x 32), every M
+              # M <= 8, K % 512 == 0 (full-width-load decode kernel): ragged row groups, every M
               (8, 100, 512), (5, 1000, 1536), (2, 17000, 512), (7, 33, 1024),
-              # M = 1, K % 1024 == 0: the 1024-wide stage form
+              # M = 1: two to six 512-wide stages, ragged row groups
               (1, 1000, 1024), (1, 17000, 2048), (1, 33, 3072),
               # K % 256 == 0 but K % 512 != 0: the slab kernels' partial last stage (8- and 16-wave forms)
               (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
@@ -78,6 +77,38 @@ def test_sp24(M, N, K, algo):
     want = ssn.ALGO_GATHER if algo == ssn.ALGO_VALU else algo     # the vector-ALU 2:4 form is skip-and-gather
     assert used != ssn.ALGO_AUTO and (algo == ssn.ALGO_AUTO or used == want)
     assert_within_bound(y_host(g), Y, B, what=f"sp24 algo={used}")
+
+
+# The decode slabs launch at most 16 workgroups per CU, each taking ceil(N / workgroups)
+# consecutive rows in 32-row groups: N = 140000 on 256 CUs gives 4096 workgroups of 35 rows, a
+# full group and then a 3-row one. The problem repeats a 4999-row block (rows are independent,
+# so the oracle's result repeats with it); a workgroup that took a wrong group would read rows
+# that differ from the right ones.
+_BASE_ROWS, _MANY_ROWS = 4999, 140000
+
+
+def _tiled_rows(a, axis):
+    reps = -(-_MANY_ROWS // _BASE_ROWS)
+    t = np.concatenate([a] * reps, axis=axis)
+    return np.ascontiguousarray(np.take(t, np.arange(_MANY_ROWS), axis=axis))
+
+
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("sparse", [False, True])
+def test_decode_several_row_groups_per_workgroup(M, sparse):
+    K = 1024
+    x, c, s, st = _problem(M, _BASE_ROWS, K, seed=40 + M, prune=sparse)
+    ts = dev(np.array([st], np.float32))
+    if sparse:
+        vals, meta, _ = sp24.compress(c)
+        Y, B = gemm.gemm_sp24(x, vals, meta, s, st)
+        g, used = ssn.gemm_nvfp4_sp24(x_dev(x), dev(_tiled_rows(vals, 0)), dev(_tiled_rows(meta, 0)),
+                                      dev(_tiled_rows(s, 0)), ts, algo=ssn.ALGO_SMFMAC)
+    else:
+        Y, B = gemm.gemm_dense(x, c, s, st)
+        g, used = ssn.gemm_nvfp4_dense(x_dev(x), dev(_tiled_rows(c, 0)), dev(_tiled_rows(s, 0)), ts,
+                                       algo=ssn.ALGO_MFMA)
+    assert_within_bound(y_host(g), _tiled_rows(Y, 1), _tiled_rows(B, 1), what=f"M={M} sparse={sparse}")
 
 
 @pytest.mark.parametrize("M,N,K", [(8, 96, 512), (270, 300, 320)])
