@@ -59,6 +59,7 @@ FP32_VECTOR_PEAK_TFLOPS = 157.3   # MI355X published fp32 vector peak
 RING = 16                         # weight copies rotated by the GEMVs (16 x 40 MB > 2 x 256 MB cache)
 W_COPIES = 3                      # copies of the 283 MB f32 W rotated by the weight-preparation calls
 TRIALS = 20                       # individually timed launches per kernel (median, min)
+ROUNDS = 5                        # alternated batches of products compared with each other
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "structured_sparse_nvfp4_amd", "csrc")
 PREFILL = dict(M=8192, N=27648, K=5120)
@@ -111,12 +112,14 @@ def bytes_gemm(M, N, K, sparse, y_bytes):
 # ------------------------------------------------------------------------------------------
 class Timer:
     """HIP events on the current stream (the stream the library's calls launch on): the average
-    over a batch of back-to-back launches, and individually timed launches."""
+    over a batch of back-to-back launches (or the median of alternated batches), and individually
+    timed launches."""
 
     def __init__(self, torch):
         self.torch = torch
         self.batches = {}
         self.trials = {}
+        self.rounded = {}
 
     def _ev(self):
         return self.torch.cuda.Event(enable_timing=True)
@@ -139,7 +142,22 @@ class Timer:
             evs.append((a, b))
         self.trials[name] = evs
 
+    def rounds(self, groups, n_rounds):
+        """Batches of several named call lists alternated round by round (A B A B ...), so that
+        clock and power drift between them falls on each alike; us() then gives the median
+        round."""
+        for _ in range(n_rounds):
+            for name, fns in groups:
+                a, b = self._ev(), self._ev()
+                a.record()
+                for f in fns:
+                    f()
+                b.record()
+                self.rounded.setdefault(name, []).append((a, b, len(fns)))
+
     def us(self, name):
+        if name in self.rounded:
+            return statistics.median(a.elapsed_time(b) * 1e3 / n for a, b, n in self.rounded[name])
         a, b, n = self.batches[name]
         return a.elapsed_time(b) * 1e3 / n
 
@@ -571,11 +589,18 @@ def run_decode(torch, ssn, synth, copy_gbps):
         for f in ("sp24", "gather"):
             _assert_bound(_rows_of(Y[(M, f)].t(), rows).T, Yr, Br, "f32", f"decode {f} M={M}")
     T = Timer(torch)
+    gemv_groups = {}
     for n, cs in calls.items():
         reps = max(TRIALS, 2 * len(cs))
         seq = [cs[i % len(cs)] for i in range(reps)]
-        T.batch(n, seq)
+        if n.startswith("gemv_"):
+            gemv_groups.setdefault(n.rsplit("_M", 1)[1], []).append((n, seq))
+        else:
+            T.batch(n, seq)
         T.each(n, seq)
+        torch.cuda.synchronize()
+    for grp in gemv_groups.values():   # the dense, 2:4 and gather GEMVs of one M, alternated
+        T.rounds(grp, ROUNDS)
         torch.cuda.synchronize()
     kb = {"prune": bytes_prune(N, K), "quantize": bytes_quantize(N, K), "quantize_given_scale": bytes_quantize(N, K),
           "check": bytes_check(N, K), "compress": bytes_compress(N, K),
@@ -655,9 +680,10 @@ def run_head(torch, ssn, synth, copy_gbps):
         for n, cs in (("dense", pd), ("sp24", ps)):
             T.batch(n + "_warm", cs)
             torch.cuda.synchronize()
-            T.batch(n, cs * (TRIALS // 2))
             T.each(n, cs * (TRIALS // 2))
             torch.cuda.synchronize()
+        T.rounds((("dense", pd * 4), ("sp24", ps * 4)), ROUNDS)   # alternated
+        torch.cuda.synchronize()
         e = {}
         for n in ("dense", "sp24"):
             us = T.us(n)

@@ -410,10 +410,9 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. 8-wave workgroups (three per CU when a wave
-// keeps to 80 registers, two above), each owning a contiguous range of weight rows (32-row
-// groups), stream the rows through a 3-deep LDS ring of
-// 512-wide K stages with direct-to-LDS loads (as the slab kernel above). The E4M3 block scale is
+// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. 8-wave workgroups, each owning a contiguous
+// range of weight rows (32-row groups), stream the rows through a 3-deep LDS ring of 512-wide K
+// stages with direct-to-LDS buffer loads. The E4M3 block scale is
 // applied after the matrix product instead of before it: one v_mfma_f32_32x32x16_bf16 per
 // 16-wide scale block takes the E2M1 codes converted to bf16 unscaled (one
 // v_cvt_scalef32_pk_bf16_fp4 per two codes, exact) and the activations, and its 32x32 result is
@@ -422,51 +421,55 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // rows >= M read row 0 and are never stored), B = weights (column = weight row lane % 32); lane
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
-// Three 8-wave workgroups fit a CU by LDS (3 x 52.6 KB dense, 3 x 46 KB 2:4) when a wave keeps
-// to 80 registers (six waves per SIMD); at 84 and more only two fit. The 2:4 slab below keeps to
-// 80 as well (measured at N = 131072, M = 1..8: 82-88 us with two workgroups per CU, 72-80 us
-// with three).
+// Workgroups per CU: a ring slot holds the stage's weights and XR activation rows (XR = 1, 2, 4,
+// 8 for M = 1, 2, <= 4, <= 8), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 KB, and the buffer
+// loads (one wave-uniform resource per row group, one 32-bit offset per lane) keep a wave to 64
+// registers: four workgroups per CU for M <= 4, three above. Measured at N = 131072 against the
+// earlier form (flat 64-bit addresses, 8-row slots, 78-84 registers, two or three workgroups per
+// CU): M = 1 70-72 -> 66 us, M = 2 75-76 -> 69-70 us, M = 4 83 -> 75 us, M = 8 89 -> 86-88 us.
 constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
 constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
-constexpr int kPsBytes = kPsXOff + kPsMaxM * kPsXRow;          // one ring slot
+// a ring slot holds the stage's weights and XR >= M activation rows
+template <int XR>
+constexpr int ps_slot_bytes() { return kPsXOff + XR * kPsXRow; }
 
 // F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4). FOLD: each block's product is
 // folded into the sums before the next block's is formed, so one 16-register result is live
-// and a wave fits 80 registers (three workgroups per CU); without it the four products are
-// formed together, which hides their latency better when the grid gives a CU fewer workgroups.
-template <int F, bool FOLD>
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(FOLD ? 6 : 1))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
+// (M <= 2: 48-51 registers); without it the four products are formed together, which hides
+// their latency better (M > 2: 4% faster at M = 4, N = 131072, within the same 64 registers).
+// XR activation rows per ring slot; WPE: waves per SIMD the registers must allow.
+template <int F, bool FOLD, int XR, int WPE>
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
                                                            const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
                                                            const float* __restrict__ ts, void* __restrict__ Y,
                                                            int y_bf16, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
   const int nst = K / kSK;
   const int h = lane >> 5, nl = lane & 31;
   const int xm = nl < M ? nl : 0;
+  // per wave per stage: codes of rows 4w..4w+3 (1 KB; lane: row rc, 16-byte piece lane % 16 to
+  // LDS piece (lane % 16) ^ (rc & 15)), their scales (lanes < 8: row rs, half lane % 2), and for
+  // w < M activation row w (1 KB). Buffer loads: a wave-uniform resource per row group and one
+  // 32-bit offset per lane (rows past the block's range repeat its last row); a stage adds its
+  // wave-uniform K offset.
+  const int rc = wave * 4 + (lane >> 4), rs = wave * 4 + ((lane >> 1) & 3);
+  const uint32_t pc = 16u * ((lane & 15) ^ (rc & 15)), psc = 16u * (lane & 1);
+  const auto xrs = buf_rsrc(X + (size_t)min(wave, M - 1) * K);
   for (int g0 = row_lo; g0 < row_hi; g0 += kPsRows) {
-    // per wave per stage: codes of rows 4w..4w+3 (1 KB), their scales, and for w < M activation
-    // row w (1 KB); rows past the block's range repeat its last row
+    const auto crs = buf_rsrc(codes + (size_t)g0 * (K / 2));
+    const auto srs = buf_rsrc(scales + (size_t)g0 * (K / 16));
+    const uint32_t vc = (uint32_t)min(rc, row_hi - 1 - g0) * (uint32_t)(K / 2) + pc;
+    const uint32_t vs = (uint32_t)min(rs, row_hi - 1 - g0) * (uint32_t)(K / 16) + psc;
     auto issue = [&](int st) {
-      uint8_t* b = smem + (st % kPsStages) * kPsBytes;
-      const int k0 = st * kSK;
-      {
-        const int rr = wave * 4 + (lane >> 4);
-        const int n = min(g0 + rr, row_hi - 1);
-        const int cb = k0 / 2 + 16 * ((lane & 15) ^ (rr & 15));
-        lds_dma16(codes + (size_t)n * (K / 2) + cb, b + kPsAOff + wave * 4 * (kSK / 2));
-      }
-      {
-        const int rr = wave * 4 + ((lane >> 1) & 3);
-        const int n = min(g0 + rr, row_hi - 1);
-        const int sb = k0 / 16 + 16 * (lane & 1);
-        if (lane < 8) lds_dma16(scales + (size_t)n * (K / 16) + sb, b + kPsScOff + wave * 4 * kSRow);
-      }
-      if (wave < M) lds_dma16(X + (size_t)wave * K + k0 + 8 * lane, b + kPsXOff + wave * kPsXRow);
+      uint8_t* b = smem + (st % kPsStages) * ps_slot_bytes<XR>();
+      lds_dma16(crs, vc, (uint32_t)st * (kSK / 2), b + kPsAOff + wave * 4 * (kSK / 2));
+      if (lane < 8) lds_dma16(srs, vs, (uint32_t)st * (kSK / 16), b + kPsScOff + wave * 4 * kSRow);
+      if (wave < M) lds_dma16(xrs, 16u * lane, (uint32_t)st * (2 * kSK), b + kPsXOff + wave * kPsXRow);
     };
     float acc[F];
 #pragma unroll
@@ -481,7 +484,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
       else wait_stages<2>(ahead);
       stage_barrier();
       if (st + kPsStages - 1 < nst) issue(st + kPsStages - 1);
-      const uint8_t* b = smem + (st % kPsStages) * kPsBytes;
+      const uint8_t* b = smem + (st % kPsStages) * ps_slot_bytes<XR>();
       // codes words of blocks 4w..4w+3 for this lane's half: 16-byte chunk c of the row run sits
       // at chunk c ^ (row & 15) (the slab's swizzle); block j's half h is word 2 (j & 1) + h
       const uint8_t* arow = b + kPsAOff + nl * (kSK / 2);
@@ -544,10 +547,10 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, three
-// per CU, 32-row groups, 512-wide K stages in a ring of kP4Stages LDS slots), with every direct
-// load a full 1 KB buffer load (one wave-uniform resource per group, one 32-bit offset per lane,
-// so a wave keeps to 80 registers): waves 0-3 load the vals of rows 8w..8w+7 (128 B each), waves 4-5 the
+// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, 32-row
+// groups, 512-wide K stages in a ring of S LDS slots), with every direct load a full 1 KB buffer
+// load (one wave-uniform resource per group, one 32-bit offset per lane): waves 0-3 load the
+// vals of rows 8w..8w+7 (128 B each), waves 4-5 the
 // meta of rows 16(w-4)..+15 (64 B each), wave 6 the scales of all 32 rows (32 B each), and wave
 // m < M activation row m. Wave w then multiplies the 64-wide K chunk w of the stage for all 32
 // rows: two v_smfmac_f32_32x32x32_bf16 with the stored vals/meta as the compressed A operand and
@@ -557,33 +560,46 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(F
 // are never stored). The eight chunk partials of a row meet in LDS at the end.
 // LDS slot: vals [32][128 B] (16-byte piece p of row r holds global piece p ^ (r & 7)), meta
 // [32][64 B] (piece p holds global piece p ^ ((r >> 1) & 3)), scales [32][32 B], activations
-// [8][1 KB + 16 B].
-constexpr int kP4Stages = 3;
-static_assert(kP4Stages >= 2 && kP4Stages <= 5, "wait_stages covers up to three stages in flight");
+// [XR][1 KB + 16 B]. The row group's partial sums meet in LDS through all eight waves' results
+// (32 KB), and one thread per output adds them, so a wave keeps to 56-59 registers (a wave 0
+// that added the seven other partials of its 16 results itself held 78 and took ~1 us per row
+// group). Geometries: M <= 8 with XR = 8 and three slots (46 KB, three workgroups per CU);
+// M <= 4 with XR = 4 and three slots (34 KB), and M <= 2 with XR = 2 and four slots (37 KB):
+// four workgroups per CU at eight waves per SIMD. Measured at N = 131072 against the wave-0
+// reduction with three workgroups per CU: M = 1 72-75 -> 65-67 us, M = 2 71-72 -> 64-66 us,
+// M = 4 72-73 -> 68-70 us, M = 8 unchanged (80 us).
 
-// One ring slot of the 2:4 slab (512-wide stage, 32 rows, up to kPsMaxM activation rows).
+// The weight part of a ring slot of the 2:4 slab (512-wide stage, 32 rows); XR activation rows
+// follow it.
 struct P4Slot {
   static constexpr int kV = kSK / 4, kMt = kSK / 8, kSc = kSK / 16;   // bytes per row per stage
   static constexpr int kVP = kV / 16, kMP = kMt / 16, kSP = kSc / 16;   // 16-byte pieces per row
   static constexpr int kVOff = 0, kMOff = kPsRows * kV, kSOff = kMOff + kPsRows * kMt;
   static constexpr int kXOff = kSOff + kPsRows * kSc;
-  static constexpr int kBytes = kXOff + kPsMaxM * kPsXRow;
   static constexpr int kVLoads = kPsRows * kV / 1024, kMLoads = kPsRows * kMt / 1024, kSLoads = kPsRows * kSc / 1024;
   static constexpr int kLoads = kVLoads + kMLoads + kSLoads;           // 1 KB weight loads per stage (7)
   static_assert(kLoads <= kPsWaves, "one weight load per wave");
+};
+template <int XR, int S>
+struct P4Ring {
+  static constexpr int kSlot = P4Slot::kXOff + XR * kPsXRow, kBytes = S * kSlot;
+  static_assert(S >= 2 && S <= 5, "wait_stages covers up to three stages in flight");
+  static_assert(kBytes >= kPsWaves * 16 * 64 * 4, "the partial sums of a row group fit the ring");
 };
 
 // 16-byte piece swizzles of a vals row (8 pieces) and a meta row (4 pieces)
 __device__ __forceinline__ int p4_vswz(int r) { return r & 7; }
 __device__ __forceinline__ int p4_mswz(int r) { return (r >> 1) & 3; }
 
-__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(6))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
+template <int XR, int S, int WPE>
+__global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemv_ps24(const uint16_t* __restrict__ X, int M, int N, int K,
                                                              const uint8_t* __restrict__ vals,
                                                              const uint8_t* __restrict__ meta,
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ ts, void* __restrict__ Y,
                                                              int y_bf16, int R) {
   using L = P4Slot;
+  constexpr int kSlot = P4Ring<XR, S>::kSlot;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
@@ -617,7 +633,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(6
     const auto wr = buf_rsrc(wbase + (size_t)g0 * rowb);
     const uint32_t voff = (uint32_t)min(r, row_hi - 1 - g0) * rowb + poff;
     auto issue = [&](int st) {
-      uint8_t* b = smem + (st % kP4Stages) * L::kBytes;
+      uint8_t* b = smem + (st % S) * kSlot;
       if (wave < L::kLoads) lds_dma16(wr, voff, (uint32_t)st * kstep, b + wdst);
       if (wave < M) lds_dma16(xr, 16u * lane, (uint32_t)st * (2 * kSK), b + L::kXOff + wave * kPsXRow);
     };
@@ -625,17 +641,17 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(6
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int st = 0; st < kP4Stages - 1; ++st)
+    for (int st = 0; st < S - 1; ++st)
       if (st < nst) issue(st);
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
-      const int ahead = min(kP4Stages - 2, nst - 1 - st);
+      const int ahead = min(S - 2, nst - 1 - st);
       if (nload == 2) wait_stages<2>(ahead);
       else if (nload == 1) wait_stages<1>(ahead);
       else wait_vmcnt<0>();
       stage_barrier();
-      if (st + kP4Stages - 1 < nst) issue(st + kP4Stages - 1);
-      const uint8_t* b = smem + (st % kP4Stages) * L::kBytes;
+      if (st + S - 1 < nst) issue(st + S - 1);
+      const uint8_t* b = smem + (st % S) * kSlot;
       const u32x2 v = *(const u32x2*)(b + L::kVOff + nl * L::kV + 16 * (wave ^ p4_vswz(nl)) + 8 * h);
       const uint32_t mw = *(const uint32_t*)(b + L::kMOff + nl * L::kMt + 16 * ((wave >> 1) ^ p4_mswz(nl)) +
                                              8 * (wave & 1) + 4 * h);
@@ -654,30 +670,25 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(6
       }
     }
     __syncthreads();                               // every stage consumed: LDS holds the partial sums
+    // lane (nl, h) of every wave holds D[8(i/4) + 4h + i%4][nl]: partial sums of weight rows of
+    // the group for activation row nl; all of them go to LDS, then thread t < 32 M adds the eight
+    // partials of output (row r = t % 32, activation row m = t / 32) in wave order
     float* red = (float*)smem;
-    if (wave != 0)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[i];
+    for (int i = 0; i < 16; ++i) red[(wave * 16 + i) * 64 + lane] = acc[i];
     __syncthreads();
-    if (wave == 0 && nl < M) {
-      // lane holds D[8(i/4) + 4h + i%4][nl]: weight rows of the group for activation row nl
-      const float st_ = *ts;
+    const int t = threadIdx.x;
+    if (t < kPsRows * M) {
+      const int r = t % kPsRows, m = t / kPsRows;
+      const int i = 4 * (r >> 3) + (r & 3), src = 32 * ((r >> 2) & 1) + m;
+      float v = red[i * 64 + src];
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        f32x4 o;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = acc[4 * b4 + i];
-          for (int q = 0; q < kPsWaves - 1; ++q) v += red[(q * 16 + 4 * b4 + i) * 64 + lane];
-          o[i] = v * st_;
-        }
-        const int n = g0 + 8 * b4 + 4 * h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n + i < row_hi) {
-            if (!y_bf16) ((float*)Y)[(size_t)nl * N + n + i] = o[i];
-            else ((uint16_t*)Y)[(size_t)nl * N + n + i] = (uint16_t)f32_to_bf16_rne(o[i]);
-          }
+      for (int w = 1; w < kPsWaves; ++w) v += red[(w * 16 + i) * 64 + src];
+      const int n = g0 + r;
+      if (n < row_hi) {
+        const float o = v * *ts;
+        if (!y_bf16) ((float*)Y)[(size_t)m * N + n] = o;
+        else ((uint16_t*)Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(o);
       }
     }
     __syncthreads();                               // LDS is reused by the next row group
@@ -797,12 +808,15 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
                        (int)a.M, (int)a.N, (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16);
     return hipGetLastError();
   }
-  if (a.K % kSK == 0 && a.M <= kPsMaxM) {   // post-scale slab
+  // post-scale slab; its buffer offsets (32 rows of a row group, an activation row) are 32-bit,
+  // so K stays below 2^27
+  if (a.K % kSK == 0 && a.M <= kPsMaxM && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce ps_once;
     hipError_t e2 = once_per_device(ps_once, [] {
-      for (const void* f : {(const void*)k_gemv_ps<1, false>, (const void*)k_gemv_ps<2, false>,
-                            (const void*)k_gemv_ps<4, false>, (const void*)k_gemv_ps<4, true>}) {
-        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, kPsStages * kPsBytes);
+      for (const void* f : {(const void*)k_gemv_ps<1, true, 1, 8>, (const void*)k_gemv_ps<2, true, 2, 8>,
+                            (const void*)k_gemv_ps<4, false, 4, 8>, (const void*)k_gemv_ps<4, false, 8, 6>}) {
+        hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kPsStages * ps_slot_bytes<kPsMaxM>());
         if (e != hipSuccess) return e;
       }
       return hipSuccess;
@@ -810,13 +824,11 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
     if (e2 != hipSuccess) return e2;
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
-    // M > 2 with at least three 32-row groups per CU: the 80-register form, three workgroups
-    // per CU (measured at N = 131072: M = 4 88 -> 81 us, M = 8 95 -> 88 us; at N = 13824 it is
-    // 5-7% slower, so smaller grids keep the four products in flight)
-    const bool fold = a.M > 2 && (a.N + kPsRows - 1) / kPsRows >= 3 * (int64_t)cu_count();
-    auto k = a.M == 1 ? k_gemv_ps<1, false> : a.M == 2 ? k_gemv_ps<2, false>
-           : fold ? k_gemv_ps<4, true> : k_gemv_ps<4, false>;
-    hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), kPsStages * kPsBytes, s, a.X, (int)a.M, (int)a.N, (int)a.K,
+    auto k = a.M == 1 ? k_gemv_ps<1, true, 1, 8> : a.M == 2 ? k_gemv_ps<2, true, 2, 8>
+           : a.M <= 4 ? k_gemv_ps<4, false, 4, 8> : k_gemv_ps<4, false, 8, 6>;
+    const int xr = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : kPsMaxM;
+    const int lds = kPsStages * (kPsXOff + xr * kPsXRow);
+    hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), lds, s, a.X, (int)a.M, (int)a.N, (int)a.K,
                        a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
@@ -856,13 +868,27 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   if (a.M <= kPsMaxM && a.K % kSK == 0 && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce p4_once;
     hipError_t e2 = once_per_device(p4_once, [] {
-      return hipFuncSetAttribute((const void*)k_gemv_ps24, hipFuncAttributeMaxDynamicSharedMemorySize, kP4Stages * P4Slot::kBytes);
+      for (const auto& f : {std::make_pair((const void*)k_gemv_ps24<8, 3, 6>, P4Ring<8, 3>::kBytes),
+                            std::make_pair((const void*)k_gemv_ps24<4, 3, 8>, P4Ring<4, 3>::kBytes),
+                            std::make_pair((const void*)k_gemv_ps24<2, 4, 8>, P4Ring<2, 4>::kBytes)}) {
+        hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, f.second);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     });
     if (e2 != hipSuccess) return e2;
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
-    hipLaunchKernelGGL(k_gemv_ps24, dim3(G), dim3(kPsWaves * 64), kP4Stages * P4Slot::kBytes, s, a.X, (int)a.M, (int)a.N,
-                       (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
+    constexpr int lds2 = P4Ring<2, 4>::kBytes, lds4 = P4Ring<4, 3>::kBytes, lds8 = P4Ring<8, 3>::kBytes;
+    if (a.M <= 2)
+      hipLaunchKernelGGL((k_gemv_ps24<2, 4, 8>), dim3(G), dim3(kPsWaves * 64), lds2, s, a.X, (int)a.M, (int)a.N,
+                         (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
+    else if (a.M <= 4)
+      hipLaunchKernelGGL((k_gemv_ps24<4, 3, 8>), dim3(G), dim3(kPsWaves * 64), lds4, s, a.X, (int)a.M, (int)a.N,
+                         (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
+    else
+      hipLaunchKernelGGL((k_gemv_ps24<8, 3, 6>), dim3(G), dim3(kPsWaves * 64), lds8, s, a.X, (int)a.M, (int)a.N,
+                         (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
   if (a.M <= 8) {    // 8-wave workgroups (two per CU at 94 registers), 32-row groups

@@ -30,7 +30,7 @@ DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 6
                (17, 40, 64), (40, 33, 128), (300, 520, 640), (257, 300, 96), (513, 257, 1056),
                (64, 1000, 2048), (257, 300, 128), (513, 257, 1088),
                (3, 17000, 512),                   # ragged last row group of the decode slabs
-               (3, 24608, 512), (8, 24608, 512),  # >= 3 row groups per CU: the 80-register fold form
+               (3, 24608, 512), (8, 24608, 512),  # more row groups than workgroups a CU holds at once
                # K % 256 == 0 but K % 512 != 0 (the decode slabs' partial last stage), M <= 8 and 9..16
                (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
                # few row groups per CU, every activation-row count of the post-scale slab
