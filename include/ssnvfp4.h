@@ -260,7 +260,10 @@ int moe_route(const int32_t* topk_ids, int64_t T, int k, int E, int32_t* expert_
  * weight rows, up to 32 routed rows), for routings with few rows per expert ("NVFP4 vs 2:4
  * sparse", robertz.co, section "Where a decode step actually spends itself": the expert weight
  * read is the cost). AUTO picks STREAM when N % 32 == 0 and R <= 4 E (dense) or R <= 10 E (2:4),
- * else the tiles (MFMA dense, SMFMAC 2:4).
+ * else the tiles (MFMA dense, SMFMAC 2:4). The tiles address X and one expert's weight arrays
+ * with 32-bit byte offsets, so they need x_rows * K * 2 < 2^31 and N * K/2 (dense) or N * K/4
+ * (2:4) < 2^31; beyond that AUTO picks STREAM (SHAPE if N % 32 != 0) and an explicit tile
+ * algorithm is refused (ALGO).
  * algo_used: host, nullable.
  * Errors: NULL, SHAPE, ALIGN, DTYPE, ALGO, RANGE, HIP.
  * ------------------------------------------------------------------------------------------- */

@@ -48,6 +48,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 constexpr int64_t kMaxRows = ((int64_t)1 << 31) - 1024;
 // the 256x256 tiles address their activation panel (256 rows of K bf16) with 32-bit byte offsets
 constexpr int64_t kMaxTileK = (int64_t)1 << 21;
+// the grouped-expert tiles address X and one expert's weight array with 32-bit byte offsets
+constexpr int64_t kMaxTileBytes = (int64_t)1 << 31;
 
 int check_nk(const char* fn, int64_t N, int64_t K) {
   if (N < 0 || K < 0) return fail(SSN_E_SHAPE, "%s: negative size (N=%lld, K=%lld)", fn, (long long)N, (long long)K);
@@ -313,13 +315,23 @@ int moe_grouped_gemm_nvfp4(const uint16_t* X, int64_t x_rows, const int32_t* row
   // measured crossover (512 experts, D = 2048, I = 512): streaming wins up to ~4 rows per expert
   // for dense weights and ~10 for 2:4 weights
   const int64_t stream_max = (sparse ? 10 : 4) * (int64_t)E;
-  const int chosen = algo == SSN_ALGO_AUTO ? (can_stream && R <= stream_max ? SSN_ALGO_STREAM : tiles) : algo;
+  // the tiles load X and each expert's weight arrays through buffer resources with 32-bit byte
+  // offsets: both must stay below 2^31 bytes (the codes, or the vals, are the largest array)
+  const bool tiles_fit = x_rows * K * 2 < kMaxTileBytes && N * (K / (sparse ? 4 : 2)) < kMaxTileBytes;
+  const int chosen = algo == SSN_ALGO_AUTO
+                         ? (can_stream && (R <= stream_max || !tiles_fit) ? SSN_ALGO_STREAM : tiles)
+                         : algo;
   const bool tile_algo = chosen == tiles || (sparse && chosen == SSN_ALGO_DECOMPRESS_MFMA);
   if (!tile_algo && chosen != SSN_ALGO_STREAM)
     return fail(SSN_E_ALGO, "%s: algorithm %d is not available for %s expert weights", fn, algo,
                 sparse ? "2:4" : "dense");
   if (chosen == SSN_ALGO_STREAM && !can_stream)
     return fail(SSN_E_ALGO, "%s: STREAM needs N %% 32 == 0 (N=%lld)", fn, (long long)N);
+  if (tile_algo && !tiles_fit)
+    return fail(algo == SSN_ALGO_AUTO ? SSN_E_SHAPE : SSN_E_ALGO,
+                "%s: the tiles need X (x_rows=%lld, K=%lld) and each expert's weights (N=%lld) below 2^31 "
+                "bytes%s", fn, (long long)x_rows, (long long)K, (long long)N,
+                algo == SSN_ALGO_AUTO ? ", and STREAM needs N % 32 == 0" : "");
   if (algo_used) *algo_used = chosen;
   if (R == 0 || N == 0) return ok();
   if (K == 0 || K % 64) return fail(SSN_E_SHAPE, "%s: K=%lld must be a positive multiple of 64", fn, (long long)K);

@@ -32,7 +32,7 @@ inline int cu_count() {
   static int cus[kMaxDevices];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
-  once_per_device(once, [&]() -> hipError_t {
+  (void)once_per_device(once, [&]() -> hipError_t {   // always succeeds: 256 CUs if the query fails
     int n = 0;
     const hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
     cus[dev] = (e == hipSuccess && n > 0) ? n : 256;

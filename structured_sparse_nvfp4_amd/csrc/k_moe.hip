@@ -9,8 +9,9 @@
 // one launch runs every (expert, 64-row tile, 256-column tile) of a projection:
 //  - rows per expert range from a handful to thousands, so the row tile is 64: small experts
 //    waste little matrix-core work and the product stays bound by the expert weight read;
-//  - the activation rows of a tile are gathered by row id straight into LDS by direct loads,
-//    the expert's weights follow the same three-stage LDS pipeline as the square tiles;
+//  - the activation rows of a tile are gathered by row id straight into LDS by direct buffer
+//    loads, and the expert's weights follow them through a two-slot LDS ring (one stage lands
+//    while the other is multiplied);
 //  - gate and up projections of one expert share a tile (128 gate + 128 up columns), so the
 //    SiLU-gate product is formed in the epilogue and only H = bf16(silu(g) * u) is written.
 #include <algorithm>
@@ -369,11 +370,15 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
     else return min(kBN * tn + tc, N - 1);
   };
 
-  // per-lane sources of the direct loads
-  const uint8_t* wb = w0 + (size_t)e * N * (WF == kDense ? K / 2 : K / 4);
-  const uint8_t* mb = WF == kDense ? nullptr : w1 + (size_t)e * N * (K / 8);
-  const uint8_t* sb = scales + (size_t)e * N * (K / 16);
-  const char* xsrc[L::kXLoads];
+  // Sources of the direct loads: buffer resources at wave-uniform bases (the whole activation
+  // matrix; this expert's codes or vals, meta and scales) with one 32-bit byte offset per lane,
+  // computed once; a stage moves only the scalar offset. The host admits the tiles only when
+  // X and every expert's weight arrays are below 2^31 bytes, so no offset wraps.
+  const auto xr = buf_rsrc(X);
+  const auto wr = buf_rsrc(w0 + (size_t)e * N * (WF == kDense ? K / 2 : K / 4));
+  const auto mr = buf_rsrc(WF == kDense ? w0 : w1 + (size_t)e * N * (K / 8));
+  const auto sr = buf_rsrc(scales + (size_t)e * N * (K / 16));
+  uint32_t xo[L::kXLoads];
 #pragma unroll
   for (int i = 0; i < L::kXLoads; ++i) {
     const int r = 8 * (L::kXLoads * wave + i) + (lane >> 3);
@@ -381,46 +386,45 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
     int src = row_token ? row_token[rr] : rr;
     src = min(max(src, 0), x_rows - 1);
     const int c = (lane & 7) ^ swz(r);
-    xsrc[i] = (const char*)(X + (size_t)src * K + 8 * c);
+    xo[i] = (uint32_t)(((size_t)src * K + 8 * c) * 2);
   }
-  // Weight sources. Row-major layout: piece kt of row n at n * row_bytes + kt * piece. 64-k tiled
+  // Weight offsets. Row-major layout: piece kt of row n at n * row_bytes + kt * piece. 64-k tiled
   // layout: at (kt * N + n) * piece, so a stage's pieces of consecutive rows are contiguous and
   // every load instruction reads whole cache lines.
   const int pw = WF == kDense ? kBK / 2 : kBK / 4, pm = kBK / 8, ps = kBK / 16;   // piece bytes
-  const size_t wrs = ktiled ? pw : (size_t)K * pw / kBK, mrs = ktiled ? pm : (size_t)K * pm / kBK,
-               srs = ktiled ? ps : (size_t)K * ps / kBK;                          // row strides
-  const size_t wst = ktiled ? (size_t)N * pw : pw, mst = ktiled ? (size_t)N * pm : pm,
-               sst = ktiled ? (size_t)N * ps : ps;                                // stage strides
-  const uint8_t* wsrc[2];
-  const uint8_t* msrc[2];
+  const uint32_t wrs = ktiled ? pw : (uint32_t)K * pw / kBK, mrs = ktiled ? pm : (uint32_t)K * pm / kBK,
+                 srs = ktiled ? ps : (uint32_t)K * ps / kBK;                      // row strides
+  const uint32_t wst = ktiled ? (uint32_t)N * pw : pw, mst = ktiled ? (uint32_t)N * pm : pm,
+                 sst = ktiled ? (uint32_t)N * ps : ps;                            // stage strides
+  uint32_t wo[2], mo[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if constexpr (WF == kDense) {
       const int tc = 32 * (2 * wave + i) + (lane >> 1);
       const int hl = (lane & 1) ^ ((tc >> 3) & 1);
-      wsrc[i] = wb + (size_t)wrow(tc) * wrs + 16 * hl;
-      msrc[i] = nullptr;
+      wo[i] = (uint32_t)wrow(tc) * wrs + 16u * hl;
+      mo[i] = 0u;
     } else {
-      wsrc[i] = i == 0 ? wb + (size_t)wrow(64 * wave + lane) * wrs : nullptr;
+      wo[i] = i == 0 ? (uint32_t)wrow(64 * wave + lane) * wrs : 0u;
       const int tc = 32 * (2 * wave + i) + (lane >> 1);
-      msrc[i] = mb + (size_t)wrow(tc) * mrs + 4 * (lane & 1);
+      mo[i] = (uint32_t)wrow(tc) * mrs + 4u * (lane & 1);
     }
   }
-  const uint8_t* ssrc = sb + (size_t)wrow(64 * wave + lane) * srs;
+  const uint32_t so = (uint32_t)wrow(64 * wave + lane) * srs;
 
   auto issue = [&](int st, char* slot) {
 #pragma unroll
     for (int i = 0; i < L::kXLoads; ++i)
-      lds_dma16(xsrc[i] + st * (kBK * 2), slot + L::kX + (L::kXLoads * wave + i) * 1024);
+      lds_dma16(xr, xo[i], (uint32_t)st * (kBK * 2), slot + L::kX + (L::kXLoads * wave + i) * 1024);
     if constexpr (WF == kDense) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma16(wsrc[i] + st * wst, slot + L::kW + (2 * wave + i) * 1024);
+      for (int i = 0; i < 2; ++i) lds_dma16(wr, wo[i], (uint32_t)st * wst, slot + L::kW + (2 * wave + i) * 1024);
     } else {
-      lds_dma16(wsrc[0] + st * wst, slot + L::kW + wave * 1024);
+      lds_dma16(wr, wo[0], (uint32_t)st * wst, slot + L::kW + wave * 1024);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma4(msrc[i] + st * mst, slot + L::kMeta + (2 * wave + i) * 256);
+      for (int i = 0; i < 2; ++i) lds_dma4(mr, mo[i], (uint32_t)st * mst, slot + L::kMeta + (2 * wave + i) * 256);
     }
-    lds_dma4(ssrc + st * sst, slot + L::kSc + wave * 256);
+    lds_dma4(sr, so, (uint32_t)st * sst, slot + L::kSc + wave * 256);
   };
 
   f32x16 acc[MT][2];
@@ -434,11 +438,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
   const int last = nst - 1;
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i) issue(min(i, last), lds + i * L::kBytes);
-  for (int st = 0; st < nst; ++st) {
-    wait_vmcnt<(kStages - 2) * L::kLoads>();   // stage st has landed (later ones may be in flight)
-    stage_barrier();            // ... for every wave; slot (st - 1) % kStages is no longer read
-    issue(min(st + kStages - 1, last), lds + ((st + kStages - 1) % kStages) * L::kBytes);
-    const char* slot = lds + (st % kStages) * L::kBytes;
+  // One stage: wait until it has landed, refill the other slot, multiply. Two stages run per trip
+  // of the loop below, so that both slot addresses are constants folded into the LDS reads.
+  static_assert(kStages == 2, "the stage loop alternates two ring slots");
+  auto stage = [&](int st, const char* slot, char* next) __attribute__((always_inline)) {
+    wait_vmcnt<0>();            // stage st has landed (the only stage in flight)
+    stage_barrier();            // ... for every wave; the other slot is no longer read
+    issue(min(st + 1, last), next);
     if constexpr (SMF) {
       static_assert(WF == kSp24, "the sparse matrix cores take 2:4 weights");
       // A: weight rows (tile columns) 64 wave + 32 at + r32; lane half h holds the kept values of
@@ -474,52 +480,56 @@ __global__ __launch_bounds__(kThreads, 2) void k_moe_gemm(
             acc[bt][at] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, as_bf16x16(bx[bt]), acc[bt][at], idx, 0, 0);
         }
       }
-      continue;
-    }
-    u32x4 wc[2];
-    uint32_t wsc[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const int tc = 64 * wave + 32 * nt + r32;
-      if constexpr (WF == kDense) {
-        wc[nt] = *(const u32x4*)(slot + L::kW + tc * 32 + 16 * (h ^ ((tc >> 3) & 1)));
-      } else {
-        const u32x2 v = *(const u32x2*)(slot + L::kW + tc * 16 + 8 * h);
-        wc[nt][0] = v[0]; wc[nt][1] = v[1];
-        wc[nt][2] = *(const uint32_t*)(slot + L::kMeta + tc * 8 + 4 * h);
-        wc[nt][3] = 0u;
-      }
-      wsc[nt] = *(const uint32_t*)(slot + L::kSc + tc * 4) >> (16 * h);
-    }
-    // activation operands of MFMA step s + 1 are read while step s runs
-    u32x4 a[2][MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int r = 32 * mt + r32;
-      a[0][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h) ^ swz(r)));
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int r = 32 * mt + r32;
-          a[(s + 1) & 1][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h + s + 1) ^ swz(r)));
-        }
-      }
-      bf16x8 b[2];
+    } else {
+      u32x4 wc[2];
+      uint32_t wsc[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const float f = s < 2 ? e4m3_f32_sel<0>(wsc[nt]) : e4m3_f32_sel<1>(wsc[nt]);
-        b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(wc[nt], s), f));
+        const int tc = 64 * wave + 32 * nt + r32;
+        if constexpr (WF == kDense) {
+          wc[nt] = *(const u32x4*)(slot + L::kW + tc * 32 + 16 * (h ^ ((tc >> 3) & 1)));
+        } else {
+          const u32x2 v = *(const u32x2*)(slot + L::kW + tc * 16 + 8 * h);
+          wc[nt][0] = v[0]; wc[nt][1] = v[1];
+          wc[nt][2] = *(const uint32_t*)(slot + L::kMeta + tc * 8 + 4 * h);
+          wc[nt][3] = 0u;
+        }
+        wsc[nt] = *(const uint32_t*)(slot + L::kSc + tc * 4) >> (16 * h);
       }
+      // activation operands of MFMA step s + 1 are read while step s runs
+      u32x4 a[2][MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 av = as_bf16x8(a[s & 1][mt]);
-        acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
-        acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
+        const int r = 32 * mt + r32;
+        a[0][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h) ^ swz(r)));
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s < 3) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int r = 32 * mt + r32;
+            a[(s + 1) & 1][mt] = *(const u32x4*)(slot + L::kX + r * 128 + 16 * ((4 * h + s + 1) ^ swz(r)));
+          }
+        }
+        bf16x8 b[2];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const float f = s < 2 ? e4m3_f32_sel<0>(wsc[nt]) : e4m3_f32_sel<1>(wsc[nt]);
+          b[nt] = as_bf16x8(fp4x8_bf16(codes_step<WF>(wc[nt], s), f));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 av = as_bf16x8(a[s & 1][mt]);
+          acc[mt][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[0], acc[mt][0], 0, 0, 0);
+          acc[mt][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[1], acc[mt][1], 0, 0, 0);
+        }
       }
     }
+  };
+  for (int st = 0; st < nst; st += 2) {
+    stage(st, lds, lds + L::kBytes);
+    if (st + 1 < nst) stage(st + 1, lds + L::kBytes, lds);
   }
   wait_vmcnt<0>();
   __syncthreads();   // ring slots are free for the epilogue staging

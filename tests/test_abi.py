@@ -127,6 +127,22 @@ def test_moe_validation_without_launch():
                                     ctypes.byref(used), n) == ssn.SSN_OK and used.value == ssn.ALGO_STREAM
     # unknown weight layout
     assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 8, 32, 64, 0, 7, p, n, p, p, 0, p, 0, 0, n, n) == ssn.SSN_E_RANGE
+    # the tiles address X and one expert's weights with 32-bit byte offsets: X of 2^31 bytes
+    # (x_rows = 2^20, K = 1024) or an expert's codes / vals of 2^31 bytes are refused for an
+    # explicit tile algorithm, and for AUTO when STREAM cannot take the shape (N % 32 != 0)
+    for sparse, algo in ((0, ssn.ALGO_MFMA), (1, ssn.ALGO_SMFMAC), (1, ssn.ALGO_DECOMPRESS_MFMA)):
+        assert L.moe_grouped_gemm_nvfp4(p, 1 << 20, p, p, 4, 64, 64, 1024, sparse, 0, p, p, p, p, 0, p, 0, algo,
+                                        ctypes.byref(used), n) == ssn.SSN_E_ALGO
+        assert b"below 2^31 bytes" in L.ssn_last_error()
+    assert L.moe_grouped_gemm_nvfp4(p, (1 << 20) - 1, n, p, 4, 0, 64, 1024, 0, 0, n, n, n, n, 0, n, 0,
+                                    ssn.ALGO_MFMA, ctypes.byref(used), n) == ssn.SSN_OK   # just below: admitted
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 64, 1 << 20, 4096, 0, 0, p, n, p, p, 0, p, 0, ssn.ALGO_MFMA,
+                                    ctypes.byref(used), n) == ssn.SSN_E_ALGO            # N * K/2 = 2^31
+    assert L.moe_grouped_gemm_nvfp4(p, 8, p, p, 4, 64, 1 << 21, 4096, 1, 0, p, p, p, p, 0, p, 0, ssn.ALGO_SMFMAC,
+                                    ctypes.byref(used), n) == ssn.SSN_E_ALGO            # N * K/4 = 2^31
+    assert L.moe_grouped_gemm_nvfp4(p, 1 << 20, p, p, 4, 64, 40, 1024, 0, 0, p, n, p, p, 0, p, 0, 0,
+                                    ctypes.byref(used), n) == ssn.SSN_E_SHAPE           # AUTO, N % 32 != 0
+    assert b"STREAM needs N % 32 == 0" in L.ssn_last_error()
     # 64-k tiling of a weight array: piece sizes, divisibility, overlap, NULL, empty
     assert L.moe_pack_ktiles(p, 2, 8, 32, 12, p2, n) == ssn.SSN_E_RANGE
     assert L.moe_pack_ktiles(p, 2, 8, 48, 32, p2, n) == ssn.SSN_E_SHAPE
