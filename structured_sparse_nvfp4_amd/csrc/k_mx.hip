@@ -209,24 +209,33 @@ void k_gemm_mx(const uint8_t* __restrict__ xc, const uint8_t* __restrict__ xs, i
     xbs[i] = min(8 * tm + BPW * wave + i, mb_last);
     wbs[i] = min(8 * tn + BPW * wave + i, nb_last);
   }
+  // Loads go through buffer resources whose (wave-uniform) base is the copied block's piece of
+  // the stage, moved on the scalar unit each stage; the lane offsets are fixed (16 bytes of a
+  // 1 KB code piece, 4 bytes of a 256-byte scale piece).
+  const uint8_t *xcb[BPW], *wcb[BPW], *xsb[BPW], *wsb[BPW];
+#pragma unroll
+  for (int i = 0; i < BPW; ++i) {
+    xcb[i] = xc + (size_t)xbs[i] * k64 * 1024;
+    wcb[i] = wc + (size_t)wbs[i] * k64 * 1024;
+    xsb[i] = xs + (size_t)xbs[i] * k256 * 256;
+    wsb[i] = ws + (size_t)wbs[i] * k256 * 256;
+  }
   auto issue = [&](int st, char* slot) {
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
+      const auto xr = buf_rsrc(xcb[i] + (size_t)st * 2048), wr = buf_rsrc(wcb[i] + (size_t)st * 2048);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const size_t xo = ((size_t)xbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
-        const size_t wo = ((size_t)wbs[i] * k64 + 2 * st + s) * 1024 + 16 * lane;
-        lds_dma16(xc + xo, slot + (BPW * wave + i) * 2048 + s * 1024);
-        lds_dma16(wc + wo, slot + kMxStageX + (BPW * wave + i) * 2048 + s * 1024);
+        lds_dma16(xr, 16u * lane + 1024u * s, 0u, slot + (BPW * wave + i) * 2048 + s * 1024);
+        lds_dma16(wr, 16u * lane + 1024u * s, 0u, slot + kMxStageX + (BPW * wave + i) * 2048 + s * 1024);
       }
     }
     // scale pieces of the stage's 256-wide group: 256 bytes per block, 4 bytes per lane
 #pragma unroll
     for (int i = 0; i < BPW; ++i) {
-      const size_t so_x = ((size_t)xbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
-      const size_t so_w = ((size_t)wbs[i] * k256 + (st >> 1)) * 256 + 4 * lane;
-      lds_dma4(xs + so_x, slot + 2 * kMxStageX + (BPW * wave + i) * 256);
-      lds_dma4(ws + so_w, slot + 2 * kMxStageX + kMxStageS + (BPW * wave + i) * 256);
+      lds_dma4(buf_rsrc(xsb[i] + (size_t)(st >> 1) * 256), 4u * lane, 0u, slot + 2 * kMxStageX + (BPW * wave + i) * 256);
+      lds_dma4(buf_rsrc(wsb[i] + (size_t)(st >> 1) * 256), 4u * lane, 0u,
+               slot + 2 * kMxStageX + kMxStageS + (BPW * wave + i) * 256);
     }
   };
 
