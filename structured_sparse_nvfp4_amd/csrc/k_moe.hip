@@ -232,8 +232,11 @@ constexpr int kBN = 256, kBK = 64;
 // Ring slots of the 64-row tiles (kStages - 1 stages in flight). Two slots (34 KB, the epilogue
 // staging 35 KB) let four workgroups share a CU, three (51 KB) three, four (68 KB) two; on the
 // 4096-token, 512-expert FFN two were the fastest (2:4 up 516 -> 484 us, down 278 -> 253 us;
-// dense 2-6%). 256-row tiles for the experts with many rows, beside 64-row tiles for the rest,
-// were slower throughout (the second launch has too few tiles to fill the chip).
+// dense 2-6%). With the buffer-resource loads (fewer registers, four workgroups per CU for every
+// form) three slots were measured again, alternated with two on one box: FFN dense 564-580 ->
+// 594-610 us, 2:4 453-456 -> 477-479 us. 256-row tiles for the experts with many rows, beside
+// 64-row tiles for the rest, were slower throughout (the second launch has too few tiles to fill
+// the chip).
 template <int BM>
 constexpr int moe_stages() { return 2; }
 constexpr int kThreads = 256;
