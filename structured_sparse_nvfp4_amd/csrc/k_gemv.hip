@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dense, M <= 8, K % 512 == 0: the "post-scale" slab. 8-wave workgroups, each owning a contiguous
+// Dense, M <= 16, K % 512 == 0: the "post-scale" slab. 8-wave workgroups, each owning a contiguous
 // range of weight rows (32-row groups), stream the rows through a 3-deep LDS ring of 512-wide K
 // stages with direct-to-LDS buffer loads. The E4M3 block scale is
 // applied after the matrix product instead of before it: one v_mfma_f32_32x32x16_bf16 per
@@ -422,12 +422,13 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
 // Workgroups per CU: a ring slot holds the stage's weights and XR activation rows (XR = 1, 2, 4,
-// 8 for M = 1, 2, <= 4, <= 8), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 KB, and the buffer
+// 8, 16 for M = 1, 2, <= 4, <= 8, <= 16), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 / 75.8 KB
+// (two workgroups per CU for M > 8), and the buffer
 // loads (one wave-uniform resource per row group, one 32-bit offset per lane) keep a wave to 64
 // registers: four workgroups per CU for M <= 4, three above. Measured at N = 131072 against the
 // earlier form (flat 64-bit addresses, 8-row slots, 78-84 registers, two or three workgroups per
 // CU): M = 1 70-72 -> 66 us, M = 2 75-76 -> 69-70 us, M = 4 83 -> 75 us, M = 8 89 -> 86-88 us.
-constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8;
+constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8, kPsMaxM16 = 16;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
 constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + kPsRows * kSRow;
@@ -435,11 +436,12 @@ constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + 
 template <int XR>
 constexpr int ps_slot_bytes() { return kPsXOff + XR * kPsXRow; }
 
-// F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4). FOLD: each block's product is
+// F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4, M <= 16 -> 8). FOLD: each block's product is
 // folded into the sums before the next block's is formed, so one 16-register result is live
 // (M <= 2: 48-51 registers); without it the four products are formed together, which hides
 // their latency better (M > 2: 4% faster at M = 4, N = 131072, within the same 64 registers).
-// XR activation rows per ring slot; WPE: waves per SIMD the registers must allow.
+// XR activation rows per ring slot (XR = 16: wave w also loads row w + 8); WPE: waves per SIMD
+// the registers must allow.
 template <int F, bool FOLD, int XR, int WPE>
 __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void k_gemv_ps(const uint16_t* __restrict__ X, int M, int N, int K,
                                                            const uint8_t* __restrict__ codes,
@@ -460,6 +462,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
   const int rc = wave * 4 + (lane >> 4), rs = wave * 4 + ((lane >> 1) & 3);
   const uint32_t pc = 16u * ((lane & 15) ^ (rc & 15)), psc = 16u * (lane & 1);
   const auto xrs = buf_rsrc(X + (size_t)min(wave, M - 1) * K);
+  const auto xrs2 = buf_rsrc(X + (size_t)min(wave + kPsWaves, M - 1) * K);   // XR = 16: row w + 8
   for (int g0 = row_lo; g0 < row_hi; g0 += kPsRows) {
     const auto crs = buf_rsrc(codes + (size_t)g0 * (K / 2));
     const auto srs = buf_rsrc(scales + (size_t)g0 * (K / 16));
@@ -470,6 +473,9 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
       lds_dma16(crs, vc, (uint32_t)st * (kSK / 2), b + kPsAOff + wave * 4 * (kSK / 2));
       if (lane < 8) lds_dma16(srs, vs, (uint32_t)st * (kSK / 16), b + kPsScOff + wave * 4 * kSRow);
       if (wave < M) lds_dma16(xrs, 16u * lane, (uint32_t)st * (2 * kSK), b + kPsXOff + wave * kPsXRow);
+      if constexpr (XR > kPsWaves)
+        if (wave + kPsWaves < M)
+          lds_dma16(xrs2, 16u * lane, (uint32_t)st * (2 * kSK), b + kPsXOff + (wave + kPsWaves) * kPsXRow);
     };
     float acc[F];
 #pragma unroll
@@ -480,7 +486,8 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
       const int ahead = min(kPsStages - 2, nst - 1 - st);
-      if (wave < M) wait_stages<3>(ahead);
+      if (XR > kPsWaves && wave + kPsWaves < M) wait_stages<4>(ahead);
+      else if (wave < M) wait_stages<3>(ahead);
       else wait_stages<2>(ahead);
       stage_barrier();
       if (st + kPsStages - 1 < nst) issue(st + kPsStages - 1);
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
       for (int i = 0; i < F; ++i) {
         float v = acc[i];
         for (int q = 0; q < kPsWaves - 1; ++q) v += red[(q * F + i) * 64 + lane];
-        const int m = 4 * h + i, n = g0 + nl;
+        const int m = 8 * (i >> 2) + 4 * h + (i & 3), n = g0 + nl;   // row of result register i
         if (m < M && n < row_hi) {
           if (!y_bf16) ((float*)Y)[(size_t)m * N + n] = v * st_;
           else ((uint16_t*)Y)[(size_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v * st_);
@@ -810,13 +817,14 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
   }
   // post-scale slab; its buffer offsets (32 rows of a row group, an activation row) are 32-bit,
   // so K stays below 2^27
-  if (a.K % kSK == 0 && a.M <= kPsMaxM && a.K <= ((int64_t)1 << 27)) {
+  if (a.K % kSK == 0 && a.M <= kPsMaxM16 && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce ps_once;
     hipError_t e2 = once_per_device(ps_once, [] {
       for (const void* f : {(const void*)k_gemv_ps<1, true, 1, 8>, (const void*)k_gemv_ps<2, true, 2, 8>,
-                            (const void*)k_gemv_ps<4, false, 4, 8>, (const void*)k_gemv_ps<4, false, 8, 6>}) {
+                            (const void*)k_gemv_ps<4, false, 4, 8>, (const void*)k_gemv_ps<4, false, 8, 6>,
+                            (const void*)k_gemv_ps<8, false, 16, 4>}) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kPsStages * ps_slot_bytes<kPsMaxM>());
+                                           kPsStages * ps_slot_bytes<kPsMaxM16>());
         if (e != hipSuccess) return e;
       }
       return hipSuccess;
@@ -825,8 +833,9 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
     auto k = a.M == 1 ? k_gemv_ps<1, true, 1, 8> : a.M == 2 ? k_gemv_ps<2, true, 2, 8>
-           : a.M <= 4 ? k_gemv_ps<4, false, 4, 8> : k_gemv_ps<4, false, 8, 6>;
-    const int xr = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : kPsMaxM;
+           : a.M <= 4 ? k_gemv_ps<4, false, 4, 8> : a.M <= kPsMaxM ? k_gemv_ps<4, false, 8, 6>
+           : k_gemv_ps<8, false, 16, 4>;
+    const int xr = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : a.M <= kPsMaxM ? kPsMaxM : kPsMaxM16;
     const int lds = kPsStages * (kPsXOff + xr * kPsXRow);
     hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), lds, s, a.X, (int)a.M, (int)a.N, (int)a.K,
                        a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);

@@ -34,7 +34,10 @@ DENSE_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 160), (16, 6
                # K % 256 == 0 but K % 512 != 0 (the decode slabs' partial last stage), M <= 8 and 9..16
                (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
                # few row groups per CU, every activation-row count of the post-scale slab
-               (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536), (7, 333, 3072)]
+               (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536), (7, 333, 3072),
+               # M = 9..16, K % 512 == 0: the 16-row post-scale slab (waves load a second
+               # activation row), ragged row groups and more row groups than the grid
+               (9, 1000, 1024), (10, 33, 1536), (13, 300, 2048), (15, 17000, 512), (16, 24608, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", DENSE_CASES)
@@ -93,7 +96,7 @@ def _tiled_rows(a, axis):
     return np.ascontiguousarray(np.take(t, np.arange(_MANY_ROWS), axis=axis))
 
 
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 3, 11])
 @pytest.mark.parametrize("sparse", [False, True])
 def test_decode_several_row_groups_per_workgroup(M, sparse):
     K = 1024
