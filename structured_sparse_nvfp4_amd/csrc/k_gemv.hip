@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
 }
 
 // ---------------------------------------------------------------------------------------------
-// 2:4, M <= 8, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, 32-row
+// 2:4, M <= 16, K % 512 == 0: the same pipeline as the post-scale slab (8-wave workgroups, 32-row
 // groups, 512-wide K stages in a ring of S LDS slots), with every direct load a full 1 KB buffer
 // load (one wave-uniform resource per group, one 32-bit offset per lane): waves 0-3 load the
 // vals of rows 8w..8w+7 (128 B each), waves 4-5 the
@@ -570,7 +570,8 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
 // [XR][1 KB + 16 B]. The row group's partial sums meet in LDS through all eight waves' results
 // (32 KB), and one thread per output adds them, so a wave keeps to 56-59 registers (a wave 0
 // that added the seven other partials of its 16 results itself held 78 and took ~1 us per row
-// group). Geometries: M <= 8 with XR = 8 and three slots (46 KB, three workgroups per CU);
+// group). Geometries: M <= 16 with XR = 16 and three slots (71 KB, two workgroups per CU; wave
+// w also loads activation row w + 8); M <= 8 with XR = 8 and three slots (46 KB, three per CU);
 // M <= 4 with XR = 4 and three slots (34 KB), and M <= 2 with XR = 2 and four slots (37 KB):
 // four workgroups per CU at eight waves per SIMD. Measured at N = 131072 against the wave-0
 // reduction with three workgroups per CU: M = 1 72-75 -> 65-67 us, M = 2 71-72 -> 64-66 us,
@@ -614,8 +615,10 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
   const int h = lane >> 5, nl = lane & 31;
   const int xm = nl < M ? nl : 0;
   // direct loads of this wave per stage: weight load `wave` (waves < 7), activation row `wave`
-  const int nload = (wave < L::kLoads ? 1 : 0) + (wave < M ? 1 : 0);
+  // and, with XR = 16, activation row wave + 8
+  const int nload = (wave < L::kLoads ? 1 : 0) + (wave < M ? 1 : 0) + (XR > kPsWaves && wave + kPsWaves < M ? 1 : 0);
   const auto xr = buf_rsrc(X + (size_t)min(wave, M - 1) * K);
+  const auto xr2 = buf_rsrc(X + (size_t)min(wave + kPsWaves, M - 1) * K);
   // this wave's weight load: row r of the group (rows past the block repeat its last row) and
   // byte offset poff in it, from a buffer resource at the group's first row; a stage adds its
   // wave-uniform K offset
@@ -643,6 +646,9 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
       uint8_t* b = smem + (st % S) * kSlot;
       if (wave < L::kLoads) lds_dma16(wr, voff, (uint32_t)st * kstep, b + wdst);
       if (wave < M) lds_dma16(xr, 16u * lane, (uint32_t)st * (2 * kSK), b + L::kXOff + wave * kPsXRow);
+      if constexpr (XR > kPsWaves)
+        if (wave + kPsWaves < M)
+          lds_dma16(xr2, 16u * lane, (uint32_t)st * (2 * kSK), b + L::kXOff + (wave + kPsWaves) * kPsXRow);
     };
     f32x16 acc;
 #pragma unroll
@@ -653,7 +659,8 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
       const int ahead = min(S - 2, nst - 1 - st);
-      if (nload == 2) wait_stages<2>(ahead);
+      if (XR > kPsWaves && nload == 3) wait_stages<3>(ahead);
+      else if (nload == 2) wait_stages<2>(ahead);
       else if (nload == 1) wait_stages<1>(ahead);
       else wait_vmcnt<0>();
       stage_barrier();
@@ -874,10 +881,11 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   }
   // full-width loads, 32x32x32 sparse MFMA per 64-k chunk; its buffer offsets (32 rows of a row
   // group, an activation row) are 32-bit, so K stays below 2^27
-  if (a.M <= kPsMaxM && a.K % kSK == 0 && a.K <= ((int64_t)1 << 27)) {
+  if (a.M <= kPsMaxM16 && a.K % kSK == 0 && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce p4_once;
     hipError_t e2 = once_per_device(p4_once, [] {
-      for (const auto& f : {std::make_pair((const void*)k_gemv_ps24<8, 3, 6>, P4Ring<8, 3>::kBytes),
+      for (const auto& f : {std::make_pair((const void*)k_gemv_ps24<16, 3, 4>, P4Ring<16, 3>::kBytes),
+                            std::make_pair((const void*)k_gemv_ps24<8, 3, 6>, P4Ring<8, 3>::kBytes),
                             std::make_pair((const void*)k_gemv_ps24<4, 3, 8>, P4Ring<4, 3>::kBytes),
                             std::make_pair((const void*)k_gemv_ps24<2, 4, 8>, P4Ring<2, 4>::kBytes)}) {
         hipError_t e = hipFuncSetAttribute(f.first, hipFuncAttributeMaxDynamicSharedMemorySize, f.second);
@@ -888,15 +896,19 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
     if (e2 != hipSuccess) return e2;
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
-    constexpr int lds2 = P4Ring<2, 4>::kBytes, lds4 = P4Ring<4, 3>::kBytes, lds8 = P4Ring<8, 3>::kBytes;
+    constexpr int lds2 = P4Ring<2, 4>::kBytes, lds4 = P4Ring<4, 3>::kBytes, lds8 = P4Ring<8, 3>::kBytes,
+                  lds16 = P4Ring<16, 3>::kBytes;
     if (a.M <= 2)
       hipLaunchKernelGGL((k_gemv_ps24<2, 4, 8>), dim3(G), dim3(kPsWaves * 64), lds2, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     else if (a.M <= 4)
       hipLaunchKernelGGL((k_gemv_ps24<4, 3, 8>), dim3(G), dim3(kPsWaves * 64), lds4, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
-    else
+    else if (a.M <= kPsMaxM)
       hipLaunchKernelGGL((k_gemv_ps24<8, 3, 6>), dim3(G), dim3(kPsWaves * 64), lds8, s, a.X, (int)a.M, (int)a.N,
+                         (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
+    else
+      hipLaunchKernelGGL((k_gemv_ps24<16, 3, 4>), dim3(G), dim3(kPsWaves * 64), lds16, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }

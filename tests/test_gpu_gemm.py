@@ -63,7 +63,9 @@ SP24_CASES = [(16, 256, 512), (1, 256, 512), (3, 37, 96), (8, 100, 320), (16, 64
               # K % 256 == 0 but K % 512 != 0: the slab kernels' partial last stage (8- and 16-wave forms)
               (1, 100, 768), (8, 300, 1280), (5, 1000, 768), (12, 64, 768),
               # few row groups per CU, every activation-row count of the 2:4 slab
-              (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536)]
+              (2, 3000, 1024), (3, 40, 512), (4, 500, 2048), (6, 1000, 1536),
+              # M = 9..16, K % 512 == 0: the 16-row 2:4 slab (waves load a second activation row)
+              (9, 1000, 1024), (10, 33, 1536), (13, 300, 2048), (15, 17000, 512), (16, 24608, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SP24_CASES)
