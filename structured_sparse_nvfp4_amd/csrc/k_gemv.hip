@@ -422,12 +422,13 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
 // Workgroups per CU: a ring slot holds the stage's weights and XR activation rows (XR = 1, 2, 4,
-// 8, 16 for M = 1, 2, <= 4, <= 8, <= 16), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 / 75.8 KB
-// (two workgroups per CU for M > 8), and the buffer
-// loads (one wave-uniform resource per row group, one 32-bit offset per lane) keep a wave to 64
-// registers: four workgroups per CU for M <= 4, three above. Measured at N = 131072 against the
-// earlier form (flat 64-bit addresses, 8-row slots, 78-84 registers, two or three workgroups per
-// CU): M = 1 70-72 -> 66 us, M = 2 75-76 -> 69-70 us, M = 4 83 -> 75 us, M = 8 89 -> 86-88 us.
+// 8, 16 for M = 1, 2, <= 4, <= 8, <= 16), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 / 75.8 KB,
+// and the buffer loads (one wave-uniform resource per row group, one 32-bit offset per lane)
+// keep a wave to 64 registers up to M = 8 (79 for 16 rows): four workgroups per CU for M <= 4,
+// three for M <= 8, two above. Measured at N = 131072 against the earlier form (flat 64-bit
+// addresses, 8-row slots, 78-84 registers, two or three workgroups per CU): M = 1 70-72 -> 66 us,
+// M = 2 75-76 -> 69-70 us, M = 4 83 -> 75 us, M = 8 89 -> 86-88 us; M = 9 on the 16-wave slab
+// 112 us, with 16-row slots 100-102 us.
 constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8, kPsMaxM16 = 16;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
@@ -436,10 +437,11 @@ constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + 
 template <int XR>
 constexpr int ps_slot_bytes() { return kPsXOff + XR * kPsXRow; }
 
-// F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4, M <= 16 -> 8). FOLD: each block's product is
-// folded into the sums before the next block's is formed, so one 16-register result is live
-// (M <= 2: 48-51 registers); without it the four products are formed together, which hides
-// their latency better (M > 2: 4% faster at M = 4, N = 131072, within the same 64 registers).
+// F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4, M <= 16 -> 8). FOLD: each
+// block's product is folded into the sums before the next block's is formed, so one 16-register
+// result is live (M <= 2: 48-51 registers); without it the four products are formed together,
+// which hides their latency better (M > 2: 4% faster at M = 4, N = 131072, within the same 64
+// registers).
 // XR activation rows per ring slot (XR = 16: wave w also loads row w + 8); WPE: waves per SIMD
 // the registers must allow.
 template <int F, bool FOLD, int XR, int WPE>
