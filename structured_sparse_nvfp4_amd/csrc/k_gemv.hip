@@ -422,13 +422,14 @@ __global__ __launch_bounds__(256) void k_gemv_smfmac(const uint16_t* __restrict_
 // half h = lane / 32 holds codes 8h..8h+7 of the block. Wave w takes the four blocks 4w..4w+3 of
 // every stage; the eight partial sums of a row are added at the end.
 // Workgroups per CU: a ring slot holds the stage's weights and XR activation rows (XR = 1, 2, 4,
-// 8, 16 for M = 1, 2, <= 4, <= 8, <= 16), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 / 75.8 KB,
-// and the buffer loads (one wave-uniform resource per row group, one 32-bit offset per lane)
-// keep a wave to 64 registers up to M = 8 (79 for 16 rows): four workgroups per CU for M <= 4,
-// three for M <= 8, two above. Measured at N = 131072 against the earlier form (flat 64-bit
+// 8, 16 for M = 1, 2, <= 4, <= 8, <= 16), so the ring takes 30.8 / 33.9 / 40.1 / 52.6 KB in
+// three slots, and 51.7 KB in two for 16 rows; the buffer loads (one wave-uniform resource per
+// row group, one 32-bit offset per lane) keep a wave to 64 registers up to M = 8 (79 for 16
+// rows): four workgroups per CU for M <= 4, three above. Measured at N = 131072 against the earlier form (flat 64-bit
 // addresses, 8-row slots, 78-84 registers, two or three workgroups per CU): M = 1 70-72 -> 66 us,
 // M = 2 75-76 -> 69-70 us, M = 4 83 -> 75 us, M = 8 89 -> 86-88 us; M = 9 on the 16-wave slab
-// 112 us, with 16-row slots 100-102 us.
+// 112 us, with 16-row slots 100-102 us in three slots and 96 us in two (alternated on one box;
+// two slots for M <= 8 were 1-2% slower).
 constexpr int kPsWaves = 8, kPsRows = 4 * kPsWaves, kPsStages = 3, kPsMaxM = 8, kPsMaxM16 = 16;
 static_assert(kPsStages >= 2 && kPsStages <= 5, "wait_stages covers up to three stages in flight");
 constexpr int kPsXRow = kSK * 2 + 16;                          // activation row stride in LDS
@@ -436,6 +437,9 @@ constexpr int kPsAOff = 0, kPsScOff = kPsRows * (kSK / 2), kPsXOff = kPsScOff + 
 // a ring slot holds the stage's weights and XR >= M activation rows
 template <int XR>
 constexpr int ps_slot_bytes() { return kPsXOff + XR * kPsXRow; }
+// ring slots: three, but two for 16 activation rows (three workgroups per CU instead of two)
+template <int XR>
+constexpr int ps_stages() { return XR > kPsWaves ? 2 : kPsStages; }
 
 // F: output rows per lane (M = 1 -> 1, M = 2 -> 2, M <= 8 -> 4, M <= 16 -> 8). FOLD: each
 // block's product is folded into the sums before the next block's is formed, so one 16-register
@@ -451,6 +455,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
                                                            const float* __restrict__ ts, void* __restrict__ Y,
                                                            int y_bf16, int R) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int S = ps_stages<XR>();
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row_lo = blockIdx.x * R, row_hi = min(row_lo + R, N);
   const int nst = K / kSK;
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
     const uint32_t vc = (uint32_t)min(rc, row_hi - 1 - g0) * (uint32_t)(K / 2) + pc;
     const uint32_t vs = (uint32_t)min(rs, row_hi - 1 - g0) * (uint32_t)(K / 16) + psc;
     auto issue = [&](int st) {
-      uint8_t* b = smem + (st % kPsStages) * ps_slot_bytes<XR>();
+      uint8_t* b = smem + (st % S) * ps_slot_bytes<XR>();
       lds_dma16(crs, vc, (uint32_t)st * (kSK / 2), b + kPsAOff + wave * 4 * (kSK / 2));
       if (lane < 8) lds_dma16(srs, vs, (uint32_t)st * (kSK / 16), b + kPsScOff + wave * 4 * kSRow);
       if (wave < M) lds_dma16(xrs, 16u * lane, (uint32_t)st * (2 * kSK), b + kPsXOff + wave * kPsXRow);
@@ -483,17 +488,17 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
 #pragma unroll
     for (int i = 0; i < F; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int st = 0; st < kPsStages - 1; ++st)
+    for (int st = 0; st < S - 1; ++st)
       if (st < nst) issue(st);
     for (int st = 0; st < nst; ++st) {
       // this wave's loads of stage st have landed (later stages may be in flight), then every wave's
-      const int ahead = min(kPsStages - 2, nst - 1 - st);
+      const int ahead = min(S - 2, nst - 1 - st);
       if (XR > kPsWaves && wave + kPsWaves < M) wait_stages<4>(ahead);
       else if (wave < M) wait_stages<3>(ahead);
       else wait_stages<2>(ahead);
       stage_barrier();
-      if (st + kPsStages - 1 < nst) issue(st + kPsStages - 1);
-      const uint8_t* b = smem + (st % kPsStages) * ps_slot_bytes<XR>();
+      if (st + S - 1 < nst) issue(st + S - 1);
+      const uint8_t* b = smem + (st % S) * ps_slot_bytes<XR>();
       // codes words of blocks 4w..4w+3 for this lane's half: 16-byte chunk c of the row run sits
       // at chunk c ^ (row & 15) (the slab's swizzle); block j's half h is word 2 (j & 1) + h
       const uint8_t* arow = b + kPsAOff + nl * (kSK / 2);
@@ -572,8 +577,9 @@ __global__ __launch_bounds__(kPsWaves * 64) __attribute__((amdgpu_waves_per_eu(W
 // [XR][1 KB + 16 B]. The row group's partial sums meet in LDS through all eight waves' results
 // (32 KB), and one thread per output adds them, so a wave keeps to 56-59 registers (a wave 0
 // that added the seven other partials of its 16 results itself held 78 and took ~1 us per row
-// group). Geometries: M <= 16 with XR = 16 and three slots (71 KB, two workgroups per CU; wave
-// w also loads activation row w + 8); M <= 8 with XR = 8 and three slots (46 KB, three per CU);
+// group). Geometries: M <= 16 with XR = 16 and two slots (48 KB, three workgroups per CU; wave
+// w also loads activation row w + 8; 4.5% faster at M = 9 than three slots with two workgroups
+// per CU); M <= 8 with XR = 8 and three slots (46 KB, three per CU);
 // M <= 4 with XR = 4 and three slots (34 KB), and M <= 2 with XR = 2 and four slots (37 KB):
 // four workgroups per CU at eight waves per SIMD. Measured at N = 131072 against the wave-0
 // reduction with three workgroups per CU: M = 1 72-75 -> 65-67 us, M = 2 71-72 -> 64-66 us,
@@ -831,7 +837,7 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
     hipError_t e2 = once_per_device(ps_once, [] {
       for (const void* f : {(const void*)k_gemv_ps<1, true, 1, 8>, (const void*)k_gemv_ps<2, true, 2, 8>,
                             (const void*)k_gemv_ps<4, false, 4, 8>, (const void*)k_gemv_ps<4, false, 8, 6>,
-                            (const void*)k_gemv_ps<8, false, 16, 4>}) {
+                            (const void*)k_gemv_ps<8, false, 16, 6>}) {
         hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
                                            kPsStages * ps_slot_bytes<kPsMaxM16>());
         if (e != hipSuccess) return e;
@@ -843,9 +849,9 @@ hipError_t launch_gemv_dense_mfma(const GemmArgs& a, hipStream_t s) {
     const int R = (int)((a.N + G - 1) / G);
     auto k = a.M == 1 ? k_gemv_ps<1, true, 1, 8> : a.M == 2 ? k_gemv_ps<2, true, 2, 8>
            : a.M <= 4 ? k_gemv_ps<4, false, 4, 8> : a.M <= kPsMaxM ? k_gemv_ps<4, false, 8, 6>
-           : k_gemv_ps<8, false, 16, 4>;
+           : k_gemv_ps<8, false, 16, 6>;
     const int xr = a.M == 1 ? 1 : a.M == 2 ? 2 : a.M <= 4 ? 4 : a.M <= kPsMaxM ? kPsMaxM : kPsMaxM16;
-    const int lds = kPsStages * (kPsXOff + xr * kPsXRow);
+    const int lds = (xr > kPsWaves ? ps_stages<kPsMaxM16>() : kPsStages) * (kPsXOff + xr * kPsXRow);
     hipLaunchKernelGGL(k, dim3(G), dim3(kPsWaves * 64), lds, s, a.X, (int)a.M, (int)a.N, (int)a.K,
                        a.w0, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
@@ -886,7 +892,7 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
   if (a.M <= kPsMaxM16 && a.K % kSK == 0 && a.K <= ((int64_t)1 << 27)) {
     static PerDeviceOnce p4_once;
     hipError_t e2 = once_per_device(p4_once, [] {
-      for (const auto& f : {std::make_pair((const void*)k_gemv_ps24<16, 3, 4>, P4Ring<16, 3>::kBytes),
+      for (const auto& f : {std::make_pair((const void*)k_gemv_ps24<16, 2, 6>, P4Ring<16, 2>::kBytes),
                             std::make_pair((const void*)k_gemv_ps24<8, 3, 6>, P4Ring<8, 3>::kBytes),
                             std::make_pair((const void*)k_gemv_ps24<4, 3, 8>, P4Ring<4, 3>::kBytes),
                             std::make_pair((const void*)k_gemv_ps24<2, 4, 8>, P4Ring<2, 4>::kBytes)}) {
@@ -899,7 +905,7 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
     const int G = (int)std::min<int64_t>((int64_t)16 * cu_count(), (a.N + kPsRows - 1) / kPsRows);
     const int R = (int)((a.N + G - 1) / G);
     constexpr int lds2 = P4Ring<2, 4>::kBytes, lds4 = P4Ring<4, 3>::kBytes, lds8 = P4Ring<8, 3>::kBytes,
-                  lds16 = P4Ring<16, 3>::kBytes;
+                  lds16 = P4Ring<16, 2>::kBytes;
     if (a.M <= 2)
       hipLaunchKernelGGL((k_gemv_ps24<2, 4, 8>), dim3(G), dim3(kPsWaves * 64), lds2, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
@@ -910,7 +916,7 @@ hipError_t launch_gemv_sp24_smfmac(const GemmArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((k_gemv_ps24<8, 3, 6>), dim3(G), dim3(kPsWaves * 64), lds8, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     else
-      hipLaunchKernelGGL((k_gemv_ps24<16, 3, 4>), dim3(G), dim3(kPsWaves * 64), lds16, s, a.X, (int)a.M, (int)a.N,
+      hipLaunchKernelGGL((k_gemv_ps24<16, 2, 6>), dim3(G), dim3(kPsWaves * 64), lds16, s, a.X, (int)a.M, (int)a.N,
                          (int)a.K, a.w0, a.w1, a.scales, a.ts, a.Y, a.y_bf16, R);
     return hipGetLastError();
   }
