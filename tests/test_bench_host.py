@@ -106,3 +106,18 @@ def test_trace_summary_lists_kernels_by_total_time_and_by_grid(tmp_path):
     assert "| `void ssn::(anonymous namespace)::k_a(int)` | 2 | 1.50 | 1.00 | 2.00 | 75.00 |" in text
     # per grid: median (upper of two) 2.00 us, mean 1.50 us, min 1.00 us
     assert "| `ssn::k_a` | 256 | 2 | 2.00 | 1.50 | 1.00 |" in text
+
+
+def test_counter_summary_averages_each_counter_per_kernel_and_grid(tmp_path):
+    a, b = "void ssn::(anonymous namespace)::k_a(int)", "void ssn::(anonymous namespace)::k_b(int)"
+    _write_csv(str(tmp_path / "f" / "run" / "run_counter_collection.csv"),
+               _pmc_rows("FETCH_SIZE", [(a, 256, 10.0), (a, 256, 30.0), (a, 512, 7.0), (b, 64, 1.0)]))
+    _write_csv(str(tmp_path / "s" / "run" / "run_counter_collection.csv"),
+               _pmc_rows("SQ_INSTS_MFMA", [(a, 256, 4.0), (a, 256, 4.0)]))
+    out = tmp_path / "c.md"
+    bench.summarize("pmc", str(out), [str(tmp_path / "f"), str(tmp_path / "s")], "rocprofv3 --pmc ...")
+    text = out.read_text()
+    assert "| kernel | grid | dispatches | FETCH_SIZE | SQ_INSTS_MFMA |" in text
+    assert f"| `{a}` | 256 | 2 | 20.0 | 4.0 |" in text       # mean of the two dispatches per counter
+    assert f"| `{a}` | 512 | 1 | 7.0 |  |" in text            # a counter not read for that grid stays empty
+    assert f"| `{b}` | 64 | 1 | 1.0 |  |" in text
